@@ -1,0 +1,358 @@
+/*
+ * CPU oracle for VQ3R / VQ4P residual vector quantization.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only tests/, __graft_entry__.smoke() and bench.py's
+ * cpu_baseline leg may load this library. The product path never calls it.
+ *
+ * A plain, sequential, obviously-correct statement of what the method computes,
+ * written from the page "3比特逼近4比特精度？WARP残差向量量化VQ3R的完整测量实验"
+ * (xdnf.cn; cited below as [VQ3R page]) and its sections:
+ *   §2  the VQ3R recipe: 3 stages, 256-entry codebooks, 8-bit indices, 8-dim
+ *       vectors, one FP16 scale per row; W ~ scale * (C1[i1] + C2[i2] + C3[i3]);
+ *       C1 fits the vector, C2 the stage-1 residual, C3 the stage-2 residual;
+ *       codebooks fit per layer with Lloyd k-means on sampled experts.
+ *   §4  the encoder keeps all 256 distances, holds an 8 KB (fp32) codebook and
+ *       writes only the winning index per stage.
+ *   §5  VQ4P: 4 stages x 64 entries, 6-bit indices packed into the same bytes.
+ * Where the page is silent the readings used are listed in the design doc; each
+ * function below names the reading it relies on.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math), so
+ * every fp32 operation is a single IEEE round-to-nearest-even operation and
+ * fmaf() is the correctly rounded fused multiply-add.
+ * OpenMP only splits independent rows / vectors; results do not depend on the
+ * thread count (the Lloyd sums are exact integers).
+ *
+ * Status codes: 0 ok, 1 invalid argument, 5 data error (non-finite weight,
+ * row RMS beyond the fp16 range, fixed-point range too small).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define VQO_OK 0
+#define VQO_EINVAL 1
+#define VQO_EDATA 5
+#define DIM 8
+
+/* ------------------------------------------------------------------------
+ * IEEE 754 binary16 conversion, written from the format definition
+ * (1 sign bit, 5 exponent bits with bias 15, 10 fraction bits; subnormals
+ * below 2^-14), rounding to nearest with ties to even.
+ * ---------------------------------------------------------------------- */
+static uint16_t f32_to_f16_rne(float f) {
+  uint32_t x;
+  memcpy(&x, &f, 4);
+  uint32_t sign = (x >> 16) & 0x8000u;
+  uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax > 0x7F800000u) return (uint16_t)(sign | 0x7E00u); /* NaN */
+  if (ax >= 0x477FF000u) return (uint16_t)(sign | 0x7C00u); /* >= 65520 rounds to inf */
+  int e = (int)(ax >> 23) - 127;
+  uint32_t m = (ax & 0x7FFFFFu) | (ax ? 0x800000u : 0u); /* 24-bit significand */
+  if (ax == 0) return (uint16_t)sign;
+  if ((ax >> 23) == 0) { e = -126; m = ax & 0x7FFFFFu; } /* fp32 subnormal */
+  if (e >= -14) {
+    /* normal: keep 11 significant bits (implicit + 10) of the 24 */
+    uint32_t h = ((uint32_t)(e + 15) << 10) | ((m >> 13) & 0x3FFu);
+    uint32_t rem = m & 0x1FFFu;
+    if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1; /* carry may bump exponent */
+    return (uint16_t)(sign | h);
+  }
+  /* subnormal result: value = m * 2^(e-23); in units of 2^-24 that is m * 2^(e+1) */
+  int sh = -(e + 1); /* > 0 */
+  if (sh > 25) return (uint16_t)sign;
+  uint32_t q = m >> sh;
+  uint32_t rem = m & ((1u << sh) - 1u);
+  uint32_t half = 1u << (sh - 1);
+  if (rem > half || (rem == half && (q & 1u))) q += 1;
+  return (uint16_t)(sign | q); /* q may reach 0x400 = smallest normal, still correct */
+}
+
+static float f16_to_f32(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1F;
+  int m = h & 0x3FF;
+  float v;
+  if (e == 0) v = ldexpf((float)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexpf((float)(m | 0x400), e - 25);
+  return sign ? -v : v;
+}
+
+uint16_t vqo_f32_to_f16(float f) { return f32_to_f16_rne(f); }
+float vqo_f16_to_f32(uint16_t h) { return f16_to_f32(h); }
+
+/* ------------------------------------------------------------------------
+ * Row scale, [VQ3R page] §2 "one FP16 per-channel scale per row". The page
+ * does not say which statistic; the reading used is the row RMS:
+ * ss = sum_k w_k^2 in fp64 (sequential), rms = sqrt(ss / n) in fp64, then
+ * rounded fp64 -> fp32 -> fp16 (each step to nearest even).
+ * Returns VQO_EDATA for a non-finite weight or an RMS beyond the fp16 range.
+ * ---------------------------------------------------------------------- */
+static int row_scale(const float* w, int64_t n, uint16_t* s_bits) {
+  double ss = 0.0;
+  for (int64_t k = 0; k < n; ++k) {
+    if (!isfinite(w[k])) return VQO_EDATA;
+    ss += (double)w[k] * (double)w[k];
+  }
+  double rms = sqrt(ss / (double)n);
+  uint16_t h = f32_to_f16_rne((float)rms);
+  if ((h & 0x7C00u) == 0x7C00u) return VQO_EDATA;
+  *s_bits = h;
+  return VQO_OK;
+}
+
+int vqo_row_scales(const float* w, int64_t rows, int64_t cols, uint16_t* s_bits) {
+  int st = VQO_OK;
+  for (int64_t r = 0; r < rows; ++r) {
+    int e = row_scale(w + r * cols, cols, &s_bits[r]);
+    if (e) st = e;
+  }
+  return st;
+}
+
+/* Normalization, [VQ3R page] §2 (W ~ scale * sum of codewords, so the
+ * codewords live in the scaled-down domain): v = w / s as one correctly
+ * rounded fp32 division; an all-zero-scale row maps to v = 0. */
+static float normalize(float w, float s) { return (s == 0.0f) ? 0.0f : w / s; }
+
+/* ------------------------------------------------------------------------
+ * Squared distance of an 8-dim residual to a codeword, [VQ3R page] §4 (the
+ * encoder evaluates all codeword distances). Fixed order: acc = 0;
+ * for k = 0..7: e = r_k - c_k; acc = fmaf(e, e, acc).
+ * ---------------------------------------------------------------------- */
+static float dist8(const float* r, const float* c) {
+  float acc = 0.0f;
+  for (int k = 0; k < DIM; ++k) {
+    float e = r[k] - c[k];
+    acc = fmaf(e, e, acc);
+  }
+  return acc;
+}
+
+float vqo_dist8(const float* r, const float* c) { return dist8(r, c); }
+
+/* Exhaustive nearest codeword over j = 0..K-1 in increasing order; a strictly
+ * smaller distance wins, so ties go to the lowest index. */
+static int argmin_codeword(const float* r, const float* cb, int K) {
+  int best = 0;
+  float bd = dist8(r, cb);
+  for (int j = 1; j < K; ++j) {
+    float d = dist8(r, cb + (int64_t)j * DIM);
+    if (d < bd) { bd = d; best = j; }
+  }
+  return best;
+}
+
+int vqo_argmin(const float* r, const float* cb, int K) { return argmin_codeword(r, cb, K); }
+
+/* Greedy residual encode of one vector, [VQ3R page] §2 (residual relay) and
+ * §4 (one pass, the winning index per stage): r <- v; for each stage t:
+ * i_t = argmin_j d(r, C_t[j]); r <- r - C_t[i_t] (fp32, elementwise). */
+static void encode_vector(const float* v, const float* cb, int stages, int K, int32_t* idx) {
+  float r[DIM];
+  for (int k = 0; k < DIM; ++k) r[k] = v[k];
+  for (int t = 0; t < stages; ++t) {
+    const float* C = cb + (int64_t)t * K * DIM;
+    int i = argmin_codeword(r, C, K);
+    idx[t] = i;
+    for (int k = 0; k < DIM; ++k) r[k] = r[k] - C[(int64_t)i * DIM + k];
+  }
+}
+
+/* Greedy encode of already-normalized vectors v [n][8] (no row scale). */
+int vqo_encode_vectors(const float* v, int64_t n, int stages, int K, const float* cb, int32_t* idx_out) {
+  if (n < 0 || stages < 1 || K < 1) return VQO_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) encode_vector(v + i * DIM, cb, stages, K, idx_out + i * stages);
+  return VQO_OK;
+}
+
+/* Encode a [rows x cols] fp32 matrix: per row the fp16 scale, then every
+ * 8-element vector v = w[8j .. 8j+7] / s is encoded greedily.
+ * idx_out: int32 [rows][cols/8][stages]. */
+int vqo_encode(const float* w, int64_t rows, int64_t cols, int stages, int K, const float* cb,
+               uint16_t* s_bits, int32_t* idx_out) {
+  if (cols % DIM || rows < 0 || stages < 1 || K < 1) return VQO_EINVAL;
+  int64_t V = cols / DIM;
+  int st = VQO_OK;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* wr = w + r * cols;
+    uint16_t h;
+    if (row_scale(wr, cols, &h)) {
+#pragma omp atomic write
+      st = VQO_EDATA;
+      continue;
+    }
+    s_bits[r] = h;
+    float s = f16_to_f32(h);
+    for (int64_t j = 0; j < V; ++j) {
+      float v[DIM];
+      for (int k = 0; k < DIM; ++k) v[k] = normalize(wr[j * DIM + k], s);
+      encode_vector(v, cb, stages, K, idx_out + (r * V + j) * stages);
+    }
+  }
+  return st;
+}
+
+/* Decode, [VQ3R page] §2: w_hat = s * (((C1[i1] + C2[i2]) + C3[i3]) [+ C4[i4]]),
+ * summed left to right in fp32, then one fp32 multiply (no fused operations).
+ * With stages_used < stages only the first stages_used codewords are summed
+ * (the partial reconstruction after that many stages, e.g. "vq2"). */
+int vqo_decode(const int32_t* idx, const uint16_t* s_bits, const float* cb, int64_t rows, int64_t cols,
+               int stages, int K, int stages_used, float* w_out) {
+  if (cols % DIM || stages_used < 1 || stages_used > stages) return VQO_EINVAL;
+  int64_t V = cols / DIM;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    float s = f16_to_f32(s_bits[r]);
+    for (int64_t j = 0; j < V; ++j) {
+      const int32_t* id = idx + (r * V + j) * stages;
+      for (int k = 0; k < DIM; ++k) {
+        float acc = cb[(int64_t)id[0] * DIM + k];
+        for (int t = 1; t < stages_used; ++t) acc = acc + cb[((int64_t)t * K + id[t]) * DIM + k];
+        w_out[r * cols + j * DIM + k] = s * acc;
+      }
+    }
+  }
+  return VQO_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Lloyd codebook fit, [VQ3R page] §2 and §4 (per-layer codebooks fit with
+ * k-means / Lloyd iterations on sampled experts; C1 on the vectors, C2 on the
+ * stage-1 residuals, C3 on the stage-2 residuals).
+ * Readings: stages are fit one after another, stage t on the
+ * residuals left by greedy assignment to the final C_1..C_{t-1}; Forgy init
+ * from caller-given distinct training-vector indices; one iteration = assign
+ * (exhaustive argmin above) + update; a cluster with no members keeps its
+ * centroid; the mean is taken from an exact int64 fixed-point sum:
+ *   F = 62 - e_max - ceil(log2 N), where max|r| < 2^e_max (frexp exponent),
+ *   S_jk = sum_i llrint(r_ik * 2^F),  c_jk = (float)(((double)S_jk * 2^-F) / n_j).
+ * After the last update every vector is assigned once more and its residual
+ * r - C_t[a] becomes the training set of stage t+1.
+ * ---------------------------------------------------------------------- */
+static int ceil_log2_i64(int64_t n) {
+  int c = 0;
+  while (((int64_t)1 << c) < n) ++c;
+  return c;
+}
+
+int vqo_fixed_point_bits(float maxabs, int64_t n) {
+  if (maxabs == 0.0f) return 62 - ceil_log2_i64(n);
+  int e;
+  frexpf(maxabs, &e); /* maxabs = m * 2^e, m in [0.5, 1): maxabs < 2^e */
+  return 62 - e - ceil_log2_i64(n);
+}
+
+/* One stage of Lloyd on R (n x 8, fp32), modified in place into the residual.
+ * obj (optional, iters+1 entries): sum over vectors of d(r, C[a]) in fp64 after
+ * each assignment (the k-means objective). */
+static int lloyd_stage(float* R, int64_t n, int K, int iters, const int64_t* init, float* C,
+                       int32_t* assign, double* obj) {
+  float maxabs = 0.0f;
+  for (int64_t i = 0; i < n * DIM; ++i) {
+    float a = fabsf(R[i]);
+    if (a > maxabs) maxabs = a;
+  }
+  int F = vqo_fixed_point_bits(maxabs, n);
+  if (F < 16) return VQO_EDATA;
+  for (int j = 0; j < K; ++j)
+    for (int k = 0; k < DIM; ++k) C[j * DIM + k] = R[init[j] * DIM + k];
+  int64_t* S = (int64_t*)malloc(sizeof(int64_t) * K * DIM);
+  int64_t* cnt = (int64_t*)malloc(sizeof(int64_t) * K);
+  for (int it = 0; it <= iters; ++it) {
+    /* assignment */
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) assign[i] = argmin_codeword(R + i * DIM, C, K);
+    if (obj) {
+      double o = 0.0;
+      for (int64_t i = 0; i < n; ++i) o += (double)dist8(R + i * DIM, C + (int64_t)assign[i] * DIM);
+      obj[it] = o;
+    }
+    if (it == iters) break;
+    /* update: exact fixed-point cluster sums, then the mean */
+    memset(S, 0, sizeof(int64_t) * K * DIM);
+    memset(cnt, 0, sizeof(int64_t) * K);
+    for (int64_t i = 0; i < n; ++i) {
+      int j = assign[i];
+      cnt[j] += 1;
+      for (int k = 0; k < DIM; ++k) S[j * DIM + k] += llrint(ldexp((double)R[i * DIM + k], F));
+    }
+    for (int j = 0; j < K; ++j) {
+      if (cnt[j] == 0) continue; /* empty cluster keeps its centroid */
+      for (int k = 0; k < DIM; ++k)
+        C[j * DIM + k] = (float)(ldexp((double)S[j * DIM + k], -F) / (double)cnt[j]);
+    }
+  }
+  for (int64_t i = 0; i < n; ++i)
+    for (int k = 0; k < DIM; ++k) R[i * DIM + k] = R[i * DIM + k] - C[(int64_t)assign[i] * DIM + k];
+  free(S);
+  free(cnt);
+  return VQO_OK;
+}
+
+/* Fit `stages` codebooks of K entries on the vectors of n_mats matrices
+ * [rows x cols] (fp32, each normalized by its own row scales).
+ * init: int64 [stages][K] distinct indices into the n = n_mats*rows*cols/8
+ * training vectors (matrix-major, then row-major, then vector).
+ * cb_out: fp32 [stages][K][8].
+ * Optional outputs: assign_out int32 [stages][n] (final assignment per stage),
+ * obj_out fp64 [stages][iters+1], energy_out fp64 [stages+1] (sum of squared
+ * training residual before stage 1 and after each stage). */
+int vqo_fit(const float* const* mats, int n_mats, int64_t rows, int64_t cols, int stages, int K,
+            int iters, const int64_t* init, float* cb_out, int32_t* assign_out, double* obj_out,
+            double* energy_out) {
+  if (cols % DIM || n_mats < 1 || rows < 1 || stages < 1 || K < 1 || iters < 0) return VQO_EINVAL;
+  int64_t V = cols / DIM;
+  int64_t n = (int64_t)n_mats * rows * V;
+  if (n < K) return VQO_EINVAL;
+  for (int t = 0; t < stages; ++t)
+    for (int j = 0; j < K; ++j) {
+      if (init[t * K + j] < 0 || init[t * K + j] >= n) return VQO_EINVAL;
+      for (int q = 0; q < j; ++q)
+        if (init[t * K + q] == init[t * K + j]) return VQO_EINVAL;
+    }
+  float* R = (float*)malloc(sizeof(float) * n * DIM);
+  int32_t* assign = (int32_t*)malloc(sizeof(int32_t) * n);
+  int st = VQO_OK;
+  for (int m = 0; m < n_mats && st == VQO_OK; ++m)
+    for (int64_t r = 0; r < rows; ++r) {
+      const float* wr = mats[m] + r * cols;
+      uint16_t h;
+      if (row_scale(wr, cols, &h)) { st = VQO_EDATA; break; }
+      float s = f16_to_f32(h);
+      float* dst = R + ((int64_t)m * rows + r) * cols;
+      for (int64_t k = 0; k < cols; ++k) dst[k] = normalize(wr[k], s);
+    }
+  if (st == VQO_OK && energy_out) {
+    double e = 0.0;
+    for (int64_t i = 0; i < n * DIM; ++i) e += (double)R[i] * (double)R[i];
+    energy_out[0] = e;
+  }
+  for (int t = 0; t < stages && st == VQO_OK; ++t) {
+    st = lloyd_stage(R, n, K, iters, init + (int64_t)t * K, cb_out + (int64_t)t * K * DIM, assign,
+                     obj_out ? obj_out + (int64_t)t * (iters + 1) : NULL);
+    if (st) break;
+    if (assign_out) memcpy(assign_out + (int64_t)t * n, assign, sizeof(int32_t) * n);
+    if (energy_out) {
+      double e = 0.0;
+      for (int64_t i = 0; i < n * DIM; ++i) e += (double)R[i] * (double)R[i];
+      energy_out[t + 1] = e;
+    }
+  }
+  free(R);
+  free(assign);
+  return st;
+}
+
+/* Lloyd on an explicit training set (n x 8 fp32, used as given), for the
+ * closed-form pins; same stage semantics as vqo_fit. R is overwritten with the
+ * final residual. */
+int vqo_lloyd_on_vectors(float* R, int64_t n, int K, int iters, const int64_t* init, float* C,
+                         int32_t* assign, double* obj) {
+  if (n < K || K < 1 || iters < 0) return VQO_EINVAL;
+  return lloyd_stage(R, n, K, iters, init, C, assign, obj);
+}
