@@ -1,0 +1,213 @@
+/*
+ * vq.h - C ABI of libvq, residual vector quantization (VQ3R and VQ4P) of
+ * Mixture-of-Experts expert weights on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the page "3比特逼近4比特精度？WARP残差向量量化VQ3R的完整测量实验"
+ * (xdnf.cn), cited as [VQ3R page] with its section numbers:
+ *   §2  VQ3R: each weight row gets one FP16 scale; the row is cut into 8-dim
+ *       vectors; 3 stages, each a 256-entry codebook with an 8-bit index;
+ *       W ~ scale * (C1[i1] + C2[i2] + C3[i3]) at exactly 3.00 bits/weight;
+ *       C1 fits the vector, C2 the stage-1 residual, C3 the stage-2 residual;
+ *       per-layer codebooks are fit with k-means (Lloyd) on sampled experts.
+ *   §3  the relative Frobenius error ||W - W_hat||_F / ||W||_F; MXFP4 experts.
+ *   §4  the encoder keeps all 256 distances and writes only the winning index.
+ *   §5  VQ4P: 4 stages x 64 entries, 6-bit indices packed in the same bytes.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument that names tensor data is a DEVICE pointer owned
+ *     by the caller, unless marked "host". The library never allocates memory:
+ *     scratch space is passed in as `workspace` (device memory of at least the
+ *     size the matching *_workspace_size() returns, 256-byte aligned).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the legacy default
+ *     stream) and is asynchronous; the call returns after validating its
+ *     arguments and launching.
+ *   - Return value: a vq_status. Argument checks happen on the host before any
+ *     launch; on error nothing is launched and no output is touched.
+ *   - Data errors detected on the device (a non-finite weight, a row RMS beyond
+ *     the fp16 range, a codebook entry that is non-finite or larger than 2048 in
+ *     magnitude, a GEMV route id out of range) set a flag in the workspace;
+ *     vq_read_status() returns it. Outputs of a flagged call are unspecified.
+ *   - Layouts (row-major throughout):
+ *       weights     [rows][cols] of vq_dtype; cols % 8 == 0
+ *       codebooks   fp32 [stages][entries][8]; VQ3R 3 x 256, VQ4P 4 x 64
+ *       scales      fp16 bit patterns, one per row
+ *       idx         3 bytes per 8-dim vector, [rows][cols/8][3]; the 3 bytes
+ *                   are a little-endian 24-bit word sum_t i_t << (t * b) with
+ *                   b = 8 (VQ3R: byte t is stage t's index) or b = 6 (VQ4P).
+ *   - Limits: 1 <= cols/8, cols <= 2^20, rows * cols / 8 < 2^32 per call.
+ *   - Calls on one stream are ordered; the library keeps no global state, so
+ *     calls on different streams with different workspaces may overlap.
+ */
+#ifndef VQ_H
+#define VQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vq_status {
+  VQ_OK = 0,
+  VQ_EINVAL = 1,     /* invalid argument (null pointer, bad size, bad enum) */
+  VQ_ERANGE = 2,     /* size beyond the supported range */
+  VQ_EWORKSPACE = 3, /* workspace missing, misaligned or too small */
+  VQ_EDEVICE = 4,    /* a HIP runtime call failed */
+  VQ_EDATA = 5       /* the device flagged a data error (vq_read_status) */
+} vq_status;
+
+typedef enum vq_dtype { VQ_DT_F32 = 0, VQ_DT_BF16 = 1, VQ_DT_F16 = 2 } vq_dtype;
+
+/* VQ3R = 3 stages x 256 entries, 8-bit indices ([VQ3R page] §2);
+ * VQ4P = 4 stages x 64 entries, 6-bit packed indices ([VQ3R page] §5). */
+typedef enum vq_format { VQ_FMT_VQ3R = 0, VQ_FMT_VQ4P = 1 } vq_format;
+
+/* How the approximate codeword scores of the encoder / Lloyd assignment are
+ * computed before the exact check (all engines give identical indices):
+ *   MFMA_F16X  fp32 values split into two fp16 halves, fp16 matrix cores
+ *   MFMA_F32   fp32 matrix cores (v_mfma_f32_32x32x2_f32)
+ *   VALU_F32   fp32 vector FMAs
+ *   EXACT      no fast scoring: every vector goes through the exact search
+ * AUTO picks the fastest measured engine (MFMA_F16X). */
+typedef enum vq_engine {
+  VQ_ENGINE_AUTO = 0,
+  VQ_ENGINE_MFMA_F16X = 1,
+  VQ_ENGINE_MFMA_F32 = 2,
+  VQ_ENGINE_VALU_F32 = 3,
+  VQ_ENGINE_EXACT = 4
+} vq_engine;
+
+/* Human-readable name of a vq_status. Never NULL. */
+const char* vq_status_string(int status);
+
+/* Library ABI version: (major << 16) | minor. */
+int vq_version(void);
+
+/* Waits for `stream`, then returns VQ_EDATA if any call that used `workspace`
+ * since the last vq_clear_status() flagged a data error, else VQ_OK.
+ * *flags_out (host, may be NULL) receives the raw flag bits. */
+int vq_read_status(const void* workspace, void* stream, uint32_t* flags_out);
+
+/* Enqueues a reset of the workspace's status flags. */
+int vq_clear_status(void* workspace, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Codebook fit ([VQ3R page] §2 and §4: per-layer codebooks fit with Lloyd
+ * k-means on sampled experts; C1 on the vectors, C2 on the stage-1 residuals,
+ * C3 on the stage-2 residuals).
+ *
+ * mats      host array of n_mats device pointers, each a [rows][cols] matrix
+ *           of `dtype`; every row is normalized by its own fp16 RMS scale and
+ *           cut into 8-dim vectors, giving N = n_mats*rows*cols/8 training
+ *           vectors ordered matrix, row, vector.
+ * iters     Lloyd iterations per stage (>= 0); one iteration = nearest-codeword
+ *           assignment + centroid update.
+ * init_idx  host int64 [stages][entries]: per stage, distinct training-vector
+ *           indices in [0, N) whose (residual) vectors are the initial
+ *           centroids (Forgy initialization; the caller draws them).
+ * codebooks out: fp32 [stages][entries][8].
+ * Centroids are cluster means computed from exact int64 fixed-point sums
+ * (F = 62 - e - ceil(log2 N) fraction bits, max|r| < 2^e); an empty cluster
+ * keeps its centroid. The result is bit-identical for any engine and launch
+ * configuration. Requires N >= entries.
+ * Workspace: vq_fit_workspace_size(format, n_mats, rows, cols).
+ * ---------------------------------------------------------------------- */
+size_t vq_fit_workspace_size(int format, int64_t n_mats, int64_t rows, int64_t cols);
+int vq_fit_codebooks(int format, const void* const* mats, int dtype, int64_t n_mats, int64_t rows,
+                     int64_t cols, int32_t iters, const int64_t* init_idx, float* codebooks,
+                     void* workspace, size_t ws_bytes, int engine, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Encode ([VQ3R page] §2 and §4): per row the fp16 scale s = fp16(RMS(row));
+ * every vector v = w[8j..8j+7] / s is encoded greedily: for each stage t,
+ * i_t = argmin_j ||r - C_t[j]||^2 over the stage's entries (fp32 distance
+ * evaluated as sum_k fma(e_k, e_k) in k order, ties to the lowest index),
+ * then r <- r - C_t[i_t]. Writes idx and scales. Indices equal those of that
+ * exhaustive search exactly; near ties are resolved by the exact evaluation.
+ * W         [rows][cols] of dtype;  codebooks fp32 [stages][entries][8]
+ * idx       out [rows][cols/8][3];  scales out fp16 bits [rows]
+ * Workspace: vq_encode_workspace_size(format, rows, cols).
+ * vq_encode selects format and engine; vq3r_encode / vq4p_encode use AUTO.
+ * ---------------------------------------------------------------------- */
+size_t vq_encode_workspace_size(int format, int64_t rows, int64_t cols);
+int vq_encode(int format, int engine, const void* W, int dtype, int64_t rows, int64_t cols,
+              const float* codebooks, uint8_t* idx, uint16_t* scales, void* workspace, size_t ws_bytes,
+              void* stream);
+int vq3r_encode(const void* W, int dtype, int64_t rows, int64_t cols, const float* codebooks, uint8_t* idx,
+                uint16_t* scales, void* workspace, size_t ws_bytes, void* stream);
+int vq4p_encode(const void* W, int dtype, int64_t rows, int64_t cols, const float* codebooks, uint8_t* idx,
+                uint16_t* scales, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode ([VQ3R page] §2, and the container round-trip check of §4):
+ * W_out[r][8j+k] = s_r * (((C1[i1][k] + C2[i2][k]) + C3[i3][k]) [+ C4[i4][k]]),
+ * summed left to right in fp32, then one fp32 multiply. stages_used < stages
+ * gives the partial reconstruction after that many stages (e.g. 2 = "vq2").
+ * W_out fp32 [rows][cols]. No workspace; cannot fail on the device.
+ * ---------------------------------------------------------------------- */
+int vq_decode(int format, const uint8_t* idx, const uint16_t* scales, const float* codebooks, int64_t rows,
+              int64_t cols, int32_t stages_used, float* W_out, void* stream);
+int vq3r_decode(const uint8_t* idx, const uint16_t* scales, const float* codebooks, int64_t rows, int64_t cols,
+                float* W_out, void* stream);
+int vq4p_decode(const uint8_t* idx, const uint16_t* scales, const float* codebooks, int64_t rows, int64_t cols,
+                float* W_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Fused dequantize-GEMV for decode-time expert mat-vecs ([VQ3R page] §1:
+ * each token activates a few experts whose stored records are decoded and
+ * multiplied): for token b and routed slot k with e = route[b][k],
+ *   y[b][k][r] = sum_c W_hat_e[r][c] * x[b][c]   (fp32 accumulation)
+ * computed from the indices without materializing W_hat.
+ * idx        base of n_experts index tensors; expert e at idx + e*expert_stride
+ *            bytes, each [rows][cols/8][3]
+ * scales     base of the row scales; expert e at scales + e*scale_stride
+ * x          fp16 bit patterns [ntok][cols];  route int32 [ntok][topk]
+ * y          out fp32 [ntok][topk][rows]
+ * Workspace: vq_gemv_workspace_size(format, rows, cols, ntok, topk).
+ * ---------------------------------------------------------------------- */
+size_t vq_gemv_workspace_size(int format, int64_t rows, int64_t cols, int32_t ntok, int32_t topk);
+int vq_dequant_gemv(int format, const uint8_t* idx, int64_t expert_stride, const uint16_t* scales,
+                    int64_t scale_stride, const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts,
+                    const uint16_t* x, int32_t ntok, const int32_t* route, int32_t topk, float* y,
+                    void* workspace, size_t ws_bytes, void* stream);
+int vq3r_dequant_gemv(const uint8_t* idx, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
+                      const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts, const uint16_t* x,
+                      int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace, size_t ws_bytes,
+                      void* stream);
+int vq4p_dequant_gemv(const uint8_t* idx, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
+                      const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts, const uint16_t* x,
+                      int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * Reconstruction error ([VQ3R page] §3.1, the Gate-3 metric
+ * ||W - W_hat||_F / ||W||_F, also after fewer stages: "vq2" = 2 stages).
+ * For n_mats consecutive matrices (matrix m at W + m*rows*cols elements,
+ * idx + m*rows*cols/8*3 bytes, scales + m*rows) writes fp64
+ * sums[m][t] = sum (w - w_hat_{t+1})^2 for t = 0..stages-1 (w_hat_t = the
+ * partial reconstruction after t stages) and sums[m][stages] = sum w^2.
+ * sums: device fp64 [n_mats][stages+1].
+ * Workspace: vq_error_workspace_size(format, n_mats, rows, cols).
+ * ---------------------------------------------------------------------- */
+size_t vq_error_workspace_size(int format, int64_t n_mats, int64_t rows, int64_t cols);
+int vq_error(int format, const void* W, int dtype, const uint8_t* idx, const uint16_t* scales,
+             const float* codebooks, int64_t n_mats, int64_t rows, int64_t cols, double* sums, void* workspace,
+             size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * MXFP4 quantize-dequantize of a [rows][cols] matrix (the MXFP4 source format
+ * of the K3 experts, [VQ3R page] §3.2; the format is the OCP Microscaling v1.0
+ * definition): blocks of 32 along the row share X = 2^(floor(log2 amax) - 2)
+ * (E8M0, clamped to 2^-127..2^127); elements are E2M1(w / X) rounded to nearest
+ * even and saturated at 6; out = X * e2m1 in fp32 (zero blocks give zeros).
+ * cols % 32 == 0. Workspace: 256 bytes (status flags).
+ * ---------------------------------------------------------------------- */
+int vq_mxfp4_qdq(const void* W, int dtype, int64_t rows, int64_t cols, float* out, void* workspace,
+                 size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VQ_H */

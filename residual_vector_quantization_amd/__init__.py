@@ -1,0 +1,291 @@
+"""MI355X-native residual vector quantization (VQ3R / VQ4P) of MoE expert weights.
+
+Thin ctypes binding over libvq.so (include/vq.h). Every step of the method
+runs in the library's HIP kernels; this module only marshals arguments:
+PyTorch tensors provide device memory and the current HIP stream.
+
+[VQ3R page] = the page "3比特逼近4比特精度？WARP残差向量量化VQ3R的完整测量实验":
+  §2 VQ3R recipe (3 x 256-entry codebooks, 8-dim vectors, FP16 row scale),
+  §3 relative Frobenius error, §4 encoder / codebook fit, §5 VQ4P.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "VQError", "lib", "FORMATS", "ENGINES", "stages_entries",
+    "encode", "decode", "fit_codebooks", "dequant_gemv", "error_sums", "rel_errors", "mxfp4_qdq",
+    "encode_workspace", "fit_workspace", "gemv_workspace", "error_workspace", "read_status",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvq.so")
+
+FORMATS = {"vq3r": 0, "vq4p": 1}
+ENGINES = {"auto": 0, "mfma_f16x": 1, "mfma_f32": 2, "valu_f32": 3, "exact": 4}
+STATUS = {0: "ok", 1: "invalid argument", 2: "size out of range", 3: "workspace", 4: "HIP runtime error",
+          5: "data error flagged on the device"}
+
+
+def stages_entries(fmt: str):
+    return (3, 256) if fmt == "vq3r" else (4, 64)
+
+
+class VQError(RuntimeError):
+    def __init__(self, status: int, where: str, flags: int = 0):
+        self.status = status
+        self.flags = flags
+        msg = "%s: %s" % (where, STATUS.get(status, "status %d" % status))
+        if flags:
+            msg += " (device flags 0x%x)" % flags
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def lib():
+    """Loads libvq.so; raises if it has not been built (no fallback path exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libvq.so is not built (%s); run residual_vector_quantization_amd.build_lib" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, L64, SZ, U32P = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    sig = {
+        "vq_status_string": ([I], ctypes.c_char_p),
+        "vq_version": ([], I),
+        "vq_read_status": ([P, P, U32P], I),
+        "vq_clear_status": ([P, P], I),
+        "vq_encode_workspace_size": ([I, L64, L64], SZ),
+        "vq_encode": ([I, I, P, I, L64, L64, P, P, P, P, SZ, P], I),
+        "vq3r_encode": ([P, I, L64, L64, P, P, P, P, SZ, P], I),
+        "vq4p_encode": ([P, I, L64, L64, P, P, P, P, SZ, P], I),
+        "vq_fit_workspace_size": ([I, L64, L64, L64], SZ),
+        "vq_fit_codebooks": ([I, P, I, L64, L64, L64, ctypes.c_int32, P, P, P, SZ, I, P], I),
+        "vq_decode": ([I, P, P, P, L64, L64, ctypes.c_int32, P, P], I),
+        "vq3r_decode": ([P, P, P, L64, L64, P, P], I),
+        "vq4p_decode": ([P, P, P, L64, L64, P, P], I),
+        "vq_gemv_workspace_size": ([I, L64, L64, ctypes.c_int32, ctypes.c_int32], SZ),
+        "vq_dequant_gemv": ([I, P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32, P,
+                             ctypes.c_int32, P, P, SZ, P], I),
+        "vq3r_dequant_gemv": ([P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32, P,
+                               ctypes.c_int32, P, P, SZ, P], I),
+        "vq4p_dequant_gemv": ([P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32, P,
+                               ctypes.c_int32, P, P, SZ, P], I),
+        "vq_error_workspace_size": ([I, L64, L64, L64], SZ),
+        "vq_error": ([I, P, I, P, P, P, L64, L64, L64, P, P, SZ, P], I),
+        "vq_mxfp4_qdq": ([P, I, L64, L64, P, P, SZ, P], I),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = L
+    return L
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+    if t.dtype not in m:
+        raise TypeError("weights must be float32, bfloat16 or float16, got %s" % t.dtype)
+    return m[t.dtype]
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensor must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+
+
+def _call(where, st, workspace=None, check=False):
+    if st != 0:
+        raise VQError(st, where)
+    if check and workspace is not None:
+        read_status(workspace, where)
+
+
+def read_status(workspace, where="vq_read_status"):
+    """Synchronizes the current stream and raises VQError if the last call that
+    used `workspace` flagged a data error on the device."""
+    flags = ctypes.c_uint32(0)
+    st = lib().vq_read_status(_ptr(workspace), _stream(), ctypes.byref(flags))
+    if st != 0:
+        raise VQError(st, where, flags.value)
+    return flags.value
+
+
+def _workspace(nbytes, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ encode
+def encode_workspace(fmt, rows, cols, device="cuda"):
+    n = lib().vq_encode_workspace_size(FORMATS[fmt], rows, cols)
+    if n == 0:
+        raise VQError(1, "vq_encode_workspace_size")
+    return _workspace(n, device)
+
+
+def encode(W, codebooks, fmt="vq3r", engine="auto", idx=None, scales=None, workspace=None, check=True):
+    """Greedy residual encode ([VQ3R page] §2, §4). W [rows, cols] (fp32/bf16/fp16),
+    codebooks fp32 [stages, entries, 8]. Returns (idx uint8 [rows, cols/8, 3],
+    scales fp16 [rows])."""
+    torch = _torch()
+    rows, cols = W.shape
+    _check_cuda(W, codebooks)
+    if idx is None:
+        idx = torch.empty((rows, cols // 8, 3), dtype=torch.uint8, device=W.device)
+    if scales is None:
+        scales = torch.empty(rows, dtype=torch.float16, device=W.device)
+    if workspace is None:
+        workspace = encode_workspace(fmt, rows, cols, W.device)
+    st = lib().vq_encode(FORMATS[fmt], ENGINES[engine], _ptr(W), _dtype_code(W), rows, cols, _ptr(codebooks),
+                         _ptr(idx), _ptr(scales), _ptr(workspace), workspace.numel(), _stream())
+    _call("vq_encode", st, workspace, check)
+    return idx, scales
+
+
+# ------------------------------------------------------------------ decode
+def decode(idx, scales, codebooks, fmt="vq3r", stages_used=None, out=None):
+    """W_hat = s * (C1[i1] + C2[i2] + ...) ([VQ3R page] §2), fp32 [rows, cols]."""
+    torch = _torch()
+    rows, V, _ = idx.shape
+    _check_cuda(idx, scales, codebooks)
+    S, _ = stages_entries(fmt)
+    if out is None:
+        out = torch.empty((rows, V * 8), dtype=torch.float32, device=idx.device)
+    st = lib().vq_decode(FORMATS[fmt], _ptr(idx), _ptr(scales), _ptr(codebooks), rows, V * 8,
+                         S if stages_used is None else stages_used, _ptr(out), _stream())
+    _call("vq_decode", st)
+    return out
+
+
+# ------------------------------------------------------------------ fit
+def fit_workspace(fmt, n_mats, rows, cols, device="cuda"):
+    n = lib().vq_fit_workspace_size(FORMATS[fmt], n_mats, rows, cols)
+    if n == 0:
+        raise VQError(1, "vq_fit_workspace_size")
+    return _workspace(n, device)
+
+
+def fit_codebooks(mats, init_idx, fmt="vq3r", iters=20, engine="auto", codebooks=None, workspace=None,
+                  check=True):
+    """Lloyd codebook fit over the vectors of `mats` ([VQ3R page] §2, §4).
+    init_idx: int64 [stages, entries] distinct training-vector indices."""
+    torch = _torch()
+    rows, cols = mats[0].shape
+    for m in mats:
+        _check_cuda(m)
+        if m.shape != (rows, cols) or m.dtype != mats[0].dtype:
+            raise ValueError("all matrices must share shape and dtype")
+    S, K = stages_entries(fmt)
+    init = np.ascontiguousarray(init_idx, dtype=np.int64).reshape(S, K)
+    if codebooks is None:
+        codebooks = torch.empty((S, K, 8), dtype=torch.float32, device=mats[0].device)
+    if workspace is None:
+        workspace = fit_workspace(fmt, len(mats), rows, cols, mats[0].device)
+    ptrs = (ctypes.c_void_p * len(mats))(*[m.data_ptr() for m in mats])
+    st = lib().vq_fit_codebooks(FORMATS[fmt], ptrs, _dtype_code(mats[0]), len(mats), rows, cols, int(iters),
+                                init.ctypes.data_as(ctypes.c_void_p), _ptr(codebooks), _ptr(workspace),
+                                workspace.numel(), ENGINES[engine], _stream())
+    _call("vq_fit_codebooks", st, workspace, check)
+    return codebooks
+
+
+# ------------------------------------------------------------------ GEMV
+def gemv_workspace(fmt, rows, cols, ntok, topk, device="cuda"):
+    n = lib().vq_gemv_workspace_size(FORMATS[fmt], rows, cols, ntok, topk)
+    if n == 0:
+        raise VQError(1, "vq_gemv_workspace_size")
+    return _workspace(n, device)
+
+
+def dequant_gemv(idx, scales, codebooks, x, route, fmt="vq3r", y=None, workspace=None, check=False):
+    """y[b][k] = W_hat_{route[b][k]} x_b for the stacked experts idx [E, rows, cols/8, 3],
+    scales [E, rows], x fp16 [ntok, cols], route int32 [ntok, topk] -> y fp32 [ntok, topk, rows]."""
+    torch = _torch()
+    E, rows, V, _ = idx.shape
+    ntok, topk = route.shape
+    _check_cuda(idx, scales, codebooks, x, route)
+    if x.dtype != torch.float16 or route.dtype != torch.int32:
+        raise TypeError("x must be float16 and route int32")
+    if y is None:
+        y = torch.empty((ntok, topk, rows), dtype=torch.float32, device=idx.device)
+    if workspace is None:
+        workspace = gemv_workspace(fmt, rows, V * 8, ntok, topk, idx.device)
+    st = lib().vq_dequant_gemv(FORMATS[fmt], _ptr(idx), rows * V * 3, _ptr(scales), rows, _ptr(codebooks), rows,
+                               V * 8, E, _ptr(x), ntok, _ptr(route), topk, _ptr(y), _ptr(workspace),
+                               workspace.numel(), _stream())
+    _call("vq_dequant_gemv", st, workspace, check)
+    return y
+
+
+# ------------------------------------------------------------------ error
+def error_workspace(fmt, n_mats, rows, cols, device="cuda"):
+    n = lib().vq_error_workspace_size(FORMATS[fmt], n_mats, rows, cols)
+    if n == 0:
+        raise VQError(1, "vq_error_workspace_size")
+    return _workspace(n, device)
+
+
+def error_sums(W, idx, scales, codebooks, fmt="vq3r", n_mats=1, sums=None, workspace=None, check=True):
+    """fp64 [n_mats, stages+1]: sum (w - w_hat_t)^2 after t = 1..stages, then sum w^2
+    ([VQ3R page] §3.1). W is [n_mats*rows, cols] (matrices stacked by rows)."""
+    torch = _torch()
+    total_rows, cols = W.shape
+    rows = total_rows // n_mats
+    S, _ = stages_entries(fmt)
+    _check_cuda(W, idx, scales, codebooks)
+    if sums is None:
+        sums = torch.empty((n_mats, S + 1), dtype=torch.float64, device=W.device)
+    if workspace is None:
+        workspace = error_workspace(fmt, n_mats, rows, cols, W.device)
+    st = lib().vq_error(FORMATS[fmt], _ptr(W), _dtype_code(W), _ptr(idx), _ptr(scales), _ptr(codebooks), n_mats,
+                        rows, cols, _ptr(sums), _ptr(workspace), workspace.numel(), _stream())
+    _call("vq_error", st, workspace, check)
+    return sums
+
+
+def rel_errors(sums):
+    """Relative Frobenius error after each stage from error_sums() output."""
+    s = sums.double()
+    return (s[:, :-1] / s[:, -1:]).sqrt()
+
+
+# ------------------------------------------------------------------ MXFP4
+def mxfp4_qdq(W, out=None, workspace=None, check=True):
+    """MXFP4 quantize-dequantize ([VQ3R page] §3.2 source format) -> fp32 [rows, cols]."""
+    torch = _torch()
+    rows, cols = W.shape
+    _check_cuda(W)
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=W.device)
+    if workspace is None:
+        workspace = _workspace(256, W.device)
+    st = lib().vq_mxfp4_qdq(_ptr(W), _dtype_code(W), rows, cols, _ptr(out), _ptr(workspace), workspace.numel(),
+                            _stream())
+    _call("vq_mxfp4_qdq", st, workspace, check)
+    return out

@@ -1,0 +1,394 @@
+// C ABI of libvq (declarations and documentation in include/vq.h): argument
+// validation, workspace layout and kernel launches. No allocation happens here.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "../../include/vq.h"
+#include "vq_launch.hpp"
+
+using namespace vqk;
+
+namespace {
+
+constexpr int kVersion = (1 << 16) | 0;
+constexpr size_t kHeader = sizeof(WsHeader);
+constexpr int64_t kMaxCols = 1 << 20;
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline bool fmt_ok(int f) { return f == VQ_FMT_VQ3R || f == VQ_FMT_VQ4P; }
+inline bool dtype_ok(int d) { return d == VQ_DT_F32 || d == VQ_DT_BF16 || d == VQ_DT_F16; }
+inline int stages_of(int f) { return f == VQ_FMT_VQ3R ? 3 : 4; }
+inline int entries_of(int f) { return f == VQ_FMT_VQ3R ? 256 : 64; }
+inline size_t esize(int d) { return d == VQ_DT_F32 ? 4 : 2; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// rows/cols shared checks: cols multiple of 8 and within range; vector count fits 32 bits
+int check_shape(int64_t rows, int64_t cols, bool allow_empty_rows = true) {
+  if (rows < 0 || cols <= 0 || cols % 8 != 0) return VQ_EINVAL;
+  if (!allow_empty_rows && rows == 0) return VQ_EINVAL;
+  if (cols > kMaxCols) return VQ_ERANGE;
+  if ((uint64_t)rows * (uint64_t)(cols / 8) >= (1ull << 32)) return VQ_ERANGE;
+  return VQ_OK;
+}
+
+int device_cus(int* ncu) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VQ_EDEVICE;
+  if (hipDeviceGetAttribute(ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return VQ_EDEVICE;
+  if (*ncu < 1) *ncu = 1;
+  return VQ_OK;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? VQ_OK : VQ_EDEVICE; }
+
+uint32_t list_capacity(uint64_t nvec) {
+  uint64_t cap = nvec / 16;
+  if (cap < 4096) cap = 4096;
+  if (cap > 0xFFFFFFFFull) cap = 0xFFFFFFFFull;
+  return (uint32_t)cap;
+}
+
+// ---- fit workspace
+struct FitLayout {
+  size_t init, r0, r1, list, partials, total;
+  uint32_t cap;
+  int ga, gf;
+};
+
+// Grid sizes of the fit kernels are fixed (not taken from the device) so that
+// the workspace size does not depend on the GPU it is queried on.
+constexpr int64_t kFitAssignBlocks = 512, kFitExactBlocks = 256;
+
+FitLayout fit_layout(int format, int64_t n) {
+  FitLayout L;
+  const int K = entries_of(format), S = stages_of(format);
+  L.cap = list_capacity((uint64_t)n);
+  int64_t groups = (n + 31) / 32;
+  int64_t ga = (groups + 3) / 4;
+  if (ga > kFitAssignBlocks) ga = kFitAssignBlocks;
+  if (ga < 1) ga = 1;
+  int64_t gf = (n / 16 + 255) / 256;
+  if (gf > kFitExactBlocks) gf = kFitExactBlocks;
+  if (gf < 1) gf = 1;
+  L.ga = (int)ga;
+  L.gf = (int)gf;
+  size_t off = kHeader;
+  L.init = off;
+  off = align256(off + sizeof(int64_t) * S * K);
+  L.r0 = off;
+  off = align256(off + sizeof(float) * 8 * (size_t)n);
+  L.r1 = off;
+  off = align256(off + sizeof(float) * 8 * (size_t)n);
+  L.list = off;
+  off = align256(off + sizeof(uint32_t) * (size_t)L.cap);
+  L.partials = off;
+  off = align256(off + sizeof(long long) * (size_t)(L.ga + L.gf) * K * 9);
+  L.total = off;
+  return L;
+}
+
+int error_blocks(int64_t nvec_per_mat, int64_t n_mats) {
+  int64_t want = (nvec_per_mat + 255) / 256;
+  int64_t cap = (2048 + n_mats - 1) / n_mats;
+  if (cap < 1) cap = 1;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  return (int)want;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vq_status_string(int status) {
+  switch (status) {
+    case VQ_OK: return "ok";
+    case VQ_EINVAL: return "invalid argument";
+    case VQ_ERANGE: return "size out of supported range";
+    case VQ_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case VQ_EDEVICE: return "HIP runtime error";
+    case VQ_EDATA: return "data error flagged on the device";
+    default: return "unknown status";
+  }
+}
+
+int vq_version(void) { return kVersion; }
+
+int vq_read_status(const void* workspace, void* stream, uint32_t* flags_out) {
+  if (!workspace || !aligned(workspace, 256)) return VQ_EWORKSPACE;
+  uint32_t flags = 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(&flags, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess) return VQ_EDEVICE;
+  if (hipStreamSynchronize(s) != hipSuccess) return VQ_EDEVICE;
+  if (flags_out) *flags_out = flags;
+  return (flags & ST_ERROR_MASK) ? VQ_EDATA : VQ_OK;
+}
+
+int vq_clear_status(void* workspace, void* stream) {
+  if (!workspace || !aligned(workspace, 256)) return VQ_EWORKSPACE;
+  return hip_status(launch_reset((WsHeader*)workspace, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------- encode
+size_t vq_encode_workspace_size(int format, int64_t rows, int64_t cols) {
+  if (!fmt_ok(format) || check_shape(rows, cols) != VQ_OK) return 0;
+  const uint64_t nvec = (uint64_t)rows * (uint64_t)(cols / 8);
+  return align256(kHeader + sizeof(uint32_t) * (size_t)list_capacity(nvec));
+}
+
+int vq_encode(int format, int engine, const void* W, int dtype, int64_t rows, int64_t cols, const float* codebooks,
+              uint8_t* idx, uint16_t* scales, void* workspace, size_t ws_bytes, void* stream) {
+  if (!fmt_ok(format) || !dtype_ok(dtype) || engine < VQ_ENGINE_AUTO || engine > VQ_ENGINE_EXACT) return VQ_EINVAL;
+  int st = check_shape(rows, cols);
+  if (st != VQ_OK) return st;
+  if (rows == 0) return VQ_OK;  // empty input: nothing is read or written
+  if (!W || !codebooks || !idx || !scales) return VQ_EINVAL;
+  if (!aligned(W, 16) || !aligned(codebooks, 16)) return VQ_EINVAL;
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < vq_encode_workspace_size(format, rows, cols))
+    return VQ_EWORKSPACE;
+  EncodeArgs a;
+  a.format = format;
+  a.engine = engine == VQ_ENGINE_AUTO ? ENGINE_F16X : engine;
+  a.dtype = dtype;
+  a.W = W;
+  a.rows = rows;
+  a.cols = cols;
+  a.codebooks = codebooks;
+  a.idx = idx;
+  a.scales = scales;
+  a.hdr = (WsHeader*)workspace;
+  a.list = (uint32_t*)((char*)workspace + kHeader);
+  a.cap = list_capacity((uint64_t)rows * (uint64_t)(cols / 8));
+  a.stream = (hipStream_t)stream;
+  if ((st = device_cus(&a.ncu)) != VQ_OK) return st;
+  return hip_status(launch_encode(a));
+}
+
+int vq3r_encode(const void* W, int dtype, int64_t rows, int64_t cols, const float* codebooks, uint8_t* idx,
+                uint16_t* scales, void* workspace, size_t ws_bytes, void* stream) {
+  return vq_encode(VQ_FMT_VQ3R, VQ_ENGINE_AUTO, W, dtype, rows, cols, codebooks, idx, scales, workspace, ws_bytes,
+                   stream);
+}
+
+int vq4p_encode(const void* W, int dtype, int64_t rows, int64_t cols, const float* codebooks, uint8_t* idx,
+                uint16_t* scales, void* workspace, size_t ws_bytes, void* stream) {
+  return vq_encode(VQ_FMT_VQ4P, VQ_ENGINE_AUTO, W, dtype, rows, cols, codebooks, idx, scales, workspace, ws_bytes,
+                   stream);
+}
+
+// ---------------------------------------------------------------- fit
+size_t vq_fit_workspace_size(int format, int64_t n_mats, int64_t rows, int64_t cols) {
+  if (!fmt_ok(format) || n_mats < 1 || check_shape(rows, cols, false) != VQ_OK) return 0;
+  const uint64_t n = (uint64_t)n_mats * (uint64_t)rows * (uint64_t)(cols / 8);
+  if (n >= (1ull << 32)) return 0;
+  return fit_layout(format, (int64_t)n).total;
+}
+
+int vq_fit_codebooks(int format, const void* const* mats, int dtype, int64_t n_mats, int64_t rows, int64_t cols,
+                     int32_t iters, const int64_t* init_idx, float* codebooks, void* workspace, size_t ws_bytes,
+                     int engine, void* stream) {
+  if (!fmt_ok(format) || !dtype_ok(dtype) || engine < VQ_ENGINE_AUTO || engine > VQ_ENGINE_EXACT) return VQ_EINVAL;
+  if (n_mats < 1 || iters < 0 || !mats || !init_idx || !codebooks) return VQ_EINVAL;
+  int st = check_shape(rows, cols, false);
+  if (st != VQ_OK) return st;
+  const uint64_t n = (uint64_t)n_mats * (uint64_t)rows * (uint64_t)(cols / 8);
+  if (n >= (1ull << 32)) return VQ_ERANGE;
+  const int S = stages_of(format), K = entries_of(format);
+  if (n < (uint64_t)K) return VQ_EINVAL;
+  for (int64_t m = 0; m < n_mats; ++m)
+    if (!mats[m] || !aligned(mats[m], 16)) return VQ_EINVAL;
+  if (!aligned(codebooks, 16)) return VQ_EINVAL;
+  for (int t = 0; t < S; ++t)
+    for (int j = 0; j < K; ++j) {
+      const int64_t v = init_idx[t * K + j];
+      if (v < 0 || (uint64_t)v >= n) return VQ_EINVAL;
+      for (int q = 0; q < j; ++q)
+        if (init_idx[t * K + q] == v) return VQ_EINVAL;
+    }
+  const FitLayout L = fit_layout(format, (int64_t)n);
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < L.total) return VQ_EWORKSPACE;
+  int ncu = 0;
+  if ((st = device_cus(&ncu)) != VQ_OK) return st;
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  // the initial indices travel through the workspace; the copy is complete
+  // (staged) when hipMemcpyAsync returns for pageable host memory
+  if (hipMemcpyAsync(ws + L.init, init_idx, sizeof(int64_t) * S * K, hipMemcpyHostToDevice, s) != hipSuccess)
+    return VQ_EDEVICE;
+  FitArgs a;
+  a.format = format;
+  a.engine = (engine == VQ_ENGINE_AUTO) ? ENGINE_F16X : engine;
+  if (a.engine == ENGINE_EXACT) a.engine = ENGINE_F16X;  // the fit's exact pass already covers every flagged vector
+  a.dtype = dtype;
+  a.mats = mats;
+  a.n_mats = n_mats;
+  a.rows = rows;
+  a.cols = cols;
+  a.n = (int64_t)n;
+  a.iters = iters;
+  int c = 0;
+  while ((1ull << c) < n) ++c;
+  a.clog2n = c;
+  a.init = (const int64_t*)(ws + L.init);
+  a.codebooks = codebooks;
+  a.hdr = (WsHeader*)ws;
+  a.R[0] = (float*)(ws + L.r0);
+  a.R[1] = (float*)(ws + L.r1);
+  a.list = (uint32_t*)(ws + L.list);
+  a.cap = L.cap;
+  a.partials = (long long*)(ws + L.partials);
+  a.n_assign_blocks = L.ga;
+  a.n_exact_blocks = L.gf;
+  a.ncu = ncu;
+  a.stream = s;
+  return hip_status(launch_fit(a));
+}
+
+// ---------------------------------------------------------------- decode
+int vq_decode(int format, const uint8_t* idx, const uint16_t* scales, const float* codebooks, int64_t rows,
+              int64_t cols, int32_t stages_used, float* W_out, void* stream) {
+  if (!fmt_ok(format)) return VQ_EINVAL;
+  int st = check_shape(rows, cols);
+  if (st != VQ_OK) return st;
+  if (stages_used < 1 || stages_used > stages_of(format)) return VQ_EINVAL;
+  if (rows == 0) return VQ_OK;
+  if (!idx || !scales || !codebooks || !W_out || !aligned(W_out, 16)) return VQ_EINVAL;
+  DecodeArgs a;
+  a.format = format;
+  a.stages_used = stages_used;
+  a.idx = idx;
+  a.scales = scales;
+  a.codebooks = codebooks;
+  a.rows = rows;
+  a.cols = cols;
+  a.out = W_out;
+  a.stream = (hipStream_t)stream;
+  if ((st = device_cus(&a.ncu)) != VQ_OK) return st;
+  return hip_status(launch_decode(a));
+}
+
+int vq3r_decode(const uint8_t* idx, const uint16_t* scales, const float* codebooks, int64_t rows, int64_t cols,
+                float* W_out, void* stream) {
+  return vq_decode(VQ_FMT_VQ3R, idx, scales, codebooks, rows, cols, 3, W_out, stream);
+}
+
+int vq4p_decode(const uint8_t* idx, const uint16_t* scales, const float* codebooks, int64_t rows, int64_t cols,
+                float* W_out, void* stream) {
+  return vq_decode(VQ_FMT_VQ4P, idx, scales, codebooks, rows, cols, 4, W_out, stream);
+}
+
+// ---------------------------------------------------------------- GEMV
+size_t vq_gemv_workspace_size(int format, int64_t rows, int64_t cols, int32_t ntok, int32_t topk) {
+  if (!fmt_ok(format) || check_shape(rows, cols) != VQ_OK || ntok < 0 || topk < 0) return 0;
+  const size_t npairs = (size_t)ntok * (size_t)topk;
+  return align256(kHeader + sizeof(float) * npairs * (size_t)gemv_nblk(cols) * (size_t)rows);
+}
+
+int vq_dequant_gemv(int format, const uint8_t* idx, int64_t expert_stride, const uint16_t* scales,
+                    int64_t scale_stride, const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts,
+                    const uint16_t* x, int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  if (!fmt_ok(format)) return VQ_EINVAL;
+  int st = check_shape(rows, cols);
+  if (st != VQ_OK) return st;
+  if (ntok < 0 || topk < 0 || n_experts < 1 || expert_stride < 0 || scale_stride < 0) return VQ_EINVAL;
+  if (n_experts > 1 && (expert_stride < rows * (cols / 8) * 3 || scale_stride < rows)) return VQ_EINVAL;
+  if (!idx || !scales || !codebooks || !x || !route || !y) return VQ_EINVAL;
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < vq_gemv_workspace_size(format, rows, cols, ntok, topk))
+    return VQ_EWORKSPACE;
+  if ((int64_t)ntok * topk >= 65536) return VQ_ERANGE;
+  GemvArgs a;
+  a.format = format;
+  a.idx = idx;
+  a.expert_stride = expert_stride;
+  a.scales = scales;
+  a.scale_stride = scale_stride;
+  a.codebooks = codebooks;
+  a.rows = rows;
+  a.cols = cols;
+  a.n_experts = n_experts;
+  a.x = x;
+  a.ntok = ntok;
+  a.topk = topk;
+  a.route = route;
+  a.y = y;
+  a.hdr = (WsHeader*)workspace;
+  a.partials = (float*)((char*)workspace + kHeader);
+  a.stream = (hipStream_t)stream;
+  if ((st = device_cus(&a.ncu)) != VQ_OK) return st;
+  return hip_status(launch_gemv(a));
+}
+
+int vq3r_dequant_gemv(const uint8_t* idx, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
+                      const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts, const uint16_t* x,
+                      int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  return vq_dequant_gemv(VQ_FMT_VQ3R, idx, expert_stride, scales, scale_stride, codebooks, rows, cols, n_experts, x,
+                         ntok, route, topk, y, workspace, ws_bytes, stream);
+}
+
+int vq4p_dequant_gemv(const uint8_t* idx, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
+                      const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts, const uint16_t* x,
+                      int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  return vq_dequant_gemv(VQ_FMT_VQ4P, idx, expert_stride, scales, scale_stride, codebooks, rows, cols, n_experts, x,
+                         ntok, route, topk, y, workspace, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------- error
+size_t vq_error_workspace_size(int format, int64_t n_mats, int64_t rows, int64_t cols) {
+  if (!fmt_ok(format) || n_mats < 1 || check_shape(rows, cols) != VQ_OK) return 0;
+  const int blocks = error_blocks(rows * (cols / 8), n_mats);
+  return align256(kHeader + sizeof(double) * (size_t)n_mats * blocks * (stages_of(format) + 1));
+}
+
+int vq_error(int format, const void* W, int dtype, const uint8_t* idx, const uint16_t* scales, const float* codebooks,
+             int64_t n_mats, int64_t rows, int64_t cols, double* sums, void* workspace, size_t ws_bytes,
+             void* stream) {
+  if (!fmt_ok(format) || !dtype_ok(dtype) || n_mats < 1) return VQ_EINVAL;
+  int st = check_shape(rows, cols);
+  if (st != VQ_OK) return st;
+  if (n_mats > 65535) return VQ_ERANGE;
+  if (!W || !idx || !scales || !codebooks || !sums || !aligned(W, 16)) return VQ_EINVAL;
+  const int blocks = error_blocks(rows * (cols / 8), n_mats);
+  const size_t need = align256(kHeader + sizeof(double) * (size_t)n_mats * blocks * (stages_of(format) + 1));
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < need) return VQ_EWORKSPACE;
+  ErrorArgs a;
+  a.format = format;
+  a.dtype = dtype;
+  a.W = W;
+  a.idx = idx;
+  a.scales = scales;
+  a.codebooks = codebooks;
+  a.n_mats = n_mats;
+  a.rows = rows;
+  a.cols = cols;
+  a.sums = sums;
+  a.partials = (double*)((char*)workspace + kHeader);
+  a.blocks = blocks;
+  a.hdr = (WsHeader*)workspace;
+  a.stream = (hipStream_t)stream;
+  return hip_status(launch_error(a));
+}
+
+// ---------------------------------------------------------------- MXFP4
+int vq_mxfp4_qdq(const void* W, int dtype, int64_t rows, int64_t cols, float* out, void* workspace, size_t ws_bytes,
+                 void* stream) {
+  if (!dtype_ok(dtype) || rows < 0 || cols <= 0 || cols % 32 != 0) return VQ_EINVAL;
+  if (!W || !out) return VQ_EINVAL;
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < kHeader) return VQ_EWORKSPACE;
+  Mxfp4Args a;
+  a.dtype = dtype;
+  a.W = W;
+  a.rows = rows;
+  a.cols = cols;
+  a.out = out;
+  a.hdr = (WsHeader*)workspace;
+  a.stream = (hipStream_t)stream;
+  int st;
+  if ((st = device_cus(&a.ncu)) != VQ_OK) return st;
+  return hip_status(launch_mxfp4(a));
+}
+
+}  // extern "C"

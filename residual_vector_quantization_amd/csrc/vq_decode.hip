@@ -1,0 +1,208 @@
+// Decode, reconstruction error and MXFP4 kernels.
+// [VQ3R page] = the page "3比特逼近4比特精度？WARP残差向量量化VQ3R的完整测量实验".
+#include "vq_launch.hpp"
+
+namespace vqk {
+
+// ------------------------------------------------------------------ decode
+// [VQ3R page] §2: w_hat = s * (((C1[i1] + C2[i2]) + C3[i3]) [+ C4[i4]]), summed
+// left to right in fp32, then one fp32 multiply. One thread per 8-dim vector;
+// the codebooks sit in LDS; each thread writes 32 contiguous bytes.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_decode(const uint8_t* idx, const uint16_t* scales, const float* cb_g,
+                                                uint32_t V, uint64_t nvec, int stages_used, float* out) {
+  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K;
+  __shared__ float cb[S][K][DIM];
+  for (int q = threadIdx.x; q < S * K * DIM; q += blockDim.x) (&cb[0][0][0])[q] = cb_g[q];
+  __syncthreads();
+  for (uint64_t vid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; vid < nvec;
+       vid += (uint64_t)gridDim.x * blockDim.x) {
+    const uint32_t row = (uint32_t)(vid / V);
+    const float s = f16_bits_to_f32(scales[row]);
+    const uint32_t word = load_record(idx + vid * 3);
+    float acc[8];
+    const float* c0 = cb[0][record_index<FMT>(word, 0)];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = c0[k];
+    for (int t = 1; t < stages_used; ++t) {
+      const float* c = cb[t][record_index<FMT>(word, t)];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = acc[k] + c[k];
+    }
+    float4* dst = reinterpret_cast<float4*>(out + vid * DIM);
+    dst[0] = make_float4(s * acc[0], s * acc[1], s * acc[2], s * acc[3]);
+    dst[1] = make_float4(s * acc[4], s * acc[5], s * acc[6], s * acc[7]);
+  }
+}
+
+hipError_t launch_decode(const DecodeArgs& a) {
+  const uint64_t V = (uint64_t)(a.cols / DIM), nvec = (uint64_t)a.rows * V;
+  if (nvec == 0) return hipSuccess;
+  uint64_t g = (nvec + 255) / 256;
+  const uint64_t gmax = (uint64_t)a.ncu * 8;
+  if (g > gmax) g = gmax;
+  if (a.format == 0)
+    k_decode<0><<<(unsigned)g, 256, 0, a.stream>>>(a.idx, a.scales, a.codebooks, (uint32_t)V, nvec, a.stages_used,
+                                                   a.out);
+  else
+    k_decode<1><<<(unsigned)g, 256, 0, a.stream>>>(a.idx, a.scales, a.codebooks, (uint32_t)V, nvec, a.stages_used,
+                                                   a.out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ error
+// [VQ3R page] §3.1: ||W - W_hat||_F / ||W||_F. Per matrix, fp64 sums of
+// (w - w_hat_t)^2 for the partial reconstructions after t = 1..S stages and of
+// w^2; block partials are reduced in a fixed order by k_error_reduce.
+template <int FMT, int DT>
+__global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx, const uint16_t* scales,
+                                               const float* cb_g, uint32_t V, uint64_t nvec_per_mat, int64_t cols,
+                                               double* partials, WsHeader* hdr) {
+  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K;
+  __shared__ float cb[S][K][DIM];
+  __shared__ double red[S + 1][256];
+  for (int q = threadIdx.x; q < S * K * DIM; q += blockDim.x) (&cb[0][0][0])[q] = cb_g[q];
+  __syncthreads();
+  const int m = blockIdx.y;
+  const size_t esz = DT == DT_F32 ? 4 : 2;
+  const uint8_t* idx_m = idx + (uint64_t)m * nvec_per_mat * 3;
+  const uint16_t* sc_m = scales + (uint64_t)m * (nvec_per_mat / V);
+  const char* W_m = (const char*)W + (uint64_t)m * nvec_per_mat * DIM * esz;
+  double acc[S + 1];
+#pragma unroll
+  for (int t = 0; t <= S; ++t) acc[t] = 0.0;
+  bool nonfinite = false;
+  for (uint64_t vid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; vid < nvec_per_mat;
+       vid += (uint64_t)gridDim.x * blockDim.x) {
+    const uint32_t row = (uint32_t)(vid / V), j = (uint32_t)(vid % V);
+    float w[8];
+    load_vec8<DT>(W_m + (uint64_t)row * cols * esz, j, w);
+    const float s = f16_bits_to_f32(sc_m[row]);
+    const uint32_t word = load_record(idx_m + vid * 3);
+    float part[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) part[k] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      const float* c = cb[t][record_index<FMT>(word, t)];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        part[k] = (t == 0) ? c[k] : part[k] + c[k];
+        const double d = (double)w[k] - (double)(s * part[k]);
+        acc[t] += d * d;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      nonfinite |= !__builtin_isfinite(w[k]);
+      acc[S] += (double)w[k] * (double)w[k];
+    }
+  }
+  if (nonfinite) flag_status(hdr, ST_NONFINITE);
+#pragma unroll
+  for (int t = 0; t <= S; ++t) red[t][threadIdx.x] = acc[t];
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o)
+#pragma unroll
+      for (int t = 0; t <= S; ++t) red[t][threadIdx.x] += red[t][threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x <= S) partials[((uint64_t)m * gridDim.x + blockIdx.x) * (S + 1) + threadIdx.x] = red[threadIdx.x][0];
+}
+
+__global__ void k_error_reduce(const double* partials, int blocks, int nv, int64_t n_mats, double* sums) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= n_mats * nv) return;
+  const int64_t m = q / nv, t = q % nv;
+  double s = 0.0;
+  for (int b = 0; b < blocks; ++b) s += partials[(m * blocks + b) * nv + t];
+  sums[q] = s;
+}
+
+template <int FMT, int DT>
+static hipError_t launch_error_t(const ErrorArgs& a) {
+  constexpr int S = Fmt<FMT>::S;
+  const uint64_t V = (uint64_t)(a.cols / DIM), nvec = (uint64_t)a.rows * V;
+  dim3 grid((unsigned)a.blocks, (unsigned)a.n_mats);
+  k_error<FMT, DT><<<grid, 256, 0, a.stream>>>(a.W, a.idx, a.scales, a.codebooks, (uint32_t)V, nvec, a.cols,
+                                               a.partials, a.hdr);
+  const int64_t nq = a.n_mats * (S + 1);
+  k_error_reduce<<<(unsigned)((nq + 255) / 256), 256, 0, a.stream>>>(a.partials, a.blocks, S + 1, a.n_mats, a.sums);
+  return hipGetLastError();
+}
+
+hipError_t launch_error(const ErrorArgs& a) {
+  hipError_t e0 = launch_reset(a.hdr, a.stream);
+  if (e0 != hipSuccess) return e0;
+  if (a.format == 0) {
+    if (a.dtype == DT_F32) return launch_error_t<0, DT_F32>(a);
+    if (a.dtype == DT_BF16) return launch_error_t<0, DT_BF16>(a);
+    return launch_error_t<0, DT_F16>(a);
+  }
+  if (a.dtype == DT_F32) return launch_error_t<1, DT_F32>(a);
+  if (a.dtype == DT_BF16) return launch_error_t<1, DT_BF16>(a);
+  return launch_error_t<1, DT_F16>(a);
+}
+
+// ------------------------------------------------------------------ MXFP4
+// [VQ3R page] §3.2 (K3 experts are MXFP4 at the source); the format is the
+// OCP Microscaling v1.0 definition: 32-element blocks along the row share the
+// E8M0 scale X = 2^(floor(log2 amax) - 2), clamped to [2^-127, 2^127]; elements
+// are E2M1(w / X), nearest with ties to the even code, saturated at 6.
+__device__ inline float e2m1_round(float a) {
+  float q = (a < 2.0f) ? __builtin_rintf(2.0f * a) * 0.5f
+                       : ((a < 4.0f) ? __builtin_rintf(a) : 2.0f * __builtin_rintf(0.5f * a));
+  return fminf(q, 6.0f);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_mxfp4(const void* W, uint64_t nblk, float* out, WsHeader* hdr) {
+  // 32 lanes per block of 32 elements (two blocks per wave)
+  const int lane = threadIdx.x & 31;
+  const uint64_t b0 = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) / 32;
+  const uint64_t stride = ((uint64_t)gridDim.x * blockDim.x) / 32;
+  for (uint64_t b = b0; b < nblk; b += stride) {  // b is uniform across each 32-lane group
+    const uint64_t e = b * 32 + lane;
+    float w = 0.0f;
+    {
+      if constexpr (DT == DT_F32) w = static_cast<const float*>(W)[e];
+      else if constexpr (DT == DT_BF16) w = __uint_as_float((uint32_t)static_cast<const uint16_t*>(W)[e] << 16);
+      else w = f16_bits_to_f32(static_cast<const uint16_t*>(W)[e]);
+    }
+    if (!__builtin_isfinite(w)) {
+      flag_status(hdr, ST_NONFINITE);
+      w = 0.0f;
+    }
+    float amax = __builtin_fabsf(w);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+    float r = 0.0f;
+    if (amax > 0.0f) {
+      int ex;
+      frexpf(amax, &ex);  // floor(log2 amax) = ex - 1
+      int xe = ex - 1 - 2;
+      xe = xe < -127 ? -127 : (xe > 127 ? 127 : xe);
+      const float X = ldexpf(1.0f, xe);
+      const float v = __fdiv_rn(w, X);
+      const float q = e2m1_round(__builtin_fabsf(v));
+      r = X * (v < 0.0f ? -q : q);
+    }
+    out[e] = r;
+  }
+}
+
+hipError_t launch_mxfp4(const Mxfp4Args& a) {
+  hipError_t e0 = launch_reset(a.hdr, a.stream);
+  if (e0 != hipSuccess) return e0;
+  const uint64_t nblk = (uint64_t)a.rows * (uint64_t)(a.cols / 32);
+  if (nblk == 0) return hipGetLastError();
+  uint64_t g = (nblk * 32 + 255) / 256;
+  if (g > (uint64_t)a.ncu * 16) g = (uint64_t)a.ncu * 16;
+  if (a.dtype == DT_F32) k_mxfp4<DT_F32><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
+  else if (a.dtype == DT_BF16) k_mxfp4<DT_BF16><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
+  else k_mxfp4<DT_F16><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
+  return hipGetLastError();
+}
+
+}  // namespace vqk

@@ -1,0 +1,465 @@
+// Encoder and Lloyd-fit kernels ([VQ3R page] §2 and §4: greedy residual
+// encode through the stages, Lloyd k-means codebook fit on sampled experts).
+// [VQ3R page] = the page "3比特逼近4比特精度？WARP残差向量量化VQ3R的完整测量实验".
+#include "vq_launch.hpp"
+#include "vq_score.hpp"
+
+namespace vqk {
+
+// ------------------------------------------------------------------ utility
+__global__ void k_reset_header(WsHeader* h, int keep_flags) {
+  if (threadIdx.x == 0) {
+    if (!keep_flags) h->flags = 0;
+    h->n_flag[0] = 0;
+    h->n_flag[1] = 0;
+    h->maxabs_bits[0] = 0;
+    h->maxabs_bits[1] = 0;
+    h->fbits = 0;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_row_scales(const void* W, int64_t rows, int64_t cols, uint16_t* scales,
+                                                    WsHeader* hdr) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t esz = DT == DT_F32 ? 4 : 2;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < rows; row += (int64_t)gridDim.x * 4) {
+    uint32_t bad;
+    uint16_t sb = wave_row_scale<DT>((const char*)W + row * cols * esz, cols, lane, &bad);
+    if (lane == 0) {
+      if (bad) flag_status(hdr, bad);
+      scales[row] = sb;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ encode
+// One wave per row: the row scale, then groups of 32 vectors through all
+// stages. Certified vectors get their final record; the others are queued for
+// the exact pass (k_encode_exact).
+template <int FMT, int ENG, int DT>
+__global__ __launch_bounds__(256, 2) void k_encode(const void* W, int64_t rows, int64_t cols, const float* cb_g,
+                                                   uint8_t* idx, uint16_t* scales, WsHeader* hdr, uint32_t* list,
+                                                   uint32_t cap) {
+  constexpr int S = Fmt<FMT>::S;
+  __shared__ SearchLds<FMT, ENG, S> L;
+  build_tables<FMT, ENG, S>(L, cb_g, hdr);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, jl = lane & 31;
+  const int64_t V = cols / DIM;
+  const size_t esz = DT == DT_F32 ? 4 : 2;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < rows; row += (int64_t)gridDim.x * 4) {
+    const void* wrow = (const char*)W + row * cols * esz;
+    uint32_t bad;
+    const uint16_t sb = wave_row_scale<DT>(wrow, cols, lane, &bad);
+    if (lane == 0) {
+      scales[row] = sb;
+      if (bad) flag_status(hdr, bad);
+    }
+    if (bad) continue;
+    const float s = f16_bits_to_f32(sb);
+    for (int64_t g = 0; g < V; g += 32) {
+      const int64_t j = g + jl;
+      const bool valid = j < V;
+      float r[8];
+      if (valid) {
+        load_vec8<DT>(wrow, j, r);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) r[k] = normalize(r[k], s);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) r[k] = 0.0f;
+      }
+      uint32_t word = 0;
+      bool fl = false;
+#pragma unroll 1
+      for (int t = 0; t < S; ++t)
+        word |= (uint32_t)search_stage<FMT, ENG, S>(L, t, r, lane, fl) << (t * Fmt<FMT>::BITS);
+      const uint64_t vid = (uint64_t)row * V + j;
+      if (valid && h == 0) store_record(idx + vid * 3, word);
+      append_flags(fl && valid && h == 0, (uint32_t)vid, &hdr->n_flag[0], list, cap, lane);
+    }
+  }
+}
+
+// Exact pass: every queued vector (or every vector when `all` is set or the
+// queue overflowed) is re-encoded with the exhaustive fp32 search, one vector
+// per thread, codebooks in LDS read in lockstep (broadcast).
+template <int FMT, int DT>
+__global__ __launch_bounds__(256) void k_encode_exact(const void* W, int64_t rows, int64_t cols, const float* cb_g,
+                                                      uint8_t* idx, const uint16_t* scales, WsHeader* hdr,
+                                                      const uint32_t* list, uint32_t cap, int all) {
+  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K;
+  __shared__ float cb[S][K][DIM];
+  const uint64_t V = (uint64_t)(cols / DIM), nvec = (uint64_t)rows * V;
+  const uint32_t n = hdr->n_flag[0];
+  const bool full = all || n > cap;
+  const uint64_t total = full ? nvec : n;
+  if ((uint64_t)blockIdx.x * blockDim.x >= total) return;
+  if (full && !all && blockIdx.x == 0 && threadIdx.x == 0) flag_status(hdr, ST_LIST_OVERFLOW);
+  for (int q = threadIdx.x; q < S * K * DIM; q += blockDim.x) (&cb[0][0][0])[q] = cb_g[q];
+  __syncthreads();
+  const size_t esz = DT == DT_F32 ? 4 : 2;
+  for (uint64_t q = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+       q += (uint64_t)gridDim.x * blockDim.x) {
+    const uint64_t vid = full ? q : list[q];
+    const uint64_t row = vid / V, j = vid % V;
+    const float s = f16_bits_to_f32(scales[row]);
+    float r[8];
+    load_vec8<DT>((const char*)W + row * (uint64_t)cols * esz, (int64_t)j, r);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r[k] = normalize(r[k], s);
+    int out[S];
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      const int w = exact_argmin<K>(r, &cb[t][0][0]);
+      out[t] = w;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) r[k] = r[k] - cb[t][w][k];
+    }
+    store_record(idx + vid * 3, record_word<FMT>(out));
+  }
+}
+
+// ------------------------------------------------------------------ Lloyd fit
+// Training set: R[N][8] fp32, the row-normalized vectors of the sampled
+// matrices (matrix, row, vector order). Stage t runs Lloyd on R_t and leaves
+// the residual R_{t+1} = R_t - C_t[a] in the other buffer.
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_fit_prepare(const void* W, int64_t rows, int64_t cols, float* R,
+                                                     WsHeader* hdr) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t V = cols / DIM;
+  const size_t esz = DT == DT_F32 ? 4 : 2;
+  uint32_t mx = 0;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < rows; row += (int64_t)gridDim.x * 4) {
+    const void* wrow = (const char*)W + row * cols * esz;
+    uint32_t bad;
+    const uint16_t sb = wave_row_scale<DT>(wrow, cols, lane, &bad);
+    if (bad) {
+      if (lane == 0) flag_status(hdr, bad);
+      continue;
+    }
+    const float s = f16_bits_to_f32(sb);
+    for (int64_t j = lane; j < V; j += WAVE) {
+      float v[8];
+      load_vec8<DT>(wrow, j, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        v[k] = normalize(v[k], s);
+        mx = max(mx, __float_as_uint(__builtin_fabsf(v[k])));
+      }
+      float4* dst = reinterpret_cast<float4*>(R + (row * V + j) * DIM);
+      dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+      dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  if (lane == 0 && mx) atomicMax(&hdr->maxabs_bits[0], mx);
+}
+
+// Stage start: initial centroids C_t[k] = R_t[init[k]], fixed-point fraction
+// bits F = 62 - e - ceil(log2 N) (max|R_t| < 2^e), counter resets.
+template <int FMT>
+__global__ void k_stage_begin(const float* R, const int64_t* init, float* C, WsHeader* hdr, int cur, int clog2n) {
+  constexpr int K = Fmt<FMT>::K;
+  for (int q = threadIdx.x; q < K * DIM; q += blockDim.x) C[q] = R[init[q / DIM] * DIM + (q % DIM)];
+  if (threadIdx.x == 0) {
+    const float mx = __uint_as_float(hdr->maxabs_bits[cur]);
+    int e = 0;
+    if (mx > 0.0f) frexpf(mx, &e);
+    int F = 62 - e - clog2n;
+    if (F < 16) {
+      flag_status(hdr, ST_FIXED_POINT);
+      F = 16;
+    }
+    hdr->fbits = F;
+    hdr->n_flag[0] = 0;
+    hdr->n_flag[1] = 0;
+    hdr->maxabs_bits[cur ^ 1] = 0;
+  }
+}
+
+template <int K>
+struct FitAccum {
+  unsigned long long sum[K][DIM + 1];  // int64 fixed-point sums (two's complement) and counts
+};
+
+template <int K>
+__device__ inline void accum_vector(FitAccum<K>& A, int w, const float r[8], int F, int k0, int k1, bool count) {
+  for (int k = k0; k < k1; ++k)
+    atomicAdd(&A.sum[w][k], (unsigned long long)__double2ll_rn(ldexp((double)r[k], F)));
+  if (count) atomicAdd(&A.sum[w][DIM], 1ull);
+}
+
+template <int K>
+__device__ inline void flush_accum(FitAccum<K>& A, long long* partials, int slot) {
+  __syncthreads();
+  long long* dst = partials + (size_t)slot * K * (DIM + 1);
+  for (int q = threadIdx.x; q < K * (DIM + 1); q += blockDim.x) dst[q] = (long long)(&A.sum[0][0])[q];
+}
+
+// Assignment pass over R_cur. MODE 0 (iteration): certified vectors add their
+// fixed-point coordinates to the block's cluster sums. MODE 1 (after the last
+// update): certified vectors write their residual to R_next. Vectors that fail
+// certification are queued for k_assign_exact.
+template <int FMT, int ENG, int MODE>
+__global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_next, int64_t n, const float* C,
+                                                   WsHeader* hdr, uint32_t* list, uint32_t cap,
+                                                   long long* partials, int parity, int nxt) {
+  constexpr int K = Fmt<FMT>::K;
+  __shared__ SearchLds<FMT, ENG, 1> L;
+  __shared__ FitAccum<K> A;
+  if (MODE == 0)
+    for (int q = threadIdx.x; q < K * (DIM + 1); q += blockDim.x) (&A.sum[0][0])[q] = 0ull;
+  build_tables<FMT, ENG, 1>(L, C, hdr);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, jl = lane & 31;
+  const int F = hdr->fbits;
+  uint32_t mx = 0;
+  const int64_t ngroups = (n + 31) / 32;
+  for (int64_t g = (int64_t)blockIdx.x * 4 + wave; g < ngroups; g += (int64_t)gridDim.x * 4) {
+    const int64_t j = g * 32 + jl;
+    const bool valid = j < n;
+    float r[8], r0[8];
+    if (valid) {
+      const float4* p = reinterpret_cast<const float4*>(R_cur + j * DIM);
+      float4 a = p[0], b = p[1];
+      r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w; r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) r[k] = 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r0[k] = r[k];
+    bool fl = false;
+    const int w = search_stage<FMT, ENG, 1>(L, 0, r, lane, fl);
+    const bool ok = valid && !fl;
+    if (MODE == 0) {
+      if (ok) accum_vector<K>(A, w, r0, F, 4 * h, 4 * h + 4, h == 0);
+    } else {
+      if (ok) {
+        float4* dst = reinterpret_cast<float4*>(R_next + j * DIM);
+        if (h == 0) dst[0] = make_float4(r[0], r[1], r[2], r[3]);
+        else dst[1] = make_float4(r[4], r[5], r[6], r[7]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) mx = max(mx, __float_as_uint(__builtin_fabsf(r[k])));
+      }
+    }
+    append_flags(fl && valid && h == 0, (uint32_t)j, &hdr->n_flag[parity], list, cap, lane);
+  }
+  if (MODE == 0) {
+    flush_accum<K>(A, partials, blockIdx.x);
+  } else {
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    if (lane == 0 && mx) atomicMax(&hdr->maxabs_bits[nxt], mx);
+  }
+}
+
+// Exact assignment of the queued vectors (or of all vectors when the queue
+// overflowed), one vector per thread. MODE 0 accumulates into this block's own
+// partial slot (slot_base + block); MODE 1 writes residuals.
+template <int FMT, int MODE>
+__global__ __launch_bounds__(256) void k_assign_exact(const float* R_cur, float* R_next, int64_t n, const float* C,
+                                                      WsHeader* hdr, const uint32_t* list, uint32_t cap,
+                                                      long long* partials, int slot_base, int parity, int nxt) {
+  constexpr int K = Fmt<FMT>::K;
+  __shared__ float cb[K][DIM];
+  __shared__ FitAccum<K> A;
+  const uint32_t nf = hdr->n_flag[parity];
+  const bool full = nf > cap;
+  const uint64_t total = full ? (uint64_t)n : nf;
+  if (MODE == 0)
+    for (int q = threadIdx.x; q < K * (DIM + 1); q += blockDim.x) (&A.sum[0][0])[q] = 0ull;
+  for (int q = threadIdx.x; q < K * DIM; q += blockDim.x) (&cb[0][0])[q] = C[q];
+  if (full && blockIdx.x == 0 && threadIdx.x == 0) flag_status(hdr, ST_LIST_OVERFLOW);
+  __syncthreads();
+  const int F = hdr->fbits;
+  uint32_t mx = 0;
+  for (uint64_t q = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+       q += (uint64_t)gridDim.x * blockDim.x) {
+    const uint64_t j = full ? q : list[q];
+    float r[8];
+    const float4* p = reinterpret_cast<const float4*>(R_cur + j * DIM);
+    float4 a = p[0], b = p[1];
+    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w; r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+    const int w = exact_argmin<K>(r, &cb[0][0]);
+    if (MODE == 0) {
+      accum_vector<K>(A, w, r, F, 0, DIM, true);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        r[k] = r[k] - cb[w][k];
+        mx = max(mx, __float_as_uint(__builtin_fabsf(r[k])));
+      }
+      float4* dst = reinterpret_cast<float4*>(R_next + j * DIM);
+      dst[0] = make_float4(r[0], r[1], r[2], r[3]);
+      dst[1] = make_float4(r[4], r[5], r[6], r[7]);
+    }
+  }
+  if (MODE == 0) {
+    flush_accum<K>(A, partials, slot_base + blockIdx.x);
+  } else {
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    if ((threadIdx.x & 63) == 0 && mx) atomicMax(&hdr->maxabs_bits[nxt], mx);
+  }
+}
+
+// Centroid update, one block per cluster: exact int64 sums over all partial
+// slots (the first n_assign slots are skipped when the exact pass covered
+// every vector), then c = (float)(((double)S * 2^-F) / n); empty clusters keep
+// their centroid. Block 0 also clears the other parity's queue counter.
+template <int FMT>
+__global__ __launch_bounds__(64) void k_update(float* C, const long long* partials, int n_assign, int n_slots,
+                                               WsHeader* hdr, int parity, uint32_t cap) {
+  constexpr int K = Fmt<FMT>::K;
+  __shared__ long long red[64][DIM + 1];
+  const int j = blockIdx.x;
+  const bool full = hdr->n_flag[parity] > cap;
+  const int s0 = full ? n_assign : 0;
+  long long acc[DIM + 1];
+#pragma unroll
+  for (int k = 0; k <= DIM; ++k) acc[k] = 0;
+  for (int s = s0 + threadIdx.x; s < n_slots; s += 64) {
+    const long long* p = partials + ((size_t)s * K + j) * (DIM + 1);
+#pragma unroll
+    for (int k = 0; k <= DIM; ++k) acc[k] += p[k];
+  }
+#pragma unroll
+  for (int k = 0; k <= DIM; ++k) red[threadIdx.x][k] = acc[k];
+  __syncthreads();
+  if (threadIdx.x < DIM) {
+    long long S = 0, cnt = 0;
+    for (int q = 0; q < 64; ++q) {
+      S += red[q][threadIdx.x];
+      cnt += red[q][DIM];
+    }
+    if (cnt > 0) {
+      const double m = __ddiv_rn(ldexp(__ll2double_rn(S), -hdr->fbits), __ll2double_rn(cnt));
+      C[j * DIM + threadIdx.x] = __double2float_rn(m);
+    }
+  }
+  if (j == 0 && threadIdx.x == 0) hdr->n_flag[parity ^ 1] = 0;
+}
+
+// ------------------------------------------------------------------ launchers
+static int grid_rows(int64_t rows, int ncu, int per_cu) {
+  int64_t g = (rows + 3) / 4;
+  int64_t m = (int64_t)ncu * per_cu;
+  return (int)(g < m ? (g < 1 ? 1 : g) : m);
+}
+
+template <int FMT, int ENG, int DT>
+static hipError_t launch_encode_t(const EncodeArgs& a) {
+  const int g = grid_rows(a.rows, a.ncu, 2);
+  k_encode<FMT, ENG, DT><<<g, 256, 0, a.stream>>>(a.W, a.rows, a.cols, a.codebooks, a.idx, a.scales, a.hdr,
+                                                  a.list, a.cap);
+  return hipGetLastError();
+}
+
+template <int FMT, int DT>
+static hipError_t launch_encode_dt(const EncodeArgs& a) {
+  hipError_t e = hipSuccess;
+  k_reset_header<<<1, 64, 0, a.stream>>>(a.hdr, 0);
+  const uint64_t nvec = (uint64_t)a.rows * (a.cols / DIM);
+  if (a.engine == ENGINE_EXACT) {
+    k_row_scales<DT><<<grid_rows(a.rows, a.ncu, 4), 256, 0, a.stream>>>(a.W, a.rows, a.cols, a.scales, a.hdr);
+  } else if (a.engine == ENG_F32) {
+    e = launch_encode_t<FMT, ENG_F32, DT>(a);
+  } else if (a.engine == ENG_VALU) {
+    e = launch_encode_t<FMT, ENG_VALU, DT>(a);
+  } else {
+    e = launch_encode_t<FMT, ENG_F16X, DT>(a);
+  }
+  if (e != hipSuccess) return e;
+  uint64_t gx = (nvec + 256 * 8 - 1) / (256 * 8);
+  const uint64_t gmax = (uint64_t)a.ncu * 4;
+  if (a.engine == ENGINE_EXACT) {
+    gx = (nvec + 255) / 256;
+    if (gx > (uint64_t)a.ncu * 16) gx = (uint64_t)a.ncu * 16;
+  } else if (gx > gmax) {
+    gx = gmax;
+  }
+  if (gx < 1) gx = 1;
+  k_encode_exact<FMT, DT><<<(unsigned)gx, 256, 0, a.stream>>>(a.W, a.rows, a.cols, a.codebooks, a.idx, a.scales,
+                                                              a.hdr, a.list, a.cap, a.engine == ENGINE_EXACT);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode(const EncodeArgs& a) {
+  if (a.format == 0) {
+    if (a.dtype == DT_F32) return launch_encode_dt<0, DT_F32>(a);
+    if (a.dtype == DT_BF16) return launch_encode_dt<0, DT_BF16>(a);
+    return launch_encode_dt<0, DT_F16>(a);
+  }
+  if (a.dtype == DT_F32) return launch_encode_dt<1, DT_F32>(a);
+  if (a.dtype == DT_BF16) return launch_encode_dt<1, DT_BF16>(a);
+  return launch_encode_dt<1, DT_F16>(a);
+}
+
+template <int FMT, int ENG>
+static hipError_t fit_stage_iters(const FitArgs& a, int t, const float* Rc, float* Rn, float* C, int cur) {
+  constexpr int K = Fmt<FMT>::K;
+  const int ga = a.n_assign_blocks, gf = a.n_exact_blocks;
+  for (int it = 0; it <= a.iters; ++it) {
+    const int parity = it & 1;
+    if (it < a.iters) {
+      k_assign<FMT, ENG, 0><<<ga, 256, 0, a.stream>>>(Rc, Rn, a.n, C, a.hdr, a.list, a.cap, a.partials, parity,
+                                                      cur ^ 1);
+      k_assign_exact<FMT, 0><<<gf, 256, 0, a.stream>>>(Rc, Rn, a.n, C, a.hdr, a.list, a.cap, a.partials, ga, parity,
+                                                       cur ^ 1);
+      k_update<FMT><<<K, 64, 0, a.stream>>>(C, a.partials, ga, ga + gf, a.hdr, parity, a.cap);
+    } else {
+      k_assign<FMT, ENG, 1><<<ga, 256, 0, a.stream>>>(Rc, Rn, a.n, C, a.hdr, a.list, a.cap, a.partials, parity,
+                                                      cur ^ 1);
+      k_assign_exact<FMT, 1><<<gf, 256, 0, a.stream>>>(Rc, Rn, a.n, C, a.hdr, a.list, a.cap, a.partials, ga, parity,
+                                                       cur ^ 1);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  (void)t;
+  return hipSuccess;
+}
+
+template <int FMT, int DT>
+static hipError_t launch_fit_t(const FitArgs& a) {
+  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K;
+  k_reset_header<<<1, 64, 0, a.stream>>>(a.hdr, 0);
+  const int64_t per = a.rows * (a.cols / DIM);
+  for (int64_t m = 0; m < a.n_mats; ++m) {
+    k_fit_prepare<DT><<<grid_rows(a.rows, a.ncu, 4), 256, 0, a.stream>>>(a.mats[m], a.rows, a.cols,
+                                                                         a.R[0] + m * per * DIM, a.hdr);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  for (int t = 0; t < S; ++t) {
+    const int cur = t & 1;
+    float* C = a.codebooks + (size_t)t * K * DIM;
+    k_stage_begin<FMT><<<1, 256, 0, a.stream>>>(a.R[cur], a.init + (size_t)t * K, C, a.hdr, cur, a.clog2n);
+    if (a.engine == ENG_F32) e = fit_stage_iters<FMT, ENG_F32>(a, t, a.R[cur], a.R[cur ^ 1], C, cur);
+    else if (a.engine == ENG_VALU) e = fit_stage_iters<FMT, ENG_VALU>(a, t, a.R[cur], a.R[cur ^ 1], C, cur);
+    else e = fit_stage_iters<FMT, ENG_F16X>(a, t, a.R[cur], a.R[cur ^ 1], C, cur);
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fit(const FitArgs& a) {
+  if (a.format == 0) {
+    if (a.dtype == DT_F32) return launch_fit_t<0, DT_F32>(a);
+    if (a.dtype == DT_BF16) return launch_fit_t<0, DT_BF16>(a);
+    return launch_fit_t<0, DT_F16>(a);
+  }
+  if (a.dtype == DT_F32) return launch_fit_t<1, DT_F32>(a);
+  if (a.dtype == DT_BF16) return launch_fit_t<1, DT_BF16>(a);
+  return launch_fit_t<1, DT_F16>(a);
+}
+
+hipError_t launch_reset(WsHeader* hdr, hipStream_t s) {
+  k_reset_header<<<1, 64, 0, s>>>(hdr, 0);
+  return hipGetLastError();
+}
+
+}  // namespace vqk

@@ -1,0 +1,109 @@
+// Host-side launch interface between the C ABI (vq_api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vq_device.hpp"
+
+namespace vqk {
+
+enum { ENGINE_AUTO = 0, ENGINE_F16X = 1, ENGINE_F32 = 2, ENGINE_VALU = 3, ENGINE_EXACT = 4 };
+
+struct EncodeArgs {
+  int format, engine, dtype;
+  const void* W;
+  int64_t rows, cols;
+  const float* codebooks;
+  uint8_t* idx;
+  uint16_t* scales;
+  WsHeader* hdr;
+  uint32_t* list;
+  uint32_t cap;
+  int ncu;
+  hipStream_t stream;
+};
+
+struct FitArgs {
+  int format, engine, dtype;
+  const void* const* mats;  // host array of device pointers
+  int64_t n_mats, rows, cols, n;
+  int iters, clog2n;
+  const int64_t* init;      // device copy, [stages][K]
+  float* codebooks;
+  WsHeader* hdr;
+  float* R[2];
+  uint32_t* list;
+  uint32_t cap;
+  long long* partials;
+  int n_assign_blocks, n_exact_blocks;
+  int ncu;
+  hipStream_t stream;
+};
+
+struct DecodeArgs {
+  int format, stages_used;
+  const uint8_t* idx;
+  const uint16_t* scales;
+  const float* codebooks;
+  int64_t rows, cols;
+  float* out;
+  int ncu;
+  hipStream_t stream;
+};
+
+struct ErrorArgs {
+  int format, dtype;
+  const void* W;
+  const uint8_t* idx;
+  const uint16_t* scales;
+  const float* codebooks;
+  int64_t n_mats, rows, cols;
+  double* sums;
+  double* partials;  // [n_mats][blocks][stages+1]
+  int blocks;
+  WsHeader* hdr;
+  hipStream_t stream;
+};
+
+struct GemvArgs {
+  int format;
+  const uint8_t* idx;
+  int64_t expert_stride;
+  const uint16_t* scales;
+  int64_t scale_stride;
+  const float* codebooks;
+  int64_t rows, cols;
+  int n_experts;
+  const uint16_t* x;
+  int ntok, topk;
+  const int32_t* route;
+  float* y;
+  float* partials;  // [ntok*topk][nblk][rows]
+  WsHeader* hdr;
+  int ncu;
+  hipStream_t stream;
+};
+
+struct Mxfp4Args {
+  int dtype;
+  const void* W;
+  int64_t rows, cols;
+  float* out;
+  WsHeader* hdr;
+  int ncu;
+  hipStream_t stream;
+};
+
+// GEMV tiling shared by the kernel and the workspace size query.
+constexpr int GEMV_SLICES = 32;  // 8-dim column slices per block (256 columns)
+inline int64_t gemv_nblk(int64_t cols) { return (cols / 8 + GEMV_SLICES - 1) / GEMV_SLICES; }
+
+hipError_t launch_reset(WsHeader* hdr, hipStream_t s);
+hipError_t launch_encode(const EncodeArgs& a);
+hipError_t launch_fit(const FitArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_error(const ErrorArgs& a);
+hipError_t launch_gemv(const GemvArgs& a);
+hipError_t launch_mxfp4(const Mxfp4Args& a);
+
+}  // namespace vqk

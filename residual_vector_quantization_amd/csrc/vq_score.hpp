@@ -1,0 +1,232 @@
+// Nearest-codeword search for 32 vectors at a time on one wave (gfx950):
+// approximate scores from one of three engines, a lane-local top-2 with the
+// candidate index packed into each score, a merge of the two half-waves and
+// the certification test of vq_device.hpp.
+//
+// Lane layout (shared by all engines): lane = 32*h + j holds the full 8-dim
+// residual of vector j of the group; its candidates are the codewords
+//   i = 32*tile + 8*(v/4) + 4*h + (v%4),  tile < K/32, v < 16,
+// which is exactly the accumulator layout of the 32x32 MFMA instructions with
+// codewords on M and vectors on N. Lane-local candidate id = 16*tile + v.
+#pragma once
+#include "vq_device.hpp"
+
+namespace vqk {
+
+enum { ENG_F16X = 1, ENG_F32 = 2, ENG_VALU = 3 };
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+// Per-stage engine tables in LDS.
+template <int K, int ENG> struct Tables;
+template <int K> struct Tables<K, ENG_F16X> {
+  // hi = fp16(c), lo = fp16(c - hi), nrm = {fp16(n'), fp16(n' - fp16(n')), 0...}
+  // with n' = ||c||^2 * 2^-sigma (the matrix-core operands of the split scheme)
+  h8 hi[K];
+  h8 lo[K];
+  h8 nrm[K];
+};
+template <int K> struct Tables<K, ENG_F32> {
+  float a[5][2][K];  // step s < 4: c_i[2s + half]; step 4: half 0 = ||c_i||^2, half 1 = 0
+};
+template <int K> struct Tables<K, ENG_VALU> {
+  float norm[K];     // ||c_i||^2
+};
+
+template <int FMT, int ENG, int NST>
+struct SearchLds {
+  static constexpr int K = Fmt<FMT>::K;
+  float cb[NST][K][DIM];       // fp32 codebooks: exact distances, residual updates
+  Tables<K, ENG> tab[NST];
+  float sig[NST];              // 2^sigma of the norm term (F16X)
+  uint32_t nmax_bits[NST];
+};
+
+// Builds the tables of stages [0, NST) from global fp32 codebooks
+// cb_g[NST][K][8] (all threads of the block take part; ends with a barrier).
+template <int FMT, int ENG, int NST>
+__device__ inline void build_tables(SearchLds<FMT, ENG, NST>& L, const float* cb_g, WsHeader* hdr) {
+  constexpr int K = Fmt<FMT>::K;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (tid < NST) L.nmax_bits[tid] = 0u;
+  __syncthreads();
+  bool bad = false;
+  for (int q = tid; q < NST * K; q += nt) {
+    const int t = q / K, i = q % K;
+    const float4* src = reinterpret_cast<const float4*>(cb_g + (size_t)q * DIM);
+    float4 a = src[0], b = src[1];
+    float c[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    double n = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      L.cb[t][i][k] = c[k];
+      bad |= !(__builtin_fabsf(c[k]) <= 2048.0f);  // also catches NaN
+      n += (double)c[k] * (double)c[k];
+    }
+    float nf = __double2float_rn(n);
+    if constexpr (ENG == ENG_F32) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        L.tab[t].a[s][0][i] = c[2 * s];
+        L.tab[t].a[s][1][i] = c[2 * s + 1];
+      }
+      L.tab[t].a[4][0][i] = nf;
+      L.tab[t].a[4][1][i] = 0.0f;
+    } else if constexpr (ENG == ENG_VALU) {
+      L.tab[t].norm[i] = nf;
+    } else {
+      atomicMax(&L.nmax_bits[t], __float_as_uint(nf));
+      h8 hi, lo;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        _Float16 x = (_Float16)c[k];
+        hi[k] = x;
+        lo[k] = (_Float16)(c[k] - (float)x);
+      }
+      L.tab[t].hi[i] = hi;
+      L.tab[t].lo[i] = lo;
+    }
+  }
+  if (bad) flag_status(hdr, ST_CODEBOOK_RANGE);
+  __syncthreads();
+  if constexpr (ENG == ENG_F16X) {
+    // sigma keeps n * 2^-sigma below 2^14, inside the fp16 range
+    if (tid < NST) {
+      int e = 0;
+      frexpf(__uint_as_float(L.nmax_bits[tid]), &e);  // nmax < 2^e
+      int sg = e > 14 ? e - 14 : 0;
+      L.sig[tid] = ldexpf(1.0f, sg);
+    }
+    __syncthreads();
+    for (int q = tid; q < NST * K; q += nt) {
+      const int t = q / K, i = q % K;
+      double n = 0.0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) n += (double)L.cb[t][i][k] * (double)L.cb[t][i][k];
+      float ns = __double2float_rn(n) / L.sig[t];  // exact: division by a power of two
+      _Float16 nh = (_Float16)ns;
+      h8 v = {};
+      v[0] = nh;
+      v[1] = (_Float16)(ns - (float)nh);
+      L.tab[t].nrm[i] = v;
+    }
+    __syncthreads();
+  }
+}
+
+// Lane-local top-2 of the packed approximate scores for stage t.
+template <int FMT, int ENG, int NST>
+__device__ inline void lane_top2(const SearchLds<FMT, ENG, NST>& L, int t, const float r[8], int lane,
+                                 float& m1, float& m2) {
+  constexpr int TILES = Fmt<FMT>::TILES, PACK = Fmt<FMT>::PACK;
+  const int h = lane >> 5, i = lane & 31;
+  m1 = __builtin_inff();
+  m2 = __builtin_inff();
+  if constexpr (ENG == ENG_F16X) {
+    h8 b0, b1;
+    const _Float16 m2h = (_Float16)(-2.0f);
+    const _Float16 sg = (_Float16)L.sig[t];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      _Float16 x = (_Float16)r[k];
+      _Float16 y = (_Float16)(r[k] - (float)x);
+      b0[k] = x * m2h;
+      b1[k] = h ? (k < 2 ? sg : (_Float16)0.0f) : y * m2h;
+    }
+    const h8* pa0 = h ? L.tab[t].lo : L.tab[t].hi;
+    const h8* pa1 = h ? L.tab[t].nrm : L.tab[t].hi;
+#pragma unroll
+    for (int tile = 0; tile < TILES; ++tile) {
+      f16v acc = {};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa0[tile * 32 + i], b0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa1[tile * 32 + i], b1, acc, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 16; v += 2)
+        top2_pair(m1, m2, pack_score<PACK>(acc[v], tile * 16 + v), pack_score<PACK>(acc[v + 1], tile * 16 + v + 1));
+    }
+  } else if constexpr (ENG == ENG_F32) {
+    float b[5];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b[s] = -2.0f * r[2 * s + h];
+    b[4] = h ? 0.0f : 1.0f;
+#pragma unroll
+    for (int tile = 0; tile < TILES; ++tile) {
+      f16v acc = {};
+#pragma unroll
+      for (int s = 0; s < 5; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(L.tab[t].a[s][h][tile * 32 + i], b[s], acc, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 16; v += 2)
+        top2_pair(m1, m2, pack_score<PACK>(acc[v], tile * 16 + v), pack_score<PACK>(acc[v + 1], tile * 16 + v + 1));
+    }
+  } else {
+    float nr[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) nr[k] = -2.0f * r[k];
+#pragma unroll 2
+    for (int tile = 0; tile < TILES; ++tile) {
+      float acc[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int ci = tile * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        const float* c = L.cb[t][ci];
+        float s = L.tab[t].norm[ci];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s = __builtin_fmaf(nr[k], c[k], s);
+        acc[v] = s;
+      }
+#pragma unroll
+      for (int v = 0; v < 16; v += 2)
+        top2_pair(m1, m2, pack_score<PACK>(acc[v], tile * 16 + v), pack_score<PACK>(acc[v + 1], tile * 16 + v + 1));
+    }
+  }
+}
+
+// Full stage: approximate search, merge of the half-waves, exact distance to
+// the winner, certification and residual update. Returns the winner index.
+template <int FMT, int ENG, int NST>
+__device__ inline int search_stage(const SearchLds<FMT, ENG, NST>& L, int t, float r[8], int lane, bool& flag) {
+  constexpr int PACK = Fmt<FMT>::PACK;
+  float m1, m2;
+  lane_top2<FMT, ENG, NST>(L, t, r, lane, m1, m2);
+  const int h = lane >> 5;
+  const float o1 = __shfl_xor(m1, 32);
+  const float o2 = __shfl_xor(m2, 32);
+  const float p1 = fmin2(m1, o1);
+  const float p2 = fmin2(__builtin_fmaxf(m1, o1), fmin2(m2, o2));
+  const uint32_t half0 = __float_as_uint(h ? o1 : m1);
+  const uint32_t pb = __float_as_uint(p1);
+  const int hw = (pb == half0) ? 0 : 1;
+  const uint32_t loc = pb & ((1u << PACK) - 1u);
+  const int tile = (int)(loc >> 4), v = (int)(loc & 15u);
+  const int w = tile * 32 + 8 * (v >> 2) + 4 * hw + (v & 3);
+  const float* c = L.cb[t][w];
+  float d = 0.0f, rr = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float e = r[k] - c[k];
+    d = __builtin_fmaf(e, e, d);
+    rr = __builtin_fmaf(r[k], r[k], rr);
+    r[k] = e;
+  }
+  flag |= !certified<PACK>(p1, p2, rr, d);
+  return w;
+}
+
+// Appends the ids of flagged lanes to a global list (one atomic per wave).
+__device__ inline void append_flags(bool f, uint32_t vid, uint32_t* counter, uint32_t* list, uint32_t cap,
+                                    int lane) {
+  const uint64_t bal = __ballot(f);
+  if (bal == 0) return;
+  const int leader = __ffsll((unsigned long long)bal) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(bal));
+  base = __shfl(base, leader);
+  if (f) {
+    const uint32_t pos = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+    if (pos < cap) list[pos] = vid;
+  }
+}
+
+}  // namespace vqk

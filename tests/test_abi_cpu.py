@@ -1,0 +1,151 @@
+"""The C-ABI library loads, exports every symbol include/vq.h declares, and its
+host-side argument checks reject bad calls before touching the GPU. CPU only:
+no call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import residual_vector_quantization_amd as vq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vq.h")
+
+VQ_OK, VQ_EINVAL, VQ_ERANGE, VQ_EWORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vq\w+)\s*\(", text)))
+
+
+def test_header_declares_north_star_entry_points():
+    names = declared_functions()
+    for n in ["vq_fit_codebooks", "vq3r_encode", "vq3r_decode", "vq3r_dequant_gemv",
+              "vq4p_encode", "vq4p_decode", "vq4p_dequant_gemv"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = vq.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    L = vq.lib()
+    for s in range(6):
+        assert L.vq_status_string(s)
+    assert L.vq_status_string(99) == b"unknown status"
+    assert L.vq_version() >> 16 == 1
+
+
+def test_workspace_sizes():
+    L = vq.lib()
+    assert L.vq_encode_workspace_size(0, 2048, 7168) >= 256 + 4 * (2048 * 896 // 16)
+    assert L.vq_encode_workspace_size(0, 4, 12) == 0            # cols % 8
+    assert L.vq_encode_workspace_size(7, 4, 16) == 0            # format
+    assert L.vq_encode_workspace_size(0, 4, (1 << 20) + 8) == 0  # cols range
+    n = 12 * 2048 * 896
+    assert L.vq_fit_workspace_size(0, 12, 2048, 7168) >= 2 * 32 * n
+    assert L.vq_fit_workspace_size(1, 1, 0, 64) == 0
+    assert L.vq_gemv_workspace_size(0, 2048, 7168, 16, 8) >= 16 * 8 * 28 * 2048 * 4
+    assert L.vq_error_workspace_size(0, 4, 256, 1024) > 256
+
+
+class _Fake:
+    """A fake device buffer: a host allocation whose address is only checked for
+    alignment / null by the host-side validation (never dereferenced)."""
+
+    def __init__(self, n=1 << 12):
+        self.buf = np.zeros(n + 256, dtype=np.uint8)
+        a = self.buf.ctypes.data
+        self.ptr = ctypes.c_void_p((a + 255) & ~255)
+
+
+def test_encode_argument_errors():
+    L = vq.lib()
+    W, cb, idx, sc, ws = _Fake(), _Fake(), _Fake(), _Fake(), _Fake(1 << 16)
+    P = lambda f: f.ptr
+    args = lambda **k: dict(fmt=0, eng=0, W=P(W), dt=0, rows=4, cols=64, cb=P(cb), idx=P(idx), sc=P(sc), ws=P(ws),
+                            wsn=1 << 16, **k)
+
+    def call(a):
+        return L.vq_encode(a["fmt"], a["eng"], a["W"], a["dt"], a["rows"], a["cols"], a["cb"], a["idx"], a["sc"],
+                           a["ws"], a["wsn"], None)
+
+    a = args()
+    assert call(dict(a, fmt=2)) == VQ_EINVAL
+    assert call(dict(a, eng=9)) == VQ_EINVAL
+    assert call(dict(a, dt=7)) == VQ_EINVAL
+    assert call(dict(a, W=None)) == VQ_EINVAL
+    assert call(dict(a, cb=None)) == VQ_EINVAL
+    assert call(dict(a, cols=60)) == VQ_EINVAL
+    assert call(dict(a, cols=0)) == VQ_EINVAL
+    assert call(dict(a, rows=-1)) == VQ_EINVAL
+    assert call(dict(a, cols=(1 << 20) + 8)) == VQ_ERANGE
+    assert call(dict(a, rows=1 << 30, cols=64)) == VQ_ERANGE
+    assert call(dict(a, ws=None)) == VQ_EWORKSPACE
+    assert call(dict(a, wsn=100)) == VQ_EWORKSPACE
+    assert call(dict(a, ws=ctypes.c_void_p(ws.ptr.value + 4))) == VQ_EWORKSPACE
+    assert call(dict(a, W=ctypes.c_void_p(W.ptr.value + 2))) == VQ_EINVAL   # 16-byte alignment
+    assert call(dict(a, rows=0)) == VQ_OK                                   # empty input: nothing to do
+
+
+def test_fit_argument_errors():
+    L = vq.lib()
+    m = _Fake()
+    cb, ws = _Fake(), _Fake(1 << 16)
+    mats = (ctypes.c_void_p * 1)(m.ptr.value)
+    rows, cols = 4, 512  # 256 vectors
+    good = np.stack([np.arange(256)] * 3).astype(np.int64)
+    n_ws = L.vq_fit_workspace_size(0, 1, rows, cols)
+
+    def call(init, fmt=0, iters=2, n_mats=1, rows_=rows, wsn=n_ws, mp=mats):
+        return L.vq_fit_codebooks(fmt, mp, 0, n_mats, rows_, cols, iters, init.ctypes.data_as(ctypes.c_void_p),
+                                  cb.ptr, ws.ptr, wsn, 0, None)
+
+    dup = good.copy()
+    dup[1, 5] = dup[1, 6]
+    assert call(dup) == VQ_EINVAL                      # indices must be distinct
+    oob = good.copy()
+    oob[2, 0] = 256
+    assert call(oob) == VQ_EINVAL                      # and inside [0, N)
+    assert call(good, iters=-1) == VQ_EINVAL
+    assert call(good, n_mats=0) == VQ_EINVAL
+    assert call(good, rows_=2) == VQ_EINVAL            # N = 128 < 256 entries
+    assert call(good, fmt=5) == VQ_EINVAL
+    assert call(good, wsn=n_ws - 1) == VQ_EWORKSPACE
+    assert call(good, mp=(ctypes.c_void_p * 1)(0)) == VQ_EINVAL
+
+
+def test_decode_gemv_error_mxfp4_argument_errors():
+    L = vq.lib()
+    a, b, c, d, e, f, ws = (_Fake() for _ in range(7))
+    assert L.vq_decode(0, a.ptr, b.ptr, c.ptr, 4, 64, 0, d.ptr, None) == VQ_EINVAL   # stages_used 0
+    assert L.vq_decode(0, a.ptr, b.ptr, c.ptr, 4, 64, 4, d.ptr, None) == VQ_EINVAL   # VQ3R has 3 stages
+    assert L.vq_decode(1, None, b.ptr, c.ptr, 4, 64, 4, d.ptr, None) == VQ_EINVAL
+    assert L.vq_encode(0, 0, None, 0, 0, 64, None, None, None, None, 0, None) == VQ_OK   # empty: no access
+    assert L.vq_decode(0, a.ptr, b.ptr, c.ptr, 0, 64, 3, d.ptr, None) == VQ_OK
+    n_ws = L.vq_gemv_workspace_size(0, 4, 64, 2, 2)
+    g = lambda **k: L.vq_dequant_gemv(0, a.ptr, k.get("es", 4 * 8 * 3), b.ptr, 4, c.ptr, 4, 64,
+                                      k.get("ne", 2), d.ptr, k.get("nt", 2), e.ptr, 2, f.ptr, ws.ptr,
+                                      k.get("wsn", n_ws), None)
+    assert g(ne=0) == VQ_EINVAL
+    assert g(es=10) == VQ_EINVAL          # stride smaller than one expert's records
+    assert g(nt=-1) == VQ_EINVAL
+    assert g(wsn=16) == VQ_EWORKSPACE
+    assert L.vq_error(0, a.ptr, 0, b.ptr, c.ptr, d.ptr, 0, 4, 64, e.ptr, ws.ptr, 1 << 12, None) == VQ_EINVAL
+    assert L.vq_mxfp4_qdq(a.ptr, 0, 4, 48, b.ptr, ws.ptr, 256, None) == VQ_EINVAL     # cols % 32
+    assert L.vq_mxfp4_qdq(a.ptr, 0, 4, 64, b.ptr, ws.ptr, 16, None) == VQ_EWORKSPACE
+    assert L.vq_read_status(None, None, None) == VQ_EWORKSPACE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(vq, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(vq, "_lib", None)
+    with pytest.raises(ImportError):
+        vq.lib()

@@ -1,0 +1,326 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded
+synthetic inputs. Bars: indices, scales, decoded weights and MXFP4 values
+bit-exact; Lloyd codebooks bit-exact; relative Frobenius error within 1e-5
+absolute; GEMV within 1e-3 of sum_k |w_hat_k x_k| per output."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import residual_vector_quantization_amd as vq  # noqa: E402
+
+DEV = "cuda"
+ENGINES = ["mfma_f16x", "mfma_f32", "valu_f32", "exact"]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return t if dtype is None else t.to(dtype)
+
+
+def bf16_dev(bits):
+    return to_dev(bits.view(np.int16)).view(torch.bfloat16)
+
+
+def rec_to_idx(fmt, rec_dev):
+    return oracle.unpack(fmt, rec_dev.cpu().numpy())
+
+
+def scales_bits(s_dev):
+    return s_dev.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.fixture(scope="module")
+def cfg1():
+    """256 x 1024 fp32, N(0,1) x per-row lognormal(0, 0.5), seed 0; codebooks from
+    the oracle's Lloyd fit (10 iterations, Forgy init from the shared generator)."""
+    W = synthetic.gaussian_rows(256, 1024, seed=0)
+    out = {"W": W}
+    for fmt in ("vq3r", "vq4p"):
+        S, K = vq.stages_entries(fmt)
+        init = synthetic.forgy_init(256 * 128, K, S, seed=0)
+        cb, _ = oracle.fit([W], S, K, 10, init)
+        out[fmt] = (init, cb)
+    return out
+
+
+# ------------------------------------------------------------------ encode
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+@pytest.mark.parametrize("engine", ENGINES)
+def test_encode_cfg1_bit_exact(cfg1, fmt, engine):
+    say("encode cfg1", fmt, engine)
+    W = cfg1["W"]
+    init, cb = cfg1[fmt]
+    idx_o, s_o = oracle.encode(W, cb)
+    rec, s = vq.encode(to_dev(W), to_dev(cb), fmt=fmt, engine=engine)
+    torch.cuda.synchronize()
+    assert np.array_equal(scales_bits(s), s_o)
+    got = rec_to_idx(fmt, rec)
+    mism = np.argwhere(np.any(got != idx_o, axis=-1))
+    assert len(mism) == 0, "%d vectors differ, first %s" % (len(mism), mism[:5].tolist())
+
+
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+@pytest.mark.parametrize("shape", [(1, 8), (3, 24), (5, 264), (7, 2056), (33, 512)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_encode_ragged_shapes_and_dtypes(cfg1, fmt, shape, dtype):
+    say("encode ragged", fmt, shape, dtype)
+    rows, cols = shape
+    _, cb = cfg1[fmt]
+    W = synthetic.gaussian_rows(rows, cols, seed=rows * 7 + cols)
+    if dtype == "bf16":
+        bits = synthetic.f32_to_bf16_bits(W)
+        Wd = bf16_dev(bits)
+        W = synthetic.bf16_bits_to_f32(bits).reshape(rows, cols)
+    elif dtype == "f16":
+        W = W.astype(np.float16).astype(np.float32)
+        Wd = to_dev(W.astype(np.float16))
+    else:
+        Wd = to_dev(W)
+    idx_o, s_o = oracle.encode(W, cb)
+    rec, s = vq.encode(Wd, to_dev(cb), fmt=fmt)
+    torch.cuda.synchronize()
+    assert np.array_equal(scales_bits(s), s_o)
+    assert np.array_equal(rec_to_idx(fmt, rec), idx_o)
+
+
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+def test_encode_near_ties_and_duplicates(cfg1, fmt):
+    """Duplicate codewords (exact ties) and vectors placed on bisectors of
+    codeword pairs: the certification must route them to the exact search."""
+    say("encode near ties", fmt)
+    S, K = vq.stages_entries(fmt)
+    _, cb = cfg1[fmt]
+    cb = cb.copy()
+    rng = np.random.default_rng(11)
+    for t in range(S):
+        for q in range(K // 8):
+            cb[t, rng.integers(K)] = cb[t, rng.integers(K)]
+    # rows made of midpoints between two stage-1 codewords (times a row factor)
+    rows, V = 64, 32
+    a = rng.integers(0, K, size=(rows, V))
+    b = rng.integers(0, K, size=(rows, V))
+    mid = 0.5 * (cb[0][a] + cb[0][b])
+    W = (mid.reshape(rows, V * 8) * rng.uniform(0.5, 2, size=(rows, 1))).astype(np.float32)
+    idx_o, s_o = oracle.encode(W, cb)
+    for engine in ENGINES[:3]:
+        rec, s = vq.encode(to_dev(W), to_dev(cb), fmt=fmt, engine=engine)
+        torch.cuda.synchronize()
+        assert np.array_equal(scales_bits(s), s_o), engine
+        assert np.array_equal(rec_to_idx(fmt, rec), idx_o), engine
+
+
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+def test_encode_all_ties_overflows_queue_and_stays_exact(fmt):
+    """Every codeword identical: every vector is a tie, the exact-pass queue
+    overflows and the exact pass covers all vectors; answer = index 0."""
+    say("encode all ties", fmt)
+    S, K = vq.stages_entries(fmt)
+    cb = np.zeros((S, K, 8), np.float32)
+    cb[:] = np.float32(0.25)
+    W = synthetic.gaussian_rows(512, 1024, seed=3)      # 65536 vectors > 16 * 4096
+    rec, s = vq.encode(to_dev(W), to_dev(cb), fmt=fmt)
+    ws = vq.encode_workspace(fmt, 512, 1024)
+    rec, s = vq.encode(to_dev(W), to_dev(cb), fmt=fmt, workspace=ws)
+    flags = vq.read_status(ws)
+    assert flags & (1 << 8)     # the exact pass covered every vector
+    assert np.all(rec_to_idx(fmt, rec) == 0)
+
+
+def test_encode_edge_rows_and_errors(cfg1):
+    say("encode edge rows")
+    _, cb = cfg1["vq3r"]
+    W = synthetic.gaussian_rows(6, 64, seed=5)
+    W[1] = 0.0                      # zero row: scale 0, vectors encoded as 0
+    W[2] = 1e-30                    # RMS below fp16 range: scale 0
+    W[3, :8] = 3e4                  # large row
+    idx_o, s_o = oracle.encode(W, cb)
+    rec, s = vq.encode(to_dev(W), to_dev(cb))
+    torch.cuda.synchronize()
+    assert np.array_equal(scales_bits(s), s_o)
+    assert np.array_equal(rec_to_idx("vq3r", rec), idx_o)
+    # a non-finite weight and an RMS beyond fp16 are data errors
+    for bad in (np.nan, np.inf):
+        Wb = W.copy()
+        Wb[4, 7] = bad
+        with pytest.raises(vq.VQError) as e:
+            vq.encode(to_dev(Wb), to_dev(cb))
+        assert e.value.status == 5
+    Wb = np.full((2, 64), 1e5, np.float32)
+    with pytest.raises(vq.VQError):
+        vq.encode(to_dev(Wb), to_dev(cb))
+    # codebook entries beyond |c| <= 2048 are rejected
+    cbb = cb.copy()
+    cbb[1, 3, 2] = 5000.0
+    with pytest.raises(vq.VQError):
+        vq.encode(to_dev(W), to_dev(cbb))
+    # empty input
+    rec, s = vq.encode(torch.empty((0, 64), device=DEV), to_dev(cb))
+    assert rec.shape == (0, 8, 3)
+
+
+def test_encode_deterministic(cfg1):
+    say("encode determinism")
+    _, cb = cfg1["vq3r"]
+    Wd = to_dev(cfg1["W"])
+    r1, s1 = vq.encode(Wd, to_dev(cb))
+    r2, s2 = vq.encode(Wd, to_dev(cb))
+    assert torch.equal(r1, r2) and torch.equal(s1.view(torch.int16), s2.view(torch.int16))
+
+
+# ------------------------------------------------------------------ decode / error
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+def test_decode_bit_exact_and_error(cfg1, fmt):
+    say("decode + error", fmt)
+    S, _ = vq.stages_entries(fmt)
+    W = cfg1["W"]
+    _, cb = cfg1[fmt]
+    idx_o, s_o = oracle.encode(W, cb)
+    rec = to_dev(oracle.pack(fmt, idx_o))
+    sd = to_dev(s_o.view(np.float16))
+    cbd = to_dev(cb)
+    for su in range(1, S + 1):
+        got = vq.decode(rec, sd, cbd, fmt=fmt, stages_used=su).cpu().numpy()
+        ref = oracle.decode(idx_o, s_o, cb, stages_used=su)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), su
+    sums = vq.error_sums(to_dev(W), rec, sd, cbd, fmt=fmt).cpu().numpy()[0]
+    for su in range(1, S + 1):
+        ref = oracle.rel_error(W, oracle.decode(idx_o, s_o, cb, stages_used=su))
+        assert abs(np.sqrt(sums[su - 1] / sums[S]) - ref) < 1e-5
+    # error is non-increasing over the stages on the fit data
+    e = np.sqrt(sums[:S] / sums[S])
+    assert np.all(np.diff(e) <= 1e-12)
+
+
+def test_error_multi_matrix_bf16(cfg1):
+    say("error multi matrix bf16")
+    _, cb = cfg1["vq3r"]
+    mats = [synthetic.student_t_rows_bf16(32, 512, seed=s) for s in range(3)]
+    Wf = [synthetic.bf16_bits_to_f32(m).reshape(32, 512) for m in mats]
+    recs, scs = [], []
+    for w in Wf:
+        i, s = oracle.encode(w, cb)
+        recs.append(oracle.pack("vq3r", i))
+        scs.append(s)
+    sums = vq.error_sums(bf16_dev(np.concatenate(mats)), to_dev(np.concatenate(recs)),
+                         to_dev(np.concatenate(scs).view(np.float16)), to_dev(cb), n_mats=3).cpu().numpy()
+    for m in range(3):
+        i = oracle.unpack("vq3r", recs[m])
+        ref = oracle.rel_error(Wf[m], oracle.decode(i, scs[m], cb))
+        assert abs(np.sqrt(sums[m, 2] / sums[m, 3]) - ref) < 1e-5
+
+
+# ------------------------------------------------------------------ fit
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+@pytest.mark.parametrize("engine", ["mfma_f16x", "mfma_f32", "valu_f32"])
+def test_fit_cfg1_bit_exact(cfg1, fmt, engine):
+    say("fit cfg1", fmt, engine)
+    init, cb_o = cfg1[fmt]
+    cb = vq.fit_codebooks([to_dev(cfg1["W"])], init, fmt=fmt, iters=10, engine=engine)
+    torch.cuda.synchronize()
+    got = cb.cpu().numpy()
+    diff = np.argwhere(got.view(np.uint32) != cb_o.view(np.uint32))
+    assert len(diff) == 0, "codebook entries differ: %d, first %s" % (len(diff), diff[:5].tolist())
+
+
+def test_fit_multi_matrix_bf16_bit_exact():
+    say("fit multi bf16")
+    mats = [synthetic.student_t_rows_bf16(64, 512, seed=100 + s) for s in range(3)]
+    Wf = [synthetic.bf16_bits_to_f32(m).reshape(64, 512) for m in mats]
+    n = 3 * 64 * 64
+    for fmt in ("vq3r", "vq4p"):
+        S, K = vq.stages_entries(fmt)
+        init = synthetic.forgy_init(n, K, S, seed=9)
+        cb_o, _ = oracle.fit(Wf, S, K, 4, init)
+        cb = vq.fit_codebooks([bf16_dev(m) for m in mats], init, fmt=fmt, iters=4)
+        assert np.array_equal(cb.cpu().numpy().view(np.uint32), cb_o.view(np.uint32)), fmt
+
+
+def test_fit_zero_iterations_and_duplicate_values():
+    say("fit iters=0 + duplicate-valued init")
+    W = synthetic.gaussian_rows(16, 256, seed=21)
+    W[:4] = W[4]                                  # identical rows -> identical vectors
+    n = 16 * 32
+    init = synthetic.forgy_init(n, 64, 4, seed=2)
+    rest = np.setdiff1d(init[0], [0, 32, 64])[:61]
+    init[0] = np.r_[[0, 32, 64], rest]             # three indices with equal vectors
+    for iters in (0, 3):
+        cb_o, _ = oracle.fit([W], 4, 64, iters, init)
+        cb = vq.fit_codebooks([to_dev(W)], init, fmt="vq4p", iters=iters)
+        assert np.array_equal(cb.cpu().numpy().view(np.uint32), cb_o.view(np.uint32)), iters
+
+
+# ------------------------------------------------------------------ GEMV
+def _experts(fmt, cb, E, rows, cols, seed):
+    recs, scs, whs = [], [], []
+    for e in range(E):
+        w = synthetic.student_t_rows_f32(rows, cols, seed=seed + e)
+        i, s = oracle.encode(w, cb)
+        recs.append(oracle.pack(fmt, i))
+        scs.append(s)
+        whs.append(oracle.decode(i, s, cb))
+    return np.stack(recs), np.stack(scs), whs
+
+
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+@pytest.mark.parametrize("shape", [(64, 256), (96, 2056), (256, 1024)])
+def test_gemv_matches_oracle(cfg1, fmt, shape):
+    say("gemv", fmt, shape)
+    rows, cols = shape
+    _, cb = cfg1[fmt]
+    E, ntok, topk = 6, 5, 3
+    recs, scs, whs = _experts(fmt, cb, E, rows, cols, seed=40)
+    x = synthetic.activations_f16(ntok, cols, seed=1)
+    route = synthetic.routing(ntok, E, topk, seed=2)
+    y = vq.dequant_gemv(to_dev(recs), to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
+                        to_dev(route), fmt=fmt).cpu().numpy()
+    xf = synthetic.f16_bits_to_f32(x).reshape(ntok, cols)
+    for b in range(ntok):
+        for k in range(topk):
+            ref, scale = oracle.gemv_ref(whs[route[b, k]], xf[b])
+            err = np.abs(y[b, k] - ref)
+            assert np.all(err <= 1e-3 * scale + 1e-30), (b, k, float((err / scale).max()))
+
+
+def test_gemv_bad_route_flagged(cfg1):
+    say("gemv bad route")
+    _, cb = cfg1["vq3r"]
+    recs, scs, _ = _experts("vq3r", cb, 2, 32, 64, seed=3)
+    x = synthetic.activations_f16(1, 64, seed=1)
+    route = np.array([[0, 5]], np.int32)
+    with pytest.raises(vq.VQError):
+        vq.dequant_gemv(to_dev(recs), to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
+                        to_dev(route), check=True)
+
+
+# ------------------------------------------------------------------ MXFP4
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mxfp4_bit_exact(dtype):
+    say("mxfp4", dtype)
+    W = synthetic.student_t_rows_f32(64, 1024, seed=8)
+    W[3, :32] = 0.0
+    W[4, :32] = 1e-42                       # subnormal block
+    W[5, 64:96] = np.float32(2.0) ** 120    # large exponent
+    if dtype == "bf16":
+        bits = synthetic.f32_to_bf16_bits(W)
+        Wd = bf16_dev(bits)
+        W = synthetic.bf16_bits_to_f32(bits).reshape(W.shape)
+    else:
+        Wd = to_dev(W)
+    got = vq.mxfp4_qdq(Wd).cpu().numpy()
+    ref = oracle.mxfp4_qdq(W)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
