@@ -164,7 +164,7 @@ def encode(W, codebooks, fmt="vq3r", engine="auto", idx=None, scales=None, works
         workspace = encode_workspace(fmt, rows, cols, W.device)
     st = lib().vq_encode(FORMATS[fmt], ENGINES[engine], _ptr(W), _dtype_code(W), rows, cols, _ptr(codebooks),
                          _ptr(idx), _ptr(scales), _ptr(workspace), workspace.numel(), _stream())
-    _call("vq_encode", st, workspace, check)
+    _call("vq_encode", st, workspace, check and rows > 0)
     return idx, scales
 
 
