@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the VQ3R / VQ4P hot path on one MI355X.
+
+One step = one pass of the whole path over one full routed-expert layer of
+synthetic weights (256 experts x w1 [2048 x 7168] bf16, Student-t(5) x 0.02 x
+per-row lognormal(0, 0.3)), inputs resident in HBM:
+  1. Lloyd fit of the 3 x 256 VQ3R codebooks on 12 seeded-sampled experts (20 iters)
+  2. VQ3R encode of all 256 experts (indices + fp16 row scales)
+  3. VQ3R decode of all 256 experts to fp32
+  4. relative Frobenius error per expert after 1, 2 and 3 stages
+  5. fused dequant-GEMV at 1, 4 and 16 tokens, top-8 seeded routing, MALL flushed
+  6. MXFP4 quantize-dequantize of the 12 sampled experts, VQ4P fit on them
+     (4 x 64, 20 iters), VQ4P encode of all 256 experts, VQ4P dequant-GEMV
+Prints one JSON line (value = layer weights per second of the whole step).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP32_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+ROWS, COLS = 2048, 7168
+VEC_PER_EXPERT = ROWS * COLS // 8
+FLOP_PER_VEC = {"vq3r": 3 * 256 * 8 * 2, "vq4p": 4 * 64 * 8 * 2}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--experts", type=int, default=256)
+    ap.add_argument("--sample", type=int, default=12)
+    ap.add_argument("--iters", type=int, default=20)
+    ap.add_argument("--engine", default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="oracle encode sample: rows of expert 0")
+    ap.add_argument("--only", default="", help="comma list: fit,encode,decode,error,gemv,vq4p (default all)")
+    ap.add_argument("--loop", default="", help="profiling helper: repeat one component (encode|gemv1|gemv16|fit) --steps times")
+    ap.add_argument("--copy-calibration", action="store_true", help="also run a plain copy of known size")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events on the current stream around each component."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.ev = {}
+
+    def __call__(self, name):
+        torch = self.torch
+        timer = self
+
+        class _Ctx:
+            def __enter__(self_):
+                self_.a = torch.cuda.Event(enable_timing=True)
+                self_.b = torch.cuda.Event(enable_timing=True)
+                self_.a.record()
+
+            def __exit__(self_, *exc):
+                self_.b.record()
+                timer.ev.setdefault(name, []).append((self_.a, self_.b))
+
+        return _Ctx()
+
+    def mean_ms(self, name, skip=0):
+        xs = [a.elapsed_time(b) for a, b in self.ev.get(name, [])[skip:]]
+        return float(np.mean(xs)) if xs else float("nan")
+
+    def reset(self):
+        self.ev = {}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the work would shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synthetic
+    import residual_vector_quantization_amd as vq
+
+    only = set(args.only.split(",")) if args.only else {"fit", "encode", "decode", "error", "gemv", "vq4p"}
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    E = args.experts
+    t0 = time.time()
+    W = torch.empty((E * ROWS, COLS), dtype=torch.bfloat16, device=dev)
+    for e in range(E):
+        synthetic.student_t_expert_torch(synthetic.expert_seed(3, e), ROWS, COLS, device=dev,
+                                         out=W[e * ROWS:(e + 1) * ROWS])
+    torch.cuda.synchronize()
+    log("generated %d experts in %.1f s" % (E, time.time() - t0))
+    sample = synthetic.sample_experts(E, min(args.sample, E), seed=3)
+    mats = [W[e * ROWS:(e + 1) * ROWS] for e in sample]
+    n_fit = len(mats) * VEC_PER_EXPERT
+    init3 = synthetic.forgy_init(n_fit, 256, 3, seed=3)
+    init4 = synthetic.forgy_init(n_fit, 64, 4, seed=4)
+    nrows = E * ROWS
+    # buffers and workspaces (allocated once, outside the timed region)
+    cb3 = torch.empty((3, 256, 8), dtype=torch.float32, device=dev)
+    cb4 = torch.empty((4, 64, 8), dtype=torch.float32, device=dev)
+    fit_ws3 = vq.fit_workspace("vq3r", len(mats), ROWS, COLS)
+    fit_ws4 = vq.fit_workspace("vq4p", len(mats), ROWS, COLS)
+    idx3 = torch.empty((nrows, COLS // 8, 3), dtype=torch.uint8, device=dev)
+    idx4 = torch.empty_like(idx3)
+    sc3 = torch.empty(nrows, dtype=torch.float16, device=dev)
+    sc4 = torch.empty_like(sc3)
+    enc_ws = vq.encode_workspace("vq3r", nrows, COLS)
+    need_dec = "decode" in only
+    w_hat = torch.empty((nrows, COLS), dtype=torch.float32, device=dev) if need_dec else None
+    err_ws = vq.error_workspace("vq3r", E, ROWS, COLS)
+    sums = torch.empty((E, 4), dtype=torch.float64, device=dev)
+    mx_out = torch.empty((len(mats) * ROWS, COLS), dtype=torch.float32, device=dev) if "vq4p" in only else None
+    mx_ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+    gemv_cases = []
+    for ntok in (1, 4, 16):
+        x = torch.from_numpy(synthetic.activations_f16(ntok, COLS, seed=10 + ntok).view(np.float16)).to(dev)
+        route = torch.from_numpy(synthetic.routing(ntok, E, 8, seed=20 + ntok)).to(dev)
+        y = torch.empty((ntok, 8, ROWS), dtype=torch.float32, device=dev)
+        ws = vq.gemv_workspace("vq3r", ROWS, COLS, ntok, 8)
+        distinct = len(np.unique(route.cpu().numpy()))
+        gemv_cases.append((ntok, x, route, y, ws, distinct))
+    idx3_e = idx3.view(E, ROWS, COLS // 8, 3)
+    sc3_e = sc3.view(E, ROWS)
+    idx4_e = idx4.view(E, ROWS, COLS // 8, 3)
+    sc4_e = sc4.view(E, ROWS)
+    T = Timer(torch)
+
+    def step():
+        if "fit" in only or not step.fitted:
+            with T("fit3"):
+                vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, engine=args.engine, codebooks=cb3,
+                                 workspace=fit_ws3, check=False)
+            step.fitted = True
+        if "encode" in only:
+            with T("encode3"):
+                vq.encode(W, cb3, fmt="vq3r", engine=args.engine, idx=idx3, scales=sc3, workspace=enc_ws,
+                          check=False)
+        if need_dec:
+            with T("decode3"):
+                vq.decode(idx3, sc3, cb3, fmt="vq3r", out=w_hat)
+        if "error" in only:
+            with T("error3"):
+                vq.error_sums(W, idx3, sc3, cb3, fmt="vq3r", n_mats=E, sums=sums, workspace=err_ws, check=False)
+        if "gemv" in only:
+            for ntok, x, route, y, ws, _ in gemv_cases:
+                flush.fill_(ntok)
+                with T("gemv3_%d" % ntok):
+                    vq.dequant_gemv(idx3_e, sc3_e, cb3, x, route, fmt="vq3r", y=y, workspace=ws)
+        if "vq4p" in only:
+            with T("mxfp4"):
+                for i, m in enumerate(mats):
+                    vq.mxfp4_qdq(m, out=mx_out[i * ROWS:(i + 1) * ROWS], workspace=mx_ws, check=False)
+            with T("fit4"):
+                vq.fit_codebooks([mx_out[i * ROWS:(i + 1) * ROWS] for i in range(len(mats))], init4, fmt="vq4p",
+                                 iters=args.iters, engine=args.engine, codebooks=cb4, workspace=fit_ws4,
+                                 check=False)
+            with T("encode4"):
+                vq.encode(W, cb4, fmt="vq4p", engine=args.engine, idx=idx4, scales=sc4, workspace=enc_ws,
+                          check=False)
+            for ntok, x, route, y, ws, _ in gemv_cases:
+                flush.fill_(ntok)
+                with T("gemv4_%d" % ntok):
+                    vq.dequant_gemv(idx4_e, sc4_e, cb4, x, route, fmt="vq4p", y=y, workspace=ws)
+    step.fitted = False
+
+    if args.loop:
+        # profiling helper: one component repeated, nothing else in the trace
+        if args.loop != "fit":
+            step_fit_only = vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3,
+                                             workspace=fit_ws3)
+            vq.encode(W, cb3, idx=idx3, scales=sc3, workspace=enc_ws)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            if args.loop == "encode":
+                vq.encode(W, cb3, idx=idx3, scales=sc3, workspace=enc_ws, check=False)
+            elif args.loop == "encode4":
+                vq.encode(W, cb4, fmt="vq4p", idx=idx4, scales=sc4, workspace=enc_ws, check=False)
+            elif args.loop == "fit":
+                vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3, workspace=fit_ws3,
+                                 check=False)
+            elif args.loop.startswith("gemv"):
+                ntok = int(args.loop[4:])
+                c = [g for g in gemv_cases if g[0] == ntok][0]
+                flush.fill_(i)
+                vq.dequant_gemv(idx3_e, sc3_e, cb3, c[1], c[2], y=c[3], workspace=c[4])
+            elif args.loop == "decode":
+                vq.decode(idx3, sc3, cb3, out=w_hat)
+            torch.cuda.synchronize()
+            log("loop %s %d done" % (args.loop, i))
+        if args.copy_calibration:
+            src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            for i in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log("copy calibration: 3 x 1 GiB copies done")
+        return
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log("warmup step %d done" % i)
+    T.reset()
+    torch.cuda.synchronize()
+    t_start = time.time()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.time() - t_start
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log("timed %d steps: %.2f ms/step (wall %.2f s)" % (args.steps, ms_step, wall))
+    # correctness of the last step (status words + sanity of the error)
+    comp = {}
+    for k in sorted(T.ev):
+        comp[k] = round(T.mean_ms(k), 4)
+    weights = E * ROWS * COLS
+    out = {}
+    enc_ms = T.mean_ms("encode3")
+    enc_tflops = E * VEC_PER_EXPERT * FLOP_PER_VEC["vq3r"] / (enc_ms * 1e-3) / 1e12
+    out["encode_gweights_s"] = round(weights / (enc_ms * 1e-3) / 1e9, 3)
+    out["encode_tflops_fp32_equiv"] = round(enc_tflops, 2)
+    out["encode_frac_fp32_peak"] = round(enc_tflops / FP32_PEAK_TFLOPS, 4)
+    gem = {}
+    for fmt in ("3", "4"):
+        for ntok, x, route, y, ws, distinct in gemv_cases:
+            key = "gemv%s_%d" % (fmt, ntok)
+            if key not in T.ev:
+                continue
+            ms = T.mean_ms(key)
+            alg = distinct * (VEC_PER_EXPERT * 3 + ROWS * 2) + ntok * COLS * 2 + ntok * 8 * ROWS * 4 + \
+                (3 * 256 * 8 * 4 if fmt == "3" else 4 * 64 * 8 * 4)
+            gbs = alg / (ms * 1e-3) / 1e9
+            gem[key] = {"us": round(ms * 1e3, 2), "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                        "distinct_experts": distinct, "alg_bytes": alg}
+    if "error3" in T.ev:
+        s = sums.double().cpu().numpy()
+        out["rel_error_mean_after_stage"] = [round(float(np.mean(np.sqrt(s[:, t] / s[:, 3]))), 5) for t in range(3)]
+    st = vq.read_status(enc_ws)
+    out["encode_device_flags"] = st
+    # roofline of the dominant kernel: the VQ3R encode
+    roof = {"bound": "alu", "achieved": round(enc_tflops, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(enc_tflops / FP32_PEAK_TFLOPS, 4), "traffic": None,
+            "kernel": "vq3r encode (k_encode + k_encode_exact)", "work": "12288 fp32 flop per 8-dim vector"}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(torch, W, cb3, args.cpu_rows)
+    line = {
+        "metric": "VQ3R encode Gweights/s (%FP32 peak) + dequant-GEMV GB/s (%HBM peak), 1 GPU",
+        "value": round(weights / (ms_step * 1e-3) / 1e9, 3),
+        "unit": "Gweights/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 (fp32 search with exact check; bf16 weights in)", "data": "synthetic",
+        "config": {"workload": "full routed-expert layer: %d experts x w1 [2048x7168] bf16, fit on %d sampled "
+                               "experts x %d Lloyd iters, VQ3R+VQ4P encode, decode, error, dequant-GEMV at "
+                               "1/4/16 tokens top-8" % (E, len(mats), args.iters),
+                   "experts": E, "rows": ROWS, "cols": COLS, "parallelism": "single GPU"},
+        "components_ms": comp,
+        "encode": out,
+        "gemv": gem,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(torch, W, cb3, nrows):
+    """The oracle (plain C, all host threads) encoding a bounded sample of the
+    same workload: the first `nrows` rows of expert 0 with the fitted codebooks."""
+    import oracle
+    w = W[:nrows].float().cpu().numpy()
+    cb = cb3.cpu().numpy()
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.time()
+    oracle.encode(w, cb)
+    dt = time.time() - t0
+    return {"value": round(w.size / dt / 1e9, 6), "unit": "Gweights/s", "cores": threads, "kind": "oracle",
+            "sample": "VQ3R encode of %d rows x 7168 of expert 0 (%.1f s)" % (nrows, dt)}
+
+
+if __name__ == "__main__":
+    main()

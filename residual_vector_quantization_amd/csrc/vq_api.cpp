@@ -282,7 +282,8 @@ int vq4p_decode(const uint8_t* idx, const uint16_t* scales, const float* codeboo
 size_t vq_gemv_workspace_size(int format, int64_t rows, int64_t cols, int32_t ntok, int32_t topk) {
   if (!fmt_ok(format) || check_shape(rows, cols) != VQ_OK || ntok < 0 || topk < 0) return 0;
   const size_t npairs = (size_t)ntok * (size_t)topk;
-  return align256(kHeader + sizeof(float) * npairs * (size_t)gemv_nblk(cols) * (size_t)rows);
+  return kHeader + align256(sizeof(uint32_t) * npairs) +
+         align256(sizeof(float) * (size_t)gemv_partials_floats(format, rows, cols, (int64_t)npairs));
 }
 
 int vq_dequant_gemv(int format, const uint8_t* idx, int64_t expert_stride, const uint16_t* scales,
@@ -314,7 +315,8 @@ int vq_dequant_gemv(int format, const uint8_t* idx, int64_t expert_stride, const
   a.route = route;
   a.y = y;
   a.hdr = (WsHeader*)workspace;
-  a.partials = (float*)((char*)workspace + kHeader);
+  a.counters = (uint32_t*)((char*)workspace + kHeader);
+  a.partials = (float*)((char*)workspace + kHeader + align256(sizeof(uint32_t) * (size_t)ntok * (size_t)topk));
   a.stream = (hipStream_t)stream;
   if ((st = device_cus(&a.ncu)) != VQ_OK) return st;
   return hip_status(launch_gemv(a));

@@ -78,7 +78,8 @@ struct GemvArgs {
   int ntok, topk;
   const int32_t* route;
   float* y;
-  float* partials;  // [ntok*topk][nblk][rows]
+  float* partials;     // [ntok*topk][nblk][rows]
+  uint32_t* counters;  // [ntok*topk] tiles finished per pair
   WsHeader* hdr;
   int ncu;
   hipStream_t stream;
@@ -94,9 +95,8 @@ struct Mxfp4Args {
   hipStream_t stream;
 };
 
-// GEMV tiling shared by the kernel and the workspace size query.
-constexpr int GEMV_SLICES = 32;  // 8-dim column slices per block (256 columns)
-inline int64_t gemv_nblk(int64_t cols) { return (cols / 8 + GEMV_SLICES - 1) / GEMV_SLICES; }
+// Floats of GEMV tile partial sums for the workspace size query.
+int64_t gemv_partials_floats(int format, int64_t rows, int64_t cols, int64_t npairs);
 
 hipError_t launch_reset(WsHeader* hdr, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs& a);

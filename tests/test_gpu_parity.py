@@ -277,7 +277,7 @@ def _experts(fmt, cb, E, rows, cols, seed):
 
 
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
-@pytest.mark.parametrize("shape", [(64, 256), (96, 2056), (256, 1024)])
+@pytest.mark.parametrize("shape", [(64, 256), (96, 2056), (256, 1024), (32, 448), (1100, 896), (64, 7168)])
 def test_gemv_matches_oracle(cfg1, fmt, shape):
     say("gemv", fmt, shape)
     rows, cols = shape
