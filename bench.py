@@ -8,7 +8,8 @@ per-row lognormal(0, 0.3)), inputs resident in HBM:
   2. VQ3R encode of all 256 experts (indices + fp16 row scales)
   3. VQ3R decode of all 256 experts to fp32
   4. relative Frobenius error per expert after 1, 2 and 3 stages
-  5. fused dequant-GEMV at 1, 4 and 16 tokens, top-8 seeded routing, MALL flushed
+  5. repack of the indices into the GEMV runtime layout, then the fused
+     dequant-GEMV at 1, 4 and 16 tokens, top-8 seeded routing, MALL flushed
   6. MXFP4 quantize-dequantize of the 12 sampled experts, VQ4P fit on them
      (4 x 64, 20 iters), VQ4P encode of all 256 experts, VQ4P dequant-GEMV
 Prints one JSON line (value = layer weights per second of the whole step).
@@ -138,10 +139,14 @@ def main():
         ws = vq.gemv_workspace("vq3r", ROWS, COLS, ntok, 8)
         distinct = len(np.unique(route.cpu().numpy()))
         gemv_cases.append((ntok, x, route, y, ws, distinct))
+    gemv_cases4 = [(ntok, x, route, y, vq.gemv_workspace("vq4p", ROWS, COLS, ntok, 8), d)
+                   for ntok, x, route, y, ws, d in gemv_cases]
     idx3_e = idx3.view(E, ROWS, COLS // 8, 3)
     sc3_e = sc3.view(E, ROWS)
     idx4_e = idx4.view(E, ROWS, COLS // 8, 3)
     sc4_e = sc4.view(E, ROWS)
+    pk3 = torch.empty((E, vq.lib().vq_gemv_packed_size(0, ROWS, COLS)), dtype=torch.uint8, device=dev)
+    pk4 = torch.empty((E, vq.lib().vq_gemv_packed_size(1, ROWS, COLS)), dtype=torch.uint8, device=dev)
     T = Timer(torch)
 
     def step():
@@ -161,10 +166,12 @@ def main():
             with T("error3"):
                 vq.error_sums(W, idx3, sc3, cb3, fmt="vq3r", n_mats=E, sums=sums, workspace=err_ws, check=False)
         if "gemv" in only:
+            with T("pack3"):
+                vq.gemv_pack(idx3_e, fmt="vq3r", out=pk3)
             for ntok, x, route, y, ws, _ in gemv_cases:
                 flush.fill_(ntok)
                 with T("gemv3_%d" % ntok):
-                    vq.dequant_gemv(idx3_e, sc3_e, cb3, x, route, fmt="vq3r", y=y, workspace=ws)
+                    vq.dequant_gemv(pk3, sc3_e, cb3, x, route, ROWS, COLS, fmt="vq3r", y=y, workspace=ws)
         if "vq4p" in only:
             with T("mxfp4"):
                 for i, m in enumerate(mats):
@@ -176,18 +183,20 @@ def main():
             with T("encode4"):
                 vq.encode(W, cb4, fmt="vq4p", engine=args.engine, idx=idx4, scales=sc4, workspace=enc_ws,
                           check=False)
-            for ntok, x, route, y, ws, _ in gemv_cases:
+            with T("pack4"):
+                vq.gemv_pack(idx4_e, fmt="vq4p", out=pk4)
+            for ntok, x, route, y, ws4, _ in gemv_cases4:
                 flush.fill_(ntok)
                 with T("gemv4_%d" % ntok):
-                    vq.dequant_gemv(idx4_e, sc4_e, cb4, x, route, fmt="vq4p", y=y, workspace=ws)
+                    vq.dequant_gemv(pk4, sc4_e, cb4, x, route, ROWS, COLS, fmt="vq4p", y=y, workspace=ws4)
     step.fitted = False
 
     if args.loop:
         # profiling helper: one component repeated, nothing else in the trace
         if args.loop != "fit":
-            step_fit_only = vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3,
-                                             workspace=fit_ws3)
+            vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3, workspace=fit_ws3)
             vq.encode(W, cb3, idx=idx3, scales=sc3, workspace=enc_ws)
+            vq.gemv_pack(idx3_e, fmt="vq3r", out=pk3)
         torch.cuda.synchronize()
         for i in range(args.steps):
             if args.loop == "encode":
@@ -201,7 +210,7 @@ def main():
                 ntok = int(args.loop[4:])
                 c = [g for g in gemv_cases if g[0] == ntok][0]
                 flush.fill_(i)
-                vq.dequant_gemv(idx3_e, sc3_e, cb3, c[1], c[2], y=c[3], workspace=c[4])
+                vq.dequant_gemv(pk3, sc3_e, cb3, c[1], c[2], ROWS, COLS, y=c[3], workspace=c[4])
             elif args.loop == "decode":
                 vq.decode(idx3, sc3, cb3, out=w_hat)
             torch.cuda.synchronize()

@@ -84,9 +84,11 @@ const char* vq_status_string(int status);
 /* Library ABI version: (major << 16) | minor. */
 int vq_version(void);
 
-/* Waits for `stream`, then returns VQ_EDATA if any call that used `workspace`
- * since the last vq_clear_status() flagged a data error, else VQ_OK.
- * *flags_out (host, may be NULL) receives the raw flag bits. */
+/* Waits for `stream`, then returns VQ_EDATA if the most recent call that used
+ * `workspace` flagged a data error, else VQ_OK (every call that takes a
+ * workspace clears its flags when it starts). *flags_out (host, may be NULL)
+ * receives the raw flag bits (bit 8 is informational: the exact search covered
+ * every vector because its queue overflowed). */
 int vq_read_status(const void* workspace, void* stream, uint32_t* flags_out);
 
 /* Enqueues a reset of the workspace's status flags. */
@@ -158,24 +160,42 @@ int vq4p_decode(const uint8_t* idx, const uint16_t* scales, const float* codeboo
  * each token activates a few experts whose stored records are decoded and
  * multiplied): for token b and routed slot k with e = route[b][k],
  *   y[b][k][r] = sum_c W_hat_e[r][c] * x[b][c]   (fp32 accumulation)
- * computed from the indices without materializing W_hat.
- * idx        base of n_experts index tensors; expert e at idx + e*expert_stride
- *            bytes, each [rows][cols/8][3]
+ * computed from the indices without materializing W_hat. The result is
+ * deterministic (fixed summation order) and within fp32 rounding of the
+ * decoded product.
+ *
+ * The GEMV reads its indices in a runtime layout that vq_gemv_pack() builds
+ * once from the stored [rows][cols/8][3] records (like loading a container):
+ * blocks of J column slices (J = 28 for VQ3R, 56 for VQ4P) by 64-row groups,
+ * each group's records interleaved in 12-byte chunks of 4 records per row.
+ * vq_gemv_packed_size() gives the bytes of one packed expert (rows are
+ * padded to a multiple of 64 and slices to a multiple of J with zeros).
+ *
+ * vq_gemv_pack: idx = n_experts consecutive [rows][cols/8][3] tensors;
+ *               packed out = n_experts consecutive packed experts of
+ *               vq_gemv_packed_size() bytes each (4-byte aligned).
+ * vq_dequant_gemv:
+ * packed     base of the packed experts; expert e at packed + e*expert_stride
+ *            bytes (expert_stride >= vq_gemv_packed_size, multiple of 4)
  * scales     base of the row scales; expert e at scales + e*scale_stride
  * x          fp16 bit patterns [ntok][cols];  route int32 [ntok][topk]
- * y          out fp32 [ntok][topk][rows]
+ * y          out fp32 [ntok][topk][rows]; a route id outside [0, n_experts)
+ *            gives y = 0 for that slot and flags a data error
  * Workspace: vq_gemv_workspace_size(format, rows, cols, ntok, topk).
  * ---------------------------------------------------------------------- */
+size_t vq_gemv_packed_size(int format, int64_t rows, int64_t cols);
+int vq_gemv_pack(int format, const uint8_t* idx, int64_t rows, int64_t cols, int64_t n_experts, uint8_t* packed,
+                 void* stream);
 size_t vq_gemv_workspace_size(int format, int64_t rows, int64_t cols, int32_t ntok, int32_t topk);
-int vq_dequant_gemv(int format, const uint8_t* idx, int64_t expert_stride, const uint16_t* scales,
+int vq_dequant_gemv(int format, const uint8_t* packed, int64_t expert_stride, const uint16_t* scales,
                     int64_t scale_stride, const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts,
                     const uint16_t* x, int32_t ntok, const int32_t* route, int32_t topk, float* y,
                     void* workspace, size_t ws_bytes, void* stream);
-int vq3r_dequant_gemv(const uint8_t* idx, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
+int vq3r_dequant_gemv(const uint8_t* packed, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
                       const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts, const uint16_t* x,
                       int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace, size_t ws_bytes,
                       void* stream);
-int vq4p_dequant_gemv(const uint8_t* idx, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
+int vq4p_dequant_gemv(const uint8_t* packed, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
                       const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts, const uint16_t* x,
                       int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace, size_t ws_bytes,
                       void* stream);

@@ -17,7 +17,7 @@ import numpy as np
 
 __all__ = [
     "VQError", "lib", "FORMATS", "ENGINES", "stages_entries",
-    "encode", "decode", "fit_codebooks", "dequant_gemv", "error_sums", "rel_errors", "mxfp4_qdq",
+    "encode", "decode", "fit_codebooks", "gemv_pack", "dequant_gemv", "error_sums", "rel_errors", "mxfp4_qdq",
     "encode_workspace", "fit_workspace", "gemv_workspace", "error_workspace", "read_status",
 ]
 
@@ -70,6 +70,8 @@ def lib():
         "vq_decode": ([I, P, P, P, L64, L64, ctypes.c_int32, P, P], I),
         "vq3r_decode": ([P, P, P, L64, L64, P, P], I),
         "vq4p_decode": ([P, P, P, L64, L64, P, P], I),
+        "vq_gemv_packed_size": ([I, L64, L64], SZ),
+        "vq_gemv_pack": ([I, P, L64, L64, L64, P, P], I),
         "vq_gemv_workspace_size": ([I, L64, L64, ctypes.c_int32, ctypes.c_int32], SZ),
         "vq_dequant_gemv": ([I, P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32, P,
                              ctypes.c_int32, P, P, SZ, P], I),
@@ -223,22 +225,40 @@ def gemv_workspace(fmt, rows, cols, ntok, topk, device="cuda"):
     return _workspace(n, device)
 
 
-def dequant_gemv(idx, scales, codebooks, x, route, fmt="vq3r", y=None, workspace=None, check=False):
-    """y[b][k] = W_hat_{route[b][k]} x_b for the stacked experts idx [E, rows, cols/8, 3],
-    scales [E, rows], x fp16 [ntok, cols], route int32 [ntok, topk] -> y fp32 [ntok, topk, rows]."""
+def gemv_pack(idx, fmt="vq3r", out=None):
+    """Repacks stored records idx [E, rows, cols/8, 3] into the GEMV runtime
+    layout (uint8 [E, packed_size])."""
     torch = _torch()
     E, rows, V, _ = idx.shape
+    _check_cuda(idx)
+    n = lib().vq_gemv_packed_size(FORMATS[fmt], rows, V * 8)
+    if n == 0:
+        raise VQError(1, "vq_gemv_packed_size")
+    if out is None:
+        out = torch.empty((E, n), dtype=torch.uint8, device=idx.device)
+    st = lib().vq_gemv_pack(FORMATS[fmt], _ptr(idx), rows, V * 8, E, _ptr(out), _stream())
+    _call("vq_gemv_pack", st)
+    return out
+
+
+def dequant_gemv(packed, scales, codebooks, x, route, rows, cols, fmt="vq3r", y=None, workspace=None,
+                 check=False):
+    """y[b][k] = W_hat_{route[b][k]} x_b for E experts packed by gemv_pack
+    (uint8 [E, packed_size]), scales [E, rows], x fp16 [ntok, cols],
+    route int32 [ntok, topk] -> y fp32 [ntok, topk, rows]."""
+    torch = _torch()
+    E = packed.shape[0]
     ntok, topk = route.shape
-    _check_cuda(idx, scales, codebooks, x, route)
+    _check_cuda(packed, scales, codebooks, x, route)
     if x.dtype != torch.float16 or route.dtype != torch.int32:
         raise TypeError("x must be float16 and route int32")
     if y is None:
-        y = torch.empty((ntok, topk, rows), dtype=torch.float32, device=idx.device)
+        y = torch.empty((ntok, topk, rows), dtype=torch.float32, device=packed.device)
     if workspace is None:
-        workspace = gemv_workspace(fmt, rows, V * 8, ntok, topk, idx.device)
-    st = lib().vq_dequant_gemv(FORMATS[fmt], _ptr(idx), rows * V * 3, _ptr(scales), rows, _ptr(codebooks), rows,
-                               V * 8, E, _ptr(x), ntok, _ptr(route), topk, _ptr(y), _ptr(workspace),
-                               workspace.numel(), _stream())
+        workspace = gemv_workspace(fmt, rows, cols, ntok, topk, packed.device)
+    st = lib().vq_dequant_gemv(FORMATS[fmt], _ptr(packed), packed.shape[1], _ptr(scales), scales.shape[-1],
+                               _ptr(codebooks), rows, cols, E, _ptr(x), ntok, _ptr(route), topk, _ptr(y),
+                               _ptr(workspace), workspace.numel(), _stream())
     _call("vq_dequant_gemv", st, workspace, check)
     return y
 

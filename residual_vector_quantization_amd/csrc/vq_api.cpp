@@ -279,14 +279,30 @@ int vq4p_decode(const uint8_t* idx, const uint16_t* scales, const float* codeboo
 }
 
 // ---------------------------------------------------------------- GEMV
+size_t vq_gemv_packed_size(int format, int64_t rows, int64_t cols) {
+  if (!fmt_ok(format) || check_shape(rows, cols) != VQ_OK) return 0;
+  return (size_t)gemv_packed_bytes(format, rows, cols);
+}
+
+int vq_gemv_pack(int format, const uint8_t* idx, int64_t rows, int64_t cols, int64_t n_experts, uint8_t* packed,
+                 void* stream) {
+  if (!fmt_ok(format) || n_experts < 0) return VQ_EINVAL;
+  int st = check_shape(rows, cols);
+  if (st != VQ_OK) return st;
+  if (rows == 0 || n_experts == 0) return VQ_OK;
+  if (!idx || !packed || !aligned(packed, 4)) return VQ_EINVAL;
+  int ncu = 0;
+  if ((st = device_cus(&ncu)) != VQ_OK) return st;
+  return hip_status(launch_gemv_pack(format, idx, rows, cols, n_experts, packed, ncu, (hipStream_t)stream));
+}
+
 size_t vq_gemv_workspace_size(int format, int64_t rows, int64_t cols, int32_t ntok, int32_t topk) {
   if (!fmt_ok(format) || check_shape(rows, cols) != VQ_OK || ntok < 0 || topk < 0) return 0;
   const size_t npairs = (size_t)ntok * (size_t)topk;
-  return kHeader + align256(sizeof(uint32_t) * npairs) +
-         align256(sizeof(float) * (size_t)gemv_partials_floats(format, rows, cols, (int64_t)npairs));
+  return kHeader + align256(sizeof(float) * (size_t)gemv_partials_floats(format, rows, cols, (int64_t)npairs));
 }
 
-int vq_dequant_gemv(int format, const uint8_t* idx, int64_t expert_stride, const uint16_t* scales,
+int vq_dequant_gemv(int format, const uint8_t* packed, int64_t expert_stride, const uint16_t* scales,
                     int64_t scale_stride, const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts,
                     const uint16_t* x, int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace,
                     size_t ws_bytes, void* stream) {
@@ -294,14 +310,16 @@ int vq_dequant_gemv(int format, const uint8_t* idx, int64_t expert_stride, const
   int st = check_shape(rows, cols);
   if (st != VQ_OK) return st;
   if (ntok < 0 || topk < 0 || n_experts < 1 || expert_stride < 0 || scale_stride < 0) return VQ_EINVAL;
-  if (n_experts > 1 && (expert_stride < rows * (cols / 8) * 3 || scale_stride < rows)) return VQ_EINVAL;
-  if (!idx || !scales || !codebooks || !x || !route || !y) return VQ_EINVAL;
+  if (n_experts > 1 && (expert_stride < gemv_packed_bytes(format, rows, cols) || scale_stride < rows))
+    return VQ_EINVAL;
+  if (expert_stride % 4 != 0) return VQ_EINVAL;
+  if (!packed || !scales || !codebooks || !x || !route || !y || !aligned(packed, 4)) return VQ_EINVAL;
   if (!workspace || !aligned(workspace, 256) || ws_bytes < vq_gemv_workspace_size(format, rows, cols, ntok, topk))
     return VQ_EWORKSPACE;
   if ((int64_t)ntok * topk >= 65536) return VQ_ERANGE;
   GemvArgs a;
   a.format = format;
-  a.idx = idx;
+  a.idx = packed;
   a.expert_stride = expert_stride;
   a.scales = scales;
   a.scale_stride = scale_stride;
@@ -315,26 +333,25 @@ int vq_dequant_gemv(int format, const uint8_t* idx, int64_t expert_stride, const
   a.route = route;
   a.y = y;
   a.hdr = (WsHeader*)workspace;
-  a.counters = (uint32_t*)((char*)workspace + kHeader);
-  a.partials = (float*)((char*)workspace + kHeader + align256(sizeof(uint32_t) * (size_t)ntok * (size_t)topk));
+  a.partials = (float*)((char*)workspace + kHeader);
   a.stream = (hipStream_t)stream;
   if ((st = device_cus(&a.ncu)) != VQ_OK) return st;
   return hip_status(launch_gemv(a));
 }
 
-int vq3r_dequant_gemv(const uint8_t* idx, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
+int vq3r_dequant_gemv(const uint8_t* packed, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
                       const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts, const uint16_t* x,
                       int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace, size_t ws_bytes,
                       void* stream) {
-  return vq_dequant_gemv(VQ_FMT_VQ3R, idx, expert_stride, scales, scale_stride, codebooks, rows, cols, n_experts, x,
+  return vq_dequant_gemv(VQ_FMT_VQ3R, packed, expert_stride, scales, scale_stride, codebooks, rows, cols, n_experts, x,
                          ntok, route, topk, y, workspace, ws_bytes, stream);
 }
 
-int vq4p_dequant_gemv(const uint8_t* idx, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
+int vq4p_dequant_gemv(const uint8_t* packed, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
                       const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts, const uint16_t* x,
                       int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace, size_t ws_bytes,
                       void* stream) {
-  return vq_dequant_gemv(VQ_FMT_VQ4P, idx, expert_stride, scales, scale_stride, codebooks, rows, cols, n_experts, x,
+  return vq_dequant_gemv(VQ_FMT_VQ4P, packed, expert_stride, scales, scale_stride, codebooks, rows, cols, n_experts, x,
                          ntok, route, topk, y, workspace, ws_bytes, stream);
 }
 

@@ -5,12 +5,19 @@
 // y[p][r] = s_r * sum_j sum_t T_t[j][i_t(r, j)],   T_t[j][e] = <C_t[e], x_j>
 // where x_j is the j-th 8-element slice of the token's activation. A work tile
 // is (token-slot pair p, block of J slices): its workgroup tabulates T for the
-// block's slices in LDS with fp32 matrix-core products (codewords x slices),
-// then streams the tile's stored records, one row per thread: each index costs
-// one table read and one add. Tile partial sums go to the workspace; the last
-// tile of a pair to finish adds the blocks in a fixed order and applies the
-// row scales, so results are deterministic. This equals sum_c W_hat[r][c] x[c]
-// up to fp32 rounding.
+// block's slices in LDS with fp32 matrix-core products (slices x codewords),
+// then streams the tile's records, one row per lane: each index costs one
+// table read and one add. Tile partial sums go to the workspace and a second
+// kernel adds the blocks in a fixed order and applies the row scales, so the
+// result is deterministic. It equals sum_c W_hat[r][c] x[c] up to fp32 rounding.
+//
+// Runtime layout ("packed"): the GEMV reads indices repacked once by
+// vq_gemv_pack into blocks of J slices x 64-row groups, with the records of
+// the 64 rows of a group interleaved in 12-byte chunks (4 records of one row):
+//   packed[b][g][c][lane][12 bytes] = records of row 64g+lane, slices J*b+4c..+3
+// so every wave load is one contiguous 768-byte piece of the stream and a
+// tile's data is contiguous (the row-interleave idea of the IQ1_S_R4 format
+// on the ik_llama.cpp page, applied to whole waves).
 #include "vq_launch.hpp"
 
 namespace vqk {
@@ -22,19 +29,68 @@ template <> struct GemvCfg<0> { static constexpr int J = 28; };  // 3 x 28 x 256
 template <> struct GemvCfg<1> { static constexpr int J = 56; };  // 4 x 56 x 64 x 4 B = 56 KB
 
 constexpr int GEMV_THREADS = 1024;
+constexpr int GROUP = 64;  // rows per interleaved group (one wave)
 
+inline int gemv_J(int format) { return format == 0 ? GemvCfg<0>::J : GemvCfg<1>::J; }
+
+int64_t gemv_packed_bytes(int format, int64_t rows, int64_t cols) {
+  const int64_t J = gemv_J(format);
+  const int64_t nblk = (cols / DIM + J - 1) / J;
+  const int64_t ng = (rows + GROUP - 1) / GROUP;
+  return nblk * ng * GROUP * J * 3;
+}
+
+// ------------------------------------------------------------------ repack
+// One thread per 12-byte chunk of the packed layout; pad rows / slices are 0.
+template <int J>
+__global__ __launch_bounds__(256) void k_gemv_pack(const uint8_t* idx, int64_t rows, int64_t V, int64_t n_experts,
+                                                   uint8_t* out, int64_t packed_stride) {
+  constexpr int NC = J / 4;
+  const int64_t ng = (rows + GROUP - 1) / GROUP, nblk = (V + J - 1) / J;
+  const int64_t per_expert = nblk * ng * NC * GROUP;
+  const int64_t total = per_expert * n_experts;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = q / per_expert, rem = q % per_expert;
+    const int lane = (int)(rem % GROUP);
+    const int64_t c = (rem / GROUP) % NC, g = (rem / (GROUP * NC)) % ng, b = rem / (GROUP * NC * ng);
+    const int64_t row = g * GROUP + lane;
+    uint8_t buf[12];
+#pragma unroll
+    for (int k = 0; k < 12; ++k) buf[k] = 0;
+    if (row < rows) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int64_t j = b * J + c * 4 + qq;
+        if (j < V) {
+          const uint8_t* src = idx + ((e * rows + row) * V + j) * 3;
+          buf[3 * qq] = src[0];
+          buf[3 * qq + 1] = src[1];
+          buf[3 * qq + 2] = src[2];
+        }
+      }
+    }
+    uint32_t* dst =
+        reinterpret_cast<uint32_t*>(out + e * packed_stride + ((b * ng + g) * NC + c) * (GROUP * 12) + lane * 12);
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      dst[k] = (uint32_t)buf[4 * k] | ((uint32_t)buf[4 * k + 1] << 8) | ((uint32_t)buf[4 * k + 2] << 16) |
+               ((uint32_t)buf[4 * k + 3] << 24);
+  }
+}
+
+// ------------------------------------------------------------------ tables
 template <int FMT>
 __device__ inline void gemv_build_lut(float* lut, const float* cb_g, const uint16_t* xrow, int64_t j0, int nsl) {
   // LUT[t][m][e] = sum_k C_t[e][k] * x[(j0 + m)*8 + k]  (slices on M, codewords on N)
   constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, J = GemvCfg<FMT>::J;
-  constexpr int MT = (J + 31) / 32;        // slice tiles of 32
-  constexpr int NT = K / 32;               // codeword tiles of 32
+  constexpr int MT = (J + 31) / 32;  // slice tiles of 32
+  constexpr int NT = K / 32;         // codeword tiles of 32
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int h = lane >> 5, i = lane & 31;
   for (int task = wave; task < S * MT * NT; task += nw) {
     const int t = task / (MT * NT), mt = (task / NT) % MT, nt = task % NT;
-    const int m = mt * 32 + i;                    // slice row of the A operand
-    const int e = nt * 32 + i;                    // codeword column of the B operand
+    const int m = mt * 32 + i;  // slice row of the A operand
+    const int e = nt * 32 + i;  // codeword column of the B operand
     const bool mv = m < nsl;
     f16v acc = {};
 #pragma unroll
@@ -53,100 +109,91 @@ __device__ inline void gemv_build_lut(float* lut, const float* cb_g, const uint1
   }
 }
 
-// Tile order: the tiles of each XCD-sized share are contiguous (pair-major,
-// block-minor) so neighbouring blocks of a row, which share cache lines of the
-// index stream, run on the same XCD (workgroups are dealt to the 8 XCDs in turn).
+// Tile order: the tiles of each XCD share are contiguous (pair-major, block-minor):
+// workgroups are dealt to the 8 XCDs in turn.
 __device__ inline int64_t tile_of_block(int64_t bid, int64_t ntiles_pad) {
   const int64_t per_xcd = ntiles_pad / 8;
   return (bid % 8) * per_xcd + bid / 8;
 }
 
-template <int FMT, bool FAST>
-__global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* idx, int64_t expert_stride,
-                                                       const uint16_t* scales, int64_t scale_stride,
-                                                       const float* cb_g, int64_t rows, int64_t cols, int n_experts,
-                                                       const uint16_t* x, int topk, const int32_t* route, float* y,
-                                                       float* partials, uint32_t* counters, int nblk,
-                                                       int64_t ntiles, int64_t ntiles_pad, WsHeader* hdr) {
-  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, J = GemvCfg<FMT>::J;
-  static_assert((3 * J) % 4 == 0, "records of a block end on a dword boundary");
+template <int FMT>
+__global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_t expert_stride, const float* cb_g,
+                                                       int64_t rows, int64_t cols, int n_experts, const uint16_t* x,
+                                                       int topk, const int32_t* route, float* partials, int nblk,
+                                                       int64_t ntiles, int64_t ntiles_pad) {
+  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, J = GemvCfg<FMT>::J, NC = J / 4;
   __shared__ float lut[S * J * K];
-  __shared__ int last_flag;
   const int64_t tile = tile_of_block(blockIdx.x, ntiles_pad);
   if (tile >= ntiles) return;
   const int p = (int)(tile / nblk), b = (int)(tile % nblk);
   const int tok = p / topk;
   const int e = route[p];
-  const bool bad = e < 0 || e >= n_experts;
+  if (e < 0 || e >= n_experts) return;  // flagged and zeroed by k_gemv_reduce
   const int64_t V = cols / DIM;
   const int64_t j0 = (int64_t)b * J;
   const int nsl = (int)((V - j0) < J ? (V - j0) : J);
-  if (!bad) gemv_build_lut<FMT>(lut, cb_g, x + (int64_t)tok * cols, j0, nsl);
+  gemv_build_lut<FMT>(lut, cb_g, x + (int64_t)tok * cols, j0, nsl);
   __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int64_t ng = (rows + GROUP - 1) / GROUP;
+  const uint8_t* tb = pk + (int64_t)e * expert_stride + (int64_t)b * ng * NC * (GROUP * 12);
   float* part = partials + ((int64_t)p * nblk + b) * rows;
-  if (bad) {
-    if (threadIdx.x == 0 && b == 0) flag_status(hdr, ST_ROUTE);
-  } else {
-    const uint8_t* base = idx + (int64_t)e * expert_stride + j0 * 3;
-    for (int64_t r = threadIdx.x; r < rows; r += blockDim.x) {
-      const uint8_t* rec = base + r * V * 3;
-      float acc = 0.0f;
-      if constexpr (FAST) {
-        // J records = 3*J bytes, dword aligned: 3*J/4 dwords
-        constexpr int ND = 3 * J / 4;
-        uint32_t d[ND];
-        const uint32_t* p32 = reinterpret_cast<const uint32_t*>(rec);
+  for (int64_t g = wave; g < ng; g += nw) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(tb + g * NC * (GROUP * 12)) + lane * 3;
+    uint32_t d[NC][3];
 #pragma unroll
-        for (int q = 0; q < ND; ++q) d[q] = __builtin_nontemporal_load(p32 + q);
+    for (int c = 0; c < NC; ++c) {
 #pragma unroll
-        for (int m = 0; m < J; ++m) {
-          // record m = bytes 3m, 3m+1, 3m+2 of the stream
-          // (3*J is a multiple of 4, so the last record starts at byte offset 1
-          // of the last dword and never needs the dword after it)
-          uint32_t w;
-          const int byte0 = 3 * m, q0 = byte0 >> 2, o = byte0 & 3;
-          if (o <= 1) w = d[q0] >> (8 * o);
-          else w = (d[q0] >> (8 * o)) | (d[q0 + 1] << (32 - 8 * o));
-          float tsum = 0.0f;
-#pragma unroll
-          for (int t = 0; t < S; ++t) tsum += lut[(t * J + m) * K + record_index<FMT>(w, t)];
-          acc += tsum;
-        }
-      } else {
-        for (int m = 0; m < nsl; ++m) {
-          const uint32_t w = load_record(rec + m * 3);
-          float tsum = 0.0f;
-#pragma unroll
-          for (int t = 0; t < S; ++t) tsum += lut[(t * J + m) * K + record_index<FMT>(w, t)];
-          acc += tsum;
-        }
-      }
-      part[r] = acc;
+      for (int k = 0; k < 3; ++k) d[c][k] = src[c * (GROUP * 3) + k];
     }
-  }
-  // the last tile of pair p to finish reduces its blocks in order
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) last_flag = (atomicAdd(&counters[p], 1u) == (uint32_t)(nblk - 1));
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  const float* pp = partials + (int64_t)p * nblk * rows;
-  for (int64_t r = threadIdx.x; r < rows; r += blockDim.x) {
     float acc = 0.0f;
-    if (!bad) {
-      for (int q = 0; q < nblk; ++q) acc += pp[(int64_t)q * rows + r];
-      acc *= f16_bits_to_f32(scales[(int64_t)e * scale_stride + r]);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // record q of the chunk = bytes 3q .. 3q+2 of the 12 bytes
+        const int byte0 = 3 * q, k0 = byte0 >> 2, o = byte0 & 3;
+        const uint32_t w =
+            (o <= 1) ? (d[c][k0] >> (8 * o)) : ((d[c][k0] >> (8 * o)) | (d[c][k0 + 1] << (32 - 8 * o)));
+        const int m = 4 * c + q;
+        float tsum = 0.0f;
+#pragma unroll
+        for (int t = 0; t < S; ++t) tsum += lut[(t * J + m) * K + record_index<FMT>(w, t)];
+        acc += tsum;
+      }
     }
-    y[(int64_t)p * rows + r] = acc;
+    const int64_t row = g * GROUP + lane;
+    if (row < rows) part[row] = acc;
   }
-  if (threadIdx.x == 0) counters[p] = 0u;  // ready for the next call
 }
 
-__global__ void k_gemv_reset(WsHeader* hdr, uint32_t* counters, int npairs) {
-  const int q = blockIdx.x * blockDim.x + threadIdx.x;
-  if (q == 0) hdr->flags = 0;
-  if (q < npairs) counters[q] = 0u;
+// y[p][r] = s_r * sum over blocks in a fixed order. Also writes the status
+// flags of the call (route ids outside [0, n_experts)), so no reset is needed.
+__global__ __launch_bounds__(256) void k_gemv_reduce(const float* partials, const uint16_t* scales,
+                                                     int64_t scale_stride, const int32_t* route, int n_experts,
+                                                     int64_t rows, int nblk, int npairs, float* y, WsHeader* hdr) {
+  const int p = blockIdx.y;
+  const int e = route[p];
+  const bool bad = e < 0 || e >= n_experts;
+  if (blockIdx.x == 0 && p == 0 && threadIdx.x < 64) {
+    bool any = false;
+    for (int q = threadIdx.x; q < npairs; q += 64) any |= (route[q] < 0 || route[q] >= n_experts);
+    any = __any(any);
+    if (threadIdx.x == 0) hdr->flags = any ? ST_ROUTE : 0u;
+  }
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  float acc = 0.0f;
+  if (!bad) {
+    const float* pp = partials + (int64_t)p * nblk * rows + r;
+    for (int q = 0; q < nblk; ++q) acc += pp[(int64_t)q * rows];
+    acc *= f16_bits_to_f32(scales[(int64_t)e * scale_stride + r]);
+  }
+  y[(int64_t)p * rows + r] = acc;
+}
+
+__global__ void k_gemv_clear(WsHeader* hdr) {
+  if (threadIdx.x == 0) hdr->flags = 0;
 }
 
 template <int FMT>
@@ -157,31 +204,43 @@ static hipError_t launch_gemv_t(const GemvArgs& a) {
   const int nblk = (int)((V + J - 1) / J);
   const int64_t ntiles = npairs * nblk;
   const int64_t ntiles_pad = (ntiles + 7) / 8 * 8;
-  k_gemv_reset<<<(unsigned)((npairs + 255) / 256), 256, 0, a.stream>>>(a.hdr, a.counters, (int)npairs);
-  const bool fast = (V % 4 == 0) && (V % J == 0);
-  if (fast)
-    k_gemv<FMT, true><<<(unsigned)ntiles_pad, GEMV_THREADS, 0, a.stream>>>(
-        a.idx, a.expert_stride, a.scales, a.scale_stride, a.codebooks, a.rows, a.cols, a.n_experts, a.x, a.topk,
-        a.route, a.y, a.partials, a.counters, nblk, ntiles, ntiles_pad, a.hdr);
-  else
-    k_gemv<FMT, false><<<(unsigned)ntiles_pad, GEMV_THREADS, 0, a.stream>>>(
-        a.idx, a.expert_stride, a.scales, a.scale_stride, a.codebooks, a.rows, a.cols, a.n_experts, a.x, a.topk,
-        a.route, a.y, a.partials, a.counters, nblk, ntiles, ntiles_pad, a.hdr);
+  k_gemv<FMT><<<(unsigned)ntiles_pad, GEMV_THREADS, 0, a.stream>>>(a.idx, a.expert_stride, a.codebooks, a.rows,
+                                                                    a.cols, a.n_experts, a.x, a.topk, a.route,
+                                                                    a.partials, nblk, ntiles, ntiles_pad);
+  dim3 g2((unsigned)((a.rows + 255) / 256), (unsigned)npairs);
+  k_gemv_reduce<<<g2, 256, 0, a.stream>>>(a.partials, a.scales, a.scale_stride, a.route, a.n_experts, a.rows, nblk,
+                                          (int)npairs, a.y, a.hdr);
   return hipGetLastError();
 }
 
 int64_t gemv_partials_floats(int format, int64_t rows, int64_t cols, int64_t npairs) {
-  const int J = format == 0 ? GemvCfg<0>::J : GemvCfg<1>::J;
+  const int64_t J = gemv_J(format);
   const int64_t nblk = (cols / DIM + J - 1) / J;
   return npairs * nblk * rows;
 }
 
 hipError_t launch_gemv(const GemvArgs& a) {
   if ((int64_t)a.ntok * a.topk == 0 || a.rows == 0) {
-    k_gemv_reset<<<1, 64, 0, a.stream>>>(a.hdr, a.counters, 0);
+    k_gemv_clear<<<1, 64, 0, a.stream>>>(a.hdr);
     return hipGetLastError();
   }
   return a.format == 0 ? launch_gemv_t<0>(a) : launch_gemv_t<1>(a);
+}
+
+hipError_t launch_gemv_pack(int format, const uint8_t* idx, int64_t rows, int64_t cols, int64_t n_experts,
+                            uint8_t* out, int ncu, hipStream_t s) {
+  const int64_t J = gemv_J(format);
+  const int64_t V = cols / DIM;
+  const int64_t nchunks = ((V + J - 1) / J) * ((rows + GROUP - 1) / GROUP) * (J / 4) * GROUP * n_experts;
+  if (nchunks == 0) return hipSuccess;
+  int64_t g = (nchunks + 255) / 256;
+  if (g > (int64_t)ncu * 32) g = (int64_t)ncu * 32;
+  const int64_t stride = gemv_packed_bytes(format, rows, cols);
+  if (format == 0)
+    k_gemv_pack<GemvCfg<0>::J><<<(unsigned)g, 256, 0, s>>>(idx, rows, V, n_experts, out, stride);
+  else
+    k_gemv_pack<GemvCfg<1>::J><<<(unsigned)g, 256, 0, s>>>(idx, rows, V, n_experts, out, stride);
+  return hipGetLastError();
 }
 
 }  // namespace vqk

@@ -78,8 +78,7 @@ struct GemvArgs {
   int ntok, topk;
   const int32_t* route;
   float* y;
-  float* partials;     // [ntok*topk][nblk][rows]
-  uint32_t* counters;  // [ntok*topk] tiles finished per pair
+  float* partials;  // [ntok*topk][nblk][rows]
   WsHeader* hdr;
   int ncu;
   hipStream_t stream;
@@ -95,8 +94,11 @@ struct Mxfp4Args {
   hipStream_t stream;
 };
 
-// Floats of GEMV tile partial sums for the workspace size query.
+// GEMV sizes: floats of tile partial sums (workspace), bytes of one packed expert.
 int64_t gemv_partials_floats(int format, int64_t rows, int64_t cols, int64_t npairs);
+int64_t gemv_packed_bytes(int format, int64_t rows, int64_t cols);
+hipError_t launch_gemv_pack(int format, const uint8_t* idx, int64_t rows, int64_t cols, int64_t n_experts,
+                            uint8_t* out, int ncu, hipStream_t s);
 
 hipError_t launch_reset(WsHeader* hdr, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs& a);

@@ -131,11 +131,16 @@ def test_decode_gemv_error_mxfp4_argument_errors():
     assert L.vq_encode(0, 0, None, 0, 0, 64, None, None, None, None, 0, None) == VQ_OK   # empty: no access
     assert L.vq_decode(0, a.ptr, b.ptr, c.ptr, 0, 64, 3, d.ptr, None) == VQ_OK
     n_ws = L.vq_gemv_workspace_size(0, 4, 64, 2, 2)
-    g = lambda **k: L.vq_dequant_gemv(0, a.ptr, k.get("es", 4 * 8 * 3), b.ptr, 4, c.ptr, 4, 64,
+    pk = L.vq_gemv_packed_size(0, 4, 64)
+    assert pk == 64 * 28 * 3            # one 64-row group x one block of 28 slices
+    assert L.vq_gemv_packed_size(1, 2048, 7168) == 2048 * 896 * 3
+    assert L.vq_gemv_pack(0, a.ptr, 4, 64, 2, ctypes.c_void_p(b.ptr.value + 2), None) == VQ_EINVAL
+    g = lambda **k: L.vq_dequant_gemv(0, a.ptr, k.get("es", pk), b.ptr, 4, c.ptr, 4, 64,
                                       k.get("ne", 2), d.ptr, k.get("nt", 2), e.ptr, 2, f.ptr, ws.ptr,
                                       k.get("wsn", n_ws), None)
     assert g(ne=0) == VQ_EINVAL
-    assert g(es=10) == VQ_EINVAL          # stride smaller than one expert's records
+    assert g(es=pk - 4) == VQ_EINVAL      # stride smaller than one packed expert
+    assert g(es=pk + 2) == VQ_EINVAL      # stride not a multiple of 4
     assert g(nt=-1) == VQ_EINVAL
     assert g(wsn=16) == VQ_EWORKSPACE
     assert L.vq_error(0, a.ptr, 0, b.ptr, c.ptr, d.ptr, 0, 4, 64, e.ptr, ws.ptr, 1 << 12, None) == VQ_EINVAL

@@ -286,8 +286,9 @@ def test_gemv_matches_oracle(cfg1, fmt, shape):
     recs, scs, whs = _experts(fmt, cb, E, rows, cols, seed=40)
     x = synthetic.activations_f16(ntok, cols, seed=1)
     route = synthetic.routing(ntok, E, topk, seed=2)
-    y = vq.dequant_gemv(to_dev(recs), to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
-                        to_dev(route), fmt=fmt).cpu().numpy()
+    packed = vq.gemv_pack(to_dev(recs), fmt=fmt)
+    y = vq.dequant_gemv(packed, to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
+                        to_dev(route), rows, cols, fmt=fmt).cpu().numpy()
     xf = synthetic.f16_bits_to_f32(x).reshape(ntok, cols)
     for b in range(ntok):
         for k in range(topk):
@@ -302,9 +303,35 @@ def test_gemv_bad_route_flagged(cfg1):
     recs, scs, _ = _experts("vq3r", cb, 2, 32, 64, seed=3)
     x = synthetic.activations_f16(1, 64, seed=1)
     route = np.array([[0, 5]], np.int32)
+    packed = vq.gemv_pack(to_dev(recs))
     with pytest.raises(vq.VQError):
-        vq.dequant_gemv(to_dev(recs), to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
-                        to_dev(route), check=True)
+        vq.dequant_gemv(packed, to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
+                        to_dev(route), 32, 64, check=True)
+    # the valid slot is still computed; the bad one is zero
+    y = vq.dequant_gemv(packed, to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
+                        to_dev(route), 32, 64).cpu().numpy()
+    assert np.all(y[0, 1] == 0) and np.any(y[0, 0] != 0)
+
+
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+@pytest.mark.parametrize("shape", [(1, 8), (64, 224), (70, 456), (128, 7168)])
+def test_gemv_pack_layout(fmt, shape):
+    """The packed layout is a pure permutation of the stored records: blocks of J
+    slices x 64-row groups, 4 records (12 bytes) per lane chunk, zero padding."""
+    say("gemv pack layout", fmt, shape)
+    rows, cols = shape
+    V = cols // 8
+    J = 28 if fmt == "vq3r" else 56
+    rng = np.random.default_rng(rows + cols)
+    E = 2
+    rec = rng.integers(0, 256, size=(E, rows, V, 3), dtype=np.uint8)
+    got = vq.gemv_pack(to_dev(rec), fmt=fmt).cpu().numpy()
+    nblk, ng = -(-V // J), -(-rows // 64)
+    pad = np.zeros((E, ng * 64, nblk * J, 3), np.uint8)
+    pad[:, :rows, :V] = rec
+    # [E][g][lane][b][c][4 records][3] -> [E][b][g][c][lane][12]
+    want = pad.reshape(E, ng, 64, nblk, J // 4, 12).transpose(0, 3, 1, 4, 2, 5).reshape(E, -1)
+    assert got.shape == want.shape and np.array_equal(got, want)
 
 
 # ------------------------------------------------------------------ MXFP4
