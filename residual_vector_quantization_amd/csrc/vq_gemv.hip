@@ -12,41 +12,46 @@
 // result is deterministic. It equals sum_c W_hat[r][c] x[c] up to fp32 rounding.
 //
 // Runtime layout ("packed"): the GEMV reads indices repacked once by
-// vq_gemv_pack into blocks of J slices x 64-row groups, with the records of
-// the 64 rows of a group interleaved in 12-byte chunks (4 records of one row):
-//   packed[b][g][c][lane][12 bytes] = records of row 64g+lane, slices J*b+4c..+3
-// so every wave load is one contiguous 768-byte piece of the stream and a
-// tile's data is contiguous (the row-interleave idea of the IQ1_S_R4 format
-// on the ik_llama.cpp page, applied to whole waves).
+// vq_gemv_pack into blocks of J = 32 slices x 64-row groups. Within a group
+// the records are interleaved in 12-byte chunks (4 records of one row), and
+// each row's slices are rotated by its lane:
+//   packed[b][g][c][lane][12 bytes] = records of row 64g+lane for the slices
+//   32b + ((4c + q + lane) mod 32), q = 0..3
+// so every wave load is one contiguous 768-byte piece of the stream, a tile's
+// data is contiguous, and at step m lane l works on slice (m + l) mod 32 (the
+// row-interleave idea of the IQ1_S_R4 format on the ik_llama.cpp page, applied
+// to whole waves). The tables are stored slice-minor,
+//   T[(e * S + t) * R + replica][slice],
+// so the lanes of one table read hit distinct slices, i.e. distinct LDS banks
+// (R = 2 replicas for VQ4P, one per half-wave, making its reads conflict-free;
+// VQ3R keeps one copy, 96 KB).
 #include "vq_launch.hpp"
 
 namespace vqk {
 
 typedef float f16v __attribute__((ext_vector_type(16)));
 
-template <int FMT> struct GemvCfg;
-template <> struct GemvCfg<0> { static constexpr int J = 28; };  // 3 x 28 x 256 x 4 B = 84 KB of tables
-template <> struct GemvCfg<1> { static constexpr int J = 56; };  // 4 x 56 x 64 x 4 B = 56 KB
-
-constexpr int GEMV_THREADS = 1024;
+constexpr int GJ = 32;     // slices per block
 constexpr int GROUP = 64;  // rows per interleaved group (one wave)
+constexpr int GEMV_THREADS = 1024;  // 16 waves (LutOps assumes 16)
 
-inline int gemv_J(int format) { return format == 0 ? GemvCfg<0>::J : GemvCfg<1>::J; }
+template <int FMT> struct GemvCfg;
+template <> struct GemvCfg<0> { static constexpr int R = 1; };  // 256 x 3 x 32 x 4 B = 96 KB
+template <> struct GemvCfg<1> { static constexpr int R = 2; };  // 64 x 4 x 2 x 32 x 4 B = 64 KB
 
 int64_t gemv_packed_bytes(int format, int64_t rows, int64_t cols) {
-  const int64_t J = gemv_J(format);
-  const int64_t nblk = (cols / DIM + J - 1) / J;
+  (void)format;
+  const int64_t nblk = (cols / DIM + GJ - 1) / GJ;
   const int64_t ng = (rows + GROUP - 1) / GROUP;
-  return nblk * ng * GROUP * J * 3;
+  return nblk * ng * GROUP * GJ * 3;
 }
 
 // ------------------------------------------------------------------ repack
 // One thread per 12-byte chunk of the packed layout; pad rows / slices are 0.
-template <int J>
 __global__ __launch_bounds__(256) void k_gemv_pack(const uint8_t* idx, int64_t rows, int64_t V, int64_t n_experts,
                                                    uint8_t* out, int64_t packed_stride) {
-  constexpr int NC = J / 4;
-  const int64_t ng = (rows + GROUP - 1) / GROUP, nblk = (V + J - 1) / J;
+  constexpr int NC = GJ / 4;
+  const int64_t ng = (rows + GROUP - 1) / GROUP, nblk = (V + GJ - 1) / GJ;
   const int64_t per_expert = nblk * ng * NC * GROUP;
   const int64_t total = per_expert * n_experts;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (int64_t)gridDim.x * blockDim.x) {
@@ -60,7 +65,7 @@ __global__ __launch_bounds__(256) void k_gemv_pack(const uint8_t* idx, int64_t r
     if (row < rows) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const int64_t j = b * J + c * 4 + qq;
+        const int64_t j = b * GJ + ((c * 4 + qq + lane) % GJ);
         if (j < V) {
           const uint8_t* src = idx + ((e * rows + row) * V + j) * 3;
           buf[3 * qq] = src[0];
@@ -79,32 +84,61 @@ __global__ __launch_bounds__(256) void k_gemv_pack(const uint8_t* idx, int64_t r
 }
 
 // ------------------------------------------------------------------ tables
+// T[(e*S + t)*R + rep][m] = sum_k C_t[e][k] * x[(j0 + m)*8 + k] with fp32
+// matrix cores, codewords on M and slices on N (so that the 32 lanes of a
+// half-wave write 32 consecutive slices). The operands of a wave's tasks are
+// loaded first (lut_load), the MFMAs run later (lut_compute): the index
+// stream prefetch is issued in between, so waiting for the table operands
+// never waits for the (later) index loads.
 template <int FMT>
-__device__ inline void gemv_build_lut(float* lut, const float* cb_g, const uint16_t* xrow, int64_t j0, int nsl) {
-  // LUT[t][m][e] = sum_k C_t[e][k] * x[(j0 + m)*8 + k]  (slices on M, codewords on N)
-  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, J = GemvCfg<FMT>::J;
-  constexpr int MT = (J + 31) / 32;  // slice tiles of 32
-  constexpr int NT = K / 32;         // codeword tiles of 32
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+struct LutOps {
+  static constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, NT = K / 32, TASKS = S * NT;
+  static constexpr int PER_WAVE = (TASKS + 15) / 16;  // 16 waves per workgroup
+  float a[PER_WAVE][4], b[PER_WAVE][4];
+};
+
+template <int FMT>
+__device__ inline void lut_load(LutOps<FMT>& op, const float* cb_g, const uint16_t* xrow, int64_t j0, int nsl) {
+  using O = LutOps<FMT>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, i = lane & 31;
-  for (int task = wave; task < S * MT * NT; task += nw) {
-    const int t = task / (MT * NT), mt = (task / NT) % MT, nt = task % NT;
-    const int m = mt * 32 + i;  // slice row of the A operand
-    const int e = nt * 32 + i;  // codeword column of the B operand
-    const bool mv = m < nsl;
-    f16v acc = {};
+  const int ic = i < nsl ? i : 0;  // clamped slice: loaded but zeroed
+#pragma unroll
+  for (int u = 0; u < O::PER_WAVE; ++u) {
+    const int task = wave + 16 * u;
+    const int tk = task < O::TASKS ? task : 0;
+    const int t = tk / O::NT, ct = tk % O::NT;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int k = 2 * s + h;
-      const float a = mv ? f16_bits_to_f32(xrow[(j0 + m) * DIM + k]) : 0.0f;
-      const float b = cb_g[((size_t)t * K + e) * DIM + k];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+      op.a[u][s] = cb_g[((size_t)t * O::K + ct * 32 + i) * DIM + k];
+      op.b[u][s] = f16_bits_to_f32(xrow[(j0 + ic) * DIM + k]);
     }
-    // lane (n = codeword, h) holds rows m = 8*(v/4) + 4h + v%4 of the tile
+  }
+}
+
+template <int FMT>
+__device__ inline void lut_compute(const LutOps<FMT>& op, float* lut, int nsl) {
+  using O = LutOps<FMT>;
+  constexpr int R = GemvCfg<FMT>::R;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, i = lane & 31;
+  const bool sv = i < nsl;
+#pragma unroll
+  for (int u = 0; u < O::PER_WAVE; ++u) {
+    const int task = wave + 16 * u;
+    if (task >= O::TASKS) break;  // wave-uniform
+    const int t = task / O::NT, ct = task % O::NT;
+    f16v acc = {};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(op.a[u][s], sv ? op.b[u][s] : 0.0f, acc, 0, 0, 0);
+    // lane (n = slice i, h) holds codewords e = 32ct + 8*(v/4) + 4h + v%4
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int mm = mt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-      if (mm < J) lut[((size_t)t * J + mm) * K + e] = acc[v];
+      const int e = ct * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+#pragma unroll
+      for (int rep = 0; rep < R; ++rep) lut[((e * O::S + t) * R + rep) * GJ + i] = acc[v];
     }
   }
 }
@@ -121,8 +155,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
                                                        int64_t rows, int64_t cols, int n_experts, const uint16_t* x,
                                                        int topk, const int32_t* route, float* partials, int nblk,
                                                        int64_t ntiles, int64_t ntiles_pad) {
-  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, J = GemvCfg<FMT>::J, NC = J / 4;
-  __shared__ float lut[S * J * K];
+  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, R = GemvCfg<FMT>::R, NC = GJ / 4;
+  __shared__ float lut[K * S * R * GJ];
   const int64_t tile = tile_of_block(blockIdx.x, ntiles_pad);
   if (tile >= ntiles) return;
   const int p = (int)(tile / nblk), b = (int)(tile % nblk);
@@ -130,22 +164,40 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
   const int e = route[p];
   if (e < 0 || e >= n_experts) return;  // flagged and zeroed by k_gemv_reduce
   const int64_t V = cols / DIM;
-  const int64_t j0 = (int64_t)b * J;
-  const int nsl = (int)((V - j0) < J ? (V - j0) : J);
-  gemv_build_lut<FMT>(lut, cb_g, x + (int64_t)tok * cols, j0, nsl);
-  __syncthreads();
+  const int64_t j0 = (int64_t)b * GJ;
+  const int nsl = (int)((V - j0) < GJ ? (V - j0) : GJ);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int64_t ng = (rows + GROUP - 1) / GROUP;
   const uint8_t* tb = pk + (int64_t)e * expert_stride + (int64_t)b * ng * NC * (GROUP * 12);
   float* part = partials + ((int64_t)p * nblk + b) * rows;
-  for (int64_t g = wave; g < ng; g += nw) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(tb + g * NC * (GROUP * 12)) + lane * 3;
-    uint32_t d[NC][3];
+  // Each wave owns row groups wave, wave + nw, wave + 2nw, ... handled two at a
+  // time. The first two groups are loaded before the tables are built (after
+  // the table operands, so waiting for those never waits for the index
+  // stream) and unconditionally (clamped group index), so the HBM latency of
+  // the index stream overlaps the table construction.
+  uint32_t dA[NC][3], dB[NC][3];
+  auto load_group = [&](uint32_t (&d)[NC][3], int64_t g) {
+    const int64_t gc = g < ng ? g : ng - 1;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(tb + gc * NC * (GROUP * 12)) + lane * 3;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
       for (int k = 0; k < 3; ++k) d[c][k] = src[c * (GROUP * 3) + k];
     }
+  };
+  LutOps<FMT> ops;
+  lut_load<FMT>(ops, cb_g, x + (int64_t)tok * cols, j0, nsl);
+  __builtin_amdgcn_sched_barrier(0);  // keep the table operand loads ahead of the index stream
+  load_group(dA, wave);
+  load_group(dB, wave + nw);
+  __builtin_amdgcn_sched_barrier(0);
+  lut_compute<FMT>(ops, lut, nsl);
+  __syncthreads();
+  // byte offset of (slice (m + lane) mod 32, replica) inside one (e, t) row of the table
+  const uint32_t rep_off = (R == 2) ? (uint32_t)(lane >> 5) * (GJ * 4) : 0u;
+  constexpr uint32_t E_STRIDE = S * R * GJ * 4, T_STRIDE = R * GJ * 4;
+  const char* lbase = reinterpret_cast<const char*>(lut);
+  auto consume = [&](const uint32_t (&d)[NC][3], int64_t g) {
     float acc = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -156,14 +208,26 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
         const uint32_t w =
             (o <= 1) ? (d[c][k0] >> (8 * o)) : ((d[c][k0] >> (8 * o)) | (d[c][k0 + 1] << (32 - 8 * o)));
         const int m = 4 * c + q;
+        const uint32_t soff = (((uint32_t)(m + lane) & (GJ - 1)) << 2) + rep_off;
         float tsum = 0.0f;
 #pragma unroll
-        for (int t = 0; t < S; ++t) tsum += lut[(t * J + m) * K + record_index<FMT>(w, t)];
+        for (int t = 0; t < S; ++t) {
+          const uint32_t ei = (uint32_t)record_index<FMT>(w, t);
+          tsum += *reinterpret_cast<const float*>(lbase + (ei * E_STRIDE + soff) + t * T_STRIDE);
+        }
         acc += tsum;
       }
     }
     const int64_t row = g * GROUP + lane;
-    if (row < rows) part[row] = acc;
+    if (g < ng && row < rows) part[row] = acc;
+  };
+  for (int64_t g = wave; g < ng; g += 2 * nw) {
+    if (g != wave) {
+      load_group(dA, g);
+      load_group(dB, g + nw);
+    }
+    consume(dA, g);
+    consume(dB, g + nw);
   }
 }
 
@@ -186,7 +250,16 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* partials, cons
   float acc = 0.0f;
   if (!bad) {
     const float* pp = partials + (int64_t)p * nblk * rows + r;
-    for (int q = 0; q < nblk; ++q) acc += pp[(int64_t)q * rows];
+    // eight independent loads in flight, added in block order
+    int q = 0;
+    for (; q + 8 <= nblk; q += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pp[(int64_t)(q + u) * rows];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; q < nblk; ++q) acc += pp[(int64_t)q * rows];
     acc *= f16_bits_to_f32(scales[(int64_t)e * scale_stride + r]);
   }
   y[(int64_t)p * rows + r] = acc;
@@ -198,10 +271,9 @@ __global__ void k_gemv_clear(WsHeader* hdr) {
 
 template <int FMT>
 static hipError_t launch_gemv_t(const GemvArgs& a) {
-  constexpr int J = GemvCfg<FMT>::J;
   const int64_t npairs = (int64_t)a.ntok * a.topk;
   const int64_t V = a.cols / DIM;
-  const int nblk = (int)((V + J - 1) / J);
+  const int nblk = (int)((V + GJ - 1) / GJ);
   const int64_t ntiles = npairs * nblk;
   const int64_t ntiles_pad = (ntiles + 7) / 8 * 8;
   k_gemv<FMT><<<(unsigned)ntiles_pad, GEMV_THREADS, 0, a.stream>>>(a.idx, a.expert_stride, a.codebooks, a.rows,
@@ -214,8 +286,8 @@ static hipError_t launch_gemv_t(const GemvArgs& a) {
 }
 
 int64_t gemv_partials_floats(int format, int64_t rows, int64_t cols, int64_t npairs) {
-  const int64_t J = gemv_J(format);
-  const int64_t nblk = (cols / DIM + J - 1) / J;
+  (void)format;
+  const int64_t nblk = (cols / DIM + GJ - 1) / GJ;
   return npairs * nblk * rows;
 }
 
@@ -229,17 +301,12 @@ hipError_t launch_gemv(const GemvArgs& a) {
 
 hipError_t launch_gemv_pack(int format, const uint8_t* idx, int64_t rows, int64_t cols, int64_t n_experts,
                             uint8_t* out, int ncu, hipStream_t s) {
-  const int64_t J = gemv_J(format);
   const int64_t V = cols / DIM;
-  const int64_t nchunks = ((V + J - 1) / J) * ((rows + GROUP - 1) / GROUP) * (J / 4) * GROUP * n_experts;
+  const int64_t nchunks = ((V + GJ - 1) / GJ) * ((rows + GROUP - 1) / GROUP) * (GJ / 4) * GROUP * n_experts;
   if (nchunks == 0) return hipSuccess;
   int64_t g = (nchunks + 255) / 256;
   if (g > (int64_t)ncu * 32) g = (int64_t)ncu * 32;
-  const int64_t stride = gemv_packed_bytes(format, rows, cols);
-  if (format == 0)
-    k_gemv_pack<GemvCfg<0>::J><<<(unsigned)g, 256, 0, s>>>(idx, rows, V, n_experts, out, stride);
-  else
-    k_gemv_pack<GemvCfg<1>::J><<<(unsigned)g, 256, 0, s>>>(idx, rows, V, n_experts, out, stride);
+  k_gemv_pack<<<(unsigned)g, 256, 0, s>>>(idx, rows, V, n_experts, out, gemv_packed_bytes(format, rows, cols));
   return hipGetLastError();
 }
 

@@ -316,12 +316,13 @@ def test_gemv_bad_route_flagged(cfg1):
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
 @pytest.mark.parametrize("shape", [(1, 8), (64, 224), (70, 456), (128, 7168)])
 def test_gemv_pack_layout(fmt, shape):
-    """The packed layout is a pure permutation of the stored records: blocks of J
-    slices x 64-row groups, 4 records (12 bytes) per lane chunk, zero padding."""
+    """The packed layout is a pure permutation of the stored records: blocks of 32
+    slices x 64-row groups, 4 records (12 bytes) per lane chunk, each row's slices
+    rotated by its lane, zero padding."""
     say("gemv pack layout", fmt, shape)
     rows, cols = shape
     V = cols // 8
-    J = 28 if fmt == "vq3r" else 56
+    J = 32
     rng = np.random.default_rng(rows + cols)
     E = 2
     rec = rng.integers(0, 256, size=(E, rows, V, 3), dtype=np.uint8)
@@ -329,8 +330,11 @@ def test_gemv_pack_layout(fmt, shape):
     nblk, ng = -(-V // J), -(-rows // 64)
     pad = np.zeros((E, ng * 64, nblk * J, 3), np.uint8)
     pad[:, :rows, :V] = rec
-    # [E][g][lane][b][c][4 records][3] -> [E][b][g][c][lane][12]
-    want = pad.reshape(E, ng, 64, nblk, J // 4, 12).transpose(0, 3, 1, 4, 2, 5).reshape(E, -1)
+    b, g, c, lane, q = np.meshgrid(np.arange(nblk), np.arange(ng), np.arange(J // 4), np.arange(64), np.arange(4),
+                                   indexing="ij")
+    row = 64 * g + lane
+    sl = J * b + (4 * c + q + lane) % J
+    want = pad[:, row, sl, :].reshape(E, -1)
     assert got.shape == want.shape and np.array_equal(got, want)
 
 
