@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--engine", default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="oracle encode sample: rows of expert 0")
+    ap.add_argument("--cpu-rows", type=int, default=32768, help="oracle encode sample: rows of expert 0")
     ap.add_argument("--only", default="", help="comma list: fit,encode,decode,error,gemv,vq4p (default all)")
     ap.add_argument("--loop", default="", help="profiling helper: repeat one component (encode|gemv1|gemv16|fit) --steps times")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a plain copy of known size")
@@ -130,7 +130,13 @@ def main():
     sums = torch.empty((E, 4), dtype=torch.float64, device=dev)
     mx_out = torch.empty((len(mats) * ROWS, COLS), dtype=torch.float32, device=dev) if "vq4p" in only else None
     mx_ws = torch.empty(256, dtype=torch.uint8, device=dev)
-    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+    # cache eviction between GEMV reps: reading 1 GiB of other data evicts the packed experts from the
+    # L2s and the MALL without leaving dirty lines whose write-back would land inside the timed kernel
+    flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def evict():
+        torch.sum(flush, dim=0, out=flush_out)
     gemv_cases = []
     for ntok in (1, 4, 16):
         x = torch.from_numpy(synthetic.activations_f16(ntok, COLS, seed=10 + ntok).view(np.float16)).to(dev)
@@ -169,7 +175,7 @@ def main():
             with T("pack3"):
                 vq.gemv_pack(idx3_e, fmt="vq3r", out=pk3)
             for ntok, x, route, y, ws, _ in gemv_cases:
-                flush.fill_(ntok)
+                evict()
                 with T("gemv3_%d" % ntok):
                     vq.dequant_gemv(pk3, sc3_e, cb3, x, route, ROWS, COLS, fmt="vq3r", y=y, workspace=ws)
         if "vq4p" in only:
@@ -186,7 +192,7 @@ def main():
             with T("pack4"):
                 vq.gemv_pack(idx4_e, fmt="vq4p", out=pk4)
             for ntok, x, route, y, ws4, _ in gemv_cases4:
-                flush.fill_(ntok)
+                evict()
                 with T("gemv4_%d" % ntok):
                     vq.dequant_gemv(pk4, sc4_e, cb4, x, route, ROWS, COLS, fmt="vq4p", y=y, workspace=ws4)
     step.fitted = False
@@ -209,7 +215,7 @@ def main():
             elif args.loop.startswith("gemv"):
                 ntok = int(args.loop[4:])
                 c = [g for g in gemv_cases if g[0] == ntok][0]
-                flush.fill_(i)
+                evict()
                 vq.dequant_gemv(pk3, sc3_e, cb3, c[1], c[2], ROWS, COLS, y=c[3], workspace=c[4])
             elif args.loop == "decode":
                 vq.decode(idx3, sc3, cb3, out=w_hat)

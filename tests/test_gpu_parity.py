@@ -277,7 +277,8 @@ def _experts(fmt, cb, E, rows, cols, seed):
 
 
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
-@pytest.mark.parametrize("shape", [(64, 256), (96, 2056), (256, 1024), (32, 448), (1100, 896), (64, 7168)])
+@pytest.mark.parametrize("shape", [(64, 256), (96, 2056), (256, 1024), (32, 448), (1100, 896), (64, 7168),
+                                   (2600, 264)])
 def test_gemv_matches_oracle(cfg1, fmt, shape):
     say("gemv", fmt, shape)
     rows, cols = shape
@@ -295,6 +296,55 @@ def test_gemv_matches_oracle(cfg1, fmt, shape):
             ref, scale = oracle.gemv_ref(whs[route[b, k]], xf[b])
             err = np.abs(y[b, k] - ref)
             assert np.all(err <= 1e-3 * scale + 1e-30), (b, k, float((err / scale).max()))
+
+
+def _check_gemv(y, whs, xf, route):
+    ntok, topk = route.shape
+    for b in range(ntok):
+        for k in range(topk):
+            ref, scale = oracle.gemv_ref(whs[route[b, k]], xf[b])
+            err = np.abs(y[b, k] - ref)
+            assert np.all(err <= 1e-3 * scale + 1e-30), (b, k, float((err / scale).max()))
+
+
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+def test_gemv_many_slots(cfg1, fmt):
+    """More token slots (1120) than the in-kernel expert ordering handles: the
+    slots are then scheduled in their own order."""
+    say("gemv many slots", fmt)
+    rows, cols = 64, 64
+    _, cb = cfg1[fmt]
+    E, ntok, topk = 6, 140, 8
+    recs, scs, whs = _experts(fmt, cb, E, rows, cols, seed=50)
+    x = synthetic.activations_f16(ntok, cols, seed=3)
+    route = synthetic.routing(ntok, E, 4, seed=4)
+    route = np.concatenate([route, route[::-1]], axis=1).astype(np.int32)
+    packed = vq.gemv_pack(to_dev(recs), fmt=fmt)
+    y = vq.dequant_gemv(packed, to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
+                        to_dev(route), rows, cols, fmt=fmt).cpu().numpy()
+    _check_gemv(y, whs, synthetic.f16_bits_to_f32(x).reshape(ntok, cols), route)
+
+
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+def test_gemv_full_layer_sampled(cfg1, fmt):
+    """The launch the benchmark times: 256 experts of [2048 x 7168], 16 tokens,
+    top-8 routing. Expert e holds the records of base expert e % 2 (two experts
+    encoded by the oracle), so every one of the 128 outputs has an oracle value."""
+    say("gemv full layer", fmt)
+    rows, cols, E, ntok, topk = 2048, 7168, 256, 16, 8
+    _, cb = cfg1[fmt]
+    recs, scs, whs = _experts(fmt, cb, 2, rows, cols, seed=60)
+    rec_d = to_dev(recs)
+    packed = torch.empty((E, vq.lib().vq_gemv_packed_size(vq.FORMATS[fmt], rows, cols)), dtype=torch.uint8,
+                         device="cuda")
+    vq.gemv_pack(rec_d, fmt=fmt, out=packed[:2])
+    packed[2:] = packed[:2].repeat(E // 2 - 1, 1)
+    scales = to_dev(scs.view(np.float16)).repeat(E // 2, 1)
+    x = synthetic.activations_f16(ntok, cols, seed=11)
+    route = synthetic.routing(ntok, E, topk, seed=12)
+    y = vq.dequant_gemv(packed, scales, to_dev(cb), to_dev(x.view(np.float16)), to_dev(route), rows, cols,
+                        fmt=fmt).cpu().numpy()
+    _check_gemv(y, [whs[e % 2] for e in range(E)], synthetic.f16_bits_to_f32(x).reshape(ntok, cols), route)
 
 
 def test_gemv_bad_route_flagged(cfg1):
