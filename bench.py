@@ -17,6 +17,7 @@ Prints one JSON line (value = layer weights per second of the whole step).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import subprocess
@@ -49,7 +50,7 @@ def parse():
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--engine", default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=32768, help="oracle encode sample: rows of expert 0")
+    ap.add_argument("--cpu-rows", type=int, default=32768, help="oracle encode sample: first rows of the layer")
     ap.add_argument("--only", default="", help="comma list: fit,encode,decode,error,gemv,vq4p (default all)")
     ap.add_argument("--loop", default="", help="profiling helper: repeat one component (encode|gemv1|gemv16|fit) --steps times")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a plain copy of known size")
@@ -90,8 +91,8 @@ class Timer:
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the work would shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(one process drives one GPU). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     import synthetic
@@ -206,9 +207,10 @@ def main():
         torch.cuda.synchronize()
         for i in range(args.steps):
             if args.loop == "encode":
-                vq.encode(W, cb3, idx=idx3, scales=sc3, workspace=enc_ws, check=False)
+                vq.encode(W, cb3, engine=args.engine, idx=idx3, scales=sc3, workspace=enc_ws, check=False)
             elif args.loop == "encode4":
-                vq.encode(W, cb4, fmt="vq4p", idx=idx4, scales=sc4, workspace=enc_ws, check=False)
+                vq.encode(W, cb4, fmt="vq4p", engine=args.engine, idx=idx4, scales=sc4, workspace=enc_ws,
+                          check=False)
             elif args.loop == "fit":
                 vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3, workspace=fit_ws3,
                                  check=False)
@@ -259,6 +261,7 @@ def main():
     out["encode_tflops_fp32_equiv"] = round(enc_tflops, 2)
     out["encode_frac_fp32_peak"] = round(enc_tflops / FP32_PEAK_TFLOPS, 4)
     gem = {}
+    floors = {}
     for fmt in ("3", "4"):
         for ntok, x, route, y, ws, distinct in gemv_cases:
             key = "gemv%s_%d" % (fmt, ntok)
@@ -268,8 +271,10 @@ def main():
             alg = distinct * (VEC_PER_EXPERT * 3 + ROWS * 2) + ntok * COLS * 2 + ntok * 8 * ROWS * 4 + \
                 (3 * 256 * 8 * 4 if fmt == "3" else 4 * 64 * 8 * 4)
             gbs = alg / (ms * 1e-3) / 1e9
+            floor = floors.setdefault(alg // (1 << 20), read_floor_us(torch, alg, evict))
             gem[key] = {"us": round(ms * 1e3, 2), "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                        "distinct_experts": distinct, "alg_bytes": alg}
+                        "distinct_experts": distinct, "alg_bytes": alg,
+                        "plain_read_us": round(floor, 2), "frac_of_plain_read": round(floor / (ms * 1e3), 4)}
     if "error3" in T.ev:
         s = sums.double().cpu().numpy()
         out["rel_error_mean_after_stage"] = [round(float(np.mean(np.sqrt(s[:, t] / s[:, 3]))), 5) for t in range(3)]
@@ -277,7 +282,8 @@ def main():
     out["encode_device_flags"] = st
     # roofline of the dominant kernel: the VQ3R encode
     roof = {"bound": "alu", "achieved": round(enc_tflops, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(enc_tflops / FP32_PEAK_TFLOPS, 4), "traffic": None,
+            "frac": round(enc_tflops / FP32_PEAK_TFLOPS, 4), "traffic": encode_traffic() if E == 256 else None,
+            "traffic_unit": "HBM bytes per encode call (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "kernel": "vq3r encode (k_encode + k_encode_exact)", "work": "12288 fp32 flop per 8-dim vector"}
     cpu = None
     if not args.no_cpu_baseline:
@@ -303,9 +309,53 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def encode_traffic():
+    """HBM bytes per VQ3R encode call from the committed FETCH_SIZE / WRITE_SIZE
+    summary, or None once the encode sources differ from the ones it measured."""
+    path = os.path.join(ROOT, "profiles", "k_encode_vq3r_layer_256x2048x7168_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and line.startswith("    "):
+            k, v = line.strip().split(":", 1)
+            kv[k.strip()] = v.strip()
+    files = kv.get("source_files", "").split()
+    if not files or "traffic_bytes_per_launch" not in kv:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(ROOT, "residual_vector_quantization_amd", "csrc", f), "rb").read())
+    if h.hexdigest() != kv.get("source_sha256"):
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
+def read_floor_us(torch, nbytes, evict, reps=5):
+    """Time of a plain device read of nbytes (torch sum of an fp32 buffer) after the
+    same cache eviction as the GEMV: the reference point for its HBM rate."""
+    buf = torch.ones(max(1, nbytes // 4), dtype=torch.float32, device="cuda")
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    best = None
+    for _ in range(reps):
+        evict()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.sum(buf, dim=0, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e3
+        best = t if best is None else min(best, t)
+    del buf
+    return best
+
+
 def cpu_baseline(torch, W, cb3, nrows):
     """The oracle (plain C, all host threads) encoding a bounded sample of the
-    same workload: the first `nrows` rows of expert 0 with the fitted codebooks."""
+    same workload: the first `nrows` weight rows of the layer (experts 0, 1, ...)
+    with the fitted codebooks."""
     import oracle
     w = W[:nrows].float().cpu().numpy()
     cb = cb3.cpu().numpy()
@@ -314,7 +364,8 @@ def cpu_baseline(torch, W, cb3, nrows):
     oracle.encode(w, cb)
     dt = time.time() - t0
     return {"value": round(w.size / dt / 1e9, 6), "unit": "Gweights/s", "cores": threads, "kind": "oracle",
-            "sample": "VQ3R encode of %d rows x 7168 of expert 0 (%.1f s)" % (nrows, dt)}
+            "sample": "VQ3R encode of the first %d rows x 7168 of the layer (%d experts, %.1f s)"
+                      % (nrows, -(-nrows // ROWS), dt)}
 
 
 if __name__ == "__main__":

@@ -19,8 +19,9 @@ parts that are most plainly written with numpy:
 
 [VQ3R page] = the page titled "3比特逼近4比特精度？WARP残差向量量化VQ3R的完整测量实验".
 
-Parity status of each function is listed in the design doc; every function here is
-pinned by tests/test_oracle_*.py against values fixed independently of it.
+Every function here is pinned by tests/test_oracle_*.py against values fixed
+independently of it (values the page prints, closed forms, brute force on tiny
+inputs, invariants).
 """
 from __future__ import annotations
 

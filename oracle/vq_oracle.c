@@ -14,8 +14,7 @@
  *   §4  the encoder keeps all 256 distances, holds an 8 KB (fp32) codebook and
  *       writes only the winning index per stage.
  *   §5  VQ4P: 4 stages x 64 entries, 6-bit indices packed into the same bytes.
- * Where the page is silent the readings used are listed in the design doc; each
- * function below names the reading it relies on.
+ * Where the page is silent, each function below states the reading it takes.
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math), so
  * every fp32 operation is a single IEEE round-to-nearest-even operation and
@@ -224,7 +223,7 @@ int vqo_decode(const int32_t* idx, const uint16_t* s_bits, const float* cb, int6
  * Lloyd codebook fit, [VQ3R page] §2 and §4 (per-layer codebooks fit with
  * k-means / Lloyd iterations on sampled experts; C1 on the vectors, C2 on the
  * stage-1 residuals, C3 on the stage-2 residuals).
- * Readings: stages are fit one after another, stage t on the
+ * Readings where the page is silent: stages are fit one after another, stage t on the
  * residuals left by greedy assignment to the final C_1..C_{t-1}; Forgy init
  * from caller-given distinct training-vector indices; one iteration = assign
  * (exhaustive argmin above) + update; a cluster with no members keeps its

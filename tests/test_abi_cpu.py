@@ -22,7 +22,7 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(vq\w+)\s*\(", text)))
 
 
-def test_header_declares_north_star_entry_points():
+def test_header_declares_hot_path_entry_points():
     names = declared_functions()
     for n in ["vq_fit_codebooks", "vq3r_encode", "vq3r_decode", "vq3r_dequant_gemv",
               "vq4p_encode", "vq4p_decode", "vq4p_dequant_gemv"]:
