@@ -166,11 +166,11 @@ int vq4p_decode(const uint8_t* idx, const uint16_t* scales, const float* codeboo
  *
  * The GEMV reads its indices in a runtime layout that vq_gemv_pack() builds
  * once from the stored [rows][cols/8][3] records (like loading a container):
- * blocks of 32 column slices by 64-row groups,
+ * blocks of 16 column slices by 64-row groups,
  * each group's records interleaved in 12-byte chunks of 4 records per row
  * and each row's slices rotated by its position in the group.
  * vq_gemv_packed_size() gives the bytes of one packed expert (rows are
- * padded to a multiple of 64 and slices to a multiple of 32 with zeros).
+ * padded to a multiple of 64 and slices to a multiple of 16 with zeros).
  *
  * vq_gemv_pack: idx = n_experts consecutive [rows][cols/8][3] tensors;
  *               packed out = n_experts consecutive packed experts of

@@ -4,40 +4,46 @@
 //
 // y[p][r] = s_r * sum_j sum_t T_t[j][i_t(r, j)],   T_t[j][e] = <C_t[e], x_j>
 // where x_j is the j-th 8-element slice of the token's activation. A work tile
-// is (token-slot pair p, block of J slices): its workgroup tabulates T for the
-// block's slices in LDS with fp32 matrix-core products (slices x codewords),
-// then streams the tile's records, one row per lane: each index costs one
-// table read and one add. Tile partial sums go to the workspace and a second
-// kernel adds the blocks in a fixed order and applies the row scales, so the
-// result is deterministic. It equals sum_c W_hat[r][c] x[c] up to fp32 rounding.
+// is (token-slot pair p, block of J = 16 slices): its workgroup tabulates T for
+// the block's slices in LDS with fp32 matrix-core products (codewords x
+// slices), then streams the tile's records, one row per lane: each index
+// costs one table read and one add. Tile partial sums go to the workspace and
+// a second kernel adds the blocks in a fixed order and applies the row
+// scales, so the result is deterministic. It equals sum_c W_hat[r][c] x[c] up
+// to fp32 rounding.
+//
+// Blocks of 16 slices keep a workgroup's tables at 48 KB (VQ3R) / 32 KB
+// (VQ4P), so that several 8-wave workgroups share a CU and one's table build
+// and start-up latency overlap the others' record streams.
 //
 // Runtime layout ("packed"): the GEMV reads indices repacked once by
-// vq_gemv_pack into blocks of J = 32 slices x 64-row groups. Within a group
+// vq_gemv_pack into blocks of J = 16 slices x 64-row groups. Within a group
 // the records are interleaved in 12-byte chunks (4 records of one row), and
 // each row's slices are rotated by its lane:
 //   packed[b][g][c][lane][12 bytes] = records of row 64g+lane for the slices
-//   32b + ((4c + q + lane) mod 32), q = 0..3
+//   16b + ((4c + q + lane) mod 16), q = 0..3
 // so every wave load is one contiguous 768-byte piece of the stream, a tile's
-// data is contiguous, and at step m lane l works on slice (m + l) mod 32 (the
+// data is contiguous, and at step m lane l works on slice (m + l) mod 16 (the
 // row-interleave idea of the IQ1_S_R4 format on the ik_llama.cpp page, applied
 // to whole waves). The tables are stored slice-minor,
 //   T[(e * S + t) * R + replica][slice],
-// so the lanes of one table read hit distinct slices, i.e. distinct LDS banks
-// (R = 2 replicas for VQ4P, one per half-wave, making its reads conflict-free;
-// VQ3R keeps one copy, 96 KB).
+// so the 16 lanes of a quarter-wave read 16 distinct slices (distinct LDS
+// banks); VQ4P keeps R = 2 replicas, lanes 16-31 (mod 32) reading the second,
+// which makes a half-wave's reads conflict-free; VQ3R keeps one copy.
 #include "vq_launch.hpp"
 
 namespace vqk {
 
 typedef float f16v __attribute__((ext_vector_type(16)));
 
-constexpr int GJ = 32;     // slices per block
+constexpr int GJ = 16;     // slices per block
 constexpr int GROUP = 64;  // rows per interleaved group (one wave)
-constexpr int GEMV_THREADS = 1024;  // 16 waves (LutOps assumes 16)
+constexpr int GEMV_WAVES = 8;
+constexpr int GEMV_THREADS = 64 * GEMV_WAVES;
 
 template <int FMT> struct GemvCfg;
-template <> struct GemvCfg<0> { static constexpr int R = 1; };  // 256 x 3 x 32 x 4 B = 96 KB
-template <> struct GemvCfg<1> { static constexpr int R = 2; };  // 64 x 4 x 2 x 32 x 4 B = 64 KB
+template <> struct GemvCfg<0> { static constexpr int R = 1; };  // 256 x 3 x 16 x 4 B = 48 KB
+template <> struct GemvCfg<1> { static constexpr int R = 2; };  // 64 x 4 x 2 x 16 x 4 B = 32 KB
 
 int64_t gemv_packed_bytes(int format, int64_t rows, int64_t cols) {
   (void)format;
@@ -85,16 +91,17 @@ __global__ __launch_bounds__(256) void k_gemv_pack(const uint8_t* idx, int64_t r
 
 // ------------------------------------------------------------------ tables
 // T[(e*S + t)*R + rep][m] = sum_k C_t[e][k] * x[(j0 + m)*8 + k] with fp32
-// matrix cores, codewords on M and slices on N (so that the 32 lanes of a
-// half-wave write 32 consecutive slices). The operands of a wave's tasks are
-// loaded first (lut_load), the MFMAs run later (lut_compute): the index
-// stream prefetch is issued in between, so waiting for the table operands
-// never waits for the (later) index loads.
+// matrix cores (32x32x2): codewords on M, slices on N (lanes 16-31 of each
+// half-wave carry zero slices). The operands of a wave's tasks are loaded
+// first (lut_load), the MFMAs run later (lut_compute): the first index loads
+// are issued in between, so waiting for the table operands never waits for
+// the (later) index loads.
 template <int FMT>
 struct LutOps {
   static constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, NT = K / 32, TASKS = S * NT;
-  static constexpr int PER_WAVE = (TASKS + 15) / 16;  // 16 waves per workgroup
-  float a[PER_WAVE][4], b[PER_WAVE][4];
+  static constexpr int PER_WAVE = (TASKS + GEMV_WAVES - 1) / GEMV_WAVES;
+  float a[PER_WAVE][4];
+  uint32_t xb[4];  // the activation operand (fp16 bits), the same for every task of the wave
 };
 
 template <int FMT>
@@ -105,16 +112,14 @@ __device__ inline void lut_load(LutOps<FMT>& op, const float* cb_g, const uint16
   const int ic = i < nsl ? i : 0;  // clamped slice: loaded but zeroed
 #pragma unroll
   for (int u = 0; u < O::PER_WAVE; ++u) {
-    const int task = wave + 16 * u;
+    const int task = wave + GEMV_WAVES * u;
     const int tk = task < O::TASKS ? task : 0;
     const int t = tk / O::NT, ct = tk % O::NT;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int k = 2 * s + h;
-      op.a[u][s] = cb_g[((size_t)t * O::K + ct * 32 + i) * DIM + k];
-      op.b[u][s] = f16_bits_to_f32(xrow[(j0 + ic) * DIM + k]);
-    }
+    for (int s = 0; s < 4; ++s) op.a[u][s] = cb_g[((size_t)t * O::K + ct * 32 + i) * DIM + 2 * s + h];
   }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) op.xb[s] = xrow[(j0 + ic) * DIM + 2 * s + h];
 }
 
 template <int FMT>
@@ -123,22 +128,26 @@ __device__ inline void lut_compute(const LutOps<FMT>& op, float* lut, int nsl) {
   constexpr int R = GemvCfg<FMT>::R;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, i = lane & 31;
-  const bool sv = i < nsl;
+  const bool sv = i < nsl;  // nsl <= 16: lanes 16-31 of a half-wave compute nothing useful
+  float b[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) b[s] = sv ? f16_bits_to_f32((uint16_t)op.xb[s]) : 0.0f;
 #pragma unroll
   for (int u = 0; u < O::PER_WAVE; ++u) {
-    const int task = wave + 16 * u;
+    const int task = wave + GEMV_WAVES * u;
     if (task >= O::TASKS) break;  // wave-uniform
     const int t = task / O::NT, ct = task % O::NT;
     f16v acc = {};
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(op.a[u][s], sv ? op.b[u][s] : 0.0f, acc, 0, 0, 0);
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(op.a[u][s], b[s], acc, 0, 0, 0);
     // lane (n = slice i, h) holds codewords e = 32ct + 8*(v/4) + 4h + v%4
+    if (i < GJ) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int e = ct * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+      for (int v = 0; v < 16; ++v) {
+        const int e = ct * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
 #pragma unroll
-      for (int rep = 0; rep < R; ++rep) lut[((e * O::S + t) * R + rep) * GJ + i] = acc[v];
+        for (int rep = 0; rep < R; ++rep) lut[((e * O::S + t) * R + rep) * GJ + i] = acc[v];
+      }
     }
   }
 }
@@ -150,12 +159,15 @@ __device__ inline int64_t tile_of_block(int64_t bid, int64_t ntiles_pad) {
   return (bid % 8) * per_xcd + bid / 8;
 }
 
-template <int FMT>
+// GPW = row groups per wave (groups g = wave + 8k), known at launch: 1..4
+// fully unrolled with exact loads (up to 2048 rows), 0 = any count.
+template <int FMT, int GPW>
 __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_t expert_stride, const float* cb_g,
                                                        int64_t rows, int64_t cols, int n_experts, const uint16_t* x,
                                                        int topk, const int32_t* route, float* partials, int nblk,
                                                        int64_t ntiles, int64_t ntiles_pad) {
   constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, R = GemvCfg<FMT>::R, NC = GJ / 4;
+  constexpr int NW = GEMV_WAVES;
   __shared__ float lut[K * S * R * GJ];
   const int64_t tile = tile_of_block(blockIdx.x, ntiles_pad);
   if (tile >= ntiles) return;
@@ -166,38 +178,26 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
   const int64_t V = cols / DIM;
   const int64_t j0 = (int64_t)b * GJ;
   const int nsl = (int)((V - j0) < GJ ? (V - j0) : GJ);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t ng = (rows + GROUP - 1) / GROUP;
   const uint8_t* tb = pk + (int64_t)e * expert_stride + (int64_t)b * ng * NC * (GROUP * 12);
   float* part = partials + ((int64_t)p * nblk + b) * rows;
-  // Each wave owns row groups wave, wave + nw, wave + 2nw, ... handled two at a
-  // time. The first two groups are loaded before the tables are built (after
-  // the table operands, so waiting for those never waits for the index
-  // stream) and unconditionally (clamped group index), so the HBM latency of
-  // the index stream overlaps the table construction.
-  uint32_t dA[NC][3], dB[NC][3];
-  auto load_group = [&](uint32_t (&d)[NC][3], int64_t g) {
+  // unconditional loads with a clamped group index keep the wait counts exact
+  uint32_t d[2][NC][3];
+  auto load_group = [&](uint32_t (&dg)[NC][3], int64_t g) {
     const int64_t gc = g < ng ? g : ng - 1;
     const uint32_t* src = reinterpret_cast<const uint32_t*>(tb + gc * NC * (GROUP * 12)) + lane * 3;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
-      for (int k = 0; k < 3; ++k) d[c][k] = src[c * (GROUP * 3) + k];
+      for (int k = 0; k < 3; ++k) dg[c][k] = src[c * (GROUP * 3) + k];
     }
   };
-  LutOps<FMT> ops;
-  lut_load<FMT>(ops, cb_g, x + (int64_t)tok * cols, j0, nsl);
-  __builtin_amdgcn_sched_barrier(0);  // keep the table operand loads ahead of the index stream
-  load_group(dA, wave);
-  load_group(dB, wave + nw);
-  __builtin_amdgcn_sched_barrier(0);
-  lut_compute<FMT>(ops, lut, nsl);
-  __syncthreads();
-  // byte offset of (slice (m + lane) mod 32, replica) inside one (e, t) row of the table
-  const uint32_t rep_off = (R == 2) ? (uint32_t)(lane >> 5) * (GJ * 4) : 0u;
+  // byte offset of (slice (m + lane) mod 16, replica) inside one (e, t) row of the table
+  const uint32_t rep_off = (R == 2) ? (uint32_t)((lane >> 4) & 1) * (GJ * 4) : 0u;
   constexpr uint32_t E_STRIDE = S * R * GJ * 4, T_STRIDE = R * GJ * 4;
   const char* lbase = reinterpret_cast<const char*>(lut);
-  auto consume = [&](const uint32_t (&d)[NC][3], int64_t g) {
+  auto consume = [&](const uint32_t (&dg)[NC][3], int64_t g) {
     float acc = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
         // record q of the chunk = bytes 3q .. 3q+2 of the 12 bytes
         const int byte0 = 3 * q, k0 = byte0 >> 2, o = byte0 & 3;
         const uint32_t w =
-            (o <= 1) ? (d[c][k0] >> (8 * o)) : ((d[c][k0] >> (8 * o)) | (d[c][k0 + 1] << (32 - 8 * o)));
+            (o <= 1) ? (dg[c][k0] >> (8 * o)) : ((dg[c][k0] >> (8 * o)) | (dg[c][k0 + 1] << (32 - 8 * o)));
         const int m = 4 * c + q;
         const uint32_t soff = (((uint32_t)(m + lane) & (GJ - 1)) << 2) + rep_off;
         float tsum = 0.0f;
@@ -221,13 +221,30 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
     const int64_t row = g * GROUP + lane;
     if (g < ng && row < rows) part[row] = acc;
   };
-  for (int64_t g = wave; g < ng; g += 2 * nw) {
-    if (g != wave) {
-      load_group(dA, g);
-      load_group(dB, g + nw);
+  LutOps<FMT> ops;
+  lut_load<FMT>(ops, cb_g, x + (int64_t)tok * cols, j0, nsl);
+  __builtin_amdgcn_sched_barrier(0);  // keep the table operand loads ahead of the index stream
+  load_group(d[0], wave);
+  if (GPW != 1) load_group(d[1], wave + NW);
+  __builtin_amdgcn_sched_barrier(0);
+  lut_compute<FMT>(ops, lut, nsl);
+  __syncthreads();
+  if constexpr (GPW > 0) {
+    // two groups in flight: the load of group k + 2 follows the consume of group k
+#pragma unroll
+    for (int k = 0; k < GPW; ++k) {
+      consume(d[k & 1], wave + (int64_t)k * NW);
+      if (k + 2 < GPW) load_group(d[k & 1], wave + (int64_t)(k + 2) * NW);
     }
-    consume(dA, g);
-    consume(dB, g + nw);
+  } else {
+    for (int64_t g = wave; g < ng; g += 2 * NW) {
+      if (g != wave) {
+        load_group(d[0], g);
+        load_group(d[1], g + NW);
+      }
+      consume(d[0], g);
+      consume(d[1], g + NW);
+    }
   }
 }
 
@@ -276,9 +293,18 @@ static hipError_t launch_gemv_t(const GemvArgs& a) {
   const int nblk = (int)((V + GJ - 1) / GJ);
   const int64_t ntiles = npairs * nblk;
   const int64_t ntiles_pad = (ntiles + 7) / 8 * 8;
-  k_gemv<FMT><<<(unsigned)ntiles_pad, GEMV_THREADS, 0, a.stream>>>(a.idx, a.expert_stride, a.codebooks, a.rows,
-                                                                    a.cols, a.n_experts, a.x, a.topk, a.route,
-                                                                    a.partials, nblk, ntiles, ntiles_pad);
+  const int64_t ng = (a.rows + GROUP - 1) / GROUP;
+  const int64_t gpw = (ng + GEMV_WAVES - 1) / GEMV_WAVES;
+  auto go = [&](auto kern) {
+    kern<<<(unsigned)ntiles_pad, GEMV_THREADS, 0, a.stream>>>(a.idx, a.expert_stride, a.codebooks, a.rows, a.cols,
+                                                               a.n_experts, a.x, a.topk, a.route, a.partials, nblk,
+                                                               ntiles, ntiles_pad);
+  };
+  if (gpw == 1) go(k_gemv<FMT, 1>);
+  else if (gpw == 2) go(k_gemv<FMT, 2>);
+  else if (gpw == 3) go(k_gemv<FMT, 3>);
+  else if (gpw == 4) go(k_gemv<FMT, 4>);
+  else go(k_gemv<FMT, 0>);
   dim3 g2((unsigned)((a.rows + 255) / 256), (unsigned)npairs);
   k_gemv_reduce<<<g2, 256, 0, a.stream>>>(a.partials, a.scales, a.scale_stride, a.route, a.n_experts, a.rows, nblk,
                                           (int)npairs, a.y, a.hdr);

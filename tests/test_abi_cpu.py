@@ -135,7 +135,7 @@ def test_decode_gemv_error_mxfp4_argument_errors():
     assert L.vq_decode(0, a.ptr, b.ptr, c.ptr, 0, 64, 3, d.ptr, None) == VQ_OK
     n_ws = L.vq_gemv_workspace_size(0, 4, 64, 2, 2)
     pk = L.vq_gemv_packed_size(0, 4, 64)
-    assert pk == 64 * 32 * 3            # one 64-row group x one block of 32 slices
+    assert pk == 64 * 16 * 3            # one 64-row group x one block of 16 slices
     assert L.vq_gemv_packed_size(1, 2048, 7168) == 2048 * 896 * 3
     assert L.vq_gemv_pack(0, a.ptr, 4, 64, 2, ctypes.c_void_p(b.ptr.value + 2), None) == VQ_EINVAL
     g = lambda **k: L.vq_dequant_gemv(0, a.ptr, k.get("es", pk), b.ptr, 4, c.ptr, 4, 64,

@@ -366,13 +366,13 @@ def test_gemv_bad_route_flagged(cfg1):
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
 @pytest.mark.parametrize("shape", [(1, 8), (64, 224), (70, 456), (128, 7168)])
 def test_gemv_pack_layout(fmt, shape):
-    """The packed layout is a pure permutation of the stored records: blocks of 32
+    """The packed layout is a pure permutation of the stored records: blocks of 16
     slices x 64-row groups, 4 records (12 bytes) per lane chunk, each row's slices
     rotated by its lane, zero padding."""
     say("gemv pack layout", fmt, shape)
     rows, cols = shape
     V = cols // 8
-    J = 32
+    J = 16
     rng = np.random.default_rng(rows + cols)
     E = 2
     rec = rng.integers(0, 256, size=(E, rows, V, 3), dtype=np.uint8)
