@@ -333,17 +333,20 @@ def encode_traffic():
 
 
 def read_floor_us(torch, nbytes, evict, reps=5):
-    """Time of a plain device read of nbytes (torch sum of an fp32 buffer) after the
-    same cache eviction as the GEMV: the reference point for its HBM rate."""
-    buf = torch.ones(max(1, nbytes // 4), dtype=torch.float32, device="cuda")
-    out = torch.empty((), dtype=torch.float32, device="cuda")
+    """Time of a plain device read of nbytes after the same cache eviction as the
+    GEMV: torch row sums over [n/1024, 1024] fp32, the fastest plain torch read
+    here (one pass; its output is 1/1024 of the input). The reference point for
+    the GEMV's HBM rate."""
+    rows = max(1, -(-nbytes // 4096))
+    buf = torch.ones((rows, 1024), dtype=torch.float32, device="cuda")
+    out = torch.empty(rows, dtype=torch.float32, device="cuda")
     best = None
     for _ in range(reps):
         evict()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        torch.sum(buf, dim=0, out=out)
+        torch.sum(buf, dim=1, out=out)
         e1.record()
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) * 1e3

@@ -34,18 +34,24 @@ __global__ __launch_bounds__(256) void k_row_scales(const void* W, int64_t rows,
 }
 
 // ------------------------------------------------------------------ encode
-// One wave per row: the row scale, then groups of 32 vectors through all
-// stages. Certified vectors get their final record; the others are queued for
-// the exact pass (k_encode_exact).
+// One wave per row: the row scale, then groups of vectors through all
+// stages (64 per group with the fp16-split engine, one per lane; 32 with the
+// others, both half-waves working on the same vector). Certified vectors get
+// their final record; the others are queued for the exact pass
+// (k_encode_exact).
 template <int FMT, int ENG, int DT>
 __global__ __launch_bounds__(256, 2) void k_encode(const void* W, int64_t rows, int64_t cols, const float* cb_g,
                                                    uint8_t* idx, uint16_t* scales, WsHeader* hdr, uint32_t* list,
                                                    uint32_t cap) {
   constexpr int S = Fmt<FMT>::S;
+  constexpr bool X2 = ENG == ENG_F16X;
+  constexpr int GV = X2 ? 64 : 32;  // vectors per group
   __shared__ SearchLds<FMT, ENG, S> L;
   build_tables<FMT, ENG, S>(L, cb_g, hdr);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = lane >> 5, jl = lane & 31;
+  const int h = lane >> 5;
+  const int jl = X2 ? lane : (lane & 31);
+  const bool writer = X2 || h == 0;
   const int64_t V = cols / DIM;
   const size_t esz = DT == DT_F32 ? 4 : 2;
   for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < rows; row += (int64_t)gridDim.x * 4) {
@@ -58,7 +64,7 @@ __global__ __launch_bounds__(256, 2) void k_encode(const void* W, int64_t rows, 
     }
     if (bad) continue;
     const float s = f16_bits_to_f32(sb);
-    for (int64_t g = 0; g < V; g += 32) {
+    for (int64_t g = 0; g < V; g += GV) {
       const int64_t j = g + jl;
       const bool valid = j < V;
       float r[8];
@@ -73,11 +79,15 @@ __global__ __launch_bounds__(256, 2) void k_encode(const void* W, int64_t rows, 
       uint32_t word = 0;
       bool fl = false;
 #pragma unroll 1
-      for (int t = 0; t < S; ++t)
-        word |= (uint32_t)search_stage<FMT, ENG, S>(L, t, r, lane, fl) << (t * Fmt<FMT>::BITS);
+      for (int t = 0; t < S; ++t) {
+        int w;
+        if constexpr (X2) w = search_stage_x2<FMT, S>(L, t, r, lane, fl);
+        else w = search_stage<FMT, ENG, S>(L, t, r, lane, fl);
+        word |= (uint32_t)w << (t * Fmt<FMT>::BITS);
+      }
       const uint64_t vid = (uint64_t)row * V + j;
-      if (valid && h == 0) store_record(idx + vid * 3, word);
-      append_flags(fl && valid && h == 0, (uint32_t)vid, &hdr->n_flag[0], list, cap, lane);
+      if (valid && writer) store_record(idx + vid * 3, word);
+      append_flags(fl && valid && writer, (uint32_t)vid, &hdr->n_flag[0], list, cap, lane);
     }
   }
 }
@@ -203,24 +213,29 @@ __device__ inline void flush_accum(FitAccum<K>& A, long long* partials, int slot
 // Assignment pass over R_cur. MODE 0 (iteration): certified vectors add their
 // fixed-point coordinates to the block's cluster sums. MODE 1 (after the last
 // update): certified vectors write their residual to R_next. Vectors that fail
-// certification are queued for k_assign_exact.
+// certification are queued for k_assign_exact. Groups of 64 vectors (one per
+// lane) with the fp16-split engine, 32 with the others.
 template <int FMT, int ENG, int MODE>
 __global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_next, int64_t n, const float* C,
                                                    WsHeader* hdr, uint32_t* list, uint32_t cap,
                                                    long long* partials, int parity, int nxt) {
   constexpr int K = Fmt<FMT>::K;
+  constexpr bool X2 = ENG == ENG_F16X;
+  constexpr int GV = X2 ? 64 : 32;
   __shared__ SearchLds<FMT, ENG, 1> L;
   __shared__ FitAccum<K> A;
   if (MODE == 0)
     for (int q = threadIdx.x; q < K * (DIM + 1); q += blockDim.x) (&A.sum[0][0])[q] = 0ull;
   build_tables<FMT, ENG, 1>(L, C, hdr);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = lane >> 5, jl = lane & 31;
+  const int h = lane >> 5;
+  const int jl = X2 ? lane : (lane & 31);
+  const bool writer = X2 || h == 0;
   const int F = hdr->fbits;
   uint32_t mx = 0;
-  const int64_t ngroups = (n + 31) / 32;
+  const int64_t ngroups = (n + GV - 1) / GV;
   for (int64_t g = (int64_t)blockIdx.x * 4 + wave; g < ngroups; g += (int64_t)gridDim.x * 4) {
-    const int64_t j = g * 32 + jl;
+    const int64_t j = g * GV + jl;
     const bool valid = j < n;
     float r[8], r0[8];
     if (valid) {
@@ -234,20 +249,25 @@ __global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_
 #pragma unroll
     for (int k = 0; k < 8; ++k) r0[k] = r[k];
     bool fl = false;
-    const int w = search_stage<FMT, ENG, 1>(L, 0, r, lane, fl);
+    int w;
+    if constexpr (X2) w = search_stage_x2<FMT, 1>(L, 0, r, lane, fl);
+    else w = search_stage<FMT, ENG, 1>(L, 0, r, lane, fl);
     const bool ok = valid && !fl;
     if (MODE == 0) {
-      if (ok) accum_vector<K>(A, w, r0, F, 4 * h, 4 * h + 4, h == 0);
+      if (ok) {
+        if constexpr (X2) accum_vector<K>(A, w, r0, F, 0, DIM, true);
+        else accum_vector<K>(A, w, r0, F, 4 * h, 4 * h + 4, h == 0);
+      }
     } else {
       if (ok) {
         float4* dst = reinterpret_cast<float4*>(R_next + j * DIM);
-        if (h == 0) dst[0] = make_float4(r[0], r[1], r[2], r[3]);
-        else dst[1] = make_float4(r[4], r[5], r[6], r[7]);
+        if (X2 || h == 0) dst[0] = make_float4(r[0], r[1], r[2], r[3]);
+        if (X2 || h == 1) dst[1] = make_float4(r[4], r[5], r[6], r[7]);
 #pragma unroll
         for (int k = 0; k < 8; ++k) mx = max(mx, __float_as_uint(__builtin_fabsf(r[k])));
       }
     }
-    append_flags(fl && valid && h == 0, (uint32_t)j, &hdr->n_flag[parity], list, cap, lane);
+    append_flags(fl && valid && writer, (uint32_t)j, &hdr->n_flag[parity], list, cap, lane);
   }
   if (MODE == 0) {
     flush_accum<K>(A, partials, blockIdx.x);

@@ -214,6 +214,90 @@ __device__ inline int search_stage(const SearchLds<FMT, ENG, NST>& L, int t, flo
   return w;
 }
 
+// Two groups per pass (fp16-split engine): lane (i, h) owns vector i of group
+// h, so the per-vector work after the search (merge, exact distance,
+// certification, residual update, next fp16 split) serves 64 vectors per wave
+// instruction. The matrix-core operands of group g need that group's residual
+// in both half-waves (the K dimension is split across them); one
+// v_permlane32_swap per register broadcasts each half's values to both
+// halves. Returns the winner for the lane's own vector.
+template <int FMT, int NST>
+__device__ inline int search_stage_x2(const SearchLds<FMT, ENG_F16X, NST>& L, int t, float r[8], int lane,
+                                      bool& flag) {
+  constexpr int TILES = Fmt<FMT>::TILES, PACK = Fmt<FMT>::PACK;
+  const int h = lane >> 5, i = lane & 31;
+  // own residual split into fp16 hi + lo, both scaled by -2 (exact)
+  h8 hi, lo;
+  const _Float16 m2h = (_Float16)(-2.0f);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const _Float16 x = (_Float16)r[k];
+    hi[k] = x * m2h;
+    lo[k] = (_Float16)(r[k] - (float)x) * m2h;
+  }
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const u4 hw = __builtin_bit_cast(u4, hi), lw = __builtin_bit_cast(u4, lo);
+  u4 hg0, hg1, lg0, lg1;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    // swap(x, x): result 0 = the low half's x in both halves, result 1 = the high half's
+    const auto a = __builtin_amdgcn_permlane32_swap(hw[q], hw[q], false, false);
+    hg0[q] = a[0];
+    hg1[q] = a[1];
+    const auto b = __builtin_amdgcn_permlane32_swap(lw[q], lw[q], false, false);
+    lg0[q] = b[0];
+    lg1[q] = b[1];
+  }
+  h8 cst = {};
+  cst[0] = (_Float16)L.sig[t];
+  cst[1] = cst[0];
+  const h8 b0g0 = __builtin_bit_cast(h8, hg0), b0g1 = __builtin_bit_cast(h8, hg1);
+  const h8 b1g0 = h ? cst : __builtin_bit_cast(h8, lg0);
+  const h8 b1g1 = h ? cst : __builtin_bit_cast(h8, lg1);
+  const h8* pa0 = h ? L.tab[t].lo : L.tab[t].hi;
+  const h8* pa1 = h ? L.tab[t].nrm : L.tab[t].hi;
+  float m1a = __builtin_inff(), m2a = __builtin_inff(), m1b = __builtin_inff(), m2b = __builtin_inff();
+#pragma unroll
+  for (int tile = 0; tile < TILES; ++tile) {
+    const h8 a0 = pa0[tile * 32 + i], a1 = pa1[tile * 32 + i];
+    f16v acc0 = {}, acc1 = {};
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0g0, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0g1, acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1g0, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1g1, acc1, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      top2_pair(m1a, m2a, pack_score<PACK>(acc0[v], tile * 16 + v), pack_score<PACK>(acc0[v + 1], tile * 16 + v + 1));
+      top2_pair(m1b, m2b, pack_score<PACK>(acc1[v], tile * 16 + v), pack_score<PACK>(acc1[v + 1], tile * 16 + v + 1));
+    }
+  }
+  // merge: for the lane's own group, q0 = top over the half-0 codeword set,
+  // q1 = top over the half-1 set (swap(a, b): result 0 = [a of the low half,
+  // b of the low half], result 1 = [a of the high half, b of the high half])
+  const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1a), __float_as_uint(m1b), false, false);
+  const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m2a), __float_as_uint(m2b), false, false);
+  const float q0 = __uint_as_float(s1[0]), q1 = __uint_as_float(s1[1]);
+  const float n0 = __uint_as_float(s2[0]), n1 = __uint_as_float(s2[1]);
+  const float p1 = fmin2(q0, q1);
+  const float p2 = fmin2(__builtin_fmaxf(q0, q1), fmin2(n0, n1));
+  const uint32_t pb = __float_as_uint(p1);
+  const int hw_ = (pb == __float_as_uint(q0)) ? 0 : 1;
+  const uint32_t loc = pb & ((1u << PACK) - 1u);
+  const int tl = (int)(loc >> 4), v = (int)(loc & 15u);
+  const int w = tl * 32 + 8 * (v >> 2) + 4 * hw_ + (v & 3);
+  const float* c = L.cb[t][w];
+  float d = 0.0f, rr = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float e = r[k] - c[k];
+    d = __builtin_fmaf(e, e, d);
+    rr = __builtin_fmaf(r[k], r[k], rr);
+    r[k] = e;
+  }
+  flag |= !certified<PACK>(p1, p2, rr, d);
+  return w;
+}
+
 // Appends the ids of flagged lanes to a global list (one atomic per wave).
 __device__ inline void append_flags(bool f, uint32_t vid, uint32_t* counter, uint32_t* list, uint32_t cap,
                                     int lane) {
