@@ -39,8 +39,13 @@ __global__ __launch_bounds__(256) void k_row_scales(const void* W, int64_t rows,
 // others, both half-waves working on the same vector). Certified vectors get
 // their final record; the others are queued for the exact pass
 // (k_encode_exact).
+// With the fp16-split engine 8 waves per workgroup share one copy of the LDS
+// tables (60 KB for VQ3R), so two workgroups give each SIMD 4 waves to
+// interleave MFMA and VALU work; the other engines use 4 waves.
+constexpr int enc_waves(int eng) { return eng == ENG_F16X ? 8 : 4; }
+
 template <int FMT, int ENG, int DT>
-__global__ __launch_bounds__(256, 2) void k_encode(const void* W, int64_t rows, int64_t cols, const float* cb_g,
+__global__ __launch_bounds__(64 * enc_waves(ENG), enc_waves(ENG) / 2) void k_encode(const void* W, int64_t rows, int64_t cols, const float* cb_g,
                                                    uint8_t* idx, uint16_t* scales, WsHeader* hdr, uint32_t* list,
                                                    uint32_t cap) {
   constexpr int S = Fmt<FMT>::S;
@@ -54,7 +59,8 @@ __global__ __launch_bounds__(256, 2) void k_encode(const void* W, int64_t rows, 
   const bool writer = X2 || h == 0;
   const int64_t V = cols / DIM;
   const size_t esz = DT == DT_F32 ? 4 : 2;
-  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < rows; row += (int64_t)gridDim.x * 4) {
+  constexpr int NWV = enc_waves(ENG);
+  for (int64_t row = (int64_t)blockIdx.x * NWV + wave; row < rows; row += (int64_t)gridDim.x * NWV) {
     const void* wrow = (const char*)W + row * cols * esz;
     uint32_t bad;
     const uint16_t sb = wave_row_scale<DT>(wrow, cols, lane, &bad);
@@ -364,16 +370,16 @@ __global__ __launch_bounds__(64) void k_update(float* C, const long long* partia
 }
 
 // ------------------------------------------------------------------ launchers
-static int grid_rows(int64_t rows, int ncu, int per_cu) {
-  int64_t g = (rows + 3) / 4;
+static int grid_rows(int64_t rows, int ncu, int per_cu, int waves = 4) {
+  int64_t g = (rows + waves - 1) / waves;
   int64_t m = (int64_t)ncu * per_cu;
   return (int)(g < m ? (g < 1 ? 1 : g) : m);
 }
 
 template <int FMT, int ENG, int DT>
 static hipError_t launch_encode_t(const EncodeArgs& a) {
-  const int g = grid_rows(a.rows, a.ncu, 2);
-  k_encode<FMT, ENG, DT><<<g, 256, 0, a.stream>>>(a.W, a.rows, a.cols, a.codebooks, a.idx, a.scales, a.hdr,
+  const int g = grid_rows(a.rows, a.ncu, 2, enc_waves(ENG));
+  k_encode<FMT, ENG, DT><<<g, 64 * enc_waves(ENG), 0, a.stream>>>(a.W, a.rows, a.cols, a.codebooks, a.idx, a.scales, a.hdr,
                                                   a.list, a.cap);
   return hipGetLastError();
 }
