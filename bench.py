@@ -204,6 +204,8 @@ def main():
             vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3, workspace=fit_ws3)
             vq.encode(W, cb3, idx=idx3, scales=sc3, workspace=enc_ws)
             vq.gemv_pack(idx3_e, fmt="vq3r", out=pk3)
+        if args.loop == "encode4":
+            vq.fit_codebooks(mats, init4, fmt="vq4p", iters=args.iters, codebooks=cb4, workspace=fit_ws4)
         torch.cuda.synchronize()
         for i in range(args.steps):
             if args.loop == "encode":

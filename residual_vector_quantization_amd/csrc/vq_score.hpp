@@ -21,8 +21,9 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 // Per-stage engine tables in LDS.
 template <int K, int ENG> struct Tables;
 template <int K> struct Tables<K, ENG_F16X> {
-  // hi = fp16(c), lo = fp16(c - hi), nrm = {fp16(n'), fp16(n' - fp16(n')), 0...}
-  // with n' = ||c||^2 * 2^-sigma (the matrix-core operands of the split scheme)
+  // hi = -2 fp16(c), lo = -2 fp16(c - fp16(c)) (the factor -2 of the score is
+  // exact in fp16), nrm = {fp16(n'), fp16(n' - fp16(n')), 0...} with
+  // n' = ||c||^2 * 2^-sigma (the matrix-core operands of the split scheme)
   h8 hi[K];
   h8 lo[K];
   h8 nrm[K];
@@ -81,8 +82,8 @@ __device__ inline void build_tables(SearchLds<FMT, ENG, NST>& L, const float* cb
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         _Float16 x = (_Float16)c[k];
-        hi[k] = x;
-        lo[k] = (_Float16)(c[k] - (float)x);
+        hi[k] = x * (_Float16)(-2.0f);
+        lo[k] = (_Float16)(c[k] - (float)x) * (_Float16)(-2.0f);
       }
       L.tab[t].hi[i] = hi;
       L.tab[t].lo[i] = lo;
@@ -125,14 +126,13 @@ __device__ inline void lane_top2(const SearchLds<FMT, ENG, NST>& L, int t, const
   m2 = __builtin_inff();
   if constexpr (ENG == ENG_F16X) {
     h8 b0, b1;
-    const _Float16 m2h = (_Float16)(-2.0f);
     const _Float16 sg = (_Float16)L.sig[t];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       _Float16 x = (_Float16)r[k];
       _Float16 y = (_Float16)(r[k] - (float)x);
-      b0[k] = x * m2h;
-      b1[k] = h ? (k < 2 ? sg : (_Float16)0.0f) : y * m2h;
+      b0[k] = x;
+      b1[k] = h ? (k < 2 ? sg : (_Float16)0.0f) : y;
     }
     const h8* pa0 = h ? L.tab[t].lo : L.tab[t].hi;
     const h8* pa1 = h ? L.tab[t].nrm : L.tab[t].hi;
@@ -226,17 +226,22 @@ __device__ inline int search_stage_x2(const SearchLds<FMT, ENG_F16X, NST>& L, in
                                       bool& flag) {
   constexpr int TILES = Fmt<FMT>::TILES, PACK = Fmt<FMT>::PACK;
   const int h = lane >> 5, i = lane & 31;
-  // own residual split into fp16 hi + lo, both scaled by -2 (exact)
-  h8 hi, lo;
-  const _Float16 m2h = (_Float16)(-2.0f);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const _Float16 x = (_Float16)r[k];
-    hi[k] = x * m2h;
-    lo[k] = (_Float16)(r[k] - (float)x) * m2h;
-  }
+  // own residual split into fp16 hi + lo (pairs converted together; the -2 of
+  // the score sits in the codebook tables)
+  typedef _Float16 hf2 __attribute__((ext_vector_type(2)));
+  typedef float ff2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-  const u4 hw = __builtin_bit_cast(u4, hi), lw = __builtin_bit_cast(u4, lo);
+  u4 hw, lw;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const ff2 rv = {r[2 * q], r[2 * q + 1]};
+    const hf2 xv = __builtin_convertvector(rv, hf2);
+    const ff2 xb = __builtin_convertvector(xv, ff2);
+    const ff2 dv = {rv[0] - xb[0], rv[1] - xb[1]};
+    const hf2 yv = __builtin_convertvector(dv, hf2);
+    hw[q] = __builtin_bit_cast(uint32_t, xv);
+    lw[q] = __builtin_bit_cast(uint32_t, yv);
+  }
   u4 hg0, hg1, lg0, lg1;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
