@@ -6,41 +6,71 @@ namespace vqk {
 
 // ------------------------------------------------------------------ decode
 // [VQ3R page] §2: w_hat = s * (((C1[i1] + C2[i2]) + C3[i3]) [+ C4[i4]]), summed
-// left to right in fp32, then one fp32 multiply. One thread per 8-dim vector;
-// the codebooks sit in LDS; each thread writes 32 contiguous bytes.
+// left to right in fp32, then one fp32 multiply. One thread per 8-dim vector
+// (neighbouring lanes write neighbouring 32-byte outputs); the codebooks sit
+// in LDS.
+template <int FMT>
+__device__ inline void decode_vec(const float (*cb)[Fmt<FMT>::K][DIM], uint32_t word, float s, int stages_used,
+                                  float4* dst) {
+  float acc[8];
+  const float* c0 = cb[0][record_index<FMT>(word, 0)];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = c0[k];
+  for (int t = 1; t < stages_used; ++t) {
+    const float* c = cb[t][record_index<FMT>(word, t)];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = acc[k] + c[k];
+  }
+  dst[0] = make_float4(s * acc[0], s * acc[1], s * acc[2], s * acc[3]);
+  dst[1] = make_float4(s * acc[4], s * acc[5], s * acc[6], s * acc[7]);
+}
+
 template <int FMT>
 __global__ __launch_bounds__(256) void k_decode(const uint8_t* idx, const uint16_t* scales, const float* cb_g,
                                                 uint32_t V, uint64_t nvec, int stages_used, float* out) {
-  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K;
+  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, U = 4;
   __shared__ float cb[S][K][DIM];
+  __shared__ float4 stage[4][128];  // per wave: the 64 vectors' 2 KB of output
   for (int q = threadIdx.x; q < S * K * DIM; q += blockDim.x) (&cb[0][0][0])[q] = cb_g[q];
   __syncthreads();
-  for (uint64_t vid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; vid < nvec;
-       vid += (uint64_t)gridDim.x * blockDim.x) {
-    const uint32_t row = (uint32_t)(vid / V);
-    const float s = f16_bits_to_f32(scales[row]);
-    const uint32_t word = load_record(idx + vid * 3);
-    float acc[8];
-    const float* c0 = cb[0][record_index<FMT>(word, 0)];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t nth = (uint64_t)gridDim.x * blockDim.x;
+  // U vectors per thread, nth apart (lanes of a wave hold 64 consecutive
+  // vectors); all their loads are issued before any is used. Each wave's
+  // 2 KB of output goes through LDS so that every store instruction writes
+  // 1 KB of contiguous memory.
+  for (uint64_t v0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; v0 - lane < nvec; v0 += U * nth) {
+    uint32_t word[U];
+    float s[U];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = c0[k];
-    for (int t = 1; t < stages_used; ++t) {
-      const float* c = cb[t][record_index<FMT>(word, t)];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = acc[k] + c[k];
+    for (int u = 0; u < U; ++u) {
+      const uint64_t vid = v0 + u * nth;
+      const uint64_t vc = vid < nvec ? vid : nvec - 1;
+      word[u] = load_record(idx + vc * 3);
+      s[u] = f16_bits_to_f32(scales[(uint32_t)(vc / V)]);
     }
-    float4* dst = reinterpret_cast<float4*>(out + vid * DIM);
-    dst[0] = make_float4(s * acc[0], s * acc[1], s * acc[2], s * acc[3]);
-    dst[1] = make_float4(s * acc[4], s * acc[5], s * acc[6], s * acc[7]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t wbase = v0 - lane + u * nth;  // the wave's first vector
+      if (wbase >= nvec) break;                    // wave-uniform
+      decode_vec<FMT>(cb, word[u], s[u], stages_used, &stage[wave][2 * lane]);
+      __builtin_amdgcn_wave_barrier();
+      const uint64_t nv = nvec - wbase;  // valid vectors of this wave (> 0)
+      float4* dst = reinterpret_cast<float4*>(out + wbase * DIM);
+      if ((uint64_t)(lane >> 1) < nv) dst[lane] = stage[wave][lane];
+      if ((uint64_t)(32 + (lane >> 1)) < nv) dst[64 + lane] = stage[wave][64 + lane];
+      __builtin_amdgcn_wave_barrier();
+    }
   }
 }
 
 hipError_t launch_decode(const DecodeArgs& a) {
   const uint64_t V = (uint64_t)(a.cols / DIM), nvec = (uint64_t)a.rows * V;
   if (nvec == 0) return hipSuccess;
-  uint64_t g = (nvec + 255) / 256;
+  uint64_t g = (nvec / 4 + 255) / 256;
   const uint64_t gmax = (uint64_t)a.ncu * 8;
   if (g > gmax) g = gmax;
+  if (g < 1) g = 1;
   if (a.format == 0)
     k_decode<0><<<(unsigned)g, 256, 0, a.stream>>>(a.idx, a.scales, a.codebooks, (uint32_t)V, nvec, a.stages_used,
                                                    a.out);
@@ -56,7 +86,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
 // w^2; block partials are reduced in a fixed order by k_error_reduce.
 template <int FMT, int DT>
 __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx, const uint16_t* scales,
-                                               const float* cb_g, uint32_t V, uint64_t nvec_per_mat, int64_t cols,
+                                               const float* cb_g, uint32_t V, int64_t rows_per_mat, int64_t cols,
                                                double* partials, WsHeader* hdr) {
   constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K;
   __shared__ float cb[S][K][DIM];
@@ -65,37 +95,42 @@ __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx
   __syncthreads();
   const int m = blockIdx.y;
   const size_t esz = DT == DT_F32 ? 4 : 2;
+  const uint64_t nvec_per_mat = (uint64_t)rows_per_mat * V;
   const uint8_t* idx_m = idx + (uint64_t)m * nvec_per_mat * 3;
-  const uint16_t* sc_m = scales + (uint64_t)m * (nvec_per_mat / V);
+  const uint16_t* sc_m = scales + (uint64_t)m * rows_per_mat;
   const char* W_m = (const char*)W + (uint64_t)m * nvec_per_mat * DIM * esz;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   double acc[S + 1];
 #pragma unroll
   for (int t = 0; t <= S; ++t) acc[t] = 0.0;
   bool nonfinite = false;
-  for (uint64_t vid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; vid < nvec_per_mat;
-       vid += (uint64_t)gridDim.x * blockDim.x) {
-    const uint32_t row = (uint32_t)(vid / V), j = (uint32_t)(vid % V);
-    float w[8];
-    load_vec8<DT>(W_m + (uint64_t)row * cols * esz, j, w);
+  // one wave per row: the row's scale once, vectors j = lane, lane + 64, ...
+  for (int64_t row = (int64_t)blockIdx.x * nw + wave; row < rows_per_mat; row += (int64_t)gridDim.x * nw) {
     const float s = f16_bits_to_f32(sc_m[row]);
-    const uint32_t word = load_record(idx_m + vid * 3);
-    float part[8];
+    const char* wrow = W_m + (uint64_t)row * cols * esz;
+    const uint8_t* rrec = idx_m + (uint64_t)row * V * 3;
+    for (uint32_t j = lane; j < V; j += 64) {
+      float w[8];
+      load_vec8<DT>(wrow, j, w);
+      const uint32_t word = load_record(rrec + (uint64_t)j * 3);
+      float part[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) part[k] = 0.0f;
+      for (int k = 0; k < 8; ++k) part[k] = 0.0f;
 #pragma unroll
-    for (int t = 0; t < S; ++t) {
-      const float* c = cb[t][record_index<FMT>(word, t)];
+      for (int t = 0; t < S; ++t) {
+        const float* c = cb[t][record_index<FMT>(word, t)];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          part[k] = (t == 0) ? c[k] : part[k] + c[k];
+          const double d = (double)w[k] - (double)(s * part[k]);
+          acc[t] += d * d;
+        }
+      }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        part[k] = (t == 0) ? c[k] : part[k] + c[k];
-        const double d = (double)w[k] - (double)(s * part[k]);
-        acc[t] += d * d;
+        nonfinite |= !__builtin_isfinite(w[k]);
+        acc[S] += (double)w[k] * (double)w[k];
       }
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      nonfinite |= !__builtin_isfinite(w[k]);
-      acc[S] += (double)w[k] * (double)w[k];
     }
   }
   if (nonfinite) flag_status(hdr, ST_NONFINITE);
@@ -123,9 +158,9 @@ __global__ void k_error_reduce(const double* partials, int blocks, int nv, int64
 template <int FMT, int DT>
 static hipError_t launch_error_t(const ErrorArgs& a) {
   constexpr int S = Fmt<FMT>::S;
-  const uint64_t V = (uint64_t)(a.cols / DIM), nvec = (uint64_t)a.rows * V;
+  const uint64_t V = (uint64_t)(a.cols / DIM);
   dim3 grid((unsigned)a.blocks, (unsigned)a.n_mats);
-  k_error<FMT, DT><<<grid, 256, 0, a.stream>>>(a.W, a.idx, a.scales, a.codebooks, (uint32_t)V, nvec, a.cols,
+  k_error<FMT, DT><<<grid, 256, 0, a.stream>>>(a.W, a.idx, a.scales, a.codebooks, (uint32_t)V, a.rows, a.cols,
                                                a.partials, a.hdr);
   const int64_t nq = a.n_mats * (S + 1);
   k_error_reduce<<<(unsigned)((nq + 255) / 256), 256, 0, a.stream>>>(a.partials, a.blocks, S + 1, a.n_mats, a.sums);

@@ -206,6 +206,25 @@ def test_decode_bit_exact_and_error(cfg1, fmt):
     assert np.all(np.diff(e) <= 1e-12)
 
 
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+def test_decode_ragged_rows_and_unaligned_records(cfg1, fmt):
+    """Rows of 13 vectors (not a multiple of 4) and records starting at an odd
+    byte address take the one-vector-per-step path; both must stay bit-exact."""
+    say("decode ragged / unaligned", fmt)
+    _, cb = cfg1[fmt]
+    cbd = to_dev(cb)
+    for rows, cols, offset in ((37, 104, 0), (16, 256, 1), (5, 104, 3)):
+        W = synthetic.student_t_rows_f32(rows, cols, seed=rows + cols)
+        idx_o, s_o = oracle.encode(W, cb)
+        packed = oracle.pack(fmt, idx_o).reshape(-1)
+        buf = torch.zeros(packed.size + 8, dtype=torch.uint8, device=DEV)
+        buf[offset:offset + packed.size] = to_dev(packed)
+        rec = buf[offset:offset + packed.size].view(rows, cols // 8, 3)
+        got = vq.decode(rec, to_dev(s_o.view(np.float16)), cbd, fmt=fmt).cpu().numpy()
+        ref = oracle.decode(idx_o, s_o, cb)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (rows, cols, offset)
+
+
 def test_error_multi_matrix_bf16(cfg1):
     say("error multi matrix bf16")
     _, cb = cfg1["vq3r"]
