@@ -53,39 +53,61 @@ int64_t gemv_packed_bytes(int format, int64_t rows, int64_t cols) {
 }
 
 // ------------------------------------------------------------------ repack
-// One thread per 12-byte chunk of the packed layout; pad rows / slices are 0.
+// One workgroup (256 threads) per tile (expert, block of 16 slices, group of
+// 64 rows): the tile's 64 x 48 record bytes are read row by row (4 threads per
+// row, 12 bytes each: three dword loads when the row segment is 4-byte aligned)
+// into LDS, then written as the 4 x 64 rotated 12-byte chunks of the packed
+// layout, one chunk per thread (contiguous across a wave). Pad rows and slices
+// are 0.
 __global__ __launch_bounds__(256) void k_gemv_pack(const uint8_t* idx, int64_t rows, int64_t V, int64_t n_experts,
                                                    uint8_t* out, int64_t packed_stride) {
-  constexpr int NC = GJ / 4;
+  constexpr int NC = GJ / 4, RB = GJ * 3;  // 4 chunks per row, 48 record bytes per row
+  __shared__ uint32_t tile[GROUP][RB / 4 + 1];
   const int64_t ng = (rows + GROUP - 1) / GROUP, nblk = (V + GJ - 1) / GJ;
-  const int64_t per_expert = nblk * ng * NC * GROUP;
-  const int64_t total = per_expert * n_experts;
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e = q / per_expert, rem = q % per_expert;
-    const int lane = (int)(rem % GROUP);
-    const int64_t c = (rem / GROUP) % NC, g = (rem / (GROUP * NC)) % ng, b = rem / (GROUP * NC * ng);
-    const int64_t row = g * GROUP + lane;
-    uint8_t buf[12];
-#pragma unroll
-    for (int k = 0; k < 12; ++k) buf[k] = 0;
+  const int64_t ntiles = n_experts * nblk * ng;
+  const int tid = threadIdx.x;
+  const int r = tid >> 2, part = tid & 3;     // load: row of the group, 12-byte part of its 48 bytes
+  const int c = tid >> 6, lane = tid & 63;    // store: chunk c of row `lane`
+  const bool dword_ok = ((V * 3) & 3) == 0 && ((uintptr_t)idx & 3) == 0;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t e = t / (nblk * ng), rem = t % (nblk * ng);
+    const int64_t b = rem / ng, g = rem % ng;
+    const int64_t row = g * GROUP + r;
+    const int64_t j0 = b * GJ;
+    uint32_t w[3] = {0u, 0u, 0u};
     if (row < rows) {
+      const uint8_t* src = idx + ((e * rows + row) * V + j0) * 3 + part * 12;
+      const int64_t nbytes = ((V - j0) < GJ ? (V - j0) : GJ) * 3 - part * 12;  // valid bytes of this part
+      if (dword_ok && nbytes >= 12) {
+        const uint32_t* s4 = reinterpret_cast<const uint32_t*>(src);
+        w[0] = s4[0];
+        w[1] = s4[1];
+        w[2] = s4[2];
+      } else {
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int64_t j = b * GJ + ((c * 4 + qq + lane) % GJ);
-        if (j < V) {
-          const uint8_t* src = idx + ((e * rows + row) * V + j) * 3;
-          buf[3 * qq] = src[0];
-          buf[3 * qq + 1] = src[1];
-          buf[3 * qq + 2] = src[2];
-        }
+        for (int k = 0; k < 12; ++k)
+          if (k < nbytes) w[k >> 2] |= (uint32_t)src[k] << (8 * (k & 3));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) tile[r][part * 3 + k] = w[k];
+    __syncthreads();
+    const uint8_t* tb = reinterpret_cast<const uint8_t*>(&tile[lane][0]);
+    uint32_t o[3] = {0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int sl = (4 * c + q + lane) & (GJ - 1);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int ob = 3 * q + k;
+        o[ob >> 2] |= (uint32_t)tb[3 * sl + k] << (8 * (ob & 3));
       }
     }
     uint32_t* dst =
         reinterpret_cast<uint32_t*>(out + e * packed_stride + ((b * ng + g) * NC + c) * (GROUP * 12) + lane * 12);
 #pragma unroll
-    for (int k = 0; k < 3; ++k)
-      dst[k] = (uint32_t)buf[4 * k] | ((uint32_t)buf[4 * k + 1] << 8) | ((uint32_t)buf[4 * k + 2] << 16) |
-               ((uint32_t)buf[4 * k + 3] << 24);
+    for (int k = 0; k < 3; ++k) dst[k] = o[k];
+    __syncthreads();  // the tile buffer is refilled next
   }
 }
 
@@ -328,9 +350,9 @@ hipError_t launch_gemv(const GemvArgs& a) {
 hipError_t launch_gemv_pack(int format, const uint8_t* idx, int64_t rows, int64_t cols, int64_t n_experts,
                             uint8_t* out, int ncu, hipStream_t s) {
   const int64_t V = cols / DIM;
-  const int64_t nchunks = ((V + GJ - 1) / GJ) * ((rows + GROUP - 1) / GROUP) * (GJ / 4) * GROUP * n_experts;
-  if (nchunks == 0) return hipSuccess;
-  int64_t g = (nchunks + 255) / 256;
+  const int64_t ntiles = ((V + GJ - 1) / GJ) * ((rows + GROUP - 1) / GROUP) * n_experts;
+  if (ntiles == 0) return hipSuccess;
+  int64_t g = ntiles;
   if (g > (int64_t)ncu * 32) g = (int64_t)ncu * 32;
   k_gemv_pack<<<(unsigned)g, 256, 0, s>>>(idx, rows, V, n_experts, out, gemv_packed_bytes(format, rows, cols));
   return hipGetLastError();
