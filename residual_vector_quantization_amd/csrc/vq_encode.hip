@@ -240,18 +240,28 @@ __global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_
   const int F = hdr->fbits;
   uint32_t mx = 0;
   const int64_t ngroups = (n + GV - 1) / GV;
-  for (int64_t g = (int64_t)blockIdx.x * 4 + wave; g < ngroups; g += (int64_t)gridDim.x * 4) {
+  const int64_t gstride = (int64_t)gridDim.x * 4;
+  // the next group's residuals are loaded while the current group is searched
+  // (unconditional loads of a clamped vector index keep the wait counts exact)
+  float4 na, nb;
+  auto load_r = [&](int64_t g) {
+    int64_t jj = g * GV + jl;
+    jj = jj < n ? jj : n - 1;
+    const float4* p = reinterpret_cast<const float4*>(R_cur + jj * DIM);
+    na = p[0];
+    nb = p[1];
+  };
+  load_r((int64_t)blockIdx.x * 4 + wave);
+  for (int64_t g = (int64_t)blockIdx.x * 4 + wave; g < ngroups; g += gstride) {
     const int64_t j = g * GV + jl;
     const bool valid = j < n;
     float r[8], r0[8];
-    if (valid) {
-      const float4* p = reinterpret_cast<const float4*>(R_cur + j * DIM);
-      float4 a = p[0], b = p[1];
-      r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w; r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
-    } else {
+    r[0] = na.x; r[1] = na.y; r[2] = na.z; r[3] = na.w; r[4] = nb.x; r[5] = nb.y; r[6] = nb.z; r[7] = nb.w;
+    if (!valid) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) r[k] = 0.0f;
     }
+    load_r(g + gstride < ngroups ? g + gstride : g);
 #pragma unroll
     for (int k = 0; k < 8; ++k) r0[k] = r[k];
     bool fl = false;

@@ -52,8 +52,8 @@ def test_workspace_sizes():
     n = 12 * 2048 * 896
     assert L.vq_fit_workspace_size(0, 12, 2048, 7168) >= 2 * 32 * n
     assert L.vq_fit_workspace_size(1, 1, 0, 64) == 0
-    # header + row sums per (slot, block of 32 slices)
-    npairs, nblk = 16 * 8, 28
+    # header + row sums per (slot, block of 16 slices): 7168 / 8 / 16 = 56 blocks
+    npairs, nblk = 16 * 8, 56
     assert L.vq_gemv_workspace_size(0, 2048, 7168, 16, 8) >= 256 + npairs * nblk * 2048 * 4
     assert L.vq_gemv_workspace_size(0, 2048, 7168, 16, 8) == L.vq_gemv_workspace_size(1, 2048, 7168, 16, 8)
     assert L.vq_error_workspace_size(0, 4, 256, 1024) > 256
