@@ -54,7 +54,9 @@ typedef enum vq_status {
   VQ_ERANGE = 2,     /* size beyond the supported range */
   VQ_EWORKSPACE = 3, /* workspace missing, misaligned or too small */
   VQ_EDEVICE = 4,    /* a HIP runtime call failed */
-  VQ_EDATA = 5       /* the device flagged a data error (vq_read_status) */
+  VQ_EDATA = 5,      /* the device flagged a data error (vq_read_status) */
+  VQ_EIO = 6,        /* container file: open, read or write failed or was short */
+  VQ_EFORMAT = 7     /* container file: bad header, checksum mismatch, missing record */
 } vq_status;
 
 typedef enum vq_dtype { VQ_DT_F32 = 0, VQ_DT_BF16 = 1, VQ_DT_F16 = 2 } vq_dtype;

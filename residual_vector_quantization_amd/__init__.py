@@ -19,6 +19,8 @@ __all__ = [
     "VQError", "lib", "FORMATS", "ENGINES", "stages_entries",
     "encode", "decode", "fit_codebooks", "gemv_pack", "dequant_gemv", "error_sums", "rel_errors", "mxfp4_qdq",
     "encode_workspace", "fit_workspace", "gemv_workspace", "error_workspace", "read_status",
+    "container_layout", "crc32", "write_container", "container_info", "read_container", "load_container",
+    "verify_container",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +29,8 @@ LIB_PATH = os.path.join(_HERE, "libvq.so")
 FORMATS = {"vq3r": 0, "vq4p": 1}
 ENGINES = {"auto": 0, "mfma_f16x": 1, "mfma_f32": 2, "valu_f32": 3, "exact": 4}
 STATUS = {0: "ok", 1: "invalid argument", 2: "size out of range", 3: "workspace", 4: "HIP runtime error",
-          5: "data error flagged on the device"}
+          5: "data error flagged on the device", 6: "container file I/O failed",
+          7: "container file malformed or corrupt"}
 
 
 def stages_entries(fmt: str):
@@ -82,6 +85,14 @@ def lib():
         "vq_error_workspace_size": ([I, L64, L64, L64], SZ),
         "vq_error": ([I, P, I, P, P, P, L64, L64, L64, P, P, SZ, P], I),
         "vq_mxfp4_qdq": ([P, I, L64, L64, P, P, SZ, P], I),
+        "vqc_layout": ([I, L64, L64, L64, P, P, P], ctypes.c_uint64),
+        "vqc_crc32": ([ctypes.c_uint32, P, SZ], ctypes.c_uint32),
+        "vqc_create": ([ctypes.c_char_p, I, L64, L64, L64, P], I),
+        "vqc_write_records": ([ctypes.c_char_p, L64, L64, P, P, P], I),
+        "vqc_info": ([ctypes.c_char_p, P, P, P, P], I),
+        "vqc_read_codebooks": ([ctypes.c_char_p, P], I),
+        "vqc_read_records": ([ctypes.c_char_p, L64, L64, P, P, P], I),
+        "vqc_load_records": ([ctypes.c_char_p, L64, L64, P, P, P, P, SZ, P], I),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -309,3 +320,133 @@ def mxfp4_qdq(W, out=None, workspace=None, check=True):
                             _stream())
     _call("vq_mxfp4_qdq", st, workspace, check)
     return out
+
+
+# ------------------------------------------------------------------ container
+# Expert records on disk (include/vq_container.h; [VQ3R page] §1 experts
+# streamed from disk, §4 codebooks stored with the container and record-by-
+# record verification against the source weights, §5 VQ4P records).
+def _host(a, dtype):
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a).view(dtype) if np.asarray(a).dtype != dtype else np.asarray(a))
+
+
+def _path(path):
+    return os.fsencode(os.fspath(path))
+
+
+def container_layout(fmt, rows, cols, n_records):
+    """Byte layout of a container: total size, table and records offsets, record stride."""
+    t, r, s = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+    total = lib().vqc_layout(FORMATS[fmt], rows, cols, n_records, ctypes.byref(t), ctypes.byref(r), ctypes.byref(s))
+    if total == 0:
+        raise VQError(1, "vqc_layout")
+    return {"bytes": int(total), "table_offset": t.value, "records_offset": r.value, "record_stride": s.value}
+
+
+def crc32(data, crc=0):
+    """CRC-32 (IEEE, as zlib) of a bytes-like object, computed by the library."""
+    b = np.frombuffer(bytes(data), dtype=np.uint8)
+    return int(lib().vqc_crc32(crc, b.ctypes.data_as(ctypes.c_void_p), b.size))
+
+
+def write_container(path, fmt, codebooks, idx, scales, rel_err=None):
+    """Writes a container of n records: codebooks fp32 [stages, entries, 8],
+    idx uint8 [n, rows, cols/8, 3], scales fp16 [n, rows] (torch tensors on any
+    device, or numpy), rel_err optional f64 [n, stages] (the measured relative
+    error after each stage, stored for verify_container)."""
+    cb = _host(codebooks, np.float32)
+    ix = _host(idx, np.uint8)
+    sc = _host(scales, np.uint16)
+    n, rows, V = ix.shape[0], ix.shape[1], ix.shape[2]
+    if ix.shape[3:] != (3,) or sc.shape != (n, rows) or cb.shape != stages_entries(fmt) + (8,):
+        raise ValueError("write_container: shapes do not match")
+    st = lib().vqc_create(_path(path), FORMATS[fmt], rows, V * 8, n, cb.ctypes.data_as(ctypes.c_void_p))
+    _call("vqc_create", st)
+    re = None
+    if rel_err is not None:
+        re = np.full((n, 4), np.nan)
+        r = np.asarray(rel_err.detach().cpu() if hasattr(rel_err, "detach") else rel_err, dtype=np.float64)
+        re[:, :r.shape[1]] = r
+    st = lib().vqc_write_records(_path(path), 0, n, sc.ctypes.data_as(ctypes.c_void_p),
+                                 ix.ctypes.data_as(ctypes.c_void_p),
+                                 re.ctypes.data_as(ctypes.c_void_p) if re is not None else None)
+    _call("vqc_write_records", st)
+
+
+def container_info(path):
+    """{'fmt', 'rows', 'cols', 'n_records'} from a validated header."""
+    f, r, c, n = ctypes.c_int(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    st = lib().vqc_info(_path(path), ctypes.byref(f), ctypes.byref(r), ctypes.byref(c), ctypes.byref(n))
+    _call("vqc_info", st)
+    fmt = {v: k for k, v in FORMATS.items()}[f.value]
+    return {"fmt": fmt, "rows": r.value, "cols": c.value, "n_records": n.value}
+
+
+def _range(info, first, count):
+    if count is None:
+        count = info["n_records"] - first
+    return first, count
+
+
+def read_container(path, first=0, count=None):
+    """Host (numpy) read with CRC checks: (codebooks f32, idx u8 [count, rows, V, 3],
+    scales fp16 bits u16 [count, rows], rel_err f64 [count, stages])."""
+    info = container_info(path)
+    first, count = _range(info, first, count)
+    S, K = stages_entries(info["fmt"])
+    rows, V = info["rows"], info["cols"] // 8
+    cb = np.empty((S, K, 8), dtype=np.float32)
+    _call("vqc_read_codebooks", lib().vqc_read_codebooks(_path(path), cb.ctypes.data_as(ctypes.c_void_p)))
+    ix = np.empty((count, rows, V, 3), dtype=np.uint8)
+    sc = np.empty((count, rows), dtype=np.uint16)
+    re = np.empty((count, 4), dtype=np.float64)
+    st = lib().vqc_read_records(_path(path), first, count, sc.ctypes.data_as(ctypes.c_void_p),
+                                ix.ctypes.data_as(ctypes.c_void_p), re.ctypes.data_as(ctypes.c_void_p))
+    _call("vqc_read_records", st)
+    return cb, ix, sc, re[:, :S]
+
+
+def load_container(path, first=0, count=None, device="cuda", staging_bytes=64 << 20):
+    """Streams records into device memory (vqc_load_records) through a pinned
+    staging buffer: (codebooks f32 [S, K, 8], idx u8 [count, rows, V, 3],
+    scales fp16 [count, rows], rel_err f64 numpy [count, stages]), all tensors on `device`."""
+    torch = _torch()
+    info = container_info(path)
+    first, count = _range(info, first, count)
+    S, K = stages_entries(info["fmt"])
+    rows, V = info["rows"], info["cols"] // 8
+    stride = container_layout(info["fmt"], rows, info["cols"], info["n_records"])["record_stride"]
+    nbytes = max(int(staging_bytes), 2 * stride)
+    raw = torch.empty(nbytes + 4096, dtype=torch.uint8, pin_memory=True)
+    off = (-raw.data_ptr()) % 4096
+    cbh = np.empty((S, K, 8), dtype=np.float32)
+    _call("vqc_read_codebooks", lib().vqc_read_codebooks(_path(path), cbh.ctypes.data_as(ctypes.c_void_p)))
+    cb = torch.from_numpy(cbh).to(device)
+    ix = torch.empty((count, rows, V, 3), dtype=torch.uint8, device=device)
+    sc = torch.empty((count, rows), dtype=torch.float16, device=device)
+    re = np.empty((count, 4), dtype=np.float64)
+    st = lib().vqc_load_records(_path(path), first, count, _ptr(sc), _ptr(ix), re.ctypes.data_as(ctypes.c_void_p),
+                                ctypes.c_void_p(raw.data_ptr() + off), nbytes, _stream())
+    _call("vqc_load_records", st)
+    return cb, ix, sc, re[:, :S]
+
+
+def verify_container(path, sources, first=0):
+    """Dequantizes each record of the container on the GPU and compares it with
+    its source matrix (sources[r] is the [rows, cols] weight tensor of record
+    first + r): returns {'stored': f64 [n, stages] errors stored at conversion,
+    'measured': the same errors recomputed from the container's bytes,
+    'match': stored == measured for every record that stored them}."""
+    info = container_info(path)
+    n = len(sources)
+    cb, ix, sc, stored = load_container(path, first, n, device=sources[0].device)
+    measured = np.empty_like(stored)
+    for r in range(n):
+        sums = error_sums(sources[r], ix[r], sc[r], cb, fmt=info["fmt"])
+        measured[r] = rel_errors(sums)[0].cpu().numpy()
+    have = ~np.isnan(stored)
+    match = bool(np.array_equal(stored[have], measured[have]))
+    return {"stored": stored, "measured": measured, "match": match}
+

@@ -109,6 +109,8 @@ const char* vq_status_string(int status) {
     case VQ_EWORKSPACE: return "workspace missing, misaligned or too small";
     case VQ_EDEVICE: return "HIP runtime error";
     case VQ_EDATA: return "data error flagged on the device";
+    case VQ_EIO: return "container file I/O failed";
+    case VQ_EFORMAT: return "container file malformed or corrupt";
     default: return "unknown status";
   }
 }

@@ -11,21 +11,25 @@ import pytest
 import residual_vector_quantization_amd as vq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "vq.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 VQ_OK, VQ_EINVAL, VQ_ERANGE, VQ_EWORKSPACE = 0, 1, 2, 3
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(vq\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(vq\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_hot_path_entry_points():
     names = declared_functions()
     for n in ["vq_fit_codebooks", "vq3r_encode", "vq3r_decode", "vq3r_dequant_gemv",
-              "vq4p_encode", "vq4p_decode", "vq4p_dequant_gemv"]:
+              "vq4p_encode", "vq4p_decode", "vq4p_dequant_gemv", "vqc_create", "vqc_write_records", "vqc_info",
+              "vqc_read_codebooks", "vqc_read_records", "vqc_load_records", "vqc_layout", "vqc_crc32"]:
         assert n in names
 
 
@@ -37,8 +41,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = vq.lib()
-    for s in range(6):
-        assert L.vq_status_string(s)
+    for s in range(8):
+        assert L.vq_status_string(s) and L.vq_status_string(s) != b"unknown status"
     assert L.vq_status_string(99) == b"unknown status"
     assert L.vq_version() >> 16 == 1
 
