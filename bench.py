@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--only", default="", help="comma list: fit,encode,decode,error,gemv,vq4p (default all)")
     ap.add_argument("--loop", default="", help="profiling helper: repeat one component (encode|gemv1|gemv16|fit) --steps times")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a plain copy of known size")
+    ap.add_argument("--container", default="", help="container measurement: write the layer's VQ3R records "
+                    "into a container under this directory, then time streaming them into device memory and "
+                    "verifying them (prints its own JSON line)")
     return ap.parse_args()
 
 
@@ -198,6 +201,10 @@ def main():
                     vq.dequant_gemv(pk4, sc4_e, cb4, x, route, ROWS, COLS, fmt="vq4p", y=y, workspace=ws4)
     step.fitted = False
 
+    if args.container:
+        container_bench(args, torch, vq, W, mats, init3, cb3, fit_ws3, idx3, sc3, enc_ws, E)
+        return
+
     if args.loop:
         # profiling helper: one component repeated, nothing else in the trace
         if args.loop != "fit":
@@ -309,6 +316,63 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def container_bench(args, torch, vq, W, mats, init3, cb3, fit_ws3, idx3, sc3, enc_ws, E):
+    """Expert-record container over the whole layer: write (host), load into
+    device memory through the pinned staging buffer, verify on the GPU. The
+    load is timed against a plain pinned host-to-device copy of the same bytes."""
+    vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3, workspace=fit_ws3)
+    vq.encode(W, cb3, idx=idx3, scales=sc3, workspace=enc_ws)
+    sums = vq.error_sums(W, idx3, sc3, cb3, fmt="vq3r", n_mats=E)
+    rel = vq.rel_errors(sums)
+    os.makedirs(args.container, exist_ok=True)
+    path = os.path.join(args.container, "w1_vq3r.vqc")
+    idx_e, sc_e = idx3.view(E, ROWS, COLS // 8, 3), sc3.view(E, ROWS)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    vq.write_container(path, "vq3r", cb3, idx_e, sc_e, rel_err=rel)
+    t_write = time.time() - t0
+    log("container written: %.1f s" % t_write)
+    payload = E * (ROWS * (COLS // 8) * 3 + ROWS * 2)
+    loads = []
+    for i in range(max(1, args.steps)):
+        torch.cuda.synchronize()
+        t0 = time.time()
+        _, ix, sc, _ = vq.load_container(path)
+        torch.cuda.synchronize()
+        loads.append(time.time() - t0)
+        log("load %d: %.3f s" % (i, loads[-1]))
+    same = bool(torch.equal(ix, idx_e) and torch.equal(sc.view(torch.int16), sc_e.view(torch.int16)))
+    del ix, sc
+    pin = torch.empty(payload, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(payload, dtype=torch.uint8, device="cuda")
+    h2d = []
+    for i in range(3):
+        torch.cuda.synchronize()
+        t0 = time.time()
+        dst.copy_(pin, non_blocking=True)
+        torch.cuda.synchronize()
+        h2d.append(time.time() - t0)
+    del pin, dst
+    sample = np.random.default_rng(0).integers(0, 256, 256 << 20, dtype=np.uint8).tobytes()
+    t0 = time.time()
+    vq.crc32(sample)
+    crc_gbs = len(sample) / (time.time() - t0) / 1e9
+    torch.cuda.synchronize()
+    t0 = time.time()
+    v = vq.verify_container(path, [W[e * ROWS:(e + 1) * ROWS] for e in range(E)])
+    torch.cuda.synchronize()
+    t_verify = time.time() - t0
+    ncpu = len(os.sched_getaffinity(0))
+    print(json.dumps({"container": {
+        "records": E, "record_shape": [ROWS, COLS], "payload_bytes": payload, "file_bytes": os.path.getsize(path),
+        "write_s": round(t_write, 3), "load_s_best": round(min(loads), 4),
+        "load_GB_s": round(payload / min(loads) / 1e9, 2),
+        "pinned_h2d_copy_GB_s": round(payload / min(h2d) / 1e9, 2),
+        "crc32_single_thread_GB_s": round(crc_gbs, 2), "host_threads": ncpu,
+        "verify_s": round(t_verify, 3), "verify_match": v["match"], "load_bit_exact": same}}), flush=True)
+    os.remove(path)
 
 
 def encode_traffic():

@@ -210,7 +210,10 @@ int vq4p_dequant_gemv(const uint8_t* packed, int64_t expert_stride, const uint16
  * idx + m*rows*cols/8*3 bytes, scales + m*rows) writes fp64
  * sums[m][t] = sum (w - w_hat_{t+1})^2 for t = 0..stages-1 (w_hat_t = the
  * partial reconstruction after t stages) and sums[m][stages] = sum w^2.
- * sums: device fp64 [n_mats][stages+1].
+ * sums: device fp64 [n_mats][stages+1]. The sums of a matrix are added in an
+ * order fixed by its row count (partials per 16-row chunk, added in chunk
+ * order), so they are bit-identical whether the matrix is passed alone or
+ * together with others.
  * Workspace: vq_error_workspace_size(format, n_mats, rows, cols).
  * ---------------------------------------------------------------------- */
 size_t vq_error_workspace_size(int format, int64_t n_mats, int64_t rows, int64_t cols);

@@ -408,7 +408,7 @@ def read_container(path, first=0, count=None):
     return cb, ix, sc, re[:, :S]
 
 
-def load_container(path, first=0, count=None, device="cuda", staging_bytes=64 << 20):
+def load_container(path, first=0, count=None, device="cuda", staging_bytes=256 << 20):
     """Streams records into device memory (vqc_load_records) through a pinned
     staging buffer: (codebooks f32 [S, K, 8], idx u8 [count, rows, V, 3],
     scales fp16 [count, rows], rel_err f64 numpy [count, stages]), all tensors on `device`."""

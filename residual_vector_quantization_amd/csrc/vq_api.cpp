@@ -88,13 +88,18 @@ FitLayout fit_layout(int format, int64_t n) {
   return L;
 }
 
-int error_blocks(int64_t nvec_per_mat, int64_t n_mats) {
-  int64_t want = (nvec_per_mat + 255) / 256;
+// grid width per matrix for vq_error: about 2048 blocks in all, at most one per chunk
+int error_blocks(int64_t rows, int64_t n_mats) {
+  int64_t want = error_chunks(rows);
   int64_t cap = (2048 + n_mats - 1) / n_mats;
   if (cap < 1) cap = 1;
   if (want > cap) want = cap;
   if (want < 1) want = 1;
   return (int)want;
+}
+
+size_t error_ws_bytes(int format, int64_t n_mats, int64_t rows) {
+  return align256(kHeader + sizeof(double) * (size_t)n_mats * (size_t)error_chunks(rows) * (stages_of(format) + 1));
 }
 
 }  // namespace
@@ -360,8 +365,7 @@ int vq4p_dequant_gemv(const uint8_t* packed, int64_t expert_stride, const uint16
 // ---------------------------------------------------------------- error
 size_t vq_error_workspace_size(int format, int64_t n_mats, int64_t rows, int64_t cols) {
   if (!fmt_ok(format) || n_mats < 1 || check_shape(rows, cols) != VQ_OK) return 0;
-  const int blocks = error_blocks(rows * (cols / 8), n_mats);
-  return align256(kHeader + sizeof(double) * (size_t)n_mats * blocks * (stages_of(format) + 1));
+  return error_ws_bytes(format, n_mats, rows);
 }
 
 int vq_error(int format, const void* W, int dtype, const uint8_t* idx, const uint16_t* scales, const float* codebooks,
@@ -372,9 +376,8 @@ int vq_error(int format, const void* W, int dtype, const uint8_t* idx, const uin
   if (st != VQ_OK) return st;
   if (n_mats > 65535) return VQ_ERANGE;
   if (!W || !idx || !scales || !codebooks || !sums || !aligned(W, 16)) return VQ_EINVAL;
-  const int blocks = error_blocks(rows * (cols / 8), n_mats);
-  const size_t need = align256(kHeader + sizeof(double) * (size_t)n_mats * blocks * (stages_of(format) + 1));
-  if (!workspace || !aligned(workspace, 256) || ws_bytes < need) return VQ_EWORKSPACE;
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < error_ws_bytes(format, n_mats, rows)) return VQ_EWORKSPACE;
+  const int blocks = error_blocks(rows, n_mats);
   ErrorArgs a;
   a.format = format;
   a.dtype = dtype;

@@ -228,25 +228,28 @@ uint32_t record_crc(const Layout& L, const uint8_t* rec) {
   return crc32_update(crc32_update(0, rec, L.sc_bytes), rec + L.idx_off, L.idx_bytes);
 }
 
-// CRC check of k consecutive records in a buffer, spread over a few host threads.
-bool check_records(const Layout& L, const uint8_t* buf, const Entry* e, int64_t k) {
+// Reads k consecutive records into a buffer and checks their CRCs, the
+// records spread over a few host threads (each thread reads and checks its
+// own records, so page-cache copies and checksums run in parallel).
+// Returns VQ_OK, VQ_EIO or VQ_EFORMAT.
+int read_check_records(int fd, const Layout& L, uint8_t* buf, const Entry* e, int64_t k) {
   const unsigned hw = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
-  const int64_t nth = std::min<int64_t>(k, (int64_t)hw);
-  std::vector<char> ok((size_t)k, 0);
+  const int64_t nth = (L.stride * (uint64_t)k < (uint64_t(8) << 20)) ? 1 : std::min<int64_t>(k, (int64_t)hw);
+  std::vector<int> st((size_t)k, VQ_OK);
   auto work = [&](int64_t t) {
-    for (int64_t r = t; r < k; r += nth) ok[(size_t)r] = record_crc(L, buf + r * L.stride) == e[r].crc;
+    for (int64_t r = t; r < k; r += nth) {
+      uint8_t* rec = buf + r * L.stride;
+      if (!pread_all(fd, rec, L.stride, e[r].offset)) st[(size_t)r] = VQ_EIO;
+      else if (record_crc(L, rec) != e[r].crc) st[(size_t)r] = VQ_EFORMAT;
+    }
   };
-  if (nth <= 1 || L.stride * (uint64_t)k < (uint64_t(8) << 20)) {
-    for (int64_t r = 0; r < k; ++r) ok[(size_t)r] = record_crc(L, buf + r * L.stride) == e[r].crc;
-  } else {
-    std::vector<std::thread> th;
-    for (int64_t t = 1; t < nth; ++t) th.emplace_back(work, t);
-    work(0);
-    for (auto& x : th) x.join();
-  }
+  std::vector<std::thread> th;
+  for (int64_t t = 1; t < nth; ++t) th.emplace_back(work, t);
+  work(0);
+  for (auto& x : th) x.join();
   for (int64_t r = 0; r < k; ++r)
-    if (!ok[(size_t)r]) return false;
-  return true;
+    if (st[(size_t)r] != VQ_OK) return st[(size_t)r];
+  return VQ_OK;
 }
 
 bool range_ok(const Layout& L, int64_t first, int64_t count) {
@@ -405,14 +408,7 @@ int vqc_load_records(const char* path, int64_t first, int64_t count, uint16_t* s
       break;
     }
     pending[h] = false;
-    if (!pread_all(f.fd, buf[h], (uint64_t)k * L.stride, ents[(size_t)r0].offset)) {
-      st = VQ_EIO;
-      break;
-    }
-    if (!check_records(L, buf[h], &ents[(size_t)r0], k)) {
-      st = VQ_EFORMAT;
-      break;
-    }
+    if ((st = read_check_records(f.fd, L, buf[h], &ents[(size_t)r0], k)) != VQ_OK) break;
     for (int64_t r = 0; r < k && st == VQ_OK; ++r) {
       const uint8_t* rec = buf[h] + r * L.stride;
       if (hipMemcpyAsync(scales_dev + (uint64_t)(r0 + r) * L.rows, rec, L.sc_bytes, hipMemcpyHostToDevice, s) !=

@@ -83,11 +83,14 @@ hipError_t launch_decode(const DecodeArgs& a) {
 // ------------------------------------------------------------------ error
 // [VQ3R page] §3.1: ||W - W_hat||_F / ||W||_F. Per matrix, fp64 sums of
 // (w - w_hat_t)^2 for the partial reconstructions after t = 1..S stages and of
-// w^2; block partials are reduced in a fixed order by k_error_reduce.
+// w^2. The sums are grouped by fixed chunks of ERR_CHUNK rows: each chunk's
+// partial has its own slot, whichever block computes it, and k_error_reduce
+// adds the slots in chunk order. A matrix's result therefore depends only on
+// its own data, not on the grid or on how many matrices share a call.
 template <int FMT, int DT>
 __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx, const uint16_t* scales,
                                                const float* cb_g, uint32_t V, int64_t rows_per_mat, int64_t cols,
-                                               double* partials, WsHeader* hdr) {
+                                               int64_t nchunks, double* partials, WsHeader* hdr) {
   constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K;
   __shared__ float cb[S][K][DIM];
   __shared__ double red[S + 1][256];
@@ -100,58 +103,62 @@ __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx
   const uint16_t* sc_m = scales + (uint64_t)m * rows_per_mat;
   const char* W_m = (const char*)W + (uint64_t)m * nvec_per_mat * DIM * esz;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  double acc[S + 1];
-#pragma unroll
-  for (int t = 0; t <= S; ++t) acc[t] = 0.0;
   bool nonfinite = false;
-  // one wave per row: the row's scale once, vectors j = lane, lane + 64, ...
-  for (int64_t row = (int64_t)blockIdx.x * nw + wave; row < rows_per_mat; row += (int64_t)gridDim.x * nw) {
-    const float s = f16_bits_to_f32(sc_m[row]);
-    const char* wrow = W_m + (uint64_t)row * cols * esz;
-    const uint8_t* rrec = idx_m + (uint64_t)row * V * 3;
-    for (uint32_t j = lane; j < V; j += 64) {
-      float w[8];
-      load_vec8<DT>(wrow, j, w);
-      const uint32_t word = load_record(rrec + (uint64_t)j * 3);
-      float part[8];
+  for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    double acc[S + 1];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) part[k] = 0.0f;
+    for (int t = 0; t <= S; ++t) acc[t] = 0.0;
+    const int64_t r1 = (c + 1) * ERR_CHUNK < rows_per_mat ? (c + 1) * ERR_CHUNK : rows_per_mat;
+    // one wave per row: the row's scale once, vectors j = lane, lane + 64, ...
+    for (int64_t row = c * ERR_CHUNK + wave; row < r1; row += nw) {
+      const float s = f16_bits_to_f32(sc_m[row]);
+      const char* wrow = W_m + (uint64_t)row * cols * esz;
+      const uint8_t* rrec = idx_m + (uint64_t)row * V * 3;
+      for (uint32_t j = lane; j < V; j += 64) {
+        float w[8];
+        load_vec8<DT>(wrow, j, w);
+        const uint32_t word = load_record(rrec + (uint64_t)j * 3);
+        float part[8];
 #pragma unroll
-      for (int t = 0; t < S; ++t) {
-        const float* c = cb[t][record_index<FMT>(word, t)];
+        for (int k = 0; k < 8; ++k) part[k] = 0.0f;
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+          const float* cw = cb[t][record_index<FMT>(word, t)];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            part[k] = (t == 0) ? cw[k] : part[k] + cw[k];
+            const double d = (double)w[k] - (double)(s * part[k]);
+            acc[t] += d * d;
+          }
+        }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          part[k] = (t == 0) ? c[k] : part[k] + c[k];
-          const double d = (double)w[k] - (double)(s * part[k]);
-          acc[t] += d * d;
+          nonfinite |= !__builtin_isfinite(w[k]);
+          acc[S] += (double)w[k] * (double)w[k];
         }
       }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        nonfinite |= !__builtin_isfinite(w[k]);
-        acc[S] += (double)w[k] * (double)w[k];
-      }
     }
+#pragma unroll
+    for (int t = 0; t <= S; ++t) red[t][threadIdx.x] = acc[t];
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if ((int)threadIdx.x < o)
+#pragma unroll
+        for (int t = 0; t <= S; ++t) red[t][threadIdx.x] += red[t][threadIdx.x + o];
+      __syncthreads();
+    }
+    if (threadIdx.x <= S) partials[((uint64_t)m * nchunks + c) * (S + 1) + threadIdx.x] = red[threadIdx.x][0];
+    __syncthreads();  // red is reused by the next chunk
   }
   if (nonfinite) flag_status(hdr, ST_NONFINITE);
-#pragma unroll
-  for (int t = 0; t <= S; ++t) red[t][threadIdx.x] = acc[t];
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o)
-#pragma unroll
-      for (int t = 0; t <= S; ++t) red[t][threadIdx.x] += red[t][threadIdx.x + o];
-    __syncthreads();
-  }
-  if (threadIdx.x <= S) partials[((uint64_t)m * gridDim.x + blockIdx.x) * (S + 1) + threadIdx.x] = red[threadIdx.x][0];
 }
 
-__global__ void k_error_reduce(const double* partials, int blocks, int nv, int64_t n_mats, double* sums) {
+__global__ void k_error_reduce(const double* partials, int64_t nchunks, int nv, int64_t n_mats, double* sums) {
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= n_mats * nv) return;
   const int64_t m = q / nv, t = q % nv;
   double s = 0.0;
-  for (int b = 0; b < blocks; ++b) s += partials[(m * blocks + b) * nv + t];
+  for (int64_t c = 0; c < nchunks; ++c) s += partials[(m * nchunks + c) * nv + t];
   sums[q] = s;
 }
 
@@ -159,11 +166,12 @@ template <int FMT, int DT>
 static hipError_t launch_error_t(const ErrorArgs& a) {
   constexpr int S = Fmt<FMT>::S;
   const uint64_t V = (uint64_t)(a.cols / DIM);
+  const int64_t nchunks = error_chunks(a.rows);
   dim3 grid((unsigned)a.blocks, (unsigned)a.n_mats);
   k_error<FMT, DT><<<grid, 256, 0, a.stream>>>(a.W, a.idx, a.scales, a.codebooks, (uint32_t)V, a.rows, a.cols,
-                                               a.partials, a.hdr);
+                                               nchunks, a.partials, a.hdr);
   const int64_t nq = a.n_mats * (S + 1);
-  k_error_reduce<<<(unsigned)((nq + 255) / 256), 256, 0, a.stream>>>(a.partials, a.blocks, S + 1, a.n_mats, a.sums);
+  k_error_reduce<<<(unsigned)((nq + 255) / 256), 256, 0, a.stream>>>(a.partials, nchunks, S + 1, a.n_mats, a.sums);
   return hipGetLastError();
 }
 

@@ -59,8 +59,8 @@ struct ErrorArgs {
   const float* codebooks;
   int64_t n_mats, rows, cols;
   double* sums;
-  double* partials;  // [n_mats][blocks][stages+1]
-  int blocks;
+  double* partials;  // [n_mats][error_chunks(rows)][stages+1]
+  int blocks;        // grid width per matrix (does not change the result)
   WsHeader* hdr;
   hipStream_t stream;
 };
@@ -106,6 +106,10 @@ hipError_t launch_fit(const FitArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_error(const ErrorArgs& a);
 hipError_t launch_gemv(const GemvArgs& a);
+
+// rows per error chunk and the chunk count of a matrix (fixed by its row count)
+constexpr int ERR_CHUNK = 16;
+inline int64_t error_chunks(int64_t rows) { return (rows + ERR_CHUNK - 1) / ERR_CHUNK; }
 hipError_t launch_mxfp4(const Mxfp4Args& a);
 
 }  // namespace vqk

@@ -243,6 +243,23 @@ def test_error_multi_matrix_bf16(cfg1):
         assert abs(np.sqrt(sums[m, 2] / sums[m, 3]) - ref) < 1e-5
 
 
+@pytest.mark.parametrize("rows,cols,n", [(2048, 7168, 3), (100, 264, 70), (1, 8, 5)])
+def test_error_sums_do_not_depend_on_batching(rows, cols, n):
+    """A matrix's fp64 sums are bit-identical alone and inside a multi-matrix
+    call (the per-matrix summation order is fixed by its row count)."""
+    say("error batching", rows, cols, n)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(rows + n)
+    W = torch.randn((n * rows, cols), generator=g, device=DEV).to(torch.bfloat16)
+    cb = torch.randn((3, 256, 8), generator=g, device=DEV) * 0.5
+    idx, sc = vq.encode(W, cb)
+    both = vq.error_sums(W, idx, sc, cb, n_mats=n)
+    for m in range(n):
+        r = slice(m * rows, (m + 1) * rows)
+        one = vq.error_sums(W[r], idx[r], sc[r], cb, n_mats=1)
+        assert torch.equal(one[0], both[m]), m
+
+
 # ------------------------------------------------------------------ fit
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
 @pytest.mark.parametrize("engine", ["mfma_f16x", "mfma_f32", "valu_f32"])
