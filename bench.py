@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--only", default="", help="comma list: fit,encode,decode,error,gemv,vq4p (default all)")
     ap.add_argument("--loop", default="", help="profiling helper: repeat one component (encode|gemv1|gemv16|fit) --steps times")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a plain copy of known size")
+    ap.add_argument("--layer", action="store_true", help="per-layer conversion measurement: w1 and w3 "
+                    "[2048x7168] and w2 [7168x2048] of every expert, each family fit, encoded and measured, plus "
+                    "the w2 dequant-GEMV (prints its own JSON line)")
     ap.add_argument("--container", default="", help="container measurement: write the layer's VQ3R records "
                     "into a container under this directory, then time streaming them into device memory and "
                     "verifying them (prints its own JSON line)")
@@ -201,6 +204,10 @@ def main():
                     vq.dequant_gemv(pk4, sc4_e, cb4, x, route, ROWS, COLS, fmt="vq4p", y=y, workspace=ws4)
     step.fitted = False
 
+    if args.layer:
+        layer_bench(args, torch, vq, synthetic, W, E, evict)
+        return
+
     if args.container:
         container_bench(args, torch, vq, W, mats, init3, cb3, fit_ws3, idx3, sc3, enc_ws, E)
         return
@@ -316,6 +323,89 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def layer_bench(args, torch, vq, synthetic, W1, E, evict):
+    """Per-layer conversion: three matrix families per expert, each with its own
+    codebooks fit on the 12 sampled experts (w1 is the main workload's matrix;
+    w3 and w2 are drawn with the same recipe and seed families 6 and 7; w2 is
+    [7168 x 2048]). Times fit, encode and error per family, then the fused
+    dequant-GEMV on w2 at 1 / 4 / 16 tokens, top-8."""
+    dev = "cuda"
+    fams = {"w1": W1.view(E, ROWS, COLS)}
+    for name, cfgid, (r, c) in (("w3", 6, (ROWS, COLS)), ("w2", 7, (COLS, ROWS))):
+        t = torch.empty((E, r, c), dtype=torch.bfloat16, device=dev)
+        for e in range(E):
+            synthetic.student_t_expert_torch(synthetic.expert_seed(cfgid, e), r, c, device=dev, out=t[e])
+        fams[name] = t
+    torch.cuda.synchronize()
+    sample = synthetic.sample_experts(E, min(args.sample, E), seed=3)
+    T = Timer(torch)
+    out = {}
+    for name, Wn in fams.items():
+        _, r, c = Wn.shape
+        n_fit = len(sample) * r * c // 8
+        init = synthetic.forgy_init(n_fit, 256, 3, seed=3)
+        mats = [Wn[e] for e in sample]
+        flat = Wn.view(E * r, c)
+        fit_ws = vq.fit_workspace("vq3r", len(mats), r, c)
+        enc_ws = vq.encode_workspace("vq3r", E * r, c)
+        cb = torch.empty((3, 256, 8), dtype=torch.float32, device=dev)
+        idx = torch.empty((E * r, c // 8, 3), dtype=torch.uint8, device=dev)
+        sc = torch.empty(E * r, dtype=torch.float16, device=dev)
+        err_ws = vq.error_workspace("vq3r", E, r, c)
+        sums = torch.empty((E, 4), dtype=torch.float64, device=dev)
+        for rep in range(args.warmup + args.steps):
+            if rep == args.warmup:
+                T.reset()
+            with T(name + "_fit"):
+                vq.fit_codebooks(mats, init, fmt="vq3r", iters=args.iters, engine=args.engine, codebooks=cb,
+                                 workspace=fit_ws, check=False)
+            with T(name + "_encode"):
+                vq.encode(flat, cb, fmt="vq3r", engine=args.engine, idx=idx, scales=sc, workspace=enc_ws,
+                          check=False)
+            with T(name + "_error"):
+                vq.error_sums(flat, idx, sc, cb, fmt="vq3r", n_mats=E, sums=sums, workspace=err_ws, check=False)
+        vq.read_status(enc_ws)
+        tot = sums.sum(dim=0)
+        enc_ms = T.mean_ms(name + "_encode")
+        wts = E * r * c
+        out[name] = {"shape": [r, c], "fit_ms": round(T.mean_ms(name + "_fit"), 3), "encode_ms": round(enc_ms, 3),
+                     "error_ms": round(T.mean_ms(name + "_error"), 3),
+                     "encode_gweights_s": round(wts / (enc_ms * 1e-3) / 1e9, 2),
+                     "encode_frac_fp32_peak": round(wts / 8 * 12288 / (enc_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4),
+                     "rel_err_all": [round(float(v), 5) for v in (tot[:3] / tot[3]).sqrt()]}
+        log("%s: fit %.1f ms, encode %.1f ms, error %.2f ms" % (name, out[name]["fit_ms"], enc_ms,
+                                                               out[name]["error_ms"]))
+        if name == "w2":
+            pk = vq.gemv_pack(idx.view(E, r, c // 8, 3), fmt="vq3r")
+            gem = {}
+            for ntok in (1, 4, 16):
+                x = torch.from_numpy(synthetic.activations_f16(ntok, c, seed=30 + ntok).view(np.float16)).to(dev)
+                route = torch.from_numpy(synthetic.routing(ntok, E, 8, seed=40 + ntok)).to(dev)
+                y = torch.empty((ntok, 8, r), dtype=torch.float32, device=dev)
+                ws = vq.gemv_workspace("vq3r", r, c, ntok, 8)
+                ts = []
+                for rep in range(10):
+                    evict()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    vq.dequant_gemv(pk, sc.view(E, r), cb, x, route, r, c, fmt="vq3r", y=y, workspace=ws)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1e3)
+                us = float(np.median(ts[2:]))
+                distinct = len(np.unique(route.cpu().numpy()))
+                alg = distinct * (r * (c // 8) * 3 + r * 2) + ntok * c * 2 + ntok * 8 * r * 4 + 3 * 256 * 8 * 4
+                floor = read_floor_us(torch, alg, evict)
+                gbs = alg / (us * 1e-6) / 1e9
+                gem["gemv_%d" % ntok] = {"us": round(us, 2), "GB_s": round(gbs, 1),
+                                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "distinct_experts": distinct,
+                                         "alg_bytes": alg, "plain_read_us": round(floor, 2),
+                                         "frac_of_plain_read": round(floor / us, 4)}
+            out["w2"]["gemv"] = gem
+    print(json.dumps({"layer": out, "experts": E, "fit_sample": len(sample), "iters": args.iters}), flush=True)
 
 
 def container_bench(args, torch, vq, W, mats, init3, cb3, fit_ws3, idx3, sc3, enc_ws, E):

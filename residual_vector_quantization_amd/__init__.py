@@ -20,7 +20,7 @@ __all__ = [
     "encode", "decode", "fit_codebooks", "gemv_pack", "dequant_gemv", "error_sums", "rel_errors", "mxfp4_qdq",
     "encode_workspace", "fit_workspace", "gemv_workspace", "error_workspace", "read_status",
     "container_layout", "crc32", "write_container", "container_info", "read_container", "load_container",
-    "verify_container",
+    "verify_container", "convert_layer",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -449,4 +449,41 @@ def verify_container(path, sources, first=0):
     have = ~np.isnan(stored)
     match = bool(np.array_equal(stored[have], measured[have]))
     return {"stored": stored, "measured": measured, "match": match}
+
+
+# ------------------------------------------------------------------ layer conversion
+def convert_layer(weights, inits, sample, fmt="vq3r", iters=20, engine="auto", out_dir=None):
+    """Converts the expert matrices of one MoE layer ([VQ3R page] §2 and §4:
+    per layer and per matrix family, codebooks fit with k-means on sampled
+    experts, then every expert encoded; §3.2 reports the w1 and w2 errors
+    separately).
+
+    weights: {name: tensor [E, rows, cols]} on the GPU, e.g. w1 and w3
+             [E, 2048, 7168] and w2 [E, 7168, 2048] (fp32, bf16 or fp16);
+    inits:   {name: int64 [stages, entries]} Forgy indices into the training
+             vectors of the sampled experts of that matrix family;
+    sample:  the expert ids whose matrices train the codebooks.
+    Returns {name: {"codebooks", "idx" [E, rows, cols/8, 3], "scales" [E, rows],
+    "rel_err" f64 [E, stages] (per expert, after each stage), "rel_err_all"
+    f64 [stages] (over the whole family)}}. With out_dir, each family is also
+    written to out_dir/<name>.vqc with its per-expert errors."""
+    torch = _torch()
+    out = {}
+    for name, Wn in weights.items():
+        E, rows, cols = Wn.shape
+        mats = [Wn[e] for e in sample]
+        cb = fit_codebooks(mats, inits[name], fmt=fmt, iters=iters, engine=engine)
+        flat = Wn.reshape(E * rows, cols)
+        idx, sc = encode(flat, cb, fmt=fmt, engine=engine)
+        sums = error_sums(flat, idx, sc, cb, fmt=fmt, n_mats=E)
+        tot = sums.sum(dim=0)
+        res = {"codebooks": cb, "idx": idx.view(E, rows, cols // 8, 3), "scales": sc.view(E, rows),
+               "rel_err": rel_errors(sums), "rel_err_all": (tot[:-1] / tot[-1]).sqrt()}
+        if out_dir is not None:
+            os.makedirs(out_dir, exist_ok=True)
+            write_container(os.path.join(out_dir, name + ".vqc"), fmt, cb, res["idx"], res["scales"],
+                            rel_err=res["rel_err"])
+        out[name] = res
+    torch.cuda.current_stream().synchronize()
+    return out
 

@@ -324,6 +324,7 @@ int vq_dequant_gemv(int format, const uint8_t* packed, int64_t expert_stride, co
   if (!workspace || !aligned(workspace, 256) || ws_bytes < vq_gemv_workspace_size(format, rows, cols, ntok, topk))
     return VQ_EWORKSPACE;
   if ((int64_t)ntok * topk >= 65536) return VQ_ERANGE;
+  if (gemv_tiles(rows, cols, (int64_t)ntok * topk) > ((int64_t)1 << 31) - 64) return VQ_ERANGE;  // grid width
   GemvArgs a;
   a.format = format;
   a.idx = packed;

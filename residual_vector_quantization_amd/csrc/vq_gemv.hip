@@ -4,7 +4,8 @@
 //
 // y[p][r] = s_r * sum_j sum_t T_t[j][i_t(r, j)],   T_t[j][e] = <C_t[e], x_j>
 // where x_j is the j-th 8-element slice of the token's activation. A work tile
-// is (token-slot pair p, block of J = 16 slices): its workgroup tabulates T for
+// is (token-slot pair p, block of J = 16 slices, chunk of at most 2048 rows):
+// its workgroup tabulates T for
 // the block's slices in LDS with fp32 matrix-core products (codewords x
 // slices), then streams the tile's records, one row per lane: each index
 // costs one table read and one add. Tile partial sums go to the workspace and
@@ -181,19 +182,23 @@ __device__ inline int64_t tile_of_block(int64_t bid, int64_t ntiles_pad) {
   return (bid % 8) * per_xcd + bid / 8;
 }
 
-// GPW = row groups per wave (groups g = wave + 8k), known at launch: 1..4
-// fully unrolled with exact loads (up to 2048 rows), 0 = any count.
+// A tile is (slot pair, block of 16 slices, row chunk). Matrices of more than
+// 2048 rows are cut into nsplit chunks of near-equal group counts (at most 32
+// groups each), so that a tile never streams more than 2048 rows and tall
+// matrices still give many tiles. GPW = row groups per wave in a chunk (groups
+// g = g0 + wave + 8k, k < GPW), 1..4, fully unrolled.
 template <int FMT, int GPW>
 __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_t expert_stride, const float* cb_g,
                                                        int64_t rows, int64_t cols, int n_experts, const uint16_t* x,
                                                        int topk, const int32_t* route, float* partials, int nblk,
-                                                       int64_t ntiles, int64_t ntiles_pad) {
+                                                       int nsplit, int64_t ntiles, int64_t ntiles_pad) {
   constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, R = GemvCfg<FMT>::R, NC = GJ / 4;
   constexpr int NW = GEMV_WAVES;
   __shared__ float lut[K * S * R * GJ];
   const int64_t tile = tile_of_block(blockIdx.x, ntiles_pad);
   if (tile >= ntiles) return;
-  const int p = (int)(tile / nblk), b = (int)(tile % nblk);
+  const int64_t pb = tile / nsplit, chunk = tile % nsplit;
+  const int p = (int)(pb / nblk), b = (int)(pb % nblk);
   const int tok = p / topk;
   const int e = route[p];
   if (e < 0 || e >= n_experts) return;  // flagged and zeroed by k_gemv_reduce
@@ -202,12 +207,13 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
   const int nsl = (int)((V - j0) < GJ ? (V - j0) : GJ);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t ng = (rows + GROUP - 1) / GROUP;
+  const int64_t g0 = chunk * ng / nsplit, g1 = (chunk + 1) * ng / nsplit;  // this tile's groups [g0, g1)
   const uint8_t* tb = pk + (int64_t)e * expert_stride + (int64_t)b * ng * NC * (GROUP * 12);
   float* part = partials + ((int64_t)p * nblk + b) * rows;
   // unconditional loads with a clamped group index keep the wait counts exact
   uint32_t d[2][NC][3];
   auto load_group = [&](uint32_t (&dg)[NC][3], int64_t g) {
-    const int64_t gc = g < ng ? g : ng - 1;
+    const int64_t gc = g < g1 ? g : g1 - 1;
     const uint32_t* src = reinterpret_cast<const uint32_t*>(tb + gc * NC * (GROUP * 12)) + lane * 3;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -241,32 +247,22 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
       }
     }
     const int64_t row = g * GROUP + lane;
-    if (g < ng && row < rows) part[row] = acc;
+    if (row < rows) part[row] = acc;
   };
   LutOps<FMT> ops;
   lut_load<FMT>(ops, cb_g, x + (int64_t)tok * cols, j0, nsl);
   __builtin_amdgcn_sched_barrier(0);  // keep the table operand loads ahead of the index stream
-  load_group(d[0], wave);
-  if (GPW != 1) load_group(d[1], wave + NW);
+  load_group(d[0], g0 + wave);
+  if (GPW != 1) load_group(d[1], g0 + wave + NW);
   __builtin_amdgcn_sched_barrier(0);
   lut_compute<FMT>(ops, lut, nsl);
   __syncthreads();
-  if constexpr (GPW > 0) {
-    // two groups in flight: the load of group k + 2 follows the consume of group k
+  // two groups in flight: the load of group k + 2 follows the consume of group k
 #pragma unroll
-    for (int k = 0; k < GPW; ++k) {
-      consume(d[k & 1], wave + (int64_t)k * NW);
-      if (k + 2 < GPW) load_group(d[k & 1], wave + (int64_t)(k + 2) * NW);
-    }
-  } else {
-    for (int64_t g = wave; g < ng; g += 2 * NW) {
-      if (g != wave) {
-        load_group(d[0], g);
-        load_group(d[1], g + NW);
-      }
-      consume(d[0], g);
-      consume(d[1], g + NW);
-    }
+  for (int k = 0; k < GPW; ++k) {
+    const int64_t g = g0 + wave + (int64_t)k * NW;
+    if (g < g1) consume(d[k & 1], g);  // wave-uniform
+    if (k + 2 < GPW) load_group(d[k & 1], g0 + wave + (int64_t)(k + 2) * NW);
   }
 }
 
@@ -313,24 +309,34 @@ static hipError_t launch_gemv_t(const GemvArgs& a) {
   const int64_t npairs = (int64_t)a.ntok * a.topk;
   const int64_t V = a.cols / DIM;
   const int nblk = (int)((V + GJ - 1) / GJ);
-  const int64_t ntiles = npairs * nblk;
-  const int64_t ntiles_pad = (ntiles + 7) / 8 * 8;
   const int64_t ng = (a.rows + GROUP - 1) / GROUP;
-  const int64_t gpw = (ng + GEMV_WAVES - 1) / GEMV_WAVES;
+  const int nsplit = gemv_row_chunks(a.rows);
+  const int64_t ntiles = npairs * nblk * nsplit;
+  const int64_t ntiles_pad = (ntiles + 7) / 8 * 8;
+  const int64_t gpw = (ng / nsplit + (ng % nsplit != 0) + GEMV_WAVES - 1) / GEMV_WAVES;  // largest chunk
   auto go = [&](auto kern) {
     kern<<<(unsigned)ntiles_pad, GEMV_THREADS, 0, a.stream>>>(a.idx, a.expert_stride, a.codebooks, a.rows, a.cols,
                                                                a.n_experts, a.x, a.topk, a.route, a.partials, nblk,
-                                                               ntiles, ntiles_pad);
+                                                               nsplit, ntiles, ntiles_pad);
   };
   if (gpw == 1) go(k_gemv<FMT, 1>);
   else if (gpw == 2) go(k_gemv<FMT, 2>);
   else if (gpw == 3) go(k_gemv<FMT, 3>);
-  else if (gpw == 4) go(k_gemv<FMT, 4>);
-  else go(k_gemv<FMT, 0>);
+  else go(k_gemv<FMT, 4>);
   dim3 g2((unsigned)((a.rows + 255) / 256), (unsigned)npairs);
   k_gemv_reduce<<<g2, 256, 0, a.stream>>>(a.partials, a.scales, a.scale_stride, a.route, a.n_experts, a.rows, nblk,
                                           (int)npairs, a.y, a.hdr);
   return hipGetLastError();
+}
+
+int gemv_row_chunks(int64_t rows) {
+  const int64_t ng = (rows + GROUP - 1) / GROUP;
+  return (int)((ng + 4 * GEMV_WAVES - 1) / (4 * GEMV_WAVES));
+}
+
+int64_t gemv_tiles(int64_t rows, int64_t cols, int64_t npairs) {
+  const int64_t nblk = (cols / DIM + GJ - 1) / GJ;
+  return npairs * nblk * gemv_row_chunks(rows);
 }
 
 int64_t gemv_partials_floats(int format, int64_t rows, int64_t cols, int64_t npairs) {

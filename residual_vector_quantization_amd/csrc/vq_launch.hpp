@@ -97,6 +97,8 @@ struct Mxfp4Args {
 // GEMV sizes: floats of tile partial sums (workspace), bytes of one packed expert.
 int64_t gemv_partials_floats(int format, int64_t rows, int64_t cols, int64_t npairs);
 int64_t gemv_packed_bytes(int format, int64_t rows, int64_t cols);
+int gemv_row_chunks(int64_t rows);                                  // row chunks of a GEMV tile column
+int64_t gemv_tiles(int64_t rows, int64_t cols, int64_t npairs);     // GEMV workgroups (before padding)
 hipError_t launch_gemv_pack(int format, const uint8_t* idx, int64_t rows, int64_t cols, int64_t n_experts,
                             uint8_t* out, int ncu, hipStream_t s);
 

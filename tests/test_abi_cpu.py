@@ -150,6 +150,10 @@ def test_decode_gemv_error_mxfp4_argument_errors():
     assert g(es=pk + 2) == VQ_EINVAL      # stride not a multiple of 4
     assert g(nt=-1) == VQ_EINVAL
     assert g(wsn=16) == VQ_EWORKSPACE
+    # more GEMV workgroups than a launch can hold: 65535 slots x 65536 row chunks
+    huge = L.vq_dequant_gemv(0, a.ptr, 0, b.ptr, 0, c.ptr, 1 << 27, 8, 1, d.ptr, 65535, e.ptr, 1, f.ptr, ws.ptr,
+                             (1 << 63) - 1, None)
+    assert huge == VQ_ERANGE
     assert L.vq_error(0, a.ptr, 0, b.ptr, c.ptr, d.ptr, 0, 4, 64, e.ptr, ws.ptr, 1 << 12, None) == VQ_EINVAL
     assert L.vq_mxfp4_qdq(a.ptr, 0, 4, 48, b.ptr, ws.ptr, 256, None) == VQ_EINVAL     # cols % 32
     assert L.vq_mxfp4_qdq(a.ptr, 0, 4, 64, b.ptr, ws.ptr, 16, None) == VQ_EWORKSPACE

@@ -314,7 +314,7 @@ def _experts(fmt, cb, E, rows, cols, seed):
 
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
 @pytest.mark.parametrize("shape", [(64, 256), (96, 2056), (256, 1024), (32, 448), (1100, 896), (64, 7168),
-                                   (2600, 264)])
+                                   (2600, 264), (2112, 64), (4160, 136), (2049, 24)])
 def test_gemv_matches_oracle(cfg1, fmt, shape):
     say("gemv", fmt, shape)
     rows, cols = shape
@@ -345,8 +345,7 @@ def _check_gemv(y, whs, xf, route):
 
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
 def test_gemv_many_slots(cfg1, fmt):
-    """More token slots (1120) than the in-kernel expert ordering handles: the
-    slots are then scheduled in their own order."""
+    """Many token slots (1120), each slot a workgroup column of its own."""
     say("gemv many slots", fmt)
     rows, cols = 64, 64
     _, cb = cfg1[fmt]
@@ -378,6 +377,27 @@ def test_gemv_full_layer_sampled(cfg1, fmt):
     scales = to_dev(scs.view(np.float16)).repeat(E // 2, 1)
     x = synthetic.activations_f16(ntok, cols, seed=11)
     route = synthetic.routing(ntok, E, topk, seed=12)
+    y = vq.dequant_gemv(packed, scales, to_dev(cb), to_dev(x.view(np.float16)), to_dev(route), rows, cols,
+                        fmt=fmt).cpu().numpy()
+    _check_gemv(y, [whs[e % 2] for e in range(E)], synthetic.f16_bits_to_f32(x).reshape(ntok, cols), route)
+
+
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+def test_gemv_full_layer_w2_sampled(cfg1, fmt):
+    """The w2 shape of the same layer: 256 experts of [7168 x 2048] (rows cut
+    into 4 chunks of 28 row groups), 16 tokens, top-8. Expert e holds the records
+    of base expert e % 2."""
+    say("gemv full layer w2", fmt)
+    rows, cols, E, ntok, topk = 7168, 2048, 256, 16, 8
+    _, cb = cfg1[fmt]
+    recs, scs, whs = _experts(fmt, cb, 2, rows, cols, seed=64)
+    packed = torch.empty((E, vq.lib().vq_gemv_packed_size(vq.FORMATS[fmt], rows, cols)), dtype=torch.uint8,
+                         device="cuda")
+    vq.gemv_pack(to_dev(recs), fmt=fmt, out=packed[:2])
+    packed[2:] = packed[:2].repeat(E // 2 - 1, 1)
+    scales = to_dev(scs.view(np.float16)).repeat(E // 2, 1)
+    x = synthetic.activations_f16(ntok, cols, seed=13)
+    route = synthetic.routing(ntok, E, topk, seed=14)
     y = vq.dequant_gemv(packed, scales, to_dev(cb), to_dev(x.view(np.float16)), to_dev(route), rows, cols,
                         fmt=fmt).cpu().numpy()
     _check_gemv(y, [whs[e % 2] for e in range(E)], synthetic.f16_bits_to_f32(x).reshape(ntok, cols), route)
