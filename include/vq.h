@@ -204,6 +204,36 @@ int vq4p_dequant_gemv(const uint8_t* packed, int64_t expert_stride, const uint16
                       void* stream);
 
 /* ------------------------------------------------------------------------
+ * Batched dequantize-GEMM for prompt processing ([VQ3R page] §1: every token
+ * reads its routed experts; §2/§5: the weights are w_hat = s * sum_t C_t[i_t]),
+ * for many tokens per expert:
+ *   y[b][k][r] = sum_c w_hat_{route[b][k]}[r][c] * x[b][c]
+ * computed from the stored records (no decoded weights in memory). The pairs
+ * (b, k) are grouped by expert on the device; each tile of up to 128 pairs of
+ * one expert x 128 rows runs on fp16 matrix cores with fp32 accumulation: the
+ * codeword sum u = (C1+C2)+C3 (+C4) of each 8-dim vector is formed in fp32 and
+ * rounded once to fp16, and the row scale is applied to the fp32 dot product.
+ * Hence |y - y_exact| <= 2^-11 * sum_c |w_hat[r][c] x[c]| plus fp32
+ * accumulation error.
+ *   idx:     [n_experts][rows][cols/8][3] records as vq_encode writes them,
+ *            expert e at idx + e * expert_stride bytes (expert_stride >=
+ *            rows*cols/8*3 when n_experts > 1);
+ *   scales:  fp16 bits, expert e at scales + e * scale_stride (>= rows);
+ *   x:       fp16 bits [ntok][cols], 16-byte aligned;
+ *   route:   int32 [ntok][topk], expert ids; an id outside [0, n_experts) sets
+ *            the data flag and gives y = 0 for that pair;
+ *   y:       fp32 [ntok][topk][rows].
+ * rows <= 8,388,480 (the row blocks of 128 fill one launch dimension);
+ * ntok * topk < 2^31 (x, route and y may be NULL when it is 0).
+ * Workspace: vq_dequant_gemm_workspace_size(...).
+ * ---------------------------------------------------------------------- */
+size_t vq_dequant_gemm_workspace_size(int format, int32_t n_experts, int32_t ntok, int32_t topk);
+int vq_dequant_gemm(int format, const uint8_t* idx, int64_t expert_stride, const uint16_t* scales,
+                    int64_t scale_stride, const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts,
+                    const uint16_t* x, int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace,
+                    size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Reconstruction error ([VQ3R page] §3.1, the Gate-3 metric
  * ||W - W_hat||_F / ||W||_F, also after fewer stages: "vq2" = 2 stages).
  * For n_mats consecutive matrices (matrix m at W + m*rows*cols elements,

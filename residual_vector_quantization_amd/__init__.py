@@ -20,7 +20,7 @@ __all__ = [
     "encode", "decode", "fit_codebooks", "gemv_pack", "dequant_gemv", "error_sums", "rel_errors", "mxfp4_qdq",
     "encode_workspace", "fit_workspace", "gemv_workspace", "error_workspace", "read_status",
     "container_layout", "crc32", "write_container", "container_info", "read_container", "load_container",
-    "verify_container", "convert_layer",
+    "verify_container", "convert_layer", "dequant_gemm", "gemm_workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -82,6 +82,9 @@ def lib():
                                ctypes.c_int32, P, P, SZ, P], I),
         "vq4p_dequant_gemv": ([P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32, P,
                                ctypes.c_int32, P, P, SZ, P], I),
+        "vq_dequant_gemm_workspace_size": ([I, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32], SZ),
+        "vq_dequant_gemm": ([I, P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32, P,
+                             ctypes.c_int32, P, P, SZ, P], I),
         "vq_error_workspace_size": ([I, L64, L64, L64], SZ),
         "vq_error": ([I, P, I, P, P, P, L64, L64, L64, P, P, SZ, P], I),
         "vq_mxfp4_qdq": ([P, I, L64, L64, P, P, SZ, P], I),
@@ -271,6 +274,36 @@ def dequant_gemv(packed, scales, codebooks, x, route, rows, cols, fmt="vq3r", y=
                                _ptr(codebooks), rows, cols, E, _ptr(x), ntok, _ptr(route), topk, _ptr(y),
                                _ptr(workspace), workspace.numel(), _stream())
     _call("vq_dequant_gemv", st, workspace, check)
+    return y
+
+
+# ------------------------------------------------------------------ prefill GEMM
+def gemm_workspace(fmt, n_experts, ntok, topk, device="cuda"):
+    n = lib().vq_dequant_gemm_workspace_size(FORMATS[fmt], n_experts, ntok, topk)
+    if n == 0:
+        raise VQError(1, "vq_dequant_gemm_workspace_size")
+    return _workspace(n, device)
+
+
+def dequant_gemm(idx, scales, codebooks, x, route, fmt="vq3r", y=None, workspace=None, check=False):
+    """Batched dequant-GEMM for many tokens per expert ([VQ3R page] §1, §2):
+    y[b][k] = W_hat_{route[b][k]} x_b from the stored records idx uint8
+    [E, rows, cols/8, 3] and scales fp16 [E, rows]; x fp16 [ntok, cols], route
+    int32 [ntok, topk] -> y fp32 [ntok, topk, rows]."""
+    torch = _torch()
+    E, rows, V, _ = idx.shape
+    ntok, topk = route.shape
+    _check_cuda(idx, scales, codebooks, x, route)
+    if x.dtype != torch.float16 or route.dtype != torch.int32:
+        raise TypeError("x must be float16 and route int32")
+    if y is None:
+        y = torch.empty((ntok, topk, rows), dtype=torch.float32, device=idx.device)
+    if workspace is None:
+        workspace = gemm_workspace(fmt, E, ntok, topk, idx.device)
+    st = lib().vq_dequant_gemm(FORMATS[fmt], _ptr(idx), rows * V * 3, _ptr(scales), scales.shape[-1], _ptr(codebooks),
+                               rows, V * 8, E, _ptr(x), ntok, _ptr(route), topk, _ptr(y), _ptr(workspace),
+                               workspace.numel(), _stream())
+    _call("vq_dequant_gemm", st, workspace, check)
     return y
 
 

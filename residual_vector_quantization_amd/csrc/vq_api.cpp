@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include "../../include/vq.h"
+#include "vq_gemm.hpp"
 #include "vq_launch.hpp"
 
 using namespace vqk;
@@ -361,6 +362,51 @@ int vq4p_dequant_gemv(const uint8_t* packed, int64_t expert_stride, const uint16
                       void* stream) {
   return vq_dequant_gemv(VQ_FMT_VQ4P, packed, expert_stride, scales, scale_stride, codebooks, rows, cols, n_experts, x,
                          ntok, route, topk, y, workspace, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------- dequant-GEMM
+size_t vq_dequant_gemm_workspace_size(int format, int32_t n_experts, int32_t ntok, int32_t topk) {
+  if (!fmt_ok(format) || n_experts < 1 || ntok < 0 || topk < 0) return 0;
+  const int64_t npairs = (int64_t)ntok * topk;
+  if (npairs >= ((int64_t)1 << 31)) return 0;
+  return align256(vqk::gemm_layout(n_experts, npairs).total);
+}
+
+int vq_dequant_gemm(int format, const uint8_t* idx, int64_t expert_stride, const uint16_t* scales,
+                    int64_t scale_stride, const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts,
+                    const uint16_t* x, int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  if (!fmt_ok(format)) return VQ_EINVAL;
+  int st = check_shape(rows, cols);
+  if (st != VQ_OK) return st;
+  if (ntok < 0 || topk < 0 || n_experts < 1 || expert_stride < 0 || scale_stride < 0) return VQ_EINVAL;
+  if (n_experts > 1 && (expert_stride < rows * (cols / 8) * 3 || scale_stride < rows)) return VQ_EINVAL;
+  const int64_t npairs = (int64_t)ntok * topk;
+  if (!idx || !scales || !codebooks) return VQ_EINVAL;
+  if (npairs > 0 && (!x || !route || !y || !aligned(x, 16))) return VQ_EINVAL;
+  if (npairs >= ((int64_t)1 << 31) || (rows + 127) / 128 > 65535) return VQ_ERANGE;
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < vq_dequant_gemm_workspace_size(format, n_experts, ntok, topk))
+    return VQ_EWORKSPACE;
+  vqk::GemmArgs a;
+  a.format = format;
+  a.idx = idx;
+  a.expert_stride = expert_stride;
+  a.scales = scales;
+  a.scale_stride = scale_stride;
+  a.codebooks = codebooks;
+  a.rows = rows;
+  a.cols = cols;
+  a.n_experts = n_experts;
+  a.x = x;
+  a.ntok = ntok;
+  a.topk = topk;
+  a.route = route;
+  a.y = y;
+  a.hdr = (WsHeader*)workspace;
+  a.ws = (char*)workspace;
+  a.L = vqk::gemm_layout(n_experts, npairs);
+  a.stream = (hipStream_t)stream;
+  return hip_status(vqk::launch_gemm(a));
 }
 
 // ---------------------------------------------------------------- error
