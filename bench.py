@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--layer", action="store_true", help="per-layer conversion measurement: w1 and w3 "
                     "[2048x7168] and w2 [7168x2048] of every expert, each family fit, encoded and measured, plus "
                     "the w2 dequant-GEMV (prints its own JSON line)")
+    ap.add_argument("--gemm", default="", help="prompt-processing dequant-GEMM measurement on the layer: comma "
+                    "list of token counts (top-8 each), e.g. 1024,4096,16384 (prints its own JSON line)")
     ap.add_argument("--container", default="", help="container measurement: write the layer's VQ3R records "
                     "into a container under this directory, then time streaming them into device memory and "
                     "verifying them (prints its own JSON line)")
@@ -204,6 +206,10 @@ def main():
                     vq.dequant_gemv(pk4, sc4_e, cb4, x, route, ROWS, COLS, fmt="vq4p", y=y, workspace=ws4)
     step.fitted = False
 
+    if args.gemm:
+        gemm_bench(args, torch, vq, synthetic, W, mats, init3, cb3, fit_ws3, idx3, sc3, enc_ws, E)
+        return
+
     if args.layer:
         layer_bench(args, torch, vq, synthetic, W, E, evict)
         return
@@ -323,6 +329,43 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+FP16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak
+
+
+def gemm_bench(args, torch, vq, synthetic, W, mats, init3, cb3, fit_ws3, idx3, sc3, enc_ws, E):
+    """Dequant-GEMM on the full layer: T tokens, top-8 routing (uniform, seeded),
+    y = W_hat_e x for all 8T pairs, timed with HIP events on the launch stream."""
+    dev = "cuda"
+    vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3, workspace=fit_ws3)
+    vq.encode(W, cb3, idx=idx3, scales=sc3, workspace=enc_ws)
+    idx_e, sc_e = idx3.view(E, ROWS, COLS // 8, 3), sc3.view(E, ROWS)
+    out = {}
+    for T in [int(t) for t in args.gemm.split(",")]:
+        x = torch.from_numpy(synthetic.activations_f16(T, COLS, seed=50 + T % 97).view(np.float16)).to(dev)
+        route = torch.from_numpy(synthetic.routing(T, E, 8, seed=60 + T % 89)).to(dev)
+        y = torch.empty((T, 8, ROWS), dtype=torch.float32, device=dev)
+        ws = vq.gemm_workspace("vq3r", E, T, 8)
+        ts = []
+        for rep in range(args.warmup + max(3, args.steps)):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            vq.dequant_gemm(idx_e, sc_e, cb3, x, route, y=y, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            if rep >= args.warmup:
+                ts.append(e0.elapsed_time(e1))
+        vq.read_status(ws)
+        ms = float(np.median(ts))
+        flop = 2.0 * T * 8 * ROWS * COLS
+        tf = flop / (ms * 1e-3) / 1e12
+        out["tokens_%d" % T] = {"pairs_per_expert": T * 8 / E, "ms": round(ms, 4), "tflops": round(tf, 1),
+                                "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4),
+                                "records_GB_s": round(E * VEC_PER_EXPERT * 3 / (ms * 1e-3) / 1e9, 1)}
+        log("gemm T=%d: %.3f ms, %.1f TFLOP/s" % (T, ms, tf))
+    print(json.dumps({"gemm": out, "experts": E, "shape": [ROWS, COLS], "topk": 8}), flush=True)
 
 
 def layer_bench(args, torch, vq, synthetic, W1, E, evict):

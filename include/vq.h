@@ -209,8 +209,8 @@ int vq4p_dequant_gemv(const uint8_t* packed, int64_t expert_stride, const uint16
  * for many tokens per expert:
  *   y[b][k][r] = sum_c w_hat_{route[b][k]}[r][c] * x[b][c]
  * computed from the stored records (no decoded weights in memory). The pairs
- * (b, k) are grouped by expert on the device; each tile of up to 128 pairs of
- * one expert x 128 rows runs on fp16 matrix cores with fp32 accumulation: the
+ * (b, k) are grouped by expert on the device; each tile of up to 256 pairs of
+ * one expert x 256 rows runs on fp16 matrix cores with fp32 accumulation: the
  * codeword sum u = (C1+C2)+C3 (+C4) of each 8-dim vector is formed in fp32 and
  * rounded once to fp16, and the row scale is applied to the fp32 dot product.
  * Hence |y - y_exact| <= 2^-11 * sum_c |w_hat[r][c] x[c]| plus fp32
@@ -223,7 +223,7 @@ int vq4p_dequant_gemv(const uint8_t* packed, int64_t expert_stride, const uint16
  *   route:   int32 [ntok][topk], expert ids; an id outside [0, n_experts) sets
  *            the data flag and gives y = 0 for that pair;
  *   y:       fp32 [ntok][topk][rows].
- * rows <= 8,388,480 (the row blocks of 128 fill one launch dimension);
+ * rows <= 16,776,960 (the row blocks of 256 fill one launch dimension);
  * ntok * topk < 2^31 (x, route and y may be NULL when it is 0).
  * Workspace: vq_dequant_gemm_workspace_size(...).
  * ---------------------------------------------------------------------- */

@@ -384,7 +384,7 @@ int vq_dequant_gemm(int format, const uint8_t* idx, int64_t expert_stride, const
   const int64_t npairs = (int64_t)ntok * topk;
   if (!idx || !scales || !codebooks) return VQ_EINVAL;
   if (npairs > 0 && (!x || !route || !y || !aligned(x, 16))) return VQ_EINVAL;
-  if (npairs >= ((int64_t)1 << 31) || (rows + 127) / 128 > 65535) return VQ_ERANGE;
+  if (npairs >= ((int64_t)1 << 31) || (rows + 255) / 256 > 65535) return VQ_ERANGE;
   if (!workspace || !aligned(workspace, 256) || ws_bytes < vq_dequant_gemm_workspace_size(format, n_experts, ntok, topk))
     return VQ_EWORKSPACE;
   vqk::GemmArgs a;

@@ -7,7 +7,7 @@
 //
 // for each (token, slot) pair p whose routed expert is e(p). The pairs are
 // grouped by expert (k_gemm_route), and a workgroup computes one tile of up to
-// 128 pairs of one expert x 128 output rows with fp16 matrix cores
+// 256 pairs of one expert x 256 output rows with fp16 matrix cores
 // (v_mfma_f32_32x32x16_f16, fp32 accumulation). The weights are decoded in
 // registers straight into the B operand: in the 32x32x16 layout, lane
 // (n, h) supplies 8 consecutive k of column n, which is exactly one 8-dim
@@ -18,9 +18,9 @@
 // sum_c |w_hat_c x_c|, inside the 1e-3 relative bar of the GEMV.
 //
 // Inside a 64-column K block (8 slices), half h of the wave takes slices
-// 4h .. 4h+3, one per k-step: the A operand (lane (m, h): 8 fp16 of token m at
-// the same slice) is then 16 contiguous bytes of the token's activation row,
-// and a lane's four records of the block are 12 contiguous bytes.
+// 4h .. 4h+3, one per k-step: the A operand (lane (m, h): 8 fp16 of pair m at
+// the same slice) is 16 contiguous bytes of an activation row, and a lane's
+// four records of the block are 12 contiguous bytes.
 #include "vq_gemm.hpp"
 
 #include <type_traits>
@@ -34,7 +34,7 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 
 GemmLayout gemm_layout(int64_t n_experts, int64_t npairs) {
   GemmLayout L;
-  L.max_tiles = (npairs + GEMM_MT - 1) / GEMM_MT + (n_experts < npairs ? n_experts : npairs);
+  L.max_tiles = (npairs + GEMM_MT_MIN - 1) / GEMM_MT_MIN + (n_experts < npairs ? n_experts : npairs);
   size_t off = sizeof(WsHeader);
   auto take = [&](int64_t n) {
     const size_t o = off;
@@ -55,16 +55,22 @@ GemmLayout gemm_layout(int64_t n_experts, int64_t npairs) {
 
 // ------------------------------------------------------------------ routing
 // One workgroup: counts the pairs per expert, scans them into list offsets
-// and tile offsets (tiles of GEMM_MT pairs), writes the tile table and the
+// and tile offsets (tiles of MT pairs), writes the tile table and the
 // pair lists. The order of pairs inside an expert's list comes from atomics;
 // it does not change any output value (each output row of a tile is computed
 // by the same operations wherever it sits). Also writes the call's status
-// (route ids outside [0, E)).
-__global__ __launch_bounds__(1024) void k_gemm_route(const int32_t* route, int64_t npairs, int E, int32_t* counts,
-                                                     int32_t* offsets, int32_t* tile_off, int32_t* list,
-                                                     int32_t* tile_e, int32_t* tile_m0, int32_t* n_tiles,
-                                                     float* y, int64_t rows, WsHeader* hdr) {
+// (route ids outside [0, E)). LDS_COUNTS: the per-expert counters live in LDS
+// (E <= 8192), else in the workspace.
+constexpr int ROUTE_LDS_MAX = 8192;
+
+template <bool LDS_COUNTS>
+__global__ __launch_bounds__(1024) void k_gemm_route(const int32_t* route, int64_t npairs, int E, int MT,
+                                                     int32_t* counts_g, int32_t* offsets, int32_t* tile_off,
+                                                     int32_t* list, int32_t* tile_e, int32_t* tile_m0,
+                                                     int32_t* n_tiles, float* y, int64_t rows, WsHeader* hdr) {
   __shared__ int32_t sp[1024], stl[1024];
+  __shared__ int32_t counts_l[LDS_COUNTS ? ROUTE_LDS_MAX : 1];
+  int32_t* counts = LDS_COUNTS ? counts_l : counts_g;
   const int tid = threadIdx.x;
   const int per = (E + 1023) / 1024;
   const int e0 = tid * per, e1 = (e0 + per < E) ? e0 + per : E;
@@ -88,7 +94,7 @@ __global__ __launch_bounds__(1024) void k_gemm_route(const int32_t* route, int64
   for (int e = e0; e < e1; ++e) {
     const int c = counts[e];
     sumc += c;
-    sumt += (c + GEMM_MT - 1) / GEMM_MT;
+    sumt += (c + MT - 1) / MT;
   }
   sp[tid] = sumc;
   stl[tid] = sumt;
@@ -103,12 +109,12 @@ __global__ __launch_bounds__(1024) void k_gemm_route(const int32_t* route, int64
   }
   int oc = sp[tid] - sumc, ot = stl[tid] - sumt;  // exclusive starts of this chunk
   for (int e = e0; e < e1; ++e) {
-    const int c = counts[e], nt = (c + GEMM_MT - 1) / GEMM_MT;
+    const int c = counts[e], nt = (c + MT - 1) / MT;
     offsets[e] = oc;
     tile_off[e] = ot;
     for (int t = 0; t < nt; ++t) {
       tile_e[ot + t] = e;
-      tile_m0[ot + t] = t * GEMM_MT;
+      tile_m0[ot + t] = t * MT;
     }
     counts[e] = oc;  // becomes the fill cursor
     oc += c;
@@ -128,47 +134,79 @@ __global__ __launch_bounds__(1024) void k_gemm_route(const int32_t* route, int64
 }
 
 // ------------------------------------------------------------------ GEMM
-// Grid: (tile slots, row blocks of 128). MSUB sub-tiles of 32 pairs (4: a
-// full 128-pair tile). FAST: cols % 64 == 0 and 4-byte aligned records, so a
-// lane's 12 record bytes of a K block are three dword loads and every slice
-// exists.
+// Grid: (tile slots, row blocks of 256). A workgroup of 8 waves computes one
+// tile of MT = 32 * MSUB pairs of one expert x 256 output rows; wave w owns
+// rows 32w .. 32w+31 and all MSUB pair sub-tiles (MSUB accumulators of 32x32).
+// Per 64-column K block:
+//   - the activation tile (MT pairs x 64 columns, fp16) is loaded with
+//     coalesced 16-byte loads and stored in LDS one block ahead (two buffers),
+//     rows padded to 144 bytes so that the 32 rows of a fragment read fall in
+//     distinct banks; the A fragment of (sub-tile, k-step) is one ds_read_b128;
+//   - each lane decodes its own row's 4 vectors of the block from LDS
+//     codebooks into B operands (one per k-step).
+// FAST: cols % 64 == 0 and 4-byte aligned records, so a lane's 12 record
+// bytes of a K block are three dword loads and every slice exists.
 constexpr int CB_STRIDE = 12;  // floats per codeword in LDS (8 used): spreads random lookups over banks
+constexpr int A_STRIDE = 72;   // fp16 per activation row in LDS (64 used)
 
-template <int FMT, bool FAST>
-__global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* idx, int64_t expert_stride, const uint16_t* scales,
-                                                 int64_t scale_stride, const float* cb_g, int64_t rows, int64_t cols,
-                                                 const uint16_t* x, int topk, float* y, const int32_t* offsets,
-                                                 const int32_t* list, const int32_t* tile_e, const int32_t* tile_m0,
-                                                 const int32_t* n_tiles) {
-  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, MSUB = GEMM_MT / 32;
+template <int FMT, int MSUB, bool FAST>
+__global__ __launch_bounds__(64 * GEMM_WAVES, 2) void k_gemm(const uint8_t* idx, int64_t expert_stride,
+                                                             const uint16_t* scales, int64_t scale_stride,
+                                                             const float* cb_g, int64_t rows, int64_t cols,
+                                                             const uint16_t* x, int topk, float* y,
+                                                             const int32_t* offsets, const int32_t* list,
+                                                             const int32_t* tile_e, const int32_t* tile_m0,
+                                                             const int32_t* n_tiles) {
+  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, MT = 32 * MSUB, NTH = 64 * GEMM_WAVES;
+  constexpr int CHUNKS = MT * 8, PER_T = (CHUNKS + NTH - 1) / NTH;  // 16-byte pieces of an activation tile
   __shared__ float cbl[S * K * CB_STRIDE];
-  __shared__ int32_t pairs[GEMM_MT];
+  __shared__ _Float16 at[2][MT * A_STRIDE];
+  __shared__ int32_t pairs[MT];
   const int tile = blockIdx.x;
   if (tile >= n_tiles[0]) return;  // uniform over the workgroup
   const int e = tile_e[tile], m0 = tile_m0[tile];
-  const int base = offsets[e], cnt = offsets[e + 1] - base - m0;  // pairs of this tile: min(cnt, 128)
-  for (int q = threadIdx.x; q < S * K * DIM; q += blockDim.x) cbl[(q >> 3) * CB_STRIDE + (q & 7)] = cb_g[q];
-  if (threadIdx.x < GEMM_MT) {
-    const int li = (int)threadIdx.x < cnt ? (int)threadIdx.x : 0;  // pad rows repeat the first pair
-    pairs[threadIdx.x] = list[base + m0 + li];
-  }
+  const int base = offsets[e], cnt = offsets[e + 1] - base - m0;  // pairs of this tile: min(cnt, MT)
+  const int tid = threadIdx.x;
+  for (int q = tid; q < S * K * DIM; q += NTH) cbl[(q >> 3) * CB_STRIDE + (q & 7)] = cb_g[q];
+  if (tid < MT) pairs[tid] = list[base + m0 + (tid < cnt ? tid : 0)];  // pad rows repeat the first pair
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 31, h = lane >> 5;
   const int64_t V = cols / DIM;
-  const int64_t r = (int64_t)blockIdx.y * GEMM_NT + wave * 32 + n;
+  const int64_t nkb = (V + 7) / 8;
+  // activation-tile pieces of this thread: piece q = row q / 8, columns 8 (q % 8) .. + 7 of the block
+  const uint16_t* arow[PER_T];
+  int aoff[PER_T];
+#pragma unroll
+  for (int i = 0; i < PER_T; ++i) {
+    const int q = tid + NTH * i, qc = q < CHUNKS ? q : 0;
+    arow[i] = x + (int64_t)(pairs[qc >> 3] / topk) * cols + (qc & 7) * DIM;
+    aoff[i] = (qc >> 3) * A_STRIDE + (qc & 7) * DIM;
+  }
+  uint4 areg[PER_T];
+  auto load_a = [&](int64_t kb) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      if (CHUNKS % NTH != 0 && tid + NTH * i >= CHUNKS) continue;
+      if (!FAST && kb * 64 + ((tid + NTH * i) & 7) * DIM >= cols) {
+        areg[i] = make_uint4(0u, 0u, 0u, 0u);  // slice beyond the row
+      } else {
+        areg[i] = *reinterpret_cast<const uint4*>(arow[i] + kb * 64);
+      }
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      if (CHUNKS % NTH != 0 && tid + NTH * i >= CHUNKS) continue;
+      *reinterpret_cast<uint4*>(&at[buf][aoff[i]]) = areg[i];
+    }
+  };
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, h = lane >> 5;
+  const int64_t r = (int64_t)blockIdx.y * (32 * GEMM_WAVES) + wave * 32 + n;
   const int64_t rc = r < rows ? r : rows - 1;
   const uint8_t* rec = idx + (int64_t)e * expert_stride + rc * V * 3;
-  const uint16_t* xr[MSUB];
-#pragma unroll
-  for (int sub = 0; sub < MSUB; ++sub) xr[sub] = x + (int64_t)(pairs[32 * sub + n] / topk) * cols;
-  f16v acc[MSUB];
-#pragma unroll
-  for (int sub = 0; sub < MSUB; ++sub) acc[sub] = (f16v){};
-  const int64_t nkb = (V + 7) / 8;
-  for (int64_t kb = 0; kb < nkb; ++kb) {
-    const int64_t j0 = kb * 8 + 4 * h;  // this half's first slice of the block
-    uint32_t w3[3];
+  auto load_rec = [&](uint32_t (&w3)[3], int64_t kb) {
+    const int64_t j0 = kb * 8 + 4 * h;
     if constexpr (FAST) {
       const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + j0 * 3);
       w3[0] = p[0];
@@ -180,12 +218,28 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* idx, int64_t exp
       for (int b = 0; b < 12; ++b)
         if (j0 + b / 3 < V) w3[b >> 2] |= (uint32_t)rec[j0 * 3 + b] << (8 * (b & 3));
     }
+  };
+  f16v acc[MSUB];
+#pragma unroll
+  for (int sub = 0; sub < MSUB; ++sub) acc[sub] = (f16v){};
+  load_a(0);
+  store_a(0);
+  uint32_t wn[3];
+  load_rec(wn, 0);
+  __syncthreads();
+  for (int64_t kb = 0; kb < nkb; ++kb) {
+    const uint32_t w3[3] = {wn[0], wn[1], wn[2]};
+    const bool more = kb + 1 < nkb;
+    if (more) {
+      load_a(kb + 1);
+      load_rec(wn, kb + 1);
+    }
+    const _Float16* ab = at[kb & 1];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int byte0 = 3 * s, k0 = byte0 >> 2, o = byte0 & 3;
       const uint32_t word =
           (o <= 1) ? (w3[k0] >> (8 * o)) : ((w3[k0] >> (8 * o)) | (w3[k0 + 1] << (32 - 8 * o)));
-      const int64_t j = j0 + s;
       // u = (C1[i1] + C2[i2]) + C3[i3] (+ C4[i4]) in fp32, then one rounding to fp16
       float4 ua, ub;
 #pragma unroll
@@ -200,31 +254,26 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* idx, int64_t exp
           ub.x += cbv.x; ub.y += cbv.y; ub.z += cbv.z; ub.w += cbv.w;
         }
       }
-      h8 bop;
-      {
-        const hf2 p0 = __builtin_convertvector((ff2){ua.x, ua.y}, hf2);
-        const hf2 p1 = __builtin_convertvector((ff2){ua.z, ua.w}, hf2);
-        const hf2 p2 = __builtin_convertvector((ff2){ub.x, ub.y}, hf2);
-        const hf2 p3 = __builtin_convertvector((ff2){ub.z, ub.w}, hf2);
-        bop = (h8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-      }
-      int64_t col = j * DIM;
+      const hf2 p0 = __builtin_convertvector((ff2){ua.x, ua.y}, hf2);
+      const hf2 p1 = __builtin_convertvector((ff2){ua.z, ua.w}, hf2);
+      const hf2 p2 = __builtin_convertvector((ff2){ub.x, ub.y}, hf2);
+      const hf2 p3 = __builtin_convertvector((ff2){ub.z, ub.w}, hf2);
+      h8 bop = (h8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
       if constexpr (!FAST) {
-        if (j >= V) {
-          bop = (h8){};
-          col = (V - 1) * DIM;  // in bounds; multiplied by zero weights
-        }
+        if (kb * 8 + 4 * h + s >= V) bop = (h8){};
       }
 #pragma unroll
       for (int sub = 0; sub < MSUB; ++sub) {
-        const h8 aop = *reinterpret_cast<const h8*>(xr[sub] + col);
+        const h8 aop = *reinterpret_cast<const h8*>(ab + (32 * sub + n) * A_STRIDE + (4 * h + s) * DIM);
         acc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop, acc[sub], 0, 0, 0);
       }
     }
+    if (more) store_a((int)((kb + 1) & 1));
+    __syncthreads();
   }
   if (r >= rows) return;
   const float sr = f16_bits_to_f32(scales[(int64_t)e * scale_stride + r]);
-  // acc[sub][v] = D[token 8(v/4) + 4h + v%4 of the sub-tile][row n]
+  // acc[sub][v] = D[pair 8(v/4) + 4h + v%4 of the sub-tile][row n]
 #pragma unroll
   for (int sub = 0; sub < MSUB; ++sub) {
 #pragma unroll
@@ -235,24 +284,41 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* idx, int64_t exp
   }
 }
 
+int gemm_msub(int64_t n_experts, int64_t npairs) {
+  const int64_t used = n_experts < npairs ? n_experts : npairs;
+  const int64_t avg = used > 0 ? npairs / used : 0;
+  return avg >= 192 ? 8 : (avg >= 96 ? 4 : (avg >= 48 ? 2 : 1));
+}
+
 template <int FMT>
 static hipError_t launch_gemm_t(const GemmArgs& a) {
   const int64_t npairs = (int64_t)a.ntok * a.topk;
+  const int msub = gemm_msub(a.n_experts, npairs);
+  const int mt = 32 * msub;
   auto at = [&](size_t off) { return reinterpret_cast<int32_t*>(a.ws + off); };
-  k_gemm_route<<<1, 1024, 0, a.stream>>>(a.route, npairs, a.n_experts, at(a.L.counts), at(a.L.offsets),
-                                         at(a.L.tile_offsets), at(a.L.list), at(a.L.tile_expert), at(a.L.tile_m0),
-                                         at(a.L.n_tiles), a.y, a.rows, a.hdr);
-  if (a.L.max_tiles == 0 || a.rows == 0) return hipGetLastError();
-  const dim3 grid((unsigned)a.L.max_tiles, (unsigned)((a.rows + GEMM_NT - 1) / GEMM_NT));
+  auto route_k = a.n_experts <= ROUTE_LDS_MAX ? k_gemm_route<true> : k_gemm_route<false>;
+  route_k<<<1, 1024, 0, a.stream>>>(a.route, npairs, a.n_experts, mt, at(a.L.counts), at(a.L.offsets),
+                                    at(a.L.tile_offsets), at(a.L.list), at(a.L.tile_expert), at(a.L.tile_m0),
+                                    at(a.L.n_tiles), a.y, a.rows, a.hdr);
+  const int64_t max_tiles = (npairs + mt - 1) / mt + (a.n_experts < npairs ? a.n_experts : npairs);
+  if (max_tiles == 0 || a.rows == 0) return hipGetLastError();
+  const dim3 grid((unsigned)max_tiles, (unsigned)((a.rows + 32 * GEMM_WAVES - 1) / (32 * GEMM_WAVES)));
   const int64_t V = a.cols / DIM;
   const bool fast = V % 8 == 0 && ((uintptr_t)a.idx & 3) == 0 && a.expert_stride % 4 == 0;
   auto go = [&](auto kern) {
-    kern<<<grid, 256, 0, a.stream>>>(a.idx, a.expert_stride, a.scales, a.scale_stride, a.codebooks, a.rows, a.cols,
-                                     a.x, a.topk, a.y, at(a.L.offsets), at(a.L.list), at(a.L.tile_expert),
-                                     at(a.L.tile_m0), at(a.L.n_tiles));
+    kern<<<grid, 64 * GEMM_WAVES, 0, a.stream>>>(a.idx, a.expert_stride, a.scales, a.scale_stride, a.codebooks,
+                                                 a.rows, a.cols, a.x, a.topk, a.y, at(a.L.offsets), at(a.L.list),
+                                                 at(a.L.tile_expert), at(a.L.tile_m0), at(a.L.n_tiles));
   };
-  if (fast) go(k_gemm<FMT, true>);
-  else go(k_gemm<FMT, false>);
+  auto pick = [&](auto msub_c) {
+    constexpr int M = decltype(msub_c)::value;
+    if (fast) go(k_gemm<FMT, M, true>);
+    else go(k_gemm<FMT, M, false>);
+  };
+  if (msub == 8) pick(std::integral_constant<int, 8>());
+  else if (msub == 4) pick(std::integral_constant<int, 4>());
+  else if (msub == 2) pick(std::integral_constant<int, 2>());
+  else pick(std::integral_constant<int, 1>());
   return hipGetLastError();
 }
 

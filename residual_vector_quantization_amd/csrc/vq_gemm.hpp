@@ -15,10 +15,11 @@ struct GemmLayout {
   int64_t max_tiles;
 };
 
-constexpr int GEMM_MT = 128;  // tokens per M tile (4 sub-tiles of 32)
-constexpr int GEMM_NT = 128;  // output rows per workgroup (4 waves x 32)
+constexpr int GEMM_MT_MIN = 32;  // smallest pair tile; the workspace is sized for it
+constexpr int GEMM_WAVES = 8;    // output rows per workgroup: 32 per wave
 
 GemmLayout gemm_layout(int64_t n_experts, int64_t npairs);
+int gemm_msub(int64_t n_experts, int64_t npairs);  // pair sub-tiles of 32 per tile for this call
 
 struct GemmArgs {
   int format;

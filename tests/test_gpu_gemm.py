@@ -96,6 +96,22 @@ def test_gemm_skewed_routing_and_single_expert(books):
     _check(y, whs, synthetic.f16_bits_to_f32(x).reshape(ntok, cols), route)
 
 
+def test_gemm_many_experts_global_counters(books):
+    """9000 experts (more than the route kernel keeps in LDS), expert e holding
+    base expert e % 2."""
+    say("gemm 9000 experts")
+    cb = books["vq3r"]
+    rows, cols, E = 40, 64, 9000
+    recs, scs, whs = _experts("vq3r", cb, 2, rows, cols, seed=88)
+    idx = to_dev(recs).repeat(E // 2, 1, 1, 1)
+    sc = to_dev(scs.view(np.float16)).repeat(E // 2, 1)
+    ntok, topk = 600, 4
+    route = synthetic.routing(ntok, E, topk, seed=12)
+    x = synthetic.activations_f16(ntok, cols, seed=13)
+    y = vq.dequant_gemm(idx, sc, to_dev(cb), to_dev(x.view(np.float16)), to_dev(route), check=True).cpu().numpy()
+    _check(y, [whs[e % 2] for e in range(E)], synthetic.f16_bits_to_f32(x).reshape(ntok, cols), route)
+
+
 def test_gemm_bad_route_and_empty(books):
     say("gemm bad route / empty")
     cb = books["vq3r"]
