@@ -72,6 +72,8 @@ def lib():
         L.vqo_fixed_point_bits.argtypes = [ctypes.c_float, i64]
         L.vqo_fit.argtypes = [P, i32, i64, i64, i32, i32, i32, P, P, P, P, P]
         L.vqo_lloyd_on_vectors.argtypes = [P, i64, i32, i32, P, P, P, P]
+        L.vqo_ttp_quantize.argtypes = [P, i64, i64, P, P, P]
+        L.vqo_ttp_dequantize.argtypes = [P, P, i64, i64, P]
         _lib = L
     return _lib
 
@@ -231,6 +233,42 @@ def pack(fmt: str, idx):
 
 def unpack(fmt: str, rec):
     return unpack_vq3r(rec) if fmt == "vq3r" else unpack_vq4p(rec)
+
+
+# ------------------------------------------------------------------ Tied Trit-Planes
+TTP_GROUP = 256
+
+
+def ttp_quantize(w: np.ndarray, want_rounds=False):
+    """Tied Trit-Planes 9-level quantizer ([TTP page], the page "Новый метод
+    квантования Tied Trit-Planes сжимает DeepSeek-V4 до 4.0625 бит на вес"):
+    w fp32 [rows, cols] (cols % 256 == 0) -> (codes uint8 [rows, cols/2], two
+    4-bit codes q+4 per byte, scales fp16 bits [rows, cols/256]). Readings in
+    vq_oracle.c."""
+    w = _f32(w)
+    rows, cols = w.shape
+    codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((rows, cols // TTP_GROUP), dtype=np.uint16)
+    rounds = np.zeros((rows, cols // TTP_GROUP), dtype=np.int32) if want_rounds else None
+    _check(lib().vqo_ttp_quantize(_p(w), rows, cols, _p(codes), _p(scales),
+                                  _p(rounds) if rounds is not None else None))
+    return (codes, scales, rounds) if want_rounds else (codes, scales)
+
+
+def ttp_levels(codes: np.ndarray) -> np.ndarray:
+    """codes uint8 [..., n/2] -> levels q int8 [..., n] in -4..4."""
+    c = np.asarray(codes, dtype=np.uint8)
+    q = np.stack([c & 0xF, c >> 4], axis=-1).reshape(c.shape[:-1] + (c.shape[-1] * 2,)).astype(np.int8)
+    return q - 4
+
+
+def ttp_dequantize(codes: np.ndarray, scales: np.ndarray):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    rows, half = codes.shape
+    out = np.zeros((rows, half * 2), dtype=np.float32)
+    _check(lib().vqo_ttp_dequantize(_p(codes), _p(scales), rows, half * 2, _p(out)))
+    return out
 
 
 # ------------------------------------------------------------------ metrics

@@ -355,3 +355,115 @@ int vqo_lloyd_on_vectors(float* R, int64_t n, int K, int iters, const int64_t* i
   if (n < K || K < 1 || iters < 0) return VQO_EINVAL;
   return lloyd_stage(R, n, K, iters, init, C, assign, obj);
 }
+
+/* ------------------------------------------------------------------------
+ * Tied Trit-Planes, from the page "Новый метод квантования Tied Trit-Planes
+ * сжимает DeepSeek-V4 до 4.0625 бит на вес" (ai-sphere.ru; cited as [TTP page]).
+ * Its summary and "what happened" sections: PTQTP writes a weight group as two
+ * ternary planes with one free scale each; tying the scales by a factor of 3
+ * turns the pair into a single uniform 9-level (balanced ternary) quantizer,
+ *   w ~ a * (3 t1 + t2) = a * q,   t1, t2 in {-1, 0, 1},  q in {-4, ..., 4},
+ * and the two planes fold without loss into one 4-bit code plane, 4.0625 bits
+ * per weight. Readings taken where the page is silent:
+ *   - a group is 256 consecutive weights of a row with one fp16 scale
+ *     (4 + 16/256 = 4.0625 bits per weight);
+ *   - the solver alternates PTQTP's two minimisations under the tie: for a
+ *     fixed scale, each weight takes its nearest level,
+ *       q = clamp(rint(w / a), -4, 4)   (fp32 division, ties to even);
+ *     for fixed levels, the least-squares scale a = sum_i w_i q_i / sum_i q_i^2,
+ *     with the numerator summed exactly in int64 fixed point:
+ *       F = 52 - e with max|w| < 2^e (frexp exponent), W_i = llrint(w_i 2^F),
+ *       a = (float)(((double) sum_i W_i q_i) 2^-F / sum_i q_i^2);
+ *     (|W_i q_i| < 2^54 and 256 terms stay below 2^62; the sum is exact and
+ *     does not depend on the order of the terms); starting from
+ *     a = max|w| / 4, for at most TTP_ITERS rounds, stopping when no level
+ *     changes;
+ *   - the stored scale is fp16(a); the levels are then chosen once more for
+ *     that stored scale. A zero group gets a = 0 and q = 0;
+ *   - code = q + 4 = 3 (t1 + 1) + (t2 + 1) in 0..8; two codes per byte, the
+ *     even element in the low nibble.
+ * ---------------------------------------------------------------------- */
+#define TTP_GROUP 256
+#define TTP_ITERS 8
+
+static int ttp_level(float w, float a) {
+  if (a == 0.0f) return 0;
+  float t = rintf(w / a);
+  if (t > 4.0f) t = 4.0f;
+  if (t < -4.0f) t = -4.0f;
+  return (int)t;
+}
+
+/* one group of n <= 256 weights; returns 0 or VQO_EDATA; *rounds = rounds run */
+static int ttp_group(const float* w, int n, uint8_t* code, uint16_t* s_bits, int* rounds) {
+  int q[TTP_GROUP];
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    if (!isfinite(w[i])) return VQO_EDATA;
+    float aw = fabsf(w[i]);
+    if (aw > amax) amax = aw;
+  }
+  float a = amax / 4.0f;
+  int e = 0;
+  (void)frexpf(amax, &e);
+  const int F = 52 - e;
+  long long W[TTP_GROUP];
+  for (int i = 0; i < n; ++i) W[i] = llrint(ldexp((double)w[i], F));
+  for (int i = 0; i < n; ++i) q[i] = ttp_level(w[i], a);
+  int it = 0;
+  while (it < TTP_ITERS) {
+    long long swq = 0, sqq = 0;
+    for (int i = 0; i < n; ++i) {
+      swq += W[i] * q[i];
+      sqq += (long long)q[i] * q[i];
+    }
+    if (sqq == 0) break;
+    a = (float)(ldexp((double)swq, -F) / (double)sqq);
+    ++it;
+    int changed = 0;
+    for (int i = 0; i < n; ++i) {
+      int nq = ttp_level(w[i], a);
+      changed |= nq != q[i];
+      q[i] = nq;
+    }
+    if (!changed) break;
+  }
+  uint16_t h = f32_to_f16_rne(a);
+  if ((h & 0x7C00u) == 0x7C00u) return VQO_EDATA; /* scale beyond the fp16 range */
+  float ah = f16_to_f32(h);
+  for (int i = 0; i < n; ++i) code[i] = (uint8_t)(ttp_level(w[i], ah) + 4);
+  *s_bits = h;
+  if (rounds) *rounds = it;
+  return VQO_OK;
+}
+
+/* w fp32 [rows][cols], cols % 256 == 0 -> codes [rows][cols/2] (two per byte),
+ * scales fp16 bits [rows][cols/256]; rounds (nullable) int32 [rows][cols/256] */
+int vqo_ttp_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* codes, uint16_t* scales, int32_t* rounds) {
+  if (rows < 0 || cols <= 0 || cols % TTP_GROUP != 0) return VQO_EINVAL;
+  const int64_t G = rows * (cols / TTP_GROUP);
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t g = 0; g < G; ++g) {
+    uint8_t c[TTP_GROUP];
+    int r = 0;
+    if (ttp_group(w + g * TTP_GROUP, TTP_GROUP, c, &scales[g], &r) != VQO_OK) {
+      bad = 1;
+      continue;
+    }
+    for (int i = 0; i < TTP_GROUP / 2; ++i) codes[g * (TTP_GROUP / 2) + i] = (uint8_t)(c[2 * i] | (c[2 * i + 1] << 4));
+    if (rounds) rounds[g] = r;
+  }
+  return bad ? VQO_EDATA : VQO_OK;
+}
+
+/* w_hat = a * (code - 4), fp32 (exact: a has 11 significant bits, |q| <= 4) */
+int vqo_ttp_dequantize(const uint8_t* codes, const uint16_t* scales, int64_t rows, int64_t cols, float* out) {
+  if (rows < 0 || cols <= 0 || cols % TTP_GROUP != 0) return VQO_EINVAL;
+  const int64_t n = rows * cols;
+  for (int64_t i = 0; i < n; ++i) {
+    int c = (codes[i / 2] >> (4 * (i & 1))) & 0xF;
+    out[i] = f16_to_f32(scales[i / TTP_GROUP]) * (float)(c - 4);
+  }
+  return VQO_OK;
+}
