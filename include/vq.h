@@ -234,6 +234,35 @@ int vq_dequant_gemm(int format, const uint8_t* idx, int64_t expert_stride, const
                     size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Tied Trit-Planes 9-level codec, from the page "Новый метод квантования Tied
+ * Trit-Planes сжимает DeepSeek-V4 до 4.0625 бит на вес" ([TTP page]; its summary
+ * and "what happened" sections): two ternary planes with scales tied by a
+ * factor of 3, i.e. w ~ a * q with q = 3 t1 + t2 in -4..4, folded into one 4-bit
+ * code, 4.0625 bits per weight. A 4-bit-class baseline beside rtn4-row.
+ * Groups of 256 consecutive weights of a row share one fp16 scale a. The
+ * quantizer alternates nearest levels q = clamp(rint(w / a), -4, 4) and the
+ * least-squares scale a = sum w q / sum q^2 (numerator summed exactly in int64
+ * fixed point), from a = max|w| / 4, at most 8 rounds, stopping when no level
+ * changes; the stored scale is fp16(a) and the levels are chosen for it.
+ *   W:      [rows][cols] of vq_dtype, 16-byte aligned, cols % 256 == 0;
+ *   codes:  [rows][cols/2] bytes, code = q + 4, even element in the low
+ *           nibble (4-byte aligned);
+ *   scales: fp16 bits [rows][cols/256].
+ * Data errors (non-finite weight, scale beyond fp16) set the workspace flag.
+ * Workspace of vq_ttp_quantize: 256 bytes. vq_ttp_dequantize writes fp32
+ * w_hat = a * q (out 16-byte aligned). vq_ttp_error writes, for n_mats
+ * consecutive matrices, sums[m] = {sum (w - w_hat)^2, sum w^2} in fp64, with a
+ * summation order fixed by the matrix shape.
+ * ---------------------------------------------------------------------- */
+int vq_ttp_quantize(const void* W, int dtype, int64_t rows, int64_t cols, uint8_t* codes, uint16_t* scales,
+                    void* workspace, size_t ws_bytes, void* stream);
+int vq_ttp_dequantize(const uint8_t* codes, const uint16_t* scales, int64_t rows, int64_t cols, float* out,
+                      void* stream);
+size_t vq_ttp_error_workspace_size(int64_t n_mats, int64_t rows, int64_t cols);
+int vq_ttp_error(const void* W, int dtype, const uint8_t* codes, const uint16_t* scales, int64_t n_mats,
+                 int64_t rows, int64_t cols, double* sums, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Reconstruction error ([VQ3R page] §3.1, the Gate-3 metric
  * ||W - W_hat||_F / ||W||_F, also after fewer stages: "vq2" = 2 stages).
  * For n_mats consecutive matrices (matrix m at W + m*rows*cols elements,

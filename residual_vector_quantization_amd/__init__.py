@@ -21,6 +21,7 @@ __all__ = [
     "encode_workspace", "fit_workspace", "gemv_workspace", "error_workspace", "read_status",
     "container_layout", "crc32", "write_container", "container_info", "read_container", "load_container",
     "verify_container", "convert_layer", "dequant_gemm", "gemm_workspace",
+    "ttp_quantize", "ttp_dequantize", "ttp_error_sums",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +86,10 @@ def lib():
         "vq_dequant_gemm_workspace_size": ([I, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32], SZ),
         "vq_dequant_gemm": ([I, P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32, P,
                              ctypes.c_int32, P, P, SZ, P], I),
+        "vq_ttp_quantize": ([P, I, L64, L64, P, P, P, SZ, P], I),
+        "vq_ttp_dequantize": ([P, P, L64, L64, P, P], I),
+        "vq_ttp_error_workspace_size": ([L64, L64, L64], SZ),
+        "vq_ttp_error": ([P, I, P, P, L64, L64, L64, P, P, SZ, P], I),
         "vq_error_workspace_size": ([I, L64, L64, L64], SZ),
         "vq_error": ([I, P, I, P, P, P, L64, L64, L64, P, P, SZ, P], I),
         "vq_mxfp4_qdq": ([P, I, L64, L64, P, P, SZ, P], I),
@@ -305,6 +310,56 @@ def dequant_gemm(idx, scales, codebooks, x, route, fmt="vq3r", y=None, workspace
                                workspace.numel(), _stream())
     _call("vq_dequant_gemm", st, workspace, check)
     return y
+
+
+# ------------------------------------------------------------------ Tied Trit-Planes
+def ttp_quantize(W, codes=None, scales=None, workspace=None, check=True):
+    """Tied Trit-Planes 9-level codec ([TTP page]: two ternary planes tied by a
+    factor of 3, 4.0625 bits per weight). W [rows, cols] (cols % 256 == 0) ->
+    (codes uint8 [rows, cols/2], scales fp16 [rows, cols/256])."""
+    torch = _torch()
+    rows, cols = W.shape
+    _check_cuda(W)
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=W.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 256), dtype=torch.float16, device=W.device)
+    if workspace is None:
+        workspace = _workspace(256, W.device)
+    st = lib().vq_ttp_quantize(_ptr(W), _dtype_code(W), rows, cols, _ptr(codes), _ptr(scales), _ptr(workspace),
+                               workspace.numel(), _stream())
+    _call("vq_ttp_quantize", st, workspace, check and rows > 0)
+    return codes, scales
+
+
+def ttp_dequantize(codes, scales, out=None):
+    torch = _torch()
+    rows, half = codes.shape
+    _check_cuda(codes, scales)
+    if out is None:
+        out = torch.empty((rows, half * 2), dtype=torch.float32, device=codes.device)
+    _call("vq_ttp_dequantize", lib().vq_ttp_dequantize(_ptr(codes), _ptr(scales), rows, half * 2, _ptr(out),
+                                                       _stream()))
+    return out
+
+
+def ttp_error_sums(W, codes, scales, n_mats=1, sums=None, workspace=None, check=True):
+    """fp64 [n_mats, 2]: sum (w - w_hat)^2 and sum w^2 per matrix."""
+    torch = _torch()
+    total_rows, cols = W.shape
+    rows = total_rows // n_mats
+    _check_cuda(W, codes, scales)
+    if sums is None:
+        sums = torch.empty((n_mats, 2), dtype=torch.float64, device=W.device)
+    if workspace is None:
+        n = lib().vq_ttp_error_workspace_size(n_mats, rows, cols)
+        if n == 0:
+            raise VQError(1, "vq_ttp_error_workspace_size")
+        workspace = _workspace(n, W.device)
+    st = lib().vq_ttp_error(_ptr(W), _dtype_code(W), _ptr(codes), _ptr(scales), n_mats, rows, cols, _ptr(sums),
+                            _ptr(workspace), workspace.numel(), _stream())
+    _call("vq_ttp_error", st, workspace, check)
+    return sums
 
 
 # ------------------------------------------------------------------ error

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvq.so")
-SOURCES = ["vq_encode.hip", "vq_decode.hip", "vq_gemv.hip", "vq_gemm.hip", "vq_api.cpp", "vq_container.cpp"]
+SOURCES = ["vq_encode.hip", "vq_decode.hip", "vq_gemv.hip", "vq_gemm.hip", "vq_ttp.hip", "vq_api.cpp", "vq_container.cpp"]
 ARCH = os.environ.get("VQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

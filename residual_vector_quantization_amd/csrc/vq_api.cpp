@@ -5,6 +5,7 @@
 
 #include "../../include/vq.h"
 #include "vq_gemm.hpp"
+#include "vq_ttp.hpp"
 #include "vq_launch.hpp"
 
 using namespace vqk;
@@ -407,6 +408,58 @@ int vq_dequant_gemm(int format, const uint8_t* idx, int64_t expert_stride, const
   a.L = vqk::gemm_layout(n_experts, npairs);
   a.stream = (hipStream_t)stream;
   return hip_status(vqk::launch_gemm(a));
+}
+
+// ---------------------------------------------------------------- Tied Trit-Planes
+static int ttp_shape(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols <= 0 || cols % TTP_GROUP != 0) return VQ_EINVAL;
+  if (cols > (1 << 20) || rows > ((int64_t)1 << 40) / cols) return VQ_ERANGE;
+  return VQ_OK;
+}
+
+int vq_ttp_quantize(const void* W, int dtype, int64_t rows, int64_t cols, uint8_t* codes, uint16_t* scales,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return VQ_EINVAL;
+  int st = ttp_shape(rows, cols);
+  if (st != VQ_OK) return st;
+  if (rows == 0) return VQ_OK;
+  if (!W || !codes || !scales || !aligned(W, 16) || !aligned(codes, 4)) return VQ_EINVAL;
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < kHeader) return VQ_EWORKSPACE;
+  int ncu = 0;
+  if ((st = device_cus(&ncu)) != VQ_OK) return st;
+  return hip_status(launch_ttp_quantize(W, dtype, rows * (cols / TTP_GROUP), codes, scales, (WsHeader*)workspace,
+                                        ncu, (hipStream_t)stream));
+}
+
+int vq_ttp_dequantize(const uint8_t* codes, const uint16_t* scales, int64_t rows, int64_t cols, float* out,
+                      void* stream) {
+  int st = ttp_shape(rows, cols);
+  if (st != VQ_OK) return st;
+  if (rows == 0) return VQ_OK;
+  if (!codes || !scales || !out || !aligned(codes, 4) || !aligned(out, 16)) return VQ_EINVAL;
+  int ncu = 0;
+  if ((st = device_cus(&ncu)) != VQ_OK) return st;
+  return hip_status(launch_ttp_dequantize(codes, scales, rows * (cols / TTP_GROUP), out, ncu, (hipStream_t)stream));
+}
+
+size_t vq_ttp_error_workspace_size(int64_t n_mats, int64_t rows, int64_t cols) {
+  if (n_mats < 1 || ttp_shape(rows, cols) != VQ_OK) return 0;
+  const int64_t chunks = (rows * (cols / TTP_GROUP) + TTP_CHUNK - 1) / TTP_CHUNK;
+  return align256(kHeader + sizeof(double) * 2 * (size_t)n_mats * (size_t)chunks);
+}
+
+int vq_ttp_error(const void* W, int dtype, const uint8_t* codes, const uint16_t* scales, int64_t n_mats,
+                 int64_t rows, int64_t cols, double* sums, void* workspace, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || n_mats < 1) return VQ_EINVAL;
+  int st = ttp_shape(rows, cols);
+  if (st != VQ_OK) return st;
+  if (n_mats > 65535 || (rows * (cols / TTP_GROUP) + TTP_CHUNK - 1) / TTP_CHUNK > 0x7FFFFFFF) return VQ_ERANGE;
+  if (!sums || (rows > 0 && (!W || !codes || !scales || !aligned(W, 16) || !aligned(codes, 4)))) return VQ_EINVAL;
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < vq_ttp_error_workspace_size(n_mats, rows, cols))
+    return VQ_EWORKSPACE;
+  return hip_status(launch_ttp_error(W, dtype, codes, scales, rows * (cols / TTP_GROUP), n_mats,
+                                     (double*)((char*)workspace + kHeader), sums, (WsHeader*)workspace,
+                                     (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------- error
