@@ -59,6 +59,8 @@ def parse():
                     "the w2 dequant-GEMV (prints its own JSON line)")
     ap.add_argument("--gemm", default="", help="prompt-processing dequant-GEMM measurement on the layer: comma "
                     "list of token counts (top-8 each), e.g. 1024,4096,16384 (prints its own JSON line)")
+    ap.add_argument("--ttp", action="store_true", help="Tied Trit-Planes codec on the layer: quantize, dequantize "
+                    "and error of all experts (prints its own JSON line)")
     ap.add_argument("--container", default="", help="container measurement: write the layer's VQ3R records "
                     "into a container under this directory, then time streaming them into device memory and "
                     "verifying them (prints its own JSON line)")
@@ -206,6 +208,10 @@ def main():
                     vq.dequant_gemv(pk4, sc4_e, cb4, x, route, ROWS, COLS, fmt="vq4p", y=y, workspace=ws4)
     step.fitted = False
 
+    if args.ttp:
+        ttp_bench(args, torch, vq, W, E)
+        return
+
     if args.gemm:
         gemm_bench(args, torch, vq, synthetic, W, mats, init3, cb3, fit_ws3, idx3, sc3, enc_ws, E)
         return
@@ -329,6 +335,38 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def ttp_bench(args, torch, vq, W, E):
+    """Tied Trit-Planes over the full layer (E x [2048 x 7168] bf16): quantize,
+    dequantize and error, HIP-event timed; the rates are against HBM bytes."""
+    dev = "cuda"
+    n = E * ROWS * COLS
+    codes = torch.empty((E * ROWS, COLS // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((E * ROWS, COLS // 256), dtype=torch.float16, device=dev)
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    out = torch.empty((E * ROWS, COLS), dtype=torch.float32, device=dev)
+    sums = torch.empty((E, 2), dtype=torch.float64, device=dev)
+    T = Timer(torch)
+    for rep in range(args.warmup + max(3, args.steps)):
+        if rep == args.warmup:
+            T.reset()
+        with T("quantize"):
+            vq.ttp_quantize(W, codes=codes, scales=scales, workspace=ws, check=False)
+        with T("dequantize"):
+            vq.ttp_dequantize(codes, scales, out=out)
+        with T("error"):
+            vq.ttp_error_sums(W, codes, scales, n_mats=E, sums=sums, check=False)
+    vq.read_status(ws)
+    tot = sums.sum(dim=0)
+    res = {}
+    for k, nbytes in (("quantize", n * 2 + n // 2 + n // 128), ("dequantize", n // 2 + n // 128 + n * 4),
+                      ("error", n * 2 + n // 2 + n // 128)):
+        ms = T.mean_ms(k)
+        res[k] = {"ms": round(ms, 3), "gweights_s": round(n / (ms * 1e-3) / 1e9, 1),
+                  "hbm_GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "alg_bytes": nbytes}
+    print(json.dumps({"ttp": res, "rel_err_layer": round(float((tot[0] / tot[1]).sqrt()), 5),
+                      "bits_per_weight": 4.0625, "experts": E, "shape": [ROWS, COLS]}), flush=True)
 
 
 FP16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak
