@@ -160,6 +160,42 @@ def test_decode_gemv_error_mxfp4_argument_errors():
     assert L.vq_read_status(None, None, None) == VQ_EWORKSPACE
 
 
+def test_gemm_and_ttp_argument_errors():
+    L = vq.lib()
+    a, b, c, d, e, f = (_Fake() for _ in range(6))
+    ws = _Fake(1 << 16)
+    n_ws = L.vq_dequant_gemm_workspace_size(0, 4, 3, 2)
+    assert n_ws >= 256 and L.vq_dequant_gemm_workspace_size(2, 4, 3, 2) == 0
+    assert L.vq_dequant_gemm_workspace_size(0, 0, 3, 2) == 0
+    G = lambda **k: L.vq_dequant_gemm(k.get("fmt", 0), a.ptr, k.get("es", 64 * 8 * 3), b.ptr, 64, c.ptr, 64, 64,
+                                      k.get("ne", 4), k.get("x", d.ptr), k.get("nt", 3), e.ptr, 2, f.ptr, ws.ptr,
+                                      k.get("wsn", n_ws), None)
+    assert G(fmt=3) == VQ_EINVAL
+    assert G(ne=0) == VQ_EINVAL
+    assert G(es=100) == VQ_EINVAL                                     # stride below one expert's records
+    assert G(x=ctypes.c_void_p(d.ptr.value + 2)) == VQ_EINVAL         # activations 16-byte aligned
+    assert G(wsn=100) == VQ_EWORKSPACE
+    assert G(nt=-1) == VQ_EINVAL
+    big = L.vq_dequant_gemm(0, a.ptr, 0, b.ptr, 0, c.ptr, 65536 * 256 + 1, 8, 1, d.ptr, 1, e.ptr, 1, f.ptr, ws.ptr,
+                            (1 << 63) - 1, None)
+    assert big == VQ_ERANGE                                           # more row blocks than one launch dimension
+    # Tied Trit-Planes
+    T = lambda **k: L.vq_ttp_quantize(a.ptr, k.get("dt", 1), k.get("rows", 4), k.get("cols", 512), b.ptr, c.ptr,
+                                      k.get("ws", ws.ptr), k.get("wsn", 256), None)
+    assert T(cols=384) == VQ_EINVAL                                   # cols % 256
+    assert T(dt=9) == VQ_EINVAL
+    assert T(rows=-1) == VQ_EINVAL
+    assert T(wsn=100) == VQ_EWORKSPACE
+    assert T(rows=0) == VQ_OK
+    assert L.vq_ttp_dequantize(a.ptr, b.ptr, 4, 300, c.ptr, None) == VQ_EINVAL
+    assert L.vq_ttp_dequantize(a.ptr, b.ptr, 4, 512, ctypes.c_void_p(c.ptr.value + 4), None) == VQ_EINVAL
+    assert L.vq_ttp_error_workspace_size(0, 4, 512) == 0
+    n_e = L.vq_ttp_error_workspace_size(3, 64, 512)
+    assert n_e >= 256 + 3 * 2 * 8
+    assert L.vq_ttp_error(a.ptr, 1, b.ptr, c.ptr, 3, 64, 512, d.ptr, ws.ptr, n_e - 8, None) == VQ_EWORKSPACE
+    assert L.vq_ttp_error(a.ptr, 1, b.ptr, c.ptr, 70000, 4, 256, d.ptr, ws.ptr, 1 << 40, None) == VQ_ERANGE
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(vq, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(vq, "_lib", None)
