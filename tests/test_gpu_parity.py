@@ -207,6 +207,41 @@ def test_decode_bit_exact_and_error(cfg1, fmt):
 
 
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+def test_encode_decode_error_full_layer_sampled(cfg1, fmt):
+    """The launches the benchmark times: the 256-expert layer of [2048 x 7168]
+    bf16 (generated on the GPU as the benchmark does) encoded, decoded and
+    measured in one call each. 64 sampled rows are checked bit-exact against
+    the oracle (indices, scales, decoded weights); two whole experts' error
+    sums against the oracle's relative error within 1e-5."""
+    say("full layer encode/decode/error", fmt)
+    E, R, C = 256, 2048, 7168
+    S, _ = vq.stages_entries(fmt)
+    _, cb = cfg1[fmt]
+    W = torch.empty((E * R, C), dtype=torch.bfloat16, device=DEV)
+    for e in range(E):
+        synthetic.student_t_expert_torch(synthetic.expert_seed(3, e), R, C, device=DEV, out=W[e * R:(e + 1) * R])
+    cbd = to_dev(cb)
+    rec, sc = vq.encode(W, cbd, fmt=fmt)
+    w_hat = vq.decode(rec, sc, cbd, fmt=fmt)
+    sums = vq.error_sums(W, rec, sc, cbd, fmt=fmt, n_mats=E).cpu().numpy()
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(7).choice(E * R, 64, replace=False))
+    rt = torch.from_numpy(rows).to(DEV)
+    wf = W[rt].float().cpu().numpy()
+    idx_o, s_o = oracle.encode(wf, cb)
+    assert np.array_equal(rec_to_idx(fmt, rec[rt]), idx_o)
+    assert np.array_equal(scales_bits(sc[rt]), s_o)
+    assert np.array_equal(w_hat[rt].cpu().numpy().view(np.uint32), oracle.decode(idx_o, s_o, cb).view(np.uint32))
+    del w_hat
+    for e in (5, 201):
+        we = W[e * R:(e + 1) * R].float().cpu().numpy()
+        i_e, s_e = oracle.encode(we, cb)
+        for su in range(1, S + 1):
+            ref = oracle.rel_error(we, oracle.decode(i_e, s_e, cb, stages_used=su))
+            assert abs(np.sqrt(sums[e, su - 1] / sums[e, S]) - ref) <= 1e-5, (e, su)
+
+
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
 def test_decode_ragged_rows_and_unaligned_records(cfg1, fmt):
     """Rows of 13 vectors (not a multiple of 4) and records starting at an odd
     byte address take the one-vector-per-step path; both must stay bit-exact."""
