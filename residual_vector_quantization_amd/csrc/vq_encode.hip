@@ -306,6 +306,9 @@ __global__ __launch_bounds__(256) void k_assign_exact(const float* R_cur, float*
   const uint32_t nf = hdr->n_flag[parity];
   const bool full = nf > cap;
   const uint64_t total = full ? (uint64_t)n : nf;
+  // blocks past the queue have no vector to take: they exit without writing
+  // their partial slot, which k_update then does not read (same count there)
+  if (!full && (uint64_t)blockIdx.x * blockDim.x >= total) return;
   if (MODE == 0)
     for (int q = threadIdx.x; q < K * (DIM + 1); q += blockDim.x) (&A.sum[0][0])[q] = 0ull;
   for (int q = threadIdx.x; q < K * DIM; q += blockDim.x) (&cb[0][0])[q] = C[q];
@@ -352,8 +355,15 @@ __global__ __launch_bounds__(64) void k_update(float* C, const long long* partia
   constexpr int K = Fmt<FMT>::K;
   __shared__ long long red[64][DIM + 1];
   const int j = blockIdx.x;
-  const bool full = hdr->n_flag[parity] > cap;
+  const uint32_t nf = hdr->n_flag[parity];
+  const bool full = nf > cap;
   const int s0 = full ? n_assign : 0;
+  // exact-pass slots that were written: all when the pass covered every vector,
+  // else one per 256 queued vectors (k_assign_exact's blocks past the queue exit)
+  if (!full) {
+    const int64_t used = ((int64_t)nf + 255) / 256;
+    if ((int64_t)n_assign + used < n_slots) n_slots = (int)(n_assign + used);
+  }
   long long acc[DIM + 1];
 #pragma unroll
   for (int k = 0; k <= DIM; ++k) acc[k] = 0;
