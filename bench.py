@@ -323,7 +323,7 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32 (fp32 search with exact check; bf16 weights in)", "data": "synthetic",
+        "dtype": "f32", "data": "synthetic",
         "config": {"workload": "full routed-expert layer: %d experts x w1 [2048x7168] bf16, fit on %d sampled "
                                "experts x %d Lloyd iters, VQ3R+VQ4P encode, decode, error, dequant-GEMV at "
                                "1/4/16 tokens top-8" % (E, len(mats), args.iters),
