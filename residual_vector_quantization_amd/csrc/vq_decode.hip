@@ -25,41 +25,129 @@ __device__ inline void decode_vec(const float (*cb)[Fmt<FMT>::K][DIM], uint32_t 
   dst[1] = make_float4(s * acc[4], s * acc[5], s * acc[6], s * acc[7]);
 }
 
-template <int FMT>
+// A wave decodes chunks of 256 consecutive vectors, four consecutive ones per
+// lane: the chunk's 768 record bytes are read as three dwords per lane (one
+// contiguous 768-byte piece per wave). The lane's 128 bytes of output go
+// through a per-wave LDS stage, slot x stored at x ^ ((x >> 3) & 7) so that
+// both the lane-strided writes and the contiguous read-back are free of bank
+// conflicts; every store instruction then writes 1 KB of contiguous output.
+// The records and scales of the wave's next chunk are loaded before the
+// current chunk's stores are issued: vector-memory counters complete in
+// order, so loads issued after the stores would make the next chunk wait for
+// them. The first chunk is peeled off the loop so that every entry into the
+// loop has the same loads and stores in flight.
+constexpr int DEC_CHUNK = 256;
+
+__device__ inline int dec_slot(int x) { return x ^ ((x >> 3) & 7); }
+
+template <int FMT, bool DWORD>
 __global__ __launch_bounds__(256) void k_decode(const uint8_t* idx, const uint16_t* scales, const float* cb_g,
                                                 uint32_t V, uint64_t nvec, int stages_used, float* out) {
-  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, U = 4;
+  constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K;
   __shared__ float cb[S][K][DIM];
-  __shared__ float4 stage[4][128];  // per wave: the 64 vectors' 2 KB of output
+  __shared__ float4 stage[4][2 * DEC_CHUNK];  // per wave: 256 vectors x 32 B
   for (int q = threadIdx.x; q < S * K * DIM; q += blockDim.x) (&cb[0][0][0])[q] = cb_g[q];
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t nth = (uint64_t)gridDim.x * blockDim.x;
-  // U vectors per thread, nth apart (lanes of a wave hold 64 consecutive
-  // vectors); all their loads are issued before any is used. Each wave's
-  // 2 KB of output goes through LDS so that every store instruction writes
-  // 1 KB of contiguous memory.
-  for (uint64_t v0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; v0 - lane < nvec; v0 += U * nth) {
-    uint32_t word[U];
-    float s[U];
+  float4* st = stage[wave];
+  const uint64_t nfull = nvec / DEC_CHUNK;  // chunks of 256 vectors
+  const uint64_t stride = (uint64_t)gridDim.x * 4;
+  // row and in-row position of the chunk the next load() reads, advanced by
+  // one wave stride per call without divisions (every call but the clamped
+  // last one reads the next chunk of the sequence)
+  const uint64_t nrows = nvec / V;
+  const uint64_t cfirst = (uint64_t)blockIdx.x * 4 + wave;
+  uint64_t lr = cfirst * DEC_CHUNK / V;
+  uint32_t lo = (uint32_t)(cfirst * DEC_CHUNK - lr * V);
+  const uint64_t dR = stride * DEC_CHUNK / V;
+  const uint32_t dO = (uint32_t)(stride * DEC_CHUNK - dR * V);
+  // records (one lane: vectors 4 lane .. 4 lane + 3) and scale bits of chunk c < nfull
+  auto load = [&](uint64_t c, uint32_t (&d)[3], uint16_t (&sb)[4]) {
+    const uint64_t v0 = c * DEC_CHUNK;
+    const uint8_t* rec = idx + v0 * 3 + 12 * lane;
+    if constexpr (DWORD) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(rec);
+      d[0] = src[0];
+      d[1] = src[1];
+      d[2] = src[2];
+    } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint64_t vid = v0 + u * nth;
-      const uint64_t vc = vid < nvec ? vid : nvec - 1;
-      word[u] = load_record(idx + vc * 3);
-      s[u] = f16_bits_to_f32(scales[(uint32_t)(vc / V)]);
+      for (int k = 0; k < 3; ++k)
+        d[k] = (uint32_t)rec[4 * k] | ((uint32_t)rec[4 * k + 1] << 8) | ((uint32_t)rec[4 * k + 2] << 16) |
+               ((uint32_t)rec[4 * k + 3] << 24);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint64_t wbase = v0 - lane + u * nth;  // the wave's first vector
-      if (wbase >= nvec) break;                    // wave-uniform
-      decode_vec<FMT>(cb, word[u], s[u], stages_used, &stage[wave][2 * lane]);
-      __builtin_amdgcn_wave_barrier();
-      const uint64_t nv = nvec - wbase;  // valid vectors of this wave (> 0)
-      float4* dst = reinterpret_cast<float4*>(out + wbase * DIM);
-      if ((uint64_t)(lane >> 1) < nv) dst[lane] = stage[wave][lane];
-      if ((uint64_t)(32 + (lane >> 1)) < nv) dst[64 + lane] = stage[wave][64 + lane];
-      __builtin_amdgcn_wave_barrier();
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t off = lo + (uint32_t)(4 * lane + q);  // relative to row lr (< V + 256)
+      uint64_t row = lr + (V >= DEC_CHUNK ? (off >= V ? 1u : 0u) : off / V);
+      row = row < nrows ? row : nrows - 1;
+      sb[q] = scales[row];
+    }
+    lo += dO;  // the next chunk of the wave: DEC_CHUNK * stride vectors further
+    lr += dR;
+    if (lo >= V) {
+      lo -= V;
+      ++lr;
+    }
+  };
+  auto body = [&](uint64_t c, const uint32_t (&d)[3], const uint16_t (&sb)[4], uint32_t (&dn)[3],
+                  uint16_t (&sn)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // record q = bytes 3q .. 3q+2 of the lane's 12 bytes
+      const int k0 = (3 * q) >> 2, o = (3 * q) & 3;
+      const uint32_t w = (o <= 1) ? (d[k0] >> (8 * o)) : ((d[k0] >> (8 * o)) | (d[k0 + 1] << (32 - 8 * o)));
+      float4 pr[2];
+      decode_vec<FMT>(cb, w, f16_bits_to_f32(sb[q]), stages_used, pr);
+      const int x = 2 * (4 * lane + q);
+      st[dec_slot(x)] = pr[0];
+      st[dec_slot(x + 1)] = pr[1];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t cn = c + stride < nfull ? c + stride : c;  // clamped: the loads are unconditional
+    load(cn, dn, sn);
+    float4* dst = reinterpret_cast<float4*>(out + c * DEC_CHUNK * DIM);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dst[64 * k + lane] = st[dec_slot(64 * k + lane)];
+    __builtin_amdgcn_wave_barrier();
+  };
+  uint64_t c = (uint64_t)blockIdx.x * 4 + wave;
+  if (c < nfull) {
+    uint32_t d[3], dn[3];
+    uint16_t sb[4], sn[4];
+    load(c, d, sb);
+    body(c, d, sb, dn, sn);
+    for (c += stride; c < nfull; c += stride) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k) d[k] = dn[k];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sb[q] = sn[q];
+      body(c, d, sb, dn, sn);
+    }
+  }
+  // the last nvec % 256 vectors: the wave whose chunk sequence reaches nfull
+  const uint64_t ntail = nvec - nfull * DEC_CHUNK;
+  if (ntail > 0 && c == nfull) {
+    const uint64_t v0 = nfull * DEC_CHUNK;
+    const int nv = (int)ntail;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = 4 * lane + q;
+      if (j < nv) {
+        const uint8_t* rec = idx + (v0 + j) * 3;
+        const uint32_t w = (uint32_t)rec[0] | ((uint32_t)rec[1] << 8) | ((uint32_t)rec[2] << 16);
+        float4 pr[2];
+        decode_vec<FMT>(cb, w, f16_bits_to_f32(scales[(v0 + j) / V]), stages_used, pr);
+        st[dec_slot(2 * j)] = pr[0];
+        st[dec_slot(2 * j + 1)] = pr[1];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    float4* dst = reinterpret_cast<float4*>(out + v0 * DIM);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int x = 64 * k + lane;
+      if (x < 2 * nv) dst[x] = st[dec_slot(x)];
     }
   }
 }
@@ -67,16 +155,17 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t* idx, const uint16
 hipError_t launch_decode(const DecodeArgs& a) {
   const uint64_t V = (uint64_t)(a.cols / DIM), nvec = (uint64_t)a.rows * V;
   if (nvec == 0) return hipSuccess;
-  uint64_t g = (nvec / 4 + 255) / 256;
+  const uint64_t nchunks = (nvec + DEC_CHUNK - 1) / DEC_CHUNK;
+  uint64_t g = (nchunks + 3) / 4;
   const uint64_t gmax = (uint64_t)a.ncu * 8;
   if (g > gmax) g = gmax;
   if (g < 1) g = 1;
-  if (a.format == 0)
-    k_decode<0><<<(unsigned)g, 256, 0, a.stream>>>(a.idx, a.scales, a.codebooks, (uint32_t)V, nvec, a.stages_used,
-                                                   a.out);
-  else
-    k_decode<1><<<(unsigned)g, 256, 0, a.stream>>>(a.idx, a.scales, a.codebooks, (uint32_t)V, nvec, a.stages_used,
-                                                   a.out);
+  const bool dw = ((uintptr_t)a.idx & 3) == 0;
+  auto go = [&](auto kern) {
+    kern<<<(unsigned)g, 256, 0, a.stream>>>(a.idx, a.scales, a.codebooks, (uint32_t)V, nvec, a.stages_used, a.out);
+  };
+  if (a.format == 0) dw ? go(k_decode<0, true>) : go(k_decode<0, false>);
+  else dw ? go(k_decode<1, true>) : go(k_decode<1, false>);
   return hipGetLastError();
 }
 
@@ -114,10 +203,22 @@ __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx
       const float s = f16_bits_to_f32(sc_m[row]);
       const char* wrow = W_m + (uint64_t)row * cols * esz;
       const uint8_t* rrec = idx_m + (uint64_t)row * V * 3;
+      // the next vector's weights and record are loaded before this one is used
+      float wn[8];
+      uint32_t wordn = 0;
+      if ((uint32_t)lane < V) {
+        load_vec8<DT>(wrow, lane, wn);
+        wordn = load_record(rrec + (uint64_t)lane * 3);
+      }
       for (uint32_t j = lane; j < V; j += 64) {
         float w[8];
-        load_vec8<DT>(wrow, j, w);
-        const uint32_t word = load_record(rrec + (uint64_t)j * 3);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w[k] = wn[k];
+        const uint32_t word = wordn;
+        if (j + 64 < V) {
+          load_vec8<DT>(wrow, j + 64, wn);
+          wordn = load_record(rrec + (uint64_t)(j + 64) * 3);
+        }
         float part[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) part[k] = 0.0f;
@@ -128,13 +229,13 @@ __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx
           for (int k = 0; k < 8; ++k) {
             part[k] = (t == 0) ? cw[k] : part[k] + cw[k];
             const double d = (double)w[k] - (double)(s * part[k]);
-            acc[t] += d * d;
+            acc[t] = __builtin_fma(d, d, acc[t]);
           }
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           nonfinite |= !__builtin_isfinite(w[k]);
-          acc[S] += (double)w[k] * (double)w[k];
+          acc[S] = __builtin_fma((double)w[k], (double)w[k], acc[S]);
         }
       }
     }
