@@ -243,12 +243,15 @@ def test_encode_decode_error_full_layer_sampled(cfg1, fmt):
 
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
 def test_decode_ragged_rows_and_unaligned_records(cfg1, fmt):
-    """Rows of 13 vectors (not a multiple of 4) and records starting at an odd
-    byte address take the one-vector-per-step path; both must stay bit-exact."""
+    """The decoder works on chunks of 256 consecutive vectors. Covered here:
+    rows of 13 vectors (several rows per chunk), rows of 256 and 257 vectors
+    (chunk starts inside a row), a ragged last chunk, a matrix smaller than
+    one chunk, and records starting at an odd byte address (byte-wise record
+    loads). All must stay bit-exact."""
     say("decode ragged / unaligned", fmt)
     _, cb = cfg1[fmt]
     cbd = to_dev(cb)
-    for rows, cols, offset in ((37, 104, 0), (16, 256, 1), (5, 104, 3)):
+    for rows, cols, offset in ((37, 104, 0), (16, 256, 1), (5, 104, 3), (300, 2056, 0), (9, 2048, 2)):
         W = synthetic.student_t_rows_f32(rows, cols, seed=rows + cols)
         idx_o, s_o = oracle.encode(W, cb)
         packed = oracle.pack(fmt, idx_o).reshape(-1)
