@@ -148,7 +148,8 @@ int vq4p_encode(const void* W, int dtype, int64_t rows, int64_t cols, const floa
  * W_out[r][8j+k] = s_r * (((C1[i1][k] + C2[i2][k]) + C3[i3][k]) [+ C4[i4][k]]),
  * summed left to right in fp32, then one fp32 multiply. stages_used < stages
  * gives the partial reconstruction after that many stages (e.g. 2 = "vq2").
- * W_out fp32 [rows][cols]. No workspace; cannot fail on the device.
+ * W_out fp32 [rows][cols], 16-byte aligned (VQ_EINVAL otherwise). No workspace;
+ * cannot fail on the device.
  * ---------------------------------------------------------------------- */
 int vq_decode(int format, const uint8_t* idx, const uint16_t* scales, const float* codebooks, int64_t rows,
               int64_t cols, int32_t stages_used, float* W_out, void* stream);
