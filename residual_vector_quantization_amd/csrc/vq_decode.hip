@@ -6,9 +6,8 @@ namespace vqk {
 
 // ------------------------------------------------------------------ decode
 // [VQ3R page] §2: w_hat = s * (((C1[i1] + C2[i2]) + C3[i3]) [+ C4[i4]]), summed
-// left to right in fp32, then one fp32 multiply. One thread per 8-dim vector
-// (neighbouring lanes write neighbouring 32-byte outputs); the codebooks sit
-// in LDS.
+// left to right in fp32, then one fp32 multiply: one 8-dim vector into two
+// float4, from codebooks in LDS.
 template <int FMT>
 __device__ inline void decode_vec(const float (*cb)[Fmt<FMT>::K][DIM], uint32_t word, float s, int stages_used,
                                   float4* dst) {
@@ -233,12 +232,12 @@ __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx
           }
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          nonfinite |= !__builtin_isfinite(w[k]);
-          acc[S] = __builtin_fma((double)w[k], (double)w[k], acc[S]);
-        }
+        for (int k = 0; k < 8; ++k) acc[S] = __builtin_fma((double)w[k], (double)w[k], acc[S]);
       }
     }
+    // a non-finite weight makes its thread's sum of squares non-finite; finite
+    // weights cannot overflow it (|w| < 2^128 and fewer than 2^32 terms)
+    nonfinite |= !__builtin_isfinite(acc[S]);
 #pragma unroll
     for (int t = 0; t <= S; ++t) red[t][threadIdx.x] = acc[t];
     __syncthreads();

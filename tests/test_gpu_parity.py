@@ -281,6 +281,26 @@ def test_error_multi_matrix_bf16(cfg1):
         assert abs(np.sqrt(sums[m, 2] / sums[m, 3]) - ref) < 1e-5
 
 
+def test_error_flags_non_finite_weights(cfg1):
+    """A non-finite weight is a data error of the error call (status 5);
+    finite weights up to the fp32 maximum are not."""
+    say("error non-finite")
+    _, cb = cfg1["vq3r"]
+    W = synthetic.gaussian_rows(40, 256, seed=12)
+    idx_o, s_o = oracle.encode(W, cb)
+    rec, sd, cbd = to_dev(oracle.pack("vq3r", idx_o)), to_dev(s_o.view(np.float16)), to_dev(cb)
+    for bad, where in ((np.nan, (3, 17)), (np.inf, (39, 255)), (-np.inf, (0, 0))):
+        Wb = W.copy()
+        Wb[where] = bad
+        with pytest.raises(vq.VQError) as e:
+            vq.error_sums(to_dev(Wb), rec, sd, cbd)
+        assert e.value.status == 5, (bad, where)
+    Wb = W.copy()
+    Wb[5, 9] = np.float32(3.4e38)
+    sums = vq.error_sums(to_dev(Wb), rec, sd, cbd).cpu().numpy()[0]
+    assert np.all(np.isfinite(sums))
+
+
 @pytest.mark.parametrize("rows,cols,n", [(2048, 7168, 3), (100, 264, 70), (1, 8, 5)])
 def test_error_sums_do_not_depend_on_batching(rows, cols, n):
     """A matrix's fp64 sums are bit-identical alone and inside a multi-matrix
