@@ -127,19 +127,18 @@ __global__ __launch_bounds__(256) void k_ttp_quantize(const void* W, int64_t n_g
   if (bad) flag_status(hdr, bad);
 }
 
-// 8 weights per thread: one 32-bit word of codes -> two float4 stores
+// 4 weights per thread and step: 16 bits of codes -> one float4 store, so each
+// store instruction of a wave writes 1 KB of contiguous output
 __global__ __launch_bounds__(256) void k_ttp_dequantize(const uint8_t* codes, const uint16_t* scales,
                                                         int64_t n_groups, float* out) {
-  const int64_t n8 = n_groups * (TTP_GROUP / 8);
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n8; t += (int64_t)gridDim.x * blockDim.x) {
-    const uint32_t c = reinterpret_cast<const uint32_t*>(codes)[t];
-    const float a = f16_bits_to_f32(scales[t / (TTP_GROUP / 8)]);
-    float v[8];
+  const int64_t n4 = n_groups * (TTP_GROUP / 4);
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n4; t += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t c = reinterpret_cast<const uint16_t*>(codes)[t];
+    const float a = f16_bits_to_f32(scales[t / (TTP_GROUP / 4)]);
+    float v[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = a * (float)((int)((c >> (4 * k)) & 0xFu) - 4);
-    float4* o = reinterpret_cast<float4*>(out + t * 8);
-    o[0] = make_float4(v[0], v[1], v[2], v[3]);
-    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    for (int k = 0; k < 4; ++k) v[k] = a * (float)((int)((c >> (4 * k)) & 0xFu) - 4);
+    reinterpret_cast<float4*>(out)[t] = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -208,8 +207,8 @@ hipError_t launch_ttp_quantize(const void* W, int dtype, int64_t n_groups, uint8
 hipError_t launch_ttp_dequantize(const uint8_t* codes, const uint16_t* scales, int64_t n_groups, float* out,
                                  int ncu, hipStream_t s) {
   if (n_groups == 0) return hipSuccess;
-  const int64_t n8 = n_groups * (TTP_GROUP / 8);
-  int64_t blocks = (n8 + 255) / 256;
+  const int64_t n4 = n_groups * (TTP_GROUP / 4);
+  int64_t blocks = (n4 + 255) / 256;
   if (blocks > (int64_t)ncu * 16) blocks = (int64_t)ncu * 16;
   k_ttp_dequantize<<<(unsigned)blocks, 256, 0, s>>>(codes, scales, n_groups, out);
   return hipGetLastError();

@@ -503,19 +503,34 @@ def test_gemv_pack_layout(fmt, shape):
 
 
 # ------------------------------------------------------------------ MXFP4
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_mxfp4_bit_exact(dtype):
+    """Aligned inputs take the 4-elements-per-lane kernel, an input one element
+    off its alignment the one-element-per-lane kernel; both bit-exact."""
     say("mxfp4", dtype)
     W = synthetic.student_t_rows_f32(64, 1024, seed=8)
     W[3, :32] = 0.0
-    W[4, :32] = 1e-42                       # subnormal block
-    W[5, 64:96] = np.float32(2.0) ** 120    # large exponent
+    W[4, :32] = 1e-42 if dtype != "f16" else 1e-7    # subnormal block
+    if dtype != "f16":
+        W[5, 64:96] = np.float32(2.0) ** 120         # large exponent
+        W[6, 0] = np.float32(3.0e38)                 # largest block scale
+        W[6, 1:32] = np.float32(1e-30)               # tiny next to it: flushed to the smallest codes
+    else:
+        W[5, 64:96] = 60000.0
     if dtype == "bf16":
         bits = synthetic.f32_to_bf16_bits(W)
         Wd = bf16_dev(bits)
         W = synthetic.bf16_bits_to_f32(bits).reshape(W.shape)
+    elif dtype == "f16":
+        W = W.astype(np.float16).astype(np.float32)
+        Wd = to_dev(W.astype(np.float16))
     else:
         Wd = to_dev(W)
-    got = vq.mxfp4_qdq(Wd).cpu().numpy()
     ref = oracle.mxfp4_qdq(W)
+    got = vq.mxfp4_qdq(Wd).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    buf = torch.empty(Wd.numel() + 8, dtype=Wd.dtype, device=DEV)
+    Wu = buf[1:1 + Wd.numel()].view(Wd.shape)
+    Wu.copy_(Wd)
+    got = vq.mxfp4_qdq(Wu).cpu().numpy()
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
