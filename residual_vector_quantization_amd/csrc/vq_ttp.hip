@@ -49,6 +49,41 @@ __device__ inline void load4(const void* W, int64_t i, float v[4]) {
   }
 }
 
+// Nearest levels from the reciprocal r = RN(1/a) where that provably gives the
+// level of the rounded quotient: |w r - w / a| <= 2^-22.9 |w / a|, so for
+// |w / a| < 5 the product and the rounded quotient lie within 1e-6 of each
+// other and round to the same integer unless the product is within 2^-18 of a
+// half-integer; at |w r| >= 5 both clamp to +-4. The weights that test leaves
+// open (and every scale whose reciprocal is not a normal number) take the
+// division.
+__device__ inline bool ttp_recip(float a, float& r) {
+  const float aa = __builtin_fabsf(a);
+  if (!(aa >= 0x1p-125f && aa <= 0x1p125f)) return false;
+  r = __fdiv_rn(1.0f, a);
+  return true;
+}
+// levels of the lane's 4 weights: the reciprocal path, then the division for
+// the weights it cannot settle, behind a wave-uniform branch
+__device__ inline void ttp_levels4(const float w[4], float a, float r, bool use_r, int q[4]) {
+  bool need = false;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float t = w[k] * r, at = __builtin_fabsf(t);
+    float qq = __builtin_rintf(t);
+    qq = qq > 4.0f ? 4.0f : (qq < -4.0f ? -4.0f : qq);
+    q[k] = (int)qq;
+    const float f = at - __builtin_floorf(at);
+    need |= !(at >= 5.0f || __builtin_fabsf(f - 0.5f) > 0x1p-18f);
+  }
+  need |= !use_r;
+  if (__builtin_expect(__any(need), 0)) {
+    if (need) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) q[k] = ttp_level(w[k], a);
+    }
+  }
+}
+
 __device__ inline float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -88,11 +123,11 @@ __global__ __launch_bounds__(256) void k_ttp_quantize(const void* W, int64_t n_g
     const int F = 52 - e;
     long long Wf[4];
     int q[4];
+    float r = 0.0f;
+    bool use_r = ttp_recip(a, r);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      Wf[k] = (long long)__builtin_rint(ldexp((double)w[k], F));
-      q[k] = ttp_level(w[k], a);
-    }
+    for (int k = 0; k < 4; ++k) Wf[k] = (long long)__builtin_rint(ldexp((double)w[k], F));
+    ttp_levels4(w, a, r, use_r, q);
     for (int it = 0; it < TTP_ITERS;) {
       long long swq = 0;
       int sqq = 0;
@@ -106,21 +141,27 @@ __global__ __launch_bounds__(256) void k_ttp_quantize(const void* W, int64_t n_g
       if (sqq == 0) break;  // uniform: the sums are the wave's
       a = (float)(ldexp((double)swq, -F) / (double)sqq);
       ++it;
+      use_r = ttp_recip(a, r);
       bool changed = false;
+      int nq[4];
+      ttp_levels4(w, a, r, use_r, nq);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int nq = ttp_level(w[k], a);
-        changed |= nq != q[k];
-        q[k] = nq;
+        changed |= nq[k] != q[k];
+        q[k] = nq[k];
       }
       if (!__any(changed)) break;
     }
     const uint16_t h = f32_to_f16_bits(a);
     if ((h & 0x7C00u) == 0x7C00u) bad |= ST_SCALE_RANGE;
     const float ah = f16_bits_to_f32(h);
+    float rh = 0.0f;
+    const bool use_rh = ttp_recip(ah, rh);
+    int qf[4];
+    ttp_levels4(w, ah, rh, use_rh, qf);
     uint32_t c2 = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) c2 |= (uint32_t)(ttp_level(w[k], ah) + 4) << (4 * k);
+    for (int k = 0; k < 4; ++k) c2 |= (uint32_t)(qf[k] + 4) << (4 * k);
     reinterpret_cast<uint16_t*>(codes + g * (TTP_GROUP / 2))[lane] = (uint16_t)c2;
     if (lane == 0) scales[g] = h;
   }
