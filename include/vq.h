@@ -93,6 +93,10 @@ int vq_version(void);
  * every vector because its queue overflowed). */
 int vq_read_status(const void* workspace, void* stream, uint32_t* flags_out);
 
+/* The same without the raw bits: VQ_EDATA if the last call on `workspace`
+ * flagged a data error, else VQ_OK (waits for `stream`). */
+int vq_read_device_status(const void* workspace, void* stream);
+
 /* Enqueues a reset of the workspace's status flags. */
 int vq_clear_status(void* workspace, void* stream);
 

@@ -64,6 +64,7 @@ def lib():
         "vq_status_string": ([I], ctypes.c_char_p),
         "vq_version": ([], I),
         "vq_read_status": ([P, P, U32P], I),
+        "vq_read_device_status": ([P, P], I),
         "vq_clear_status": ([P, P], I),
         "vq_encode_workspace_size": ([I, L64, L64], SZ),
         "vq_encode": ([I, I, P, I, L64, L64, P, P, P, P, SZ, P], I),

@@ -134,6 +134,8 @@ int vq_read_status(const void* workspace, void* stream, uint32_t* flags_out) {
   return (flags & ST_ERROR_MASK) ? VQ_EDATA : VQ_OK;
 }
 
+int vq_read_device_status(const void* workspace, void* stream) { return vq_read_status(workspace, stream, nullptr); }
+
 int vq_clear_status(void* workspace, void* stream) {
   if (!workspace || !aligned(workspace, 256)) return VQ_EWORKSPACE;
   return hip_status(launch_reset((WsHeader*)workspace, (hipStream_t)stream));

@@ -297,8 +297,13 @@ def test_error_flags_non_finite_weights(cfg1):
         assert e.value.status == 5, (bad, where)
     Wb = W.copy()
     Wb[5, 9] = np.float32(3.4e38)
-    sums = vq.error_sums(to_dev(Wb), rec, sd, cbd).cpu().numpy()[0]
+    ws = vq.error_workspace("vq3r", 1, 40, 256)
+    sums = vq.error_sums(to_dev(Wb), rec, sd, cbd, workspace=ws).cpu().numpy()[0]
     assert np.all(np.isfinite(sums))
+    assert vq.lib().vq_read_device_status(ws.data_ptr(), vq._stream()) == 0
+    Wb[5, 9] = np.nan
+    vq.error_sums(to_dev(Wb), rec, sd, cbd, workspace=ws, check=False)
+    assert vq.lib().vq_read_device_status(ws.data_ptr(), vq._stream()) == 5
 
 
 @pytest.mark.parametrize("rows,cols,n", [(2048, 7168, 3), (100, 264, 70), (1, 8, 5)])
