@@ -539,3 +539,61 @@ def test_mxfp4_bit_exact(dtype):
     Wu.copy_(Wd)
     got = vq.mxfp4_qdq(Wu).cpu().numpy()
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ random sweep
+@pytest.mark.parametrize("seed", [0, 1])
+def test_random_shapes_parity(cfg1, seed):
+    """Seeded random cases: format, dtype, shape (1-199 rows, 8-2392 columns),
+    magnitude (10^-3 .. 10^2) and zero rows, each through encode (indices and
+    scales bit-exact), decode (bit-exact), error (within 1e-5) and the
+    dequant-GEMV over 1-4 copies of the matrix with random routing (within
+    1e-3 of sum |w_hat x|)."""
+    say("random sweep", seed)
+    rng = np.random.default_rng(100 + seed)
+    for case in range(60):
+        fmt = ["vq3r", "vq4p"][rng.integers(2)]
+        _, cb = cfg1[fmt]
+        S = cb.shape[0]
+        rows, V = int(rng.integers(1, 200)), int(rng.integers(1, 300))
+        cols = 8 * V
+        dt = ["f32", "bf16", "f16"][rng.integers(3)]
+        W = (synthetic.gaussian_rows(rows, cols, seed=5000 + 100 * seed + case) *
+             float(10.0 ** rng.uniform(-3, 2))).astype(np.float32)
+        if rng.random() < 0.2:
+            W[rng.integers(rows)] = 0.0
+        if dt == "bf16":
+            bits = synthetic.f32_to_bf16_bits(W)
+            Wd = bf16_dev(bits)
+            W = synthetic.bf16_bits_to_f32(bits).reshape(rows, cols)
+        elif dt == "f16":
+            W = np.clip(W, -60000, 60000).astype(np.float16).astype(np.float32)
+            Wd = to_dev(W.astype(np.float16))
+        else:
+            Wd = to_dev(W)
+        tag = (case, fmt, rows, cols, dt)
+        idx_o, s_o = oracle.encode(W, cb)
+        cbd = to_dev(cb)
+        rec, s = vq.encode(Wd, cbd, fmt=fmt)
+        assert np.array_equal(rec_to_idx(fmt, rec), idx_o), tag
+        assert np.array_equal(scales_bits(s), s_o), tag
+        w_ref = oracle.decode(idx_o, s_o, cb)
+        got = vq.decode(rec, s, cbd, fmt=fmt).cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), w_ref.view(np.uint32)), tag
+        sums = vq.error_sums(Wd, rec, s, cbd, fmt=fmt).cpu().numpy()[0]
+        if np.any(W):
+            for su in range(1, S + 1):
+                ref = oracle.rel_error(W, oracle.decode(idx_o, s_o, cb, stages_used=su))
+                assert abs(np.sqrt(sums[su - 1] / sums[S]) - ref) <= 1e-5, tag + (su,)
+        E, ntok = int(rng.integers(1, 5)), int(rng.integers(1, 6))
+        topk = int(rng.integers(1, E + 1))
+        packed = vq.gemv_pack(rec[None].expand(E, -1, -1, -1).contiguous(), fmt=fmt)
+        x = synthetic.activations_f16(ntok, cols, seed=case)
+        route = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(ntok)]).astype(np.int32)
+        y = vq.dequant_gemv(packed, s[None].expand(E, -1).contiguous(), cbd, to_dev(x.view(np.float16)),
+                            to_dev(route), rows, cols, fmt=fmt).cpu().numpy()
+        xf = synthetic.f16_bits_to_f32(x).reshape(ntok, cols)
+        for b in range(ntok):
+            ref, scale = oracle.gemv_ref(w_ref, xf[b])
+            for k in range(topk):
+                assert np.all(np.abs(y[b, k] - ref) <= 1e-3 * scale), tag + (b, k)
