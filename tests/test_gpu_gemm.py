@@ -151,3 +151,24 @@ def test_gemm_full_layer_sampled(books, fmt):
     sample = np.random.default_rng(0).choice(ntok * topk, 48, replace=False)
     yh = y.cpu().numpy()
     _check(yh, [whs[e % 2] for e in range(E)], synthetic.f16_bits_to_f32(x).reshape(ntok, cols), route, sample)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_gemm_random_shapes(books, seed):
+    """Seeded random cases: format, shape (1-299 rows, 8-1600 columns), 1-6
+    experts, 1-199 tokens, top-1..4 routing; every pair within 1e-3 of
+    sum |w_hat x|."""
+    say("gemm random sweep", seed)
+    rng = np.random.default_rng(300 + seed)
+    for case in range(16):
+        fmt = ["vq3r", "vq4p"][rng.integers(2)]
+        cb = books[fmt]
+        rows, cols = int(rng.integers(1, 300)), 8 * int(rng.integers(1, 201))
+        E = int(rng.integers(1, 7))
+        ntok, topk = int(rng.integers(1, 200)), int(rng.integers(1, min(E, 4) + 1))
+        recs, scs, whs = _experts(fmt, cb, E, rows, cols, seed=4000 + 10 * case + seed)
+        x = synthetic.activations_f16(ntok, cols, seed=case)
+        route = synthetic.routing(ntok, E, topk, seed=7 + case)
+        y = vq.dequant_gemm(to_dev(recs), to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
+                            to_dev(route), fmt=fmt).cpu().numpy()
+        _check(y, whs, synthetic.f16_bits_to_f32(x).reshape(ntok, cols), route)

@@ -93,3 +93,55 @@ def test_ttp_error_does_not_depend_on_batching():
     for m in range(3):
         r = slice(200 * m, 200 * (m + 1))
         assert torch.equal(vq.ttp_error_sums(wd[r], c[r], s[r])[0], both[m])
+
+
+def test_ttp_half_integer_quotients():
+    """Weights at and just beside half-integer multiples of the starting scale
+    a = max|w| / 4: the nearest level of the rounded quotient is a tie (to
+    even) or a near tie, where a level taken from the reciprocal of the scale
+    could differ; codes and scales must still be the oracle's."""
+    say("ttp half-integer quotients")
+    a0 = np.float32(0.0371)
+    half = np.array([0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, -3.5], np.float32)
+    rows = []
+    for rel in (0.0, 2.0 ** -22, -(2.0 ** -22), 2.0 ** -19, -(2.0 ** -19)):
+        w = np.resize(half * np.float32(1.0 + rel), 256).astype(np.float32) * a0
+        w[0] = 4 * a0                              # sets max|w| = 4 a0
+        rows.append(w)
+    w = np.stack(rows).astype(np.float32)
+    c, s = vq.ttp_quantize(to_dev(w))
+    c_o, s_o = oracle.ttp_quantize(w)
+    assert np.array_equal(c.cpu().numpy(), c_o)
+    assert np.array_equal(s.cpu().view(torch.int16).numpy().view(np.uint16), s_o)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_ttp_random_shapes(seed):
+    """Seeded random cases: dtype, shape (1-40 rows, 256-4096 columns) and
+    magnitude (10^-4 .. 10^3), with some all-zero and constant groups; codes
+    and scales bit-exact."""
+    say("ttp random sweep", seed)
+    rng = np.random.default_rng(500 + seed)
+    for case in range(20):
+        dtype = ["f32", "bf16", "f16"][rng.integers(3)]
+        rows, cols = int(rng.integers(1, 41)), 256 * int(rng.integers(1, 17))
+        wf = (synthetic.student_t_rows_f32(rows, cols, seed=6000 + 50 * seed + case) *
+              np.float32(10.0 ** rng.uniform(-4, 3))).astype(np.float32)
+        if rng.random() < 0.3:
+            wf[rng.integers(rows), :256] = 0.0
+        if rng.random() < 0.3:
+            wf[rng.integers(rows), :256] = np.float32(rng.uniform(-1, 1))
+        if dtype == "bf16":
+            bits = synthetic.f32_to_bf16_bits(wf)
+            wd = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+            wf = synthetic.bf16_bits_to_f32(bits).reshape(rows, cols)
+        elif dtype == "f16":
+            wf = np.clip(wf, -60000, 60000).astype(np.float16).astype(np.float32)
+            wd = to_dev(wf.astype(np.float16))
+        else:
+            wd = to_dev(wf)
+        c, s = vq.ttp_quantize(wd)
+        c_o, s_o = oracle.ttp_quantize(wf)
+        tag = (case, dtype, rows, cols)
+        assert np.array_equal(c.cpu().numpy(), c_o), tag
+        assert np.array_equal(s.cpu().view(torch.int16).numpy().view(np.uint16), s_o), tag
