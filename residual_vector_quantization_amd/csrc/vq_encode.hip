@@ -51,7 +51,9 @@ __global__ __launch_bounds__(64 * enc_waves(ENG), enc_waves(ENG) / 2) void k_enc
   constexpr int S = Fmt<FMT>::S;
   constexpr bool X2 = ENG == ENG_F16X;
   constexpr int GV = X2 ? 64 : 32;  // vectors per group
+  constexpr int NWV = enc_waves(ENG);
   __shared__ SearchLds<FMT, ENG, S> L;
+  __shared__ uint32_t fbuf[NWV][FLAG_STAGE];
   build_tables<FMT, ENG, S>(L, cb_g, hdr);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5;
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(64 * enc_waves(ENG), enc_waves(ENG) / 2) void k_enc
   const bool writer = X2 || h == 0;
   const int64_t V = cols / DIM;
   const size_t esz = DT == DT_F32 ? 4 : 2;
-  constexpr int NWV = enc_waves(ENG);
+  FlagStage fs{fbuf[wave], 0};
   for (int64_t row = (int64_t)blockIdx.x * NWV + wave; row < rows; row += (int64_t)gridDim.x * NWV) {
     const void* wrow = (const char*)W + row * cols * esz;
     uint32_t bad;
@@ -93,9 +95,10 @@ __global__ __launch_bounds__(64 * enc_waves(ENG), enc_waves(ENG) / 2) void k_enc
       }
       const uint64_t vid = (uint64_t)row * V + j;
       if (valid && writer) store_record(idx + vid * 3, word);
-      append_flags(fl && valid && writer, (uint32_t)vid, &hdr->n_flag[0], list, cap, lane);
+      flag_stage(fs, fl && valid && writer, (uint32_t)vid, &hdr->n_flag[0], list, cap, lane);
     }
   }
+  flag_flush(fs, &hdr->n_flag[0], list, cap, lane);
 }
 
 // Exact pass: every queued vector (or every vector when `all` is set or the
@@ -230,6 +233,7 @@ __global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_
   constexpr int GV = X2 ? 64 : 32;
   __shared__ SearchLds<FMT, ENG, 1> L;
   __shared__ FitAccum<K> A;
+  __shared__ uint32_t fbuf[4][FLAG_STAGE];
   if (MODE == 0)
     for (int q = threadIdx.x; q < K * (DIM + 1); q += blockDim.x) (&A.sum[0][0])[q] = 0ull;
   build_tables<FMT, ENG, 1>(L, C, hdr);
@@ -239,6 +243,7 @@ __global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_
   const bool writer = X2 || h == 0;
   const int F = hdr->fbits;
   uint32_t mx = 0;
+  FlagStage fs{fbuf[wave], 0};
   const int64_t ngroups = (n + GV - 1) / GV;
   const int64_t gstride = (int64_t)gridDim.x * 4;
   // the next group's residuals are loaded while the current group is searched
@@ -283,8 +288,9 @@ __global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_
         for (int k = 0; k < 8; ++k) mx = max(mx, __float_as_uint(__builtin_fabsf(r[k])));
       }
     }
-    append_flags(fl && valid && writer, (uint32_t)j, &hdr->n_flag[parity], list, cap, lane);
+    flag_stage(fs, fl && valid && writer, (uint32_t)j, &hdr->n_flag[parity], list, cap, lane);
   }
+  flag_flush(fs, &hdr->n_flag[parity], list, cap, lane);
   if (MODE == 0) {
     flush_accum<K>(A, partials, blockIdx.x);
   } else {

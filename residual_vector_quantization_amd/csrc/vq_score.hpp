@@ -303,19 +303,41 @@ __device__ inline int search_stage_x2(const SearchLds<FMT, ENG_F16X, NST>& L, in
   return w;
 }
 
-// Appends the ids of flagged lanes to a global list (one atomic per wave).
-__device__ inline void append_flags(bool f, uint32_t vid, uint32_t* counter, uint32_t* list, uint32_t cap,
-                                    int lane) {
+// Per-wave staging of flagged vector ids in LDS. The ids of a wave gather in
+// its LDS buffer and move to the global list in batches: one atomic on the
+// shared list counter per batch instead of one per group with a flagged
+// vector, each of which the wave had to wait for. The counter still ends at
+// the total number of flagged vectors, and ids past `cap` are dropped as
+// before (the overflow is detected from the counter).
+constexpr int FLAG_STAGE = 128;  // staged ids per wave
+
+struct FlagStage {
+  uint32_t* buf;  // this wave's FLAG_STAGE LDS entries
+  int cnt;        // fill, the same in every lane
+};
+
+__device__ inline void flag_flush(FlagStage& fs, uint32_t* counter, uint32_t* list, uint32_t cap, int lane) {
+  if (fs.cnt == 0) return;
+  uint32_t base = 0;
+  if (lane == 0) base = atomicAdd(counter, (uint32_t)fs.cnt);
+  base = __shfl(base, 0);
+  for (int i = lane; i < fs.cnt; i += WAVE) {
+    const uint32_t pos = base + (uint32_t)i;
+    if (pos < cap) list[pos] = fs.buf[i];
+  }
+  __builtin_amdgcn_wave_barrier();  // the entries are read before they are overwritten
+  fs.cnt = 0;
+}
+
+__device__ inline void flag_stage(FlagStage& fs, bool f, uint32_t vid, uint32_t* counter, uint32_t* list,
+                                  uint32_t cap, int lane) {
   const uint64_t bal = __ballot(f);
   if (bal == 0) return;
-  const int leader = __ffsll((unsigned long long)bal) - 1;
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(bal));
-  base = __shfl(base, leader);
-  if (f) {
-    const uint32_t pos = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-    if (pos < cap) list[pos] = vid;
-  }
+  const int n = __popcll(bal);
+  if (fs.cnt + n > FLAG_STAGE) flag_flush(fs, counter, list, cap, lane);
+  if (f) fs.buf[fs.cnt + __popcll(bal & ((1ull << lane) - 1ull))] = vid;
+  __builtin_amdgcn_wave_barrier();
+  fs.cnt += n;
 }
 
 }  // namespace vqk
