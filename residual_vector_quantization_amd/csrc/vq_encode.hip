@@ -71,25 +71,25 @@ __global__ __launch_bounds__(64 * enc_waves(ENG), enc_waves(ENG) / 2) void k_enc
       if (bad) flag_status(hdr, bad);
     }
     if (bad) continue;
-    const float s = f16_bits_to_f32(sb);
+    const float s = f16_bits_to_f32(sb), y = row_recip(s);
     for (int64_t g = 0; g < V; g += GV) {
       const int64_t j = g + jl;
       const bool valid = j < V;
       float r[8];
       if (valid) {
         load_vec8<DT>(wrow, j, r);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) r[k] = normalize(r[k], s);
+        normalize8(r, s, y);
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) r[k] = 0.0f;
       }
       uint32_t word = 0;
       bool fl = false;
+      float rr = norm2_8(r);
 #pragma unroll 1
       for (int t = 0; t < S; ++t) {
         int w;
-        if constexpr (X2) w = search_stage_x2<FMT, S>(L, t, r, lane, fl);
+        if constexpr (X2) w = search_stage_x2<FMT, S, true>(L, t, r, lane, fl, rr);
         else w = search_stage<FMT, ENG, S>(L, t, r, lane, fl);
         word |= (uint32_t)w << (t * Fmt<FMT>::BITS);
       }
@@ -160,15 +160,13 @@ __global__ __launch_bounds__(256) void k_fit_prepare(const void* W, int64_t rows
       if (lane == 0) flag_status(hdr, bad);
       continue;
     }
-    const float s = f16_bits_to_f32(sb);
+    const float s = f16_bits_to_f32(sb), y = row_recip(s);
     for (int64_t j = lane; j < V; j += WAVE) {
       float v[8];
       load_vec8<DT>(wrow, j, v);
+      normalize8(v, s, y);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        v[k] = normalize(v[k], s);
-        mx = max(mx, __float_as_uint(__builtin_fabsf(v[k])));
-      }
+      for (int k = 0; k < 8; ++k) mx = max(mx, __float_as_uint(__builtin_fabsf(v[k])));
       float4* dst = reinterpret_cast<float4*>(R + (row * V + j) * DIM);
       dst[0] = make_float4(v[0], v[1], v[2], v[3]);
       dst[1] = make_float4(v[4], v[5], v[6], v[7]);
@@ -271,7 +269,8 @@ __global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_
     for (int k = 0; k < 8; ++k) r0[k] = r[k];
     bool fl = false;
     int w;
-    if constexpr (X2) w = search_stage_x2<FMT, 1>(L, 0, r, lane, fl);
+    float rr;
+    if constexpr (X2) w = search_stage_x2<FMT, 1, false>(L, 0, r, lane, fl, rr);
     else w = search_stage<FMT, ENG, 1>(L, 0, r, lane, fl);
     const bool ok = valid && !fl;
     if (MODE == 0) {

@@ -214,6 +214,14 @@ __device__ inline int search_stage(const SearchLds<FMT, ENG, NST>& L, int t, flo
   return w;
 }
 
+// ||r||^2 as the fmaf chain over k = 0..7 starting from 0.
+__device__ inline float norm2_8(const float r[8]) {
+  float rr = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) rr = __builtin_fmaf(r[k], r[k], rr);
+  return rr;
+}
+
 // Two groups per pass (fp16-split engine): lane (i, h) owns vector i of group
 // h, so the per-vector work after the search (merge, exact distance,
 // certification, residual update, next fp16 split) serves 64 vectors per wave
@@ -221,9 +229,14 @@ __device__ inline int search_stage(const SearchLds<FMT, ENG, NST>& L, int t, flo
 // in both half-waves (the K dimension is split across them); one
 // v_permlane32_swap per register broadcasts each half's values to both
 // halves. Returns the winner for the lane's own vector.
-template <int FMT, int NST>
+// rr: on return ||r'||^2 of the updated residual r' = r - C[w] (the fmaf chain
+// over k = 0..7 from 0). That is the exact distance d_w itself: the same chain
+// over the same values r_k - c_k, so a later stage gets its ||r||^2 without
+// recomputing it. RR_IN: rr holds ||r||^2 on entry; otherwise it is computed
+// here, next to d_w.
+template <int FMT, int NST, bool RR_IN>
 __device__ inline int search_stage_x2(const SearchLds<FMT, ENG_F16X, NST>& L, int t, float r[8], int lane,
-                                      bool& flag) {
+                                      bool& flag, float& rr) {
   constexpr int TILES = Fmt<FMT>::TILES, PACK = Fmt<FMT>::PACK;
   const int h = lane >> 5, i = lane & 31;
   // own residual split into fp16 hi + lo (pairs converted together; the -2 of
@@ -291,15 +304,17 @@ __device__ inline int search_stage_x2(const SearchLds<FMT, ENG_F16X, NST>& L, in
   const int tl = (int)(loc >> 4), v = (int)(loc & 15u);
   const int w = tl * 32 + 8 * (v >> 2) + 4 * hw_ + (v & 3);
   const float* c = L.cb[t][w];
-  float d = 0.0f, rr = 0.0f;
+  float d = 0.0f;
+  if constexpr (!RR_IN) rr = 0.0f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     float e = r[k] - c[k];
     d = __builtin_fmaf(e, e, d);
-    rr = __builtin_fmaf(r[k], r[k], rr);
+    if constexpr (!RR_IN) rr = __builtin_fmaf(r[k], r[k], rr);
     r[k] = e;
   }
   flag |= !certified<PACK>(p1, p2, rr, d);
+  rr = d;
   return w;
 }
 

@@ -173,6 +173,40 @@ def test_encode_edge_rows_and_errors(cfg1):
     assert rec.shape == (0, 8, 3)
 
 
+def _normalization_edge_matrix():
+    """48 x 64 fp32 rows where vectors leave the reciprocal normalization's
+    range |w| in [2^-100, 2^100] (zeros, -0, fp32 subnormals, 2^-101) or sit on
+    its edge (2^-100), rows with an fp16-subnormal scale, large rows."""
+    W = synthetic.gaussian_rows(48, 64, seed=31)
+    W[0, ::3] = 0.0
+    W[0, 1::5] = -0.0
+    W[1] = W[1] * np.float32(1e-6)                  # scale below fp16's normal range
+    W[1, 3], W[1, 17], W[1, 40] = 1e-42, -1e-31, 2.0 ** -101
+    W[2, 5], W[2, 6], W[2, 7] = 2.0 ** -100, -(2.0 ** -100), np.float32(2.0 ** -100) * np.float32(1 - 2 ** -24)
+    W[2, 20], W[2, 21] = 2.0 ** -99, 2.0 ** -60
+    W[3] = W[3] * np.float32(1e3)
+    W[4, 8:16] = 0.0                                 # a whole zero vector
+    W[5] = W[5] * np.float32(3e-8)                   # smallest fp16 subnormal scales
+    return W.astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+def test_encode_and_fit_normalization_edges(cfg1, fmt):
+    say("normalization edges", fmt)
+    W = _normalization_edge_matrix()
+    _, cb = cfg1[fmt]
+    idx_o, s_o = oracle.encode(W, cb)
+    rec, s = vq.encode(to_dev(W), to_dev(cb), fmt=fmt)
+    torch.cuda.synchronize()
+    assert np.array_equal(scales_bits(s), s_o)
+    assert np.array_equal(rec_to_idx(fmt, rec), idx_o)
+    S, K = vq.stages_entries(fmt)
+    init = synthetic.forgy_init(48 * 8, K, S, seed=12)
+    cb_o, _ = oracle.fit([W], S, K, 3, init)
+    cb_g = vq.fit_codebooks([to_dev(W)], init, fmt=fmt, iters=3)
+    assert np.array_equal(cb_g.cpu().numpy().view(np.uint32), cb_o.view(np.uint32))
+
+
 def test_encode_deterministic(cfg1):
     say("encode determinism")
     _, cb = cfg1["vq3r"]
