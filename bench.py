@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32768, help="oracle encode sample: first rows of the layer")
     ap.add_argument("--only", default="", help="comma list: fit,encode,decode,error,gemv,vq4p (default all)")
-    ap.add_argument("--loop", default="", help="profiling helper: repeat one component (encode|gemv1|gemv16|fit) --steps times")
+    ap.add_argument("--loop", default="", help="profiling helper: repeat one component (encode|encode4|fit|fit4|gemv1|gemv4|gemv16|decode) --steps times")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a plain copy of known size")
     ap.add_argument("--layer", action="store_true", help="per-layer conversion measurement: w1 and w3 "
                     "[2048x7168] and w2 [7168x2048] of every expert, each family fit, encoded and measured, plus "
@@ -226,7 +226,7 @@ def main():
 
     if args.loop:
         # profiling helper: one component repeated, nothing else in the trace
-        if args.loop != "fit":
+        if args.loop not in ("fit", "fit4"):
             vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3, workspace=fit_ws3)
             vq.encode(W, cb3, idx=idx3, scales=sc3, workspace=enc_ws)
             vq.gemv_pack(idx3_e, fmt="vq3r", out=pk3)
@@ -241,6 +241,9 @@ def main():
                           check=False)
             elif args.loop == "fit":
                 vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3, workspace=fit_ws3,
+                                 check=False)
+            elif args.loop == "fit4":
+                vq.fit_codebooks(mats, init4, fmt="vq4p", iters=args.iters, codebooks=cb4, workspace=fit_ws4,
                                  check=False)
             elif args.loop.startswith("gemv"):
                 ntok = int(args.loop[4:])

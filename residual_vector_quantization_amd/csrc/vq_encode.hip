@@ -210,11 +210,33 @@ __device__ inline void accum_vector(FitAccum<K>& A, int w, const float r[8], int
   if (count) atomicAdd(&A.sum[w][DIM], 1ull);
 }
 
+// The same sums with a two-instruction conversion, for |r 2^F| < 2^51: the
+// fp64 fma x = r 2^F + 1.5 2^52 (the product is exact) lands in [2^52, 2^53),
+// where consecutive doubles are consecutive integers, so x = 1.5 2^52 +
+// rint(r 2^F) with ties to even, as llrint, and the bit pattern of x is that
+// of 1.5 2^52 plus rint(r 2^F) as a two's complement int64. The block adds
+// the patterns (mod 2^64) and subtracts count * bits(1.5 2^52) per cluster at
+// the flush, leaving the exact sums.
+constexpr unsigned long long FIX_BIAS_BITS = 0x4338000000000000ull;  // 1.5 * 2^52
+
 template <int K>
-__device__ inline void flush_accum(FitAccum<K>& A, long long* partials, int slot) {
+__device__ inline void accum_vector_biased(FitAccum<K>& A, int w, const float r[8], double scale, int k0, int k1,
+                                           bool count) {
+  for (int k = k0; k < k1; ++k)
+    atomicAdd(&A.sum[w][k], (unsigned long long)__double_as_longlong(__builtin_fma((double)r[k], scale, 0x1.8p52)));
+  if (count) atomicAdd(&A.sum[w][DIM], 1ull);
+}
+
+template <int K>
+__device__ inline void flush_accum(FitAccum<K>& A, long long* partials, int slot, bool biased) {
   __syncthreads();
   long long* dst = partials + (size_t)slot * K * (DIM + 1);
-  for (int q = threadIdx.x; q < K * (DIM + 1); q += blockDim.x) dst[q] = (long long)(&A.sum[0][0])[q];
+  for (int q = threadIdx.x; q < K * (DIM + 1); q += blockDim.x) {
+    const int c = q / (DIM + 1), k = q % (DIM + 1);
+    unsigned long long v = (&A.sum[0][0])[q];
+    if (biased && k < DIM) v -= A.sum[c][DIM] * FIX_BIAS_BITS;
+    dst[q] = (long long)v;
+  }
 }
 
 // Assignment pass over R_cur. MODE 0 (iteration): certified vectors add their
@@ -240,6 +262,12 @@ __global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_
   const int jl = X2 ? lane : (lane & 31);
   const bool writer = X2 || h == 0;
   const int F = hdr->fbits;
+  // every |r| of this pass is below 2^e (the stage's residual maximum), so the
+  // biased conversion applies when e + F <= 51
+  int emax = 0;
+  frexpf(__uint_as_float(hdr->maxabs_bits[nxt ^ 1]), &emax);
+  const bool biased = emax + F <= 51;
+  const double fscale = ldexp(1.0, F);
   uint32_t mx = 0;
   FlagStage fs{fbuf[wave], 0};
   const int64_t ngroups = (n + GV - 1) / GV;
@@ -275,8 +303,13 @@ __global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_
     const bool ok = valid && !fl;
     if (MODE == 0) {
       if (ok) {
-        if constexpr (X2) accum_vector<K>(A, w, r0, F, 0, DIM, true);
-        else accum_vector<K>(A, w, r0, F, 4 * h, 4 * h + 4, h == 0);
+        if (biased) {
+          if constexpr (X2) accum_vector_biased<K>(A, w, r0, fscale, 0, DIM, true);
+          else accum_vector_biased<K>(A, w, r0, fscale, 4 * h, 4 * h + 4, h == 0);
+        } else {
+          if constexpr (X2) accum_vector<K>(A, w, r0, F, 0, DIM, true);
+          else accum_vector<K>(A, w, r0, F, 4 * h, 4 * h + 4, h == 0);
+        }
       }
     } else {
       if (ok) {
@@ -291,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_
   }
   flag_flush(fs, &hdr->n_flag[parity], list, cap, lane);
   if (MODE == 0) {
-    flush_accum<K>(A, partials, blockIdx.x);
+    flush_accum<K>(A, partials, blockIdx.x, biased);
   } else {
     for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
     if (lane == 0 && mx) atomicMax(&hdr->maxabs_bits[nxt], mx);
@@ -343,7 +376,7 @@ __global__ __launch_bounds__(256) void k_assign_exact(const float* R_cur, float*
     }
   }
   if (MODE == 0) {
-    flush_accum<K>(A, partials, slot_base + blockIdx.x);
+    flush_accum<K>(A, partials, slot_base + blockIdx.x, false);
   } else {
     for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
     if ((threadIdx.x & 63) == 0 && mx) atomicMax(&hdr->maxabs_bits[nxt], mx);
