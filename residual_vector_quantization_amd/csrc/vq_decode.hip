@@ -8,8 +8,15 @@ namespace vqk {
 // [VQ3R page] §2: w_hat = s * (((C1[i1] + C2[i2]) + C3[i3]) [+ C4[i4]]), summed
 // left to right in fp32, then one fp32 multiply: one 8-dim vector into two
 // float4, from codebooks in LDS.
+// The decode kernels pad their LDS codebooks to CbPad<FMT>::P floats per codeword: with
+// 32-byte rows codeword j starts on one of only 8 bank groups and the random
+// lookups of a wave collide more often; 48-byte rows spread them (VQ3R decode
+// 3.33 -> 3.02 ms on a 256-expert layer). VQ4P's 64-entry codebooks gain
+// nothing from it and keep 32-byte rows.
+template <int FMT> struct CbPad { static constexpr int P = FMT == 0 ? 12 : DIM; };
+
 template <int FMT>
-__device__ inline void decode_vec(const float (*cb)[Fmt<FMT>::K][DIM], uint32_t word, float s, int stages_used,
+__device__ inline void decode_vec(const float (*cb)[Fmt<FMT>::K][CbPad<FMT>::P], uint32_t word, float s, int stages_used,
                                   float4* dst) {
   float acc[8];
   const float* c0 = cb[0][record_index<FMT>(word, 0)];
@@ -43,9 +50,10 @@ template <int FMT, bool DWORD>
 __global__ __launch_bounds__(256) void k_decode(const uint8_t* idx, const uint16_t* scales, const float* cb_g,
                                                 uint32_t V, uint64_t nvec, int stages_used, float* out) {
   constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K;
-  __shared__ float cb[S][K][DIM];
+  constexpr int CBP = CbPad<FMT>::P;
+  __shared__ __align__(16) float cb[S][K][CBP];
   __shared__ float4 stage[4][2 * DEC_CHUNK];  // per wave: 256 vectors x 32 B
-  for (int q = threadIdx.x; q < S * K * DIM; q += blockDim.x) (&cb[0][0][0])[q] = cb_g[q];
+  for (int q = threadIdx.x; q < S * K * DIM; q += blockDim.x) (&cb[0][0][0])[(q >> 3) * CBP + (q & 7)] = cb_g[q];
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float4* st = stage[wave];
@@ -180,7 +188,7 @@ __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx
                                                const float* cb_g, uint32_t V, int64_t rows_per_mat, int64_t cols,
                                                int64_t nchunks, double* partials, WsHeader* hdr) {
   constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K;
-  __shared__ float cb[S][K][DIM];
+  __shared__ float cb[S][K][DIM];  // unpadded: padding costs this kernel a workgroup per CU
   __shared__ double red[S + 1][256];
   for (int q = threadIdx.x; q < S * K * DIM; q += blockDim.x) (&cb[0][0][0])[q] = cb_g[q];
   __syncthreads();
