@@ -141,6 +141,30 @@ def test_encode_all_ties_overflows_queue_and_stays_exact(fmt):
     assert np.all(rec_to_idx(fmt, rec) == 0)
 
 
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+@pytest.mark.parametrize("rows,cols", [(16, 2048), (8, 4096), (13, 1544)])
+def test_encode_flag_list_complete(fmt, rows, cols):
+    """Every vector a tie but the queue does not overflow: each wave stages 256+
+    flagged ids in LDS and flushes them in batches. The list (after the 256-byte
+    header, count in header word 1) must hold every vector id exactly once."""
+    say("encode flag list", fmt, rows, cols)
+    S, K = vq.stages_entries(fmt)
+    cb = np.zeros((S, K, 8), np.float32)
+    cb[:] = np.float32(0.25)
+    W = synthetic.gaussian_rows(rows, cols, seed=4)
+    nvec = rows * cols // 8
+    assert nvec <= 4096                                  # the smallest queue capacity
+    ws = vq.encode_workspace(fmt, rows, cols)
+    rec, s = vq.encode(to_dev(W), to_dev(cb), fmt=fmt, workspace=ws)
+    torch.cuda.synchronize()
+    assert vq.read_status(ws) == 0
+    words = ws[: 256 + 4 * nvec].cpu().numpy().view(np.uint32)
+    assert int(words[1]) == nvec
+    ids = np.sort(words[64:64 + nvec])
+    assert np.array_equal(ids, np.arange(nvec, dtype=np.uint32))
+    assert np.all(rec_to_idx(fmt, rec) == 0)
+
+
 def test_encode_edge_rows_and_errors(cfg1):
     say("encode edge rows")
     _, cb = cfg1["vq3r"]
