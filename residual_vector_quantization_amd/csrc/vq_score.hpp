@@ -244,16 +244,22 @@ __device__ inline int search_stage_x2(const SearchLds<FMT, ENG_F16X, NST>& L, in
   typedef _Float16 hf2 __attribute__((ext_vector_type(2)));
   typedef float ff2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  // lo = RN16(r - hi) in one mixed-precision fma per element: v_fma_mix
+  // forms r * 1 - hi exactly and rounds once to fp16 (into the low / high
+  // half). r - hi is itself exact in fp32 (a rounding error of r, a multiple
+  // of r's fp32 ulp below 2^13 of them), so these are the bits of converting hi
+  // back, subtracting in fp32 and converting again, fp16 subnormals included
+  // (the default fp16 denormal mode keeps them).
   u4 hw, lw;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const ff2 rv = {r[2 * q], r[2 * q + 1]};
-    const hf2 xv = __builtin_convertvector(rv, hf2);
-    const ff2 xb = __builtin_convertvector(xv, ff2);
-    const ff2 dv = {rv[0] - xb[0], rv[1] - xb[1]};
-    const hf2 yv = __builtin_convertvector(dv, hf2);
-    hw[q] = __builtin_bit_cast(uint32_t, xv);
-    lw[q] = __builtin_bit_cast(uint32_t, yv);
+    const uint32_t hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(rv, hf2));
+    uint32_t lo;
+    asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(lo) : "v"(rv[0]), "v"(hp));
+    asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(lo) : "v"(rv[1]), "v"(hp));
+    hw[q] = hp;
+    lw[q] = lo;
   }
   u4 hg0, hg1, lg0, lg1;
 #pragma unroll
