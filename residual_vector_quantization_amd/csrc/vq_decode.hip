@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx
                                                int64_t nchunks, double* partials, WsHeader* hdr) {
   constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K;
   __shared__ float cb[S][K][DIM];  // unpadded: padding costs this kernel a workgroup per CU
-  __shared__ double red[S + 1][256];
+  __shared__ double red[S + 1][4];  // per-wave sums of a chunk
   for (int q = threadIdx.x; q < S * K * DIM; q += blockDim.x) (&cb[0][0][0])[q] = cb_g[q];
   __syncthreads();
   const int m = blockIdx.y;
@@ -246,16 +246,22 @@ __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx
     // a non-finite weight makes its thread's sum of squares non-finite; finite
     // weights cannot overflow it (|w| < 2^128 and fewer than 2^32 terms)
     nonfinite |= !__builtin_isfinite(acc[S]);
+    // fixed-order reduction (butterfly within each wave, then the 4 waves in
+    // order): a small LDS footprint, so 6 workgroups fit a CU with VQ3R's
+    // 24 KB of codebooks (a 256-entry tree buffer allowed 4)
 #pragma unroll
-    for (int t = 0; t <= S; ++t) red[t][threadIdx.x] = acc[t];
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-      if ((int)threadIdx.x < o)
+    for (int t = 0; t <= S; ++t) {
 #pragma unroll
-        for (int t = 0; t <= S; ++t) red[t][threadIdx.x] += red[t][threadIdx.x + o];
-      __syncthreads();
+      for (int o = 32; o > 0; o >>= 1) acc[t] += __shfl_xor(acc[t], o);
     }
-    if (threadIdx.x <= S) partials[((uint64_t)m * nchunks + c) * (S + 1) + threadIdx.x] = red[threadIdx.x][0];
+    if (lane == 0) {
+#pragma unroll
+      for (int t = 0; t <= S; ++t) red[t][wave] = acc[t];
+    }
+    __syncthreads();
+    if (threadIdx.x <= S)
+      partials[((uint64_t)m * nchunks + c) * (S + 1) + threadIdx.x] =
+          ((red[threadIdx.x][0] + red[threadIdx.x][1]) + red[threadIdx.x][2]) + red[threadIdx.x][3];
     __syncthreads();  // red is reused by the next chunk
   }
   if (nonfinite) flag_status(hdr, ST_NONFINITE);
