@@ -387,11 +387,13 @@ __global__ __launch_bounds__(256) void k_assign_exact(const float* R_cur, float*
 // slots (the first n_assign slots are skipped when the exact pass covered
 // every vector), then c = (float)(((double)S * 2^-F) / n); empty clusters keep
 // their centroid. Block 0 also clears the other parity's queue counter.
+constexpr int UPD_THREADS = 256;  // partial slots summed in parallel per cluster
+
 template <int FMT>
-__global__ __launch_bounds__(64) void k_update(float* C, const long long* partials, int n_assign, int n_slots,
-                                               WsHeader* hdr, int parity, uint32_t cap) {
+__global__ __launch_bounds__(UPD_THREADS) void k_update(float* C, const long long* partials, int n_assign,
+                                                        int n_slots, WsHeader* hdr, int parity, uint32_t cap) {
   constexpr int K = Fmt<FMT>::K;
-  __shared__ long long red[64][DIM + 1];
+  __shared__ long long red[UPD_THREADS][DIM + 1];
   const int j = blockIdx.x;
   const uint32_t nf = hdr->n_flag[parity];
   const bool full = nf > cap;
@@ -405,7 +407,7 @@ __global__ __launch_bounds__(64) void k_update(float* C, const long long* partia
   long long acc[DIM + 1];
 #pragma unroll
   for (int k = 0; k <= DIM; ++k) acc[k] = 0;
-  for (int s = s0 + threadIdx.x; s < n_slots; s += 64) {
+  for (int s = s0 + threadIdx.x; s < n_slots; s += UPD_THREADS) {
     const long long* p = partials + ((size_t)s * K + j) * (DIM + 1);
 #pragma unroll
     for (int k = 0; k <= DIM; ++k) acc[k] += p[k];
@@ -413,12 +415,15 @@ __global__ __launch_bounds__(64) void k_update(float* C, const long long* partia
 #pragma unroll
   for (int k = 0; k <= DIM; ++k) red[threadIdx.x][k] = acc[k];
   __syncthreads();
+  // integer sums: exact in any order
+  for (int o = UPD_THREADS / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o)
+#pragma unroll
+      for (int k = 0; k <= DIM; ++k) red[threadIdx.x][k] += red[threadIdx.x + o][k];
+    __syncthreads();
+  }
   if (threadIdx.x < DIM) {
-    long long S = 0, cnt = 0;
-    for (int q = 0; q < 64; ++q) {
-      S += red[q][threadIdx.x];
-      cnt += red[q][DIM];
-    }
+    const long long S = red[0][threadIdx.x], cnt = red[0][DIM];
     if (cnt > 0) {
       const double m = __ddiv_rn(ldexp(__ll2double_rn(S), -hdr->fbits), __ll2double_rn(cnt));
       C[j * DIM + threadIdx.x] = __double2float_rn(m);
@@ -493,7 +498,7 @@ static hipError_t fit_stage_iters(const FitArgs& a, int t, const float* Rc, floa
                                                       cur ^ 1);
       k_assign_exact<FMT, 0><<<gf, 256, 0, a.stream>>>(Rc, Rn, a.n, C, a.hdr, a.list, a.cap, a.partials, ga, parity,
                                                        cur ^ 1);
-      k_update<FMT><<<K, 64, 0, a.stream>>>(C, a.partials, ga, ga + gf, a.hdr, parity, a.cap);
+      k_update<FMT><<<K, UPD_THREADS, 0, a.stream>>>(C, a.partials, ga, ga + gf, a.hdr, parity, a.cap);
     } else {
       k_assign<FMT, ENG, 1><<<ga, 256, 0, a.stream>>>(Rc, Rn, a.n, C, a.hdr, a.list, a.cap, a.partials, parity,
                                                       cur ^ 1);
