@@ -344,6 +344,85 @@ def test_rel_error_closed_forms():
     assert abs(oracle.rel_error(np.float32([[3, 4]]), np.float32([[0, 4]])) - 0.6) < 1e-15
 
 
+def test_error_sums_closed_forms():
+    # (sum (w - w_hat)^2, sum w^2): both sums exact on dyadic values
+    w = np.float32([[3, 4], [1, -2]])
+    assert oracle.error_sums(w, np.zeros_like(w)) == (30.0, 30.0)
+    assert oracle.error_sums(w, w) == (0.0, 30.0)
+    # the second sum is over w, not w_hat: swapping the operands changes it
+    a, b = np.float32([[1, 1]]), np.float32([[2, 2]])
+    assert oracle.error_sums(a, b) == (2.0, 2.0)
+    assert oracle.error_sums(b, a) == (2.0, 8.0)
+    # constant rows: n d^2 and n c^2
+    n, c, d = 1000, 0.75, 0.125
+    w = np.full((10, 100), c, np.float32)
+    assert oracle.error_sums(w, w - np.float32(d)) == (n * d * d, n * c * c)
+    # every element contributes once (no dropped row or column): a single
+    # nonzero difference anywhere gives exactly its square
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        w = np.zeros((7, 9), np.float32)
+        w_hat = np.zeros_like(w)
+        r, k = rng.integers(7), rng.integers(9)
+        w_hat[r, k] = np.float32(-1.5)
+        assert oracle.error_sums(w, w_hat) == (2.25, 0.0)
+
+
+def _gemv_exact(W, x):
+    """y and sum_k |W_rk x_k| in exact rational arithmetic."""
+    y, s = [], []
+    for row in np.asarray(W, dtype=np.float64):
+        y.append(sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(row, x)))
+        s.append(sum(abs(Fraction(float(a)) * Fraction(float(b))) for a, b in zip(row, x)))
+    return y, s
+
+
+def test_gemv_ref_closed_forms():
+    # one-hot rows: y_r = a_r x_{c_r}, and the condition scale is |a_r x_{c_r}|
+    rng = np.random.default_rng(5)
+    rows, cols = 12, 40
+    W = np.zeros((rows, cols), np.float32)
+    cr = rng.integers(0, cols, rows)
+    a = (rng.integers(-64, 64, rows) / 16.0).astype(np.float32)
+    W[np.arange(rows), cr] = a
+    x = (rng.integers(-32, 32, cols) / 8.0).astype(np.float32)
+    y, s = oracle.gemv_ref(W, x)
+    assert np.array_equal(y, a.astype(np.float64) * x[cr])
+    assert np.array_equal(s, np.abs(a.astype(np.float64) * x[cr]))
+    # rank one u v^T: y = u (v . x), scale = |u| sum |v x|; dyadic values keep fp64 exact
+    u = (rng.integers(-8, 8, rows) / 4.0).astype(np.float32)
+    v = (rng.integers(-8, 8, cols) / 2.0).astype(np.float32)
+    y, s = oracle.gemv_ref(np.outer(u, v).astype(np.float32), x)
+    vx = sum(Fraction(float(p)) * Fraction(float(q)) for p, q in zip(v, x))
+    avx = sum(abs(Fraction(float(p)) * Fraction(float(q))) for p, q in zip(v, x))
+    assert [Fraction(t) for t in y] == [Fraction(float(t)) * vx for t in u]
+    assert [Fraction(t) for t in s] == [abs(Fraction(float(t))) * avx for t in u]
+    # cancellation: y = 0 while the scale keeps every term
+    y, s = oracle.gemv_ref(np.float32([[1, -1, 2, -2]]), np.float32([1, 1, 0.5, 0.5]))
+    assert y[0] == 0.0 and s[0] == 4.0
+    # a non-square matrix against brute force in exact arithmetic (catches a
+    # transposed operand or a dropped row/column)
+    W = (rng.integers(-100, 100, (5, 13)) / 32.0).astype(np.float32)
+    x = (rng.integers(-100, 100, 13) / 64.0).astype(np.float32)
+    y, s = oracle.gemv_ref(W, x)
+    ye, se = _gemv_exact(W, x)
+    assert [Fraction(t) for t in y] == ye and [Fraction(t) for t in s] == se
+
+
+def test_gemv_ref_within_fp64_rounding_of_exact_on_random_inputs():
+    # general fp32 inputs: the fp64 result is within n * 2^-53 * sum |w x| of the
+    # exact rational value (the textbook bound for a length-n fp64 dot product
+    # of exactly representable products)
+    rng = np.random.default_rng(6)
+    W = rng.standard_normal((6, 300)).astype(np.float32)
+    x = rng.standard_normal(300).astype(np.float16).astype(np.float32)
+    y, s = oracle.gemv_ref(W, x)
+    ye, se = _gemv_exact(W, x)
+    for r in range(6):
+        assert abs(Fraction(float(y[r])) - ye[r]) <= Fraction(300, 2 ** 53) * se[r]
+        assert abs(Fraction(float(s[r])) - se[r]) <= Fraction(300, 2 ** 53) * se[r]
+
+
 # ------------------------------------------------------------- RTN
 def test_rtn_grid_exact_and_ties():
     sc = np.float32(np.float16(0.03125))
