@@ -38,11 +38,23 @@ __device__ inline void flag_status(WsHeader* h, uint32_t f) { atomicOr(&h->flags
 // VQ3R: [VQ3R page] §2, 3 stages x 256 entries, 8-bit indices.
 // VQ4P: [VQ3R page] §5, 4 stages x 64 entries, 6-bit indices in the same 3 bytes.
 template <int FMT> struct Fmt;
+// The search keeps one value per group of GS consecutive codewords (see
+// vq_score.hpp); PACK = bits of the lane-local group id carried in a packed
+// value (16 / GS groups per 32-codeword tile and lane: 16 * TILES / GS ids).
+constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+#ifndef VQ_GS_VQ3R
+#define VQ_GS_VQ3R 4
+#endif
+#ifndef VQ_GS_VQ4P
+#define VQ_GS_VQ4P 2
+#endif
 template <> struct Fmt<0> {
-  static constexpr int S = 3, K = 256, BITS = 8, TILES = K / 32, PACK = 7;
+  static constexpr int S = 3, K = 256, BITS = 8, TILES = K / 32, GS = VQ_GS_VQ3R;
+  static constexpr int PACK = ilog2c(16 * TILES / GS);
 };
 template <> struct Fmt<1> {
-  static constexpr int S = 4, K = 64, BITS = 6, TILES = K / 32, PACK = 5;
+  static constexpr int S = 4, K = 64, BITS = 6, TILES = K / 32, GS = VQ_GS_VQ4P;
+  static constexpr int PACK = ilog2c(16 * TILES / GS);
 };
 
 // 3-byte record = little-endian 24-bit word sum_t i_t << (t * BITS).
@@ -94,6 +106,12 @@ __device__ inline void load_vec8(const void* row, int64_t j, float v[8]) {
 }
 
 __device__ inline float f16_bits_to_f32(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+// Non-finite (inf or NaN) test on the bit pattern: an all-ones exponent. The
+// search kernels are compiled with NaN-free floating-point semantics (so that
+// fminf / fmaxf need no sNaN-quieting operand canonicalization), under which a
+// floating-point isfinite may be folded; the bit test cannot be.
+__device__ inline bool is_nonfinite_bits(float x) { return (__float_as_uint(x) & 0x7F800000u) == 0x7F800000u; }
 __device__ inline uint16_t f32_to_f16_bits(float f) { return __half_as_ushort(__float2half_rn(f)); }
 
 // ---------------------------------------------------------------- row scale
@@ -111,7 +129,7 @@ __device__ inline uint16_t wave_row_scale(const void* row, int64_t cols, int lan
     load_vec8<DT>(row, j, v);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      nonfinite |= !__builtin_isfinite(v[k]);
+      nonfinite |= is_nonfinite_bits(v[k]);
       ss += (double)v[k] * (double)v[k];
     }
   }
@@ -189,18 +207,36 @@ __device__ inline int exact_argmin(const float r[8], const float* cb) {
 }
 
 // ---------------------------------------------------------------- certification
-// The fast scorers produce approximate scores s_i ~ ||c_i||^2 - 2<r, c_i>
-// (= d_i - ||r||^2) with |error| <= ALPHA * (||r|| + ||c_i||)^2 + BETA, then
-// replace the low PACK bits of each score by its lane-local candidate index.
-// With p1 <= p2 the two smallest packed scores, w the index carried by p1,
-// d_w the exact fp32 distance to C[w] and rr = ||r||^2, the exhaustive search
-// (the oracle) provably picks w whenever
-//   p2 - p1 > delta = 1.25 * (2^-18 d_w + 2 ALPHA M + 2^(PACK-22) (rr + d_w)
-//                             + 2^-22 sqrt(M) + 2^-120),
-//   M = (2 ||r|| + sqrt(1.001 d_w))^2,
-// because any codeword at least as close as C[w] has ||c|| <= ||r|| + sqrt(d).
-// Vectors that fail the test are re-encoded by the exact search.
-constexpr float ALPHA = 1.52587890625e-05f;  // 2^-16, >= 4x the worst-case analysis
+// The fast scorers produce approximate scores s_j ~ ||c_j||^2 - 2<r, c_j>
+// (= T_j - ||r||^2, T_j the exact real distance) with
+//   |error| <= ALPHA (||r|| + ||c_j||)^2 + 2^-22.5 (||r|| + ||c_j||) + 2^(sigma-25) + 2^-121.
+// For the fp16-split engine: the three split products leave at most
+// 6 2^-22 ||r|| ||c|| + 2^-22.5 (||r|| + ||c||) (fp16-subnormal parts round to
+// 2^-25 absolute), the split norm term at most 1.25 2^-22 ||c||^2 + 2^(sigma-25)
+// (its fp16 lo part is scaled by 2^-sigma), and fp32 accumulation of the 26
+// exact products in any order at most 25 2^-24 (||r|| + ||c||)^2: 2^-18.6 in all,
+// so ALPHA = 2^-16 has a 6x margin. The fp32 engines stay far inside the same
+// bound with sigma = -inf.
+// Codewords are taken in groups of GS (1, 2 or 4) consecutive indices; each
+// group contributes one value, the minimum of its scores with the low PACK
+// bits replaced by a lane-local group id. Let p1 <= p2 be the two smallest
+// packed group values, G* the group of p1, d_j the exact fp32 distances (the
+// fmaf chain of the definition) of the members of G*, w
+// their argmin (lowest index on ties), dmax their maximum and rr = ||r||^2.
+// Then the exhaustive search (the oracle) provably picks w whenever
+//   p2 - p1 > delta = 1.25 * (2^-18 d_w + ALPHA (M_w + M_D) + 2^(PACK-22) (rr + dmax)
+//                             + 2^-21 sqrt(M_D) + 2^-24 2^sigma + 2^-120),
+//   M_w = (2 ||r|| + sqrt(1.001 d_w))^2,  M_D = (2 ||r|| + sqrt(1.001 dmax))^2.
+// Reason: take j outside G* with d_j <= d_w and s* the member of G* with the
+// smallest score (d_s* >= d_w). The chains are within 2^-20.7 relative of the
+// real distances, so T_j - T_s* <= 2^-18 d_w, ||c_j|| <= ||r|| + sqrt(1.001 d_w)
+// and ||c_s*|| <= ||r|| + sqrt(1.001 dmax), hence ||r|| + ||c|| <= sqrt(M_D) for
+// both; their score errors add up to at most ALPHA (M_w + M_D) +
+// 2^-21.5 sqrt(M_D) + 2^(sigma-24) + 2^-120, and the packing moves each of the
+// two values by at most 2^(PACK-23) (rr + dmax). So p2 <= packed value of j's
+// group <= p1 + delta / 1.25. Vectors that fail the test are re-encoded by the
+// exact search.
+constexpr float ALPHA = 1.52587890625e-05f;  // 2^-16
 // Square root inside the bound only: the hardware instruction (within 1 ulp
 // for normal arguments) on an argument raised to at least 2^-100. Its error is
 // of the order of the fp32 roundings of the bound itself, which the factors
@@ -209,31 +245,90 @@ __device__ inline float bound_sqrt(float x) {
   return __builtin_amdgcn_sqrtf(__builtin_fmaxf(x, 7.888609052210118e-31f));
 }
 
+// sig = 2^sigma of the split norm term (0 for the fp32 engines).
 template <int PACK>
-__device__ inline bool certified(float p1, float p2, float rr, float dw) {
-  const float m = 2.0f * bound_sqrt(rr) + bound_sqrt(1.001f * dw);  // sqrt(M)
-  const float M = m * m;
+__device__ inline bool certified(float p1, float p2, float rr, float dw, float dmax, float sig) {
+  const float sr2 = 2.0f * bound_sqrt(rr);
+  const float mw = sr2 + bound_sqrt(1.001f * dw);    // sqrt(M_w)
+  const float md = sr2 + bound_sqrt(1.001f * dmax);  // sqrt(M_D)
   const float pk = (float)(1u << PACK) * 2.384185791015625e-07f;  // 2^(PACK-22)
-  float delta = 3.814697265625e-06f * dw + 2.0f * ALPHA * M + pk * (rr + dw) + 2.384185791015625e-07f * m +
-                7.52316384526264e-37f;
+  float delta = 3.814697265625e-06f * dw;             // 2^-18 d_w
+  delta += ALPHA * (mw * mw + md * md);
+  delta += pk * (rr + dmax);
+  delta += 4.76837158203125e-07f * md;                // 2^-21 sqrt(M_D)
+  delta += 5.9604644775390625e-08f * sig;             // 2^-24 2^sigma
+  delta += 7.52316384526264e-37f;                     // 2^-120
   delta *= 1.25f;
   return (p2 - p1) > delta;
 }
 
-// Packs a lane-local candidate index into the low PACK bits of a score.
+// Packs a lane-local group id into the low PACK bits of a score.
 template <int PACK>
 __device__ inline float pack_score(float s, uint32_t local) {
   return __uint_as_float((__float_as_uint(s) & ~((1u << PACK) - 1u)) | local);
 }
 
 __device__ inline float fmin2(float a, float b) { return __builtin_fminf(a, b); }
+__device__ inline float fmin3(float a, float b, float c) { return __builtin_fminf(__builtin_fminf(a, b), c); }
+__device__ inline float fmax2(float a, float b) { return __builtin_fmaxf(a, b); }
 
 // Top-2 streaming update with two new packed values x, y (m1 <= m2):
 // second smallest of {m1, m2, x, y} = min(m2, med3(m1, x, y)).
 __device__ inline void top2_pair(float& m1, float& m2, float x, float y) {
   float s = __builtin_amdgcn_fmed3f(m1, x, y);
   m2 = fmin2(m2, s);
-  m1 = fmin2(m1, fmin2(x, y));
+  m1 = fmin3(m1, x, y);
+}
+
+// Packed group value of accumulator entries v0 .. v0+GS-1 (GS consecutive
+// codewords of the lane's layout): their minimum (for GS = 4: min3 + min) with
+// the lane-local group id g packed in.
+template <int PACK, int GS, typename A>
+__device__ inline float group_value(const A& acc, int v0, uint32_t g) {
+  float m = acc[v0];
+  if constexpr (GS == 2) m = fmin2(acc[v0], acc[v0 + 1]);
+  if constexpr (GS == 4) m = fmin3(acc[v0], acc[v0 + 1], fmin2(acc[v0 + 2], acc[v0 + 3]));
+  return pack_score<PACK>(m, g);
+}
+
+// First codeword of lane-local group g in half h (accumulator entries
+// v0 = GS * (g mod 16/GS) of tile g / (16/GS)).
+template <int GS>
+__device__ inline int group_first(int g, int h) {
+  constexpr int GPT = 16 / GS;  // groups per tile and lane
+  const int tile = g / GPT, v0 = GS * (g % GPT);
+  return tile * 32 + 8 * (v0 >> 2) + 4 * h + (v0 & 3);
+}
+
+// Exact resolution of the winning group: the exact fp32 distances of its GS
+// codewords j0 .. j0+GS-1 (the fmaf chain of the definition), their argmin with
+// the lowest index on ties, the certificate against the runner-up group value
+// p2 (sig: 2^sigma of the split norm term, 0 for the fp32 engines), and the
+// residual update r <- r - C[w]. rr holds ||r||^2 on entry and
+// ||r'||^2 of the updated residual on return (the winner's exact distance is
+// the same fmaf chain over the same differences). Returns w.
+template <int PACK, int GS>
+__device__ inline int resolve_group(const float (*cb)[DIM], int j0, float r[8], float p1, float p2, float sig,
+                                    float& rr, bool& flag) {
+  float d[GS];
+#pragma unroll
+  for (int u = 0; u < GS; ++u) d[u] = dist8(r, cb[j0 + u]);
+  int wu = 0;
+  float dw = d[0], dmax = d[0];
+#pragma unroll
+  for (int u = 1; u < GS; ++u) {
+    if (d[u] < dw) {  // strictly smaller: ties keep the lower index
+      dw = d[u];
+      wu = u;
+    }
+    dmax = __builtin_fmaxf(dmax, d[u]);
+  }
+  flag |= !certified<PACK>(p1, p2, rr, dw, dmax, sig);
+  const float* c = cb[j0 + wu];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r[k] = r[k] - c[k];
+  rr = dw;
+  return j0 + wu;
 }
 
 }  // namespace vqk

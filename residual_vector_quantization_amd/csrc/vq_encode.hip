@@ -35,21 +35,22 @@ __global__ __launch_bounds__(256) void k_row_scales(const void* W, int64_t rows,
 
 // ------------------------------------------------------------------ encode
 // One wave per row: the row scale, then groups of vectors through all
-// stages (64 per group with the fp16-split engine, one per lane; 32 with the
-// others, both half-waves working on the same vector). Certified vectors get
-// their final record; the others are queued for the exact pass
+// stages (64 per group with the matrix-core engines, one per lane; 32 with the
+// VALU engine, both half-waves working on the same vector). Certified vectors
+// get their final record; the others are queued for the exact pass
 // (k_encode_exact).
-// With the fp16-split engine 8 waves per workgroup share one copy of the LDS
-// tables (60 KB for VQ3R), so two workgroups give each SIMD 4 waves to
-// interleave MFMA and VALU work; the other engines use 4 waves.
-constexpr int enc_waves(int eng) { return eng == ENG_F16X ? 8 : 4; }
+// With the matrix-core engines 8 waves per workgroup share one copy of the LDS
+// tables (60 KB for VQ3R fp16-split, 72 KB fp32), so two workgroups give each
+// SIMD 4 waves to interleave MFMA and VALU work; the VALU engine uses 4 waves.
+constexpr bool two_groups(int eng) { return eng == ENG_F16X || eng == ENG_F32; }
+constexpr int enc_waves(int eng) { return two_groups(eng) ? 8 : 4; }
 
 template <int FMT, int ENG, int DT>
 __global__ __launch_bounds__(64 * enc_waves(ENG), enc_waves(ENG) / 2) void k_encode(const void* W, int64_t rows, int64_t cols, const float* cb_g,
                                                    uint8_t* idx, uint16_t* scales, WsHeader* hdr, uint32_t* list,
                                                    uint32_t cap) {
   constexpr int S = Fmt<FMT>::S;
-  constexpr bool X2 = ENG == ENG_F16X;
+  constexpr bool X2 = two_groups(ENG);
   constexpr int GV = X2 ? 64 : 32;  // vectors per group
   constexpr int NWV = enc_waves(ENG);
   __shared__ SearchLds<FMT, ENG, S> L;
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(64 * enc_waves(ENG), enc_waves(ENG) / 2) void k_enc
 #pragma unroll 1
       for (int t = 0; t < S; ++t) {
         int w;
-        if constexpr (X2) w = search_stage_x2<FMT, S, true>(L, t, r, lane, fl, rr);
+        if constexpr (X2) w = search_stage_x2<FMT, ENG, S, true>(L, t, r, lane, fl, rr);
         else w = search_stage<FMT, ENG, S>(L, t, r, lane, fl);
         word |= (uint32_t)w << (t * Fmt<FMT>::BITS);
       }
@@ -243,13 +244,13 @@ __device__ inline void flush_accum(FitAccum<K>& A, long long* partials, int slot
 // fixed-point coordinates to the block's cluster sums. MODE 1 (after the last
 // update): certified vectors write their residual to R_next. Vectors that fail
 // certification are queued for k_assign_exact. Groups of 64 vectors (one per
-// lane) with the fp16-split engine, 32 with the others.
+// lane) with the matrix-core engines, 32 with the VALU engine.
 template <int FMT, int ENG, int MODE>
 __global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_next, int64_t n, const float* C,
                                                    WsHeader* hdr, uint32_t* list, uint32_t cap,
                                                    long long* partials, int parity, int nxt) {
   constexpr int K = Fmt<FMT>::K;
-  constexpr bool X2 = ENG == ENG_F16X;
+  constexpr bool X2 = two_groups(ENG);
   constexpr int GV = X2 ? 64 : 32;
   __shared__ SearchLds<FMT, ENG, 1> L;
   __shared__ FitAccum<K> A;
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_
     bool fl = false;
     int w;
     float rr;
-    if constexpr (X2) w = search_stage_x2<FMT, 1, false>(L, 0, r, lane, fl, rr);
+    if constexpr (X2) w = search_stage_x2<FMT, ENG, 1, false>(L, 0, r, lane, fl, rr);
     else w = search_stage<FMT, ENG, 1>(L, 0, r, lane, fl);
     const bool ok = valid && !fl;
     if (MODE == 0) {

@@ -1,13 +1,17 @@
-// Nearest-codeword search for 32 vectors at a time on one wave (gfx950):
-// approximate scores from one of three engines, a lane-local top-2 with the
-// candidate index packed into each score, a merge of the two half-waves and
+// Nearest-codeword search on one wave (gfx950): approximate scores from one of
+// three engines, one value per group of GS consecutive codewords (the group's
+// minimum score with the group id packed into its low bits; GS per format,
+// Fmt<>::GS), a lane-local top-2 of those values, a merge of the two
+// half-waves, then the exact distances of the winning group's codewords and
 // the certification test of vq_device.hpp.
 //
 // Lane layout (shared by all engines): lane = 32*h + j holds the full 8-dim
 // residual of vector j of the group; its candidates are the codewords
 //   i = 32*tile + 8*(v/4) + 4*h + (v%4),  tile < K/32, v < 16,
 // which is exactly the accumulator layout of the 32x32 MFMA instructions with
-// codewords on M and vectors on N. Lane-local candidate id = 16*tile + v.
+// codewords on M and vectors on N. Accumulator entries v0 .. v0+GS-1 (v0 a
+// multiple of GS) of a tile are GS consecutive codewords: lane-local group id
+// g = (16/GS)*tile + v0/GS (group_first gives its first codeword).
 #pragma once
 #include "vq_device.hpp"
 
@@ -62,7 +66,7 @@ __device__ inline void build_tables(SearchLds<FMT, ENG, NST>& L, const float* cb
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       L.cb[t][i][k] = c[k];
-      bad |= !(__builtin_fabsf(c[k]) <= 2048.0f);  // also catches NaN
+      bad |= (__float_as_uint(c[k]) & 0x7FFFFFFFu) > 0x45000000u;  // |c| > 2048, inf or NaN (bit test)
       n += (double)c[k] * (double)c[k];
     }
     float nf = __double2float_rn(n);
@@ -116,11 +120,20 @@ __device__ inline void build_tables(SearchLds<FMT, ENG, NST>& L, const float* cb
   }
 }
 
-// Lane-local top-2 of the packed approximate scores for stage t.
+// ||r||^2 as the fmaf chain over k = 0..7 starting from 0.
+__device__ inline float norm2_8(const float r[8]) {
+  float rr = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) rr = __builtin_fmaf(r[k], r[k], rr);
+  return rr;
+}
+
+// Lane-local top-2 of the packed group values for stage t (one group of 32
+// vectors per wave; both half-waves hold the same vector).
 template <int FMT, int ENG, int NST>
 __device__ inline void lane_top2(const SearchLds<FMT, ENG, NST>& L, int t, const float r[8], int lane,
                                  float& m1, float& m2) {
-  constexpr int TILES = Fmt<FMT>::TILES, PACK = Fmt<FMT>::PACK;
+  constexpr int TILES = Fmt<FMT>::TILES, PACK = Fmt<FMT>::PACK, GS = Fmt<FMT>::GS, GPT = 16 / GS;
   const int h = lane >> 5, i = lane & 31;
   m1 = __builtin_inff();
   m2 = __builtin_inff();
@@ -142,8 +155,9 @@ __device__ inline void lane_top2(const SearchLds<FMT, ENG, NST>& L, int t, const
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa0[tile * 32 + i], b0, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa1[tile * 32 + i], b1, acc, 0, 0, 0);
 #pragma unroll
-      for (int v = 0; v < 16; v += 2)
-        top2_pair(m1, m2, pack_score<PACK>(acc[v], tile * 16 + v), pack_score<PACK>(acc[v + 1], tile * 16 + v + 1));
+      for (int q = 0; q < GPT; q += 2)
+        top2_pair(m1, m2, group_value<PACK, GS>(acc, GS * q, tile * GPT + q),
+                  group_value<PACK, GS>(acc, GS * q + GS, tile * GPT + q + 1));
     }
   } else if constexpr (ENG == ENG_F32) {
     float b[5];
@@ -157,8 +171,9 @@ __device__ inline void lane_top2(const SearchLds<FMT, ENG, NST>& L, int t, const
       for (int s = 0; s < 5; ++s)
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(L.tab[t].a[s][h][tile * 32 + i], b[s], acc, 0, 0, 0);
 #pragma unroll
-      for (int v = 0; v < 16; v += 2)
-        top2_pair(m1, m2, pack_score<PACK>(acc[v], tile * 16 + v), pack_score<PACK>(acc[v + 1], tile * 16 + v + 1));
+      for (int q = 0; q < GPT; q += 2)
+        top2_pair(m1, m2, group_value<PACK, GS>(acc, GS * q, tile * GPT + q),
+                  group_value<PACK, GS>(acc, GS * q + GS, tile * GPT + q + 1));
     }
   } else {
     float nr[8];
@@ -177,122 +192,150 @@ __device__ inline void lane_top2(const SearchLds<FMT, ENG, NST>& L, int t, const
         acc[v] = s;
       }
 #pragma unroll
-      for (int v = 0; v < 16; v += 2)
-        top2_pair(m1, m2, pack_score<PACK>(acc[v], tile * 16 + v), pack_score<PACK>(acc[v + 1], tile * 16 + v + 1));
+      for (int q = 0; q < GPT; q += 2)
+        top2_pair(m1, m2, group_value<PACK, GS>(acc, GS * q, tile * GPT + q),
+                  group_value<PACK, GS>(acc, GS * q + GS, tile * GPT + q + 1));
     }
   }
 }
 
-// Full stage: approximate search, merge of the half-waves, exact distance to
-// the winner, certification and residual update. Returns the winner index.
+// Merge of the two half-waves' top-2 (q0, n0: the low half's set; q1, n1: the
+// high half's) into the overall p1 <= p2 and the first codeword of p1's group.
+template <int PACK, int GS>
+__device__ inline int merge_halves(float q0, float n0, float q1, float n1, float& p1, float& p2) {
+  p1 = fmin2(q0, q1);
+  p2 = fmin2(fmax2(q0, q1), fmin2(n0, n1));
+  const uint32_t pb = __float_as_uint(p1);
+  const int hw = (pb == __float_as_uint(q0)) ? 0 : 1;
+  return group_first<GS>((int)(pb & ((1u << PACK) - 1u)), hw);
+}
+
+// Full stage (one group of 32 vectors per wave): approximate search, merge of
+// the half-waves, exact resolution of the winning group, certification and
+// residual update. Returns the winner index.
 template <int FMT, int ENG, int NST>
 __device__ inline int search_stage(const SearchLds<FMT, ENG, NST>& L, int t, float r[8], int lane, bool& flag) {
-  constexpr int PACK = Fmt<FMT>::PACK;
+  constexpr int PACK = Fmt<FMT>::PACK, GS = Fmt<FMT>::GS;
   float m1, m2;
   lane_top2<FMT, ENG, NST>(L, t, r, lane, m1, m2);
   const int h = lane >> 5;
   const float o1 = __shfl_xor(m1, 32);
   const float o2 = __shfl_xor(m2, 32);
-  const float p1 = fmin2(m1, o1);
-  const float p2 = fmin2(__builtin_fmaxf(m1, o1), fmin2(m2, o2));
-  const uint32_t half0 = __float_as_uint(h ? o1 : m1);
-  const uint32_t pb = __float_as_uint(p1);
-  const int hw = (pb == half0) ? 0 : 1;
-  const uint32_t loc = pb & ((1u << PACK) - 1u);
-  const int tile = (int)(loc >> 4), v = (int)(loc & 15u);
-  const int w = tile * 32 + 8 * (v >> 2) + 4 * hw + (v & 3);
-  const float* c = L.cb[t][w];
-  float d = 0.0f, rr = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    float e = r[k] - c[k];
-    d = __builtin_fmaf(e, e, d);
-    rr = __builtin_fmaf(r[k], r[k], rr);
-    r[k] = e;
-  }
-  flag |= !certified<PACK>(p1, p2, rr, d);
-  return w;
+  float p1, p2;
+  const int j0 = h ? merge_halves<PACK, GS>(o1, o2, m1, m2, p1, p2) : merge_halves<PACK, GS>(m1, m2, o1, o2, p1, p2);
+  float rr = norm2_8(r);
+  return resolve_group<PACK, GS>(L.cb[t], j0, r, p1, p2, ENG == ENG_F16X ? L.sig[t] : 0.0f, rr, flag);
 }
 
-// ||r||^2 as the fmaf chain over k = 0..7 starting from 0.
-__device__ inline float norm2_8(const float r[8]) {
-  float rr = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) rr = __builtin_fmaf(r[k], r[k], rr);
-  return rr;
-}
-
-// Two groups per pass (fp16-split engine): lane (i, h) owns vector i of group
-// h, so the per-vector work after the search (merge, exact distance,
-// certification, residual update, next fp16 split) serves 64 vectors per wave
-// instruction. The matrix-core operands of group g need that group's residual
-// in both half-waves (the K dimension is split across them); one
+// Two groups per pass (the matrix-core engines): lane (i, h) owns vector i of
+// group h, so the per-vector work after the search (merge, exact resolution,
+// certification, residual update, next operand set-up) serves 64 vectors per
+// wave instruction. The matrix-core operands of group g need that group's
+// residual in both half-waves (the K dimension is split across them); one
 // v_permlane32_swap per register broadcasts each half's values to both
 // halves. Returns the winner for the lane's own vector.
-// rr: on return ||r'||^2 of the updated residual r' = r - C[w] (the fmaf chain
-// over k = 0..7 from 0). That is the exact distance d_w itself: the same chain
-// over the same values r_k - c_k, so a later stage gets its ||r||^2 without
-// recomputing it. RR_IN: rr holds ||r||^2 on entry; otherwise it is computed
-// here, next to d_w.
-template <int FMT, int NST, bool RR_IN>
-__device__ inline int search_stage_x2(const SearchLds<FMT, ENG_F16X, NST>& L, int t, float r[8], int lane,
+// rr: ||r||^2 on entry when RR_IN (else computed here); on return ||r'||^2 of
+// the updated residual r' = r - C[w] (the winner's exact distance: the same
+// fmaf chain over the same differences), so a later stage does not recompute it.
+template <int FMT, int ENG, int NST, bool RR_IN>
+__device__ inline int search_stage_x2(const SearchLds<FMT, ENG, NST>& L, int t, float r[8], int lane,
                                       bool& flag, float& rr) {
-  constexpr int TILES = Fmt<FMT>::TILES, PACK = Fmt<FMT>::PACK;
+  static_assert(ENG == ENG_F16X || ENG == ENG_F32, "two-group search runs on the matrix-core engines");
+  constexpr int TILES = Fmt<FMT>::TILES, PACK = Fmt<FMT>::PACK, GS = Fmt<FMT>::GS, GPT = 16 / GS;
   const int h = lane >> 5, i = lane & 31;
-  // own residual split into fp16 hi + lo (pairs converted together; the -2 of
-  // the score sits in the codebook tables)
-  typedef _Float16 hf2 __attribute__((ext_vector_type(2)));
-  typedef float ff2 __attribute__((ext_vector_type(2)));
-  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-  // lo = RN16(r - hi) in one mixed-precision fma per element: v_fma_mix
-  // forms r * 1 - hi exactly and rounds once to fp16 (into the low / high
-  // half). r - hi is itself exact in fp32 (a rounding error of r, a multiple
-  // of r's fp32 ulp below 2^13 of them), so these are the bits of converting hi
-  // back, subtracting in fp32 and converting again, fp16 subnormals included
-  // (the default fp16 denormal mode keeps them).
-  u4 hw, lw;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const ff2 rv = {r[2 * q], r[2 * q + 1]};
-    const uint32_t hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(rv, hf2));
-    uint32_t lo;
-    asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(lo) : "v"(rv[0]), "v"(hp));
-    asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(lo) : "v"(rv[1]), "v"(hp));
-    hw[q] = hp;
-    lw[q] = lo;
-  }
-  u4 hg0, hg1, lg0, lg1;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    // swap(x, x): result 0 = the low half's x in both halves, result 1 = the high half's
-    const auto a = __builtin_amdgcn_permlane32_swap(hw[q], hw[q], false, false);
-    hg0[q] = a[0];
-    hg1[q] = a[1];
-    const auto b = __builtin_amdgcn_permlane32_swap(lw[q], lw[q], false, false);
-    lg0[q] = b[0];
-    lg1[q] = b[1];
-  }
-  h8 cst = {};
-  cst[0] = (_Float16)L.sig[t];
-  cst[1] = cst[0];
-  const h8 b0g0 = __builtin_bit_cast(h8, hg0), b0g1 = __builtin_bit_cast(h8, hg1);
-  const h8 b1g0 = h ? cst : __builtin_bit_cast(h8, lg0);
-  const h8 b1g1 = h ? cst : __builtin_bit_cast(h8, lg1);
-  const h8* pa0 = h ? L.tab[t].lo : L.tab[t].hi;
-  const h8* pa1 = h ? L.tab[t].nrm : L.tab[t].hi;
   float m1a = __builtin_inff(), m2a = __builtin_inff(), m1b = __builtin_inff(), m2b = __builtin_inff();
+  if constexpr (ENG == ENG_F16X) {
+    // own residual split into fp16 hi + lo (pairs converted together; the -2 of
+    // the score sits in the codebook tables)
+    typedef _Float16 hf2 __attribute__((ext_vector_type(2)));
+    typedef float ff2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    // lo = RN16(r - hi) in one mixed-precision fma per element: v_fma_mix
+    // forms r * 1 - hi exactly and rounds once to fp16 (into the low / high
+    // half). r - hi is itself exact in fp32 (a rounding error of r, a multiple
+    // of r's fp32 ulp below 2^13 of them), so these are the bits of converting hi
+    // back, subtracting in fp32 and converting again, fp16 subnormals included
+    // (the default fp16 denormal mode keeps them).
+    u4 hw, lw;
 #pragma unroll
-  for (int tile = 0; tile < TILES; ++tile) {
-    const h8 a0 = pa0[tile * 32 + i], a1 = pa1[tile * 32 + i];
-    f16v acc0 = {}, acc1 = {};
-    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0g0, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0g1, acc1, 0, 0, 0);
-    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1g0, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1g1, acc1, 0, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+      const ff2 rv = {r[2 * q], r[2 * q + 1]};
+      const uint32_t hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(rv, hf2));
+      uint32_t lo;
+      asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(lo) : "v"(rv[0]), "v"(hp));
+      asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(lo) : "v"(rv[1]), "v"(hp));
+      hw[q] = hp;
+      lw[q] = lo;
+    }
+    u4 hg0, hg1, lg0, lg1;
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      top2_pair(m1a, m2a, pack_score<PACK>(acc0[v], tile * 16 + v), pack_score<PACK>(acc0[v + 1], tile * 16 + v + 1));
-      top2_pair(m1b, m2b, pack_score<PACK>(acc1[v], tile * 16 + v), pack_score<PACK>(acc1[v + 1], tile * 16 + v + 1));
+    for (int q = 0; q < 4; ++q) {
+      // swap(x, x): result 0 = the low half's x in both halves, result 1 = the high half's
+      const auto a = __builtin_amdgcn_permlane32_swap(hw[q], hw[q], false, false);
+      hg0[q] = a[0];
+      hg1[q] = a[1];
+      const auto b = __builtin_amdgcn_permlane32_swap(lw[q], lw[q], false, false);
+      lg0[q] = b[0];
+      lg1[q] = b[1];
+    }
+    h8 cst = {};
+    cst[0] = (_Float16)L.sig[t];
+    cst[1] = cst[0];
+    const h8 b0g0 = __builtin_bit_cast(h8, hg0), b0g1 = __builtin_bit_cast(h8, hg1);
+    const h8 b1g0 = h ? cst : __builtin_bit_cast(h8, lg0);
+    const h8 b1g1 = h ? cst : __builtin_bit_cast(h8, lg1);
+    const h8* pa0 = h ? L.tab[t].lo : L.tab[t].hi;
+    const h8* pa1 = h ? L.tab[t].nrm : L.tab[t].hi;
+#pragma unroll
+    for (int tile = 0; tile < TILES; ++tile) {
+      const h8 a0 = pa0[tile * 32 + i], a1 = pa1[tile * 32 + i];
+      f16v acc0 = {}, acc1 = {};
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0g0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0g1, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1g0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1g1, acc1, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < GPT; q += 2) {
+        top2_pair(m1a, m2a, group_value<PACK, GS>(acc0, GS * q, tile * GPT + q),
+                  group_value<PACK, GS>(acc0, GS * q + GS, tile * GPT + q + 1));
+        top2_pair(m1b, m2b, group_value<PACK, GS>(acc1, GS * q, tile * GPT + q),
+                  group_value<PACK, GS>(acc1, GS * q + GS, tile * GPT + q + 1));
+      }
+    }
+  } else {
+    // fp32 matrix cores (32x32x2): step s < 4 contracts dims 2s (low half) and
+    // 2s+1 (high half), step 4 adds ||c||^2. swap(a = r[2s], b = r[2s+1]) gives
+    // result 0 = [low half's r[2s] | low half's r[2s+1]] = group 0's operand and
+    // result 1 = [high half's r[2s] | high half's r[2s+1]] = group 1's.
+    float bg0[4], bg1[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(-2.0f * r[2 * s]),
+                                                       __float_as_uint(-2.0f * r[2 * s + 1]), false, false);
+      bg0[s] = __uint_as_float(sw[0]);
+      bg1[s] = __uint_as_float(sw[1]);
+    }
+    const float b4 = h ? 0.0f : 1.0f;
+#pragma unroll
+    for (int tile = 0; tile < TILES; ++tile) {
+      float a[5];
+#pragma unroll
+      for (int s = 0; s < 5; ++s) a[s] = L.tab[t].a[s][h][tile * 32 + i];
+      f16v acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], bg0[s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], bg1[s], acc1, 0, 0, 0);
+      }
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[4], b4, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[4], b4, acc1, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < GPT; q += 2) {
+        top2_pair(m1a, m2a, group_value<PACK, GS>(acc0, GS * q, tile * GPT + q),
+                  group_value<PACK, GS>(acc0, GS * q + GS, tile * GPT + q + 1));
+        top2_pair(m1b, m2b, group_value<PACK, GS>(acc1, GS * q, tile * GPT + q),
+                  group_value<PACK, GS>(acc1, GS * q + GS, tile * GPT + q + 1));
+      }
     }
   }
   // merge: for the lane's own group, q0 = top over the half-0 codeword set,
@@ -300,28 +343,11 @@ __device__ inline int search_stage_x2(const SearchLds<FMT, ENG_F16X, NST>& L, in
   // b of the low half], result 1 = [a of the high half, b of the high half])
   const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1a), __float_as_uint(m1b), false, false);
   const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m2a), __float_as_uint(m2b), false, false);
-  const float q0 = __uint_as_float(s1[0]), q1 = __uint_as_float(s1[1]);
-  const float n0 = __uint_as_float(s2[0]), n1 = __uint_as_float(s2[1]);
-  const float p1 = fmin2(q0, q1);
-  const float p2 = fmin2(__builtin_fmaxf(q0, q1), fmin2(n0, n1));
-  const uint32_t pb = __float_as_uint(p1);
-  const int hw_ = (pb == __float_as_uint(q0)) ? 0 : 1;
-  const uint32_t loc = pb & ((1u << PACK) - 1u);
-  const int tl = (int)(loc >> 4), v = (int)(loc & 15u);
-  const int w = tl * 32 + 8 * (v >> 2) + 4 * hw_ + (v & 3);
-  const float* c = L.cb[t][w];
-  float d = 0.0f;
-  if constexpr (!RR_IN) rr = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    float e = r[k] - c[k];
-    d = __builtin_fmaf(e, e, d);
-    if constexpr (!RR_IN) rr = __builtin_fmaf(r[k], r[k], rr);
-    r[k] = e;
-  }
-  flag |= !certified<PACK>(p1, p2, rr, d);
-  rr = d;
-  return w;
+  float p1, p2;
+  const int j0 = merge_halves<PACK, GS>(__uint_as_float(s1[0]), __uint_as_float(s2[0]), __uint_as_float(s1[1]),
+                                    __uint_as_float(s2[1]), p1, p2);
+  if constexpr (!RR_IN) rr = norm2_8(r);
+  return resolve_group<PACK, GS>(L.cb[t], j0, r, p1, p2, ENG == ENG_F16X ? L.sig[t] : 0.0f, rr, flag);
 }
 
 // Per-wave staging of flagged vector ids in LDS. The ids of a wave gather in
