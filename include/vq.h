@@ -171,42 +171,63 @@ int vq4p_decode(const uint8_t* idx, const uint16_t* scales, const float* codeboo
  * deterministic (fixed summation order) and within fp32 rounding of the
  * decoded product.
  *
- * The GEMV reads its indices in a runtime layout that vq_gemv_pack() builds
- * once from the stored [rows][cols/8][3] records (like loading a container):
- * blocks of 16 column slices by 64-row groups,
- * each group's records interleaved in 12-byte chunks of 4 records per row
- * and each row's slices rotated by its position in the group.
- * vq_gemv_packed_size() gives the bytes of one packed expert (rows are
- * padded to a multiple of 64 and slices to a multiple of 16 with zeros).
+ * Two entry points, same result:
+ *   vq_dequant_gemv / vq3r_dequant_gemv / vq4p_dequant_gemv read the stored
+ *     records ([rows][cols/8][3], as vq_encode writes them). Each call lists
+ *     the distinct routed experts on the device, copies just those into the
+ *     workspace in the GEMV layout below, and runs the GEMV on the copies
+ *     (about three times the record traffic of the packed call).
+ *   vq_dequant_gemv_packed reads experts already in the GEMV layout, built
+ *     once with vq_gemv_pack (like loading a container into memory): the path
+ *     for repeated decode steps.
+ * GEMV layout: blocks of 16 column slices by 64-row groups, each group's
+ * records interleaved in 12-byte chunks of 4 records per row and each row's
+ * slices rotated by its position in the group; vq_gemv_packed_size() gives the
+ * bytes of one packed expert (rows padded to a multiple of 64 and slices to a
+ * multiple of 16 with zeros).
+ *
+ * Arguments of both:
+ * idx / packed  base of the experts; expert e at base + e*expert_stride bytes
+ *            (stored: expert_stride >= rows*cols/8*3; packed: >=
+ *            vq_gemv_packed_size and a multiple of 4; both when n_experts > 1)
+ * scales     base of the row scales; expert e at scales + e*scale_stride
+ * n_experts  number of experts behind the bases: a route id outside
+ *            [0, n_experts) gives y = 0 for that slot and flags a data error
+ *            (no expert is read out of bounds)
+ * x          fp16 bit patterns [ntok][cols];  route int32 [ntok][topk]
+ * y          out fp32 [ntok][topk][rows]
+ * ntok * topk < 65536.
+ * Workspace: vq_gemv_workspace_size(format, rows, cols, ntok, topk, n_experts)
+ * for the stored call (it holds the packed copies of up to
+ * min(ntok*topk, n_experts) experts), vq_gemv_packed_workspace_size(...) for
+ * the packed call.
  *
  * vq_gemv_pack: idx = n_experts consecutive [rows][cols/8][3] tensors;
  *               packed out = n_experts consecutive packed experts of
  *               vq_gemv_packed_size() bytes each (4-byte aligned).
- * vq_dequant_gemv:
- * packed     base of the packed experts; expert e at packed + e*expert_stride
- *            bytes (expert_stride >= vq_gemv_packed_size, multiple of 4)
- * scales     base of the row scales; expert e at scales + e*scale_stride
- * x          fp16 bit patterns [ntok][cols];  route int32 [ntok][topk]
- * y          out fp32 [ntok][topk][rows]; a route id outside [0, n_experts)
- *            gives y = 0 for that slot and flags a data error
- * Workspace: vq_gemv_workspace_size(format, rows, cols, ntok, topk).
  * ---------------------------------------------------------------------- */
-size_t vq_gemv_packed_size(int format, int64_t rows, int64_t cols);
-int vq_gemv_pack(int format, const uint8_t* idx, int64_t rows, int64_t cols, int64_t n_experts, uint8_t* packed,
-                 void* stream);
-size_t vq_gemv_workspace_size(int format, int64_t rows, int64_t cols, int32_t ntok, int32_t topk);
-int vq_dequant_gemv(int format, const uint8_t* packed, int64_t expert_stride, const uint16_t* scales,
+size_t vq_gemv_workspace_size(int format, int64_t rows, int64_t cols, int32_t ntok, int32_t topk,
+                              int32_t n_experts);
+int vq_dequant_gemv(int format, const uint8_t* idx, int64_t expert_stride, const uint16_t* scales,
                     int64_t scale_stride, const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts,
                     const uint16_t* x, int32_t ntok, const int32_t* route, int32_t topk, float* y,
                     void* workspace, size_t ws_bytes, void* stream);
-int vq3r_dequant_gemv(const uint8_t* packed, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
+int vq3r_dequant_gemv(const uint8_t* idx, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
                       const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts, const uint16_t* x,
                       int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace, size_t ws_bytes,
                       void* stream);
-int vq4p_dequant_gemv(const uint8_t* packed, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
+int vq4p_dequant_gemv(const uint8_t* idx, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
                       const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts, const uint16_t* x,
                       int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace, size_t ws_bytes,
                       void* stream);
+size_t vq_gemv_packed_size(int format, int64_t rows, int64_t cols);
+int vq_gemv_pack(int format, const uint8_t* idx, int64_t rows, int64_t cols, int64_t n_experts, uint8_t* packed,
+                 void* stream);
+size_t vq_gemv_packed_workspace_size(int format, int64_t rows, int64_t cols, int32_t ntok, int32_t topk);
+int vq_dequant_gemv_packed(int format, const uint8_t* packed, int64_t expert_stride, const uint16_t* scales,
+                           int64_t scale_stride, const float* codebooks, int64_t rows, int64_t cols,
+                           int32_t n_experts, const uint16_t* x, int32_t ntok, const int32_t* route, int32_t topk,
+                           float* y, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Batched dequantize-GEMM for prompt processing ([VQ3R page] §1: every token
@@ -273,17 +294,22 @@ int vq_ttp_error(const void* W, int dtype, const uint8_t* codes, const uint16_t*
  * For n_mats consecutive matrices (matrix m at W + m*rows*cols elements,
  * idx + m*rows*cols/8*3 bytes, scales + m*rows) writes fp64
  * sums[m][t] = sum (w - w_hat_{t+1})^2 for t = 0..stages-1 (w_hat_t = the
- * partial reconstruction after t stages) and sums[m][stages] = sum w^2.
- * sums: device fp64 [n_mats][stages+1]. The sums of a matrix are added in an
- * order fixed by its row count (partials per 16-row chunk, added in chunk
- * order), so they are bit-identical whether the matrix is passed alone or
- * together with others.
+ * partial reconstruction after t stages) and sums[m][stages] = sum w^2, and
+ * from them the metric itself:
+ *   rel[m][t]   = sqrt(sums[m][t] / sums[m][stages])            (per matrix)
+ *   rel_all[t]  = sqrt(sum_m sums[m][t] / sum_m sums[m][stages]) (all matrices)
+ * (correctly rounded fp64 division and square root; 0 for a zero matrix
+ * reconstructed as zeros). sums: device fp64 [n_mats][stages+1]; rel: device
+ * fp64 [n_mats][stages] or NULL; rel_all: device fp64 [stages] or NULL. The
+ * sums of a matrix are added in an order fixed by its row count (partials per
+ * 16-row chunk, added in chunk order), so they are bit-identical whether the
+ * matrix is passed alone or together with others.
  * Workspace: vq_error_workspace_size(format, n_mats, rows, cols).
  * ---------------------------------------------------------------------- */
 size_t vq_error_workspace_size(int format, int64_t n_mats, int64_t rows, int64_t cols);
 int vq_error(int format, const void* W, int dtype, const uint8_t* idx, const uint16_t* scales,
-             const float* codebooks, int64_t n_mats, int64_t rows, int64_t cols, double* sums, void* workspace,
-             size_t ws_bytes, void* stream);
+             const float* codebooks, int64_t n_mats, int64_t rows, int64_t cols, double* sums, double* rel,
+             double* rel_all, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * MXFP4 quantize-dequantize of a [rows][cols] matrix (the MXFP4 source format
@@ -295,6 +321,15 @@ int vq_error(int format, const void* W, int dtype, const uint8_t* idx, const uin
  * ---------------------------------------------------------------------- */
 int vq_mxfp4_qdq(const void* W, int dtype, int64_t rows, int64_t cols, float* out, void* workspace,
                  size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Bandwidth reference (a measurement helper, not a step of the method): a plain
+ * coalesced streaming read of nbytes (a multiple of 16; src 16-byte aligned),
+ * the read floor that the dequant-GEMV's HBM rate is compared with. out: one
+ * device uint32, written only for data whose XOR of all 32-bit words equals
+ * 0x9E3779B9 (the read cannot be skipped).
+ * ---------------------------------------------------------------------- */
+int vq_stream_read(const void* src, size_t nbytes, uint32_t* out, void* stream);
 
 #ifdef __cplusplus
 }

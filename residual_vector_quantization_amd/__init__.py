@@ -17,11 +17,12 @@ import numpy as np
 
 __all__ = [
     "VQError", "lib", "FORMATS", "ENGINES", "stages_entries",
-    "encode", "decode", "fit_codebooks", "gemv_pack", "dequant_gemv", "error_sums", "rel_errors", "mxfp4_qdq",
-    "encode_workspace", "fit_workspace", "gemv_workspace", "error_workspace", "read_status",
+    "encode", "decode", "fit_codebooks", "gemv_pack", "dequant_gemv", "dequant_gemv_packed", "error_sums",
+    "rel_errors", "mxfp4_qdq", "encode_workspace", "fit_workspace", "gemv_workspace", "gemv_packed_workspace",
+    "error_workspace", "read_status",
     "container_layout", "crc32", "write_container", "container_info", "read_container", "load_container",
     "verify_container", "convert_layer", "dequant_gemm", "gemm_workspace",
-    "ttp_quantize", "ttp_dequantize", "ttp_error_sums",
+    "ttp_quantize", "ttp_dequantize", "ttp_error_sums", "stream_read",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,9 +78,12 @@ def lib():
         "vq4p_decode": ([P, P, P, L64, L64, P, P], I),
         "vq_gemv_packed_size": ([I, L64, L64], SZ),
         "vq_gemv_pack": ([I, P, L64, L64, L64, P, P], I),
-        "vq_gemv_workspace_size": ([I, L64, L64, ctypes.c_int32, ctypes.c_int32], SZ),
+        "vq_gemv_workspace_size": ([I, L64, L64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32], SZ),
+        "vq_gemv_packed_workspace_size": ([I, L64, L64, ctypes.c_int32, ctypes.c_int32], SZ),
         "vq_dequant_gemv": ([I, P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32, P,
                              ctypes.c_int32, P, P, SZ, P], I),
+        "vq_dequant_gemv_packed": ([I, P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32, P,
+                                    ctypes.c_int32, P, P, SZ, P], I),
         "vq3r_dequant_gemv": ([P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32, P,
                                ctypes.c_int32, P, P, SZ, P], I),
         "vq4p_dequant_gemv": ([P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32, P,
@@ -92,8 +96,9 @@ def lib():
         "vq_ttp_error_workspace_size": ([L64, L64, L64], SZ),
         "vq_ttp_error": ([P, I, P, P, L64, L64, L64, P, P, SZ, P], I),
         "vq_error_workspace_size": ([I, L64, L64, L64], SZ),
-        "vq_error": ([I, P, I, P, P, P, L64, L64, L64, P, P, SZ, P], I),
+        "vq_error": ([I, P, I, P, P, P, L64, L64, L64, P, P, P, P, SZ, P], I),
         "vq_mxfp4_qdq": ([P, I, L64, L64, P, P, SZ, P], I),
+        "vq_stream_read": ([P, SZ, P, P], I),
         "vqc_layout": ([I, L64, L64, L64, P, P, P], ctypes.c_uint64),
         "vqc_crc32": ([ctypes.c_uint32, P, SZ], ctypes.c_uint32),
         "vqc_create": ([ctypes.c_char_p, I, L64, L64, L64, P], I),
@@ -238,10 +243,19 @@ def fit_codebooks(mats, init_idx, fmt="vq3r", iters=20, engine="auto", codebooks
 
 
 # ------------------------------------------------------------------ GEMV
-def gemv_workspace(fmt, rows, cols, ntok, topk, device="cuda"):
-    n = lib().vq_gemv_workspace_size(FORMATS[fmt], rows, cols, ntok, topk)
+def gemv_workspace(fmt, rows, cols, ntok, topk, n_experts, device="cuda"):
+    """Workspace of the stored-record GEMV (dequant_gemv)."""
+    n = lib().vq_gemv_workspace_size(FORMATS[fmt], rows, cols, ntok, topk, n_experts)
     if n == 0:
         raise VQError(1, "vq_gemv_workspace_size")
+    return _workspace(n, device)
+
+
+def gemv_packed_workspace(fmt, rows, cols, ntok, topk, device="cuda"):
+    """Workspace of the packed-layout GEMV (dequant_gemv_packed)."""
+    n = lib().vq_gemv_packed_workspace_size(FORMATS[fmt], rows, cols, ntok, topk)
+    if n == 0:
+        raise VQError(1, "vq_gemv_packed_workspace_size")
     return _workspace(n, device)
 
 
@@ -261,25 +275,44 @@ def gemv_pack(idx, fmt="vq3r", out=None):
     return out
 
 
-def dequant_gemv(packed, scales, codebooks, x, route, rows, cols, fmt="vq3r", y=None, workspace=None,
-                 check=False):
-    """y[b][k] = W_hat_{route[b][k]} x_b for E experts packed by gemv_pack
-    (uint8 [E, packed_size]), scales [E, rows], x fp16 [ntok, cols],
-    route int32 [ntok, topk] -> y fp32 [ntok, topk, rows]."""
+def _gemv_io(x, route, rows, device, y):
     torch = _torch()
-    E = packed.shape[0]
-    ntok, topk = route.shape
-    _check_cuda(packed, scales, codebooks, x, route)
     if x.dtype != torch.float16 or route.dtype != torch.int32:
         raise TypeError("x must be float16 and route int32")
+    ntok, topk = route.shape
     if y is None:
-        y = torch.empty((ntok, topk, rows), dtype=torch.float32, device=packed.device)
+        y = torch.empty((ntok, topk, rows), dtype=torch.float32, device=device)
+    return ntok, topk, y
+
+
+def dequant_gemv(idx, scales, codebooks, x, route, fmt="vq3r", y=None, workspace=None, check=False):
+    """y[b][k] = W_hat_{route[b][k]} x_b from the stored records idx uint8
+    [E, rows, cols/8, 3] and scales fp16 [E, rows]; x fp16 [ntok, cols], route
+    int32 [ntok, topk] -> y fp32 [ntok, topk, rows] ([VQ3R page] §1)."""
+    E, rows, V, _ = idx.shape
+    _check_cuda(idx, scales, codebooks, x, route)
+    ntok, topk, y = _gemv_io(x, route, rows, idx.device, y)
     if workspace is None:
-        workspace = gemv_workspace(fmt, rows, cols, ntok, topk, packed.device)
-    st = lib().vq_dequant_gemv(FORMATS[fmt], _ptr(packed), packed.shape[1], _ptr(scales), scales.shape[-1],
-                               _ptr(codebooks), rows, cols, E, _ptr(x), ntok, _ptr(route), topk, _ptr(y),
+        workspace = gemv_workspace(fmt, rows, V * 8, ntok, topk, E, idx.device)
+    st = lib().vq_dequant_gemv(FORMATS[fmt], _ptr(idx), rows * V * 3, _ptr(scales), scales.shape[-1],
+                               _ptr(codebooks), rows, V * 8, E, _ptr(x), ntok, _ptr(route), topk, _ptr(y),
                                _ptr(workspace), workspace.numel(), _stream())
     _call("vq_dequant_gemv", st, workspace, check)
+    return y
+
+
+def dequant_gemv_packed(packed, scales, codebooks, x, route, rows, cols, fmt="vq3r", y=None, workspace=None,
+                        check=False):
+    """The same from experts packed by gemv_pack (uint8 [E, packed_size])."""
+    E = packed.shape[0]
+    _check_cuda(packed, scales, codebooks, x, route)
+    ntok, topk, y = _gemv_io(x, route, rows, packed.device, y)
+    if workspace is None:
+        workspace = gemv_packed_workspace(fmt, rows, cols, ntok, topk, packed.device)
+    st = lib().vq_dequant_gemv_packed(FORMATS[fmt], _ptr(packed), packed.shape[1], _ptr(scales), scales.shape[-1],
+                                      _ptr(codebooks), rows, cols, E, _ptr(x), ntok, _ptr(route), topk, _ptr(y),
+                                      _ptr(workspace), workspace.numel(), _stream())
+    _call("vq_dequant_gemv_packed", st, workspace, check)
     return y
 
 
@@ -371,9 +404,12 @@ def error_workspace(fmt, n_mats, rows, cols, device="cuda"):
     return _workspace(n, device)
 
 
-def error_sums(W, idx, scales, codebooks, fmt="vq3r", n_mats=1, sums=None, workspace=None, check=True):
+def error_sums(W, idx, scales, codebooks, fmt="vq3r", n_mats=1, sums=None, workspace=None, check=True, rel=None,
+               rel_all=None):
     """fp64 [n_mats, stages+1]: sum (w - w_hat_t)^2 after t = 1..stages, then sum w^2
-    ([VQ3R page] §3.1). W is [n_mats*rows, cols] (matrices stacked by rows)."""
+    ([VQ3R page] §3.1). W is [n_mats*rows, cols] (matrices stacked by rows).
+    rel / rel_all (optional fp64 [n_mats, stages] / [stages] device tensors)
+    receive the library's relative Frobenius errors per matrix / over all."""
     torch = _torch()
     total_rows, cols = W.shape
     rows = total_rows // n_mats
@@ -384,15 +420,24 @@ def error_sums(W, idx, scales, codebooks, fmt="vq3r", n_mats=1, sums=None, works
     if workspace is None:
         workspace = error_workspace(fmt, n_mats, rows, cols, W.device)
     st = lib().vq_error(FORMATS[fmt], _ptr(W), _dtype_code(W), _ptr(idx), _ptr(scales), _ptr(codebooks), n_mats,
-                        rows, cols, _ptr(sums), _ptr(workspace), workspace.numel(), _stream())
+                        rows, cols, _ptr(sums), _ptr(rel) if rel is not None else None,
+                        _ptr(rel_all) if rel_all is not None else None, _ptr(workspace), workspace.numel(),
+                        _stream())
     _call("vq_error", st, workspace, check)
     return sums
 
 
-def rel_errors(sums):
-    """Relative Frobenius error after each stage from error_sums() output."""
-    s = sums.double()
-    return (s[:, :-1] / s[:, -1:]).sqrt()
+def rel_errors(W, idx, scales, codebooks, fmt="vq3r", n_mats=1, workspace=None, check=True):
+    """Relative Frobenius errors computed by the library ([VQ3R page] §3.1):
+    (per matrix fp64 [n_mats, stages], over all matrices fp64 [stages], the
+    sums of error_sums)."""
+    torch = _torch()
+    S, _ = stages_entries(fmt)
+    rel = torch.empty((n_mats, S), dtype=torch.float64, device=W.device)
+    rel_all = torch.empty(S, dtype=torch.float64, device=W.device)
+    sums = error_sums(W, idx, scales, codebooks, fmt=fmt, n_mats=n_mats, workspace=workspace, check=check, rel=rel,
+                      rel_all=rel_all)
+    return rel, rel_all, sums
 
 
 # ------------------------------------------------------------------ MXFP4
@@ -409,6 +454,14 @@ def mxfp4_qdq(W, out=None, workspace=None, check=True):
                             _stream())
     _call("vq_mxfp4_qdq", st, workspace, check)
     return out
+
+
+# ------------------------------------------------------------------ read reference
+def stream_read(buf, out):
+    """Plain streaming read of a device buffer (the GEMV's bandwidth reference);
+    out: one-element int32 device tensor."""
+    _check_cuda(buf)
+    _call("vq_stream_read", lib().vq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out), _stream()))
 
 
 # ------------------------------------------------------------------ container
@@ -533,8 +586,7 @@ def verify_container(path, sources, first=0):
     cb, ix, sc, stored = load_container(path, first, n, device=sources[0].device)
     measured = np.empty_like(stored)
     for r in range(n):
-        sums = error_sums(sources[r], ix[r], sc[r], cb, fmt=info["fmt"])
-        measured[r] = rel_errors(sums)[0].cpu().numpy()
+        measured[r] = rel_errors(sources[r], ix[r], sc[r], cb, fmt=info["fmt"])[0][0].cpu().numpy()
     have = ~np.isnan(stored)
     match = bool(np.array_equal(stored[have], measured[have]))
     return {"stored": stored, "measured": measured, "match": match}
@@ -564,10 +616,9 @@ def convert_layer(weights, inits, sample, fmt="vq3r", iters=20, engine="auto", o
         cb = fit_codebooks(mats, inits[name], fmt=fmt, iters=iters, engine=engine)
         flat = Wn.reshape(E * rows, cols)
         idx, sc = encode(flat, cb, fmt=fmt, engine=engine)
-        sums = error_sums(flat, idx, sc, cb, fmt=fmt, n_mats=E)
-        tot = sums.sum(dim=0)
+        rel, rel_all, _ = rel_errors(flat, idx, sc, cb, fmt=fmt, n_mats=E)
         res = {"codebooks": cb, "idx": idx.view(E, rows, cols // 8, 3), "scales": sc.view(E, rows),
-               "rel_err": rel_errors(sums), "rel_err_all": (tot[:-1] / tot[-1]).sqrt()}
+               "rel_err": rel, "rel_err_all": rel_all}
         if out_dir is not None:
             os.makedirs(out_dir, exist_ok=True)
             write_container(os.path.join(out_dir, name + ".vqc"), fmt, cb, res["idx"], res["scales"],

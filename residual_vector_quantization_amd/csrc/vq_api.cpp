@@ -106,6 +106,76 @@ size_t error_ws_bytes(int format, int64_t n_mats, int64_t rows) {
   return align256(kHeader + sizeof(double) * (size_t)n_mats * (size_t)error_chunks(rows) * (stages_of(format) + 1));
 }
 
+
+// argument checks shared by the packed and the stored-record GEMV
+int gemv_check(int format, int64_t rows, int64_t cols, int32_t n_experts, int64_t expert_stride,
+               int64_t min_stride, int64_t scale_stride, int32_t ntok, int32_t topk, const void* recs,
+               const void* scales, const void* codebooks, const void* x, const void* route, const void* y) {
+  if (!fmt_ok(format)) return VQ_EINVAL;
+  int st = check_shape(rows, cols);
+  if (st != VQ_OK) return st;
+  if (ntok < 0 || topk < 0 || n_experts < 1 || expert_stride < 0 || scale_stride < 0) return VQ_EINVAL;
+  if (n_experts > 1 && (expert_stride < min_stride || scale_stride < rows)) return VQ_EINVAL;
+  if (!recs || !scales || !codebooks || !x || !route || !y) return VQ_EINVAL;
+  if ((int64_t)ntok * topk >= 65536) return VQ_ERANGE;
+  if (gemv_tiles(rows, cols, (int64_t)ntok * topk) > ((int64_t)1 << 31) - 64) return VQ_ERANGE;  // grid width
+  return VQ_OK;
+}
+
+void gemv_fill(GemvArgs& a, int format, const uint16_t* scales, int64_t scale_stride, const float* codebooks,
+               int64_t rows, int64_t cols, int32_t n_experts, const uint16_t* x, int32_t ntok, const int32_t* route,
+               int32_t topk, float* y, void* workspace, hipStream_t s) {
+  a.format = format;
+  a.scales = scales;
+  a.scale_stride = scale_stride;
+  a.codebooks = codebooks;
+  a.rows = rows;
+  a.cols = cols;
+  a.n_experts = n_experts;
+  a.x = x;
+  a.ntok = ntok;
+  a.topk = topk;
+  a.route = route;
+  a.y = y;
+  a.hdr = (WsHeader*)workspace;
+  a.remap = nullptr;
+  a.stream = s;
+}
+
+size_t gemv_partials_bytes(int format, int64_t rows, int64_t cols, int32_t ntok, int32_t topk) {
+  return align256(sizeof(float) * (size_t)gemv_partials_floats(format, rows, cols, (int64_t)ntok * topk));
+}
+
+// stored-record GEMV workspace: header, partial sums, expert marks, pair slots,
+// expert list and count, then the packed copies of up to min(pairs, experts)
+// experts
+struct GemvStoredLayout {
+  size_t partials, mark, slot, list, count, packed, total;
+  int64_t n_slots;
+};
+
+GemvStoredLayout gemv_stored_layout(int format, int64_t rows, int64_t cols, int32_t ntok, int32_t topk,
+                                    int32_t n_experts) {
+  GemvStoredLayout L;
+  const int64_t npairs = (int64_t)ntok * topk;
+  L.n_slots = npairs < n_experts ? npairs : n_experts;
+  size_t off = kHeader;
+  L.partials = off;
+  off += gemv_partials_bytes(format, rows, cols, ntok, topk);
+  L.mark = off;
+  off = align256(off + sizeof(int32_t) * (size_t)n_experts);
+  L.slot = off;
+  off = align256(off + sizeof(int32_t) * (size_t)(npairs > 0 ? npairs : 1));
+  L.list = off;
+  off = align256(off + sizeof(int32_t) * (size_t)(npairs > 0 ? npairs : 1));
+  L.count = off;
+  off = align256(off + sizeof(int32_t));
+  L.packed = off;
+  off = align256(off + (size_t)gemv_packed_bytes(format, rows, cols) * (size_t)L.n_slots);
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -306,66 +376,93 @@ int vq_gemv_pack(int format, const uint8_t* idx, int64_t rows, int64_t cols, int
   if (!idx || !packed || !aligned(packed, 4)) return VQ_EINVAL;
   int ncu = 0;
   if ((st = device_cus(&ncu)) != VQ_OK) return st;
-  return hip_status(launch_gemv_pack(format, idx, rows, cols, n_experts, packed, ncu, (hipStream_t)stream));
+  return hip_status(launch_gemv_pack(format, idx, rows * (cols / 8) * 3, rows, cols, n_experts, nullptr, nullptr,
+                                     packed, ncu, (hipStream_t)stream));
 }
 
-size_t vq_gemv_workspace_size(int format, int64_t rows, int64_t cols, int32_t ntok, int32_t topk) {
+size_t vq_gemv_packed_workspace_size(int format, int64_t rows, int64_t cols, int32_t ntok, int32_t topk) {
   if (!fmt_ok(format) || check_shape(rows, cols) != VQ_OK || ntok < 0 || topk < 0) return 0;
-  const size_t npairs = (size_t)ntok * (size_t)topk;
-  return kHeader + align256(sizeof(float) * (size_t)gemv_partials_floats(format, rows, cols, (int64_t)npairs));
+  return kHeader + gemv_partials_bytes(format, rows, cols, ntok, topk);
 }
 
-int vq_dequant_gemv(int format, const uint8_t* packed, int64_t expert_stride, const uint16_t* scales,
-                    int64_t scale_stride, const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts,
-                    const uint16_t* x, int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace,
-                    size_t ws_bytes, void* stream) {
-  if (!fmt_ok(format)) return VQ_EINVAL;
-  int st = check_shape(rows, cols);
+int vq_dequant_gemv_packed(int format, const uint8_t* packed, int64_t expert_stride, const uint16_t* scales,
+                           int64_t scale_stride, const float* codebooks, int64_t rows, int64_t cols,
+                           int32_t n_experts, const uint16_t* x, int32_t ntok, const int32_t* route, int32_t topk,
+                           float* y, void* workspace, size_t ws_bytes, void* stream) {
+  int st = gemv_check(format, rows, cols, n_experts, expert_stride,
+                      fmt_ok(format) ? gemv_packed_bytes(format, rows, cols) : 0, scale_stride, ntok, topk, packed,
+                      scales, codebooks, x, route, y);
   if (st != VQ_OK) return st;
-  if (ntok < 0 || topk < 0 || n_experts < 1 || expert_stride < 0 || scale_stride < 0) return VQ_EINVAL;
-  if (n_experts > 1 && (expert_stride < gemv_packed_bytes(format, rows, cols) || scale_stride < rows))
-    return VQ_EINVAL;
-  if (expert_stride % 4 != 0) return VQ_EINVAL;
-  if (!packed || !scales || !codebooks || !x || !route || !y || !aligned(packed, 4)) return VQ_EINVAL;
-  if (!workspace || !aligned(workspace, 256) || ws_bytes < vq_gemv_workspace_size(format, rows, cols, ntok, topk))
+  if (expert_stride % 4 != 0 || !aligned(packed, 4)) return VQ_EINVAL;
+  if (!workspace || !aligned(workspace, 256) ||
+      ws_bytes < vq_gemv_packed_workspace_size(format, rows, cols, ntok, topk))
     return VQ_EWORKSPACE;
-  if ((int64_t)ntok * topk >= 65536) return VQ_ERANGE;
-  if (gemv_tiles(rows, cols, (int64_t)ntok * topk) > ((int64_t)1 << 31) - 64) return VQ_ERANGE;  // grid width
   GemvArgs a;
-  a.format = format;
+  gemv_fill(a, format, scales, scale_stride, codebooks, rows, cols, n_experts, x, ntok, route, topk, y, workspace,
+            (hipStream_t)stream);
   a.idx = packed;
   a.expert_stride = expert_stride;
-  a.scales = scales;
-  a.scale_stride = scale_stride;
-  a.codebooks = codebooks;
-  a.rows = rows;
-  a.cols = cols;
-  a.n_experts = n_experts;
-  a.x = x;
-  a.ntok = ntok;
-  a.topk = topk;
-  a.route = route;
-  a.y = y;
-  a.hdr = (WsHeader*)workspace;
   a.partials = (float*)((char*)workspace + kHeader);
-  a.stream = (hipStream_t)stream;
   if ((st = device_cus(&a.ncu)) != VQ_OK) return st;
   return hip_status(launch_gemv(a));
 }
 
-int vq3r_dequant_gemv(const uint8_t* packed, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
+size_t vq_gemv_workspace_size(int format, int64_t rows, int64_t cols, int32_t ntok, int32_t topk,
+                              int32_t n_experts) {
+  if (!fmt_ok(format) || check_shape(rows, cols) != VQ_OK || ntok < 0 || topk < 0 || n_experts < 1) return 0;
+  return gemv_stored_layout(format, rows, cols, ntok, topk, n_experts).total;
+}
+
+int vq_dequant_gemv(int format, const uint8_t* idx, int64_t expert_stride, const uint16_t* scales,
+                    int64_t scale_stride, const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts,
+                    const uint16_t* x, int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  int st = gemv_check(format, rows, cols, n_experts, expert_stride, rows * (cols / 8) * 3, scale_stride, ntok, topk,
+                      idx, scales, codebooks, x, route, y);
+  if (st != VQ_OK) return st;
+  if (!workspace || !aligned(workspace, 256) ||
+      ws_bytes < vq_gemv_workspace_size(format, rows, cols, ntok, topk, n_experts))
+    return VQ_EWORKSPACE;
+  const GemvStoredLayout L = gemv_stored_layout(format, rows, cols, ntok, topk, n_experts);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  GemvArgs a;
+  gemv_fill(a, format, scales, scale_stride, codebooks, rows, cols, n_experts, x, ntok, route, topk, y, workspace, s);
+  if ((st = device_cus(&a.ncu)) != VQ_OK) return st;
+  const int npairs = ntok * topk;
+  if (npairs > 0 && rows > 0) {
+    int32_t* slot = (int32_t*)(ws + L.slot);
+    int32_t* list = (int32_t*)(ws + L.list);
+    int32_t* count = (int32_t*)(ws + L.count);
+    uint8_t* packed = (uint8_t*)(ws + L.packed);
+    hipError_t e = launch_gemv_route_stored(route, npairs, n_experts, (int32_t*)(ws + L.mark), slot, list, count, s);
+    if (e == hipSuccess)
+      e = launch_gemv_pack(format, idx, expert_stride, rows, cols, L.n_slots, list, count, packed, a.ncu, s);
+    if (e != hipSuccess) return VQ_EDEVICE;
+    a.idx = packed;
+    a.expert_stride = gemv_packed_bytes(format, rows, cols);
+    a.remap = slot;
+  } else {
+    a.idx = idx;
+    a.expert_stride = 0;
+  }
+  a.partials = (float*)(ws + L.partials);
+  return hip_status(launch_gemv(a));
+}
+
+int vq3r_dequant_gemv(const uint8_t* idx, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
                       const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts, const uint16_t* x,
                       int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace, size_t ws_bytes,
                       void* stream) {
-  return vq_dequant_gemv(VQ_FMT_VQ3R, packed, expert_stride, scales, scale_stride, codebooks, rows, cols, n_experts, x,
+  return vq_dequant_gemv(VQ_FMT_VQ3R, idx, expert_stride, scales, scale_stride, codebooks, rows, cols, n_experts, x,
                          ntok, route, topk, y, workspace, ws_bytes, stream);
 }
 
-int vq4p_dequant_gemv(const uint8_t* packed, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
+int vq4p_dequant_gemv(const uint8_t* idx, int64_t expert_stride, const uint16_t* scales, int64_t scale_stride,
                       const float* codebooks, int64_t rows, int64_t cols, int32_t n_experts, const uint16_t* x,
                       int32_t ntok, const int32_t* route, int32_t topk, float* y, void* workspace, size_t ws_bytes,
                       void* stream) {
-  return vq_dequant_gemv(VQ_FMT_VQ4P, packed, expert_stride, scales, scale_stride, codebooks, rows, cols, n_experts, x,
+  return vq_dequant_gemv(VQ_FMT_VQ4P, idx, expert_stride, scales, scale_stride, codebooks, rows, cols, n_experts, x,
                          ntok, route, topk, y, workspace, ws_bytes, stream);
 }
 
@@ -473,8 +570,8 @@ size_t vq_error_workspace_size(int format, int64_t n_mats, int64_t rows, int64_t
 }
 
 int vq_error(int format, const void* W, int dtype, const uint8_t* idx, const uint16_t* scales, const float* codebooks,
-             int64_t n_mats, int64_t rows, int64_t cols, double* sums, void* workspace, size_t ws_bytes,
-             void* stream) {
+             int64_t n_mats, int64_t rows, int64_t cols, double* sums, double* rel, double* rel_all, void* workspace,
+             size_t ws_bytes, void* stream) {
   if (!fmt_ok(format) || !dtype_ok(dtype) || n_mats < 1) return VQ_EINVAL;
   int st = check_shape(rows, cols);
   if (st != VQ_OK) return st;
@@ -493,6 +590,8 @@ int vq_error(int format, const void* W, int dtype, const uint8_t* idx, const uin
   a.rows = rows;
   a.cols = cols;
   a.sums = sums;
+  a.rel = rel;
+  a.rel_all = rel_all;
   a.partials = (double*)((char*)workspace + kHeader);
   a.blocks = blocks;
   a.hdr = (WsHeader*)workspace;
@@ -517,6 +616,15 @@ int vq_mxfp4_qdq(const void* W, int dtype, int64_t rows, int64_t cols, float* ou
   int st;
   if ((st = device_cus(&a.ncu)) != VQ_OK) return st;
   return hip_status(launch_mxfp4(a));
+}
+
+// ---------------------------------------------------------------- read reference
+int vq_stream_read(const void* src, size_t nbytes, uint32_t* out, void* stream) {
+  if (nbytes == 0) return VQ_OK;
+  if (!src || !out || !aligned(src, 16) || nbytes % 16 != 0) return VQ_EINVAL;
+  int ncu = 0, st;
+  if ((st = device_cus(&ncu)) != VQ_OK) return st;
+  return hip_status(launch_stream_read(src, nbytes, out, ncu, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -276,6 +276,34 @@ __global__ void k_error_reduce(const double* partials, int64_t nchunks, int nv, 
   sums[q] = s;
 }
 
+// The Gate-3 metric ([VQ3R page] §3.1) from the sums: rel[m][t] =
+// sqrt(sum (w - w_hat_{t+1})^2 / sum w^2) per matrix, and rel_all[t] over all
+// matrices (numerator and denominator added over m in order, then the same
+// ratio), in fp64 with correctly rounded division and square root. A matrix of
+// zeros reconstructed as zeros has error 0. One workgroup; rel / rel_all may be
+// NULL.
+__global__ __launch_bounds__(256) void k_error_rel(const double* sums, int64_t n_mats, int S, double* rel,
+                                                   double* rel_all) {
+  auto ratio = [](double num, double den) {
+    if (num == 0.0) return 0.0;
+    return __dsqrt_rn(__ddiv_rn(num, den));
+  };
+  if (rel)
+    for (int64_t q = threadIdx.x; q < n_mats * S; q += blockDim.x) {
+      const int64_t m = q / S, t = q % S;
+      rel[q] = ratio(sums[m * (S + 1) + t], sums[m * (S + 1) + S]);
+    }
+  if (rel_all && threadIdx.x < (unsigned)S) {
+    const int t = threadIdx.x;
+    double num = 0.0, den = 0.0;
+    for (int64_t m = 0; m < n_mats; ++m) {
+      num += sums[m * (S + 1) + t];
+      den += sums[m * (S + 1) + S];
+    }
+    rel_all[t] = ratio(num, den);
+  }
+}
+
 template <int FMT, int DT>
 static hipError_t launch_error_t(const ErrorArgs& a) {
   constexpr int S = Fmt<FMT>::S;
@@ -286,6 +314,7 @@ static hipError_t launch_error_t(const ErrorArgs& a) {
                                                nchunks, a.partials, a.hdr);
   const int64_t nq = a.n_mats * (S + 1);
   k_error_reduce<<<(unsigned)((nq + 255) / 256), 256, 0, a.stream>>>(a.partials, nchunks, S + 1, a.n_mats, a.sums);
+  if (a.rel || a.rel_all) k_error_rel<<<1, 256, 0, a.stream>>>(a.sums, a.n_mats, S, a.rel, a.rel_all);
   return hipGetLastError();
 }
 
@@ -405,6 +434,38 @@ __global__ __launch_bounds__(256) void k_mxfp4_v4(const void* W, uint64_t nblk, 
     *reinterpret_cast<float4*>(out + e) = make_float4(r[0], r[1], r[2], r[3]);
   }
   if (bad) flag_status(hdr, ST_NONFINITE);
+}
+
+// ------------------------------------------------------------------ read reference
+// A plain streaming read of n16 16-byte words (coalesced dwordx4 loads, grid
+// stride, 8 loads in flight per thread): the bandwidth reference that the
+// dequant-GEMV's HBM rate is compared with. The XOR of everything read decides
+// a store that never happens for the bench's data, so no load is dead.
+__global__ __launch_bounds__(512) void k_stream_read(const uint4* src, uint64_t n16, uint32_t* out) {
+  uint32_t acc = 0;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) out[0] = acc;
+}
+
+hipError_t launch_stream_read(const void* src, uint64_t nbytes, uint32_t* out, int ncu, hipStream_t s) {
+  const uint64_t n16 = nbytes / 16;
+  if (n16 == 0) return hipSuccess;
+  uint64_t g = (n16 + 511) / 512;
+  if (g > (uint64_t)ncu * 4) g = (uint64_t)ncu * 4;
+  k_stream_read<<<(unsigned)g, 512, 0, s>>>(reinterpret_cast<const uint4*>(src), n16, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_mxfp4(const Mxfp4Args& a) {

@@ -4,20 +4,23 @@
 //
 // y[p][r] = s_r * sum_j sum_t T_t[j][i_t(r, j)],   T_t[j][e] = <C_t[e], x_j>
 // where x_j is the j-th 8-element slice of the token's activation. A work tile
-// is (token-slot pair p, block of J = 16 slices, chunk of at most 2048 rows):
-// its workgroup tabulates T for
-// the block's slices in LDS with fp32 matrix-core products (codewords x
-// slices), then streams the tile's records, one row per lane: each index
-// costs one table read and one add. Tile partial sums go to the workspace and
-// a second kernel adds the blocks in a fixed order and applies the row
-// scales, so the result is deterministic. It equals sum_c W_hat[r][c] x[c] up
-// to fp32 rounding.
+// is (token-slot pair p, row chunk of at most 2048 rows, range of NB blocks of
+// 16 slices). For each block of its range the workgroup tabulates T for the
+// block's slices in LDS with fp32 matrix-core products (codewords x slices),
+// then streams the block's records, one row per lane: each index costs one
+// table read and one add. Row sums stay in registers across the blocks of the
+// range; one partial sum per (pair, range, row) goes to the workspace and a
+// second kernel adds the ranges in a fixed order and applies the row scales,
+// so the result is deterministic. It equals sum_c W_hat[r][c] x[c] up to fp32
+// rounding.
 //
 // Blocks of 16 slices keep a workgroup's tables at 48 KB (VQ3R) / 32 KB
-// (VQ4P), so that several 8-wave workgroups share a CU and one's table build
-// and start-up latency overlap the others' record streams.
+// (VQ4P), so that three 8-wave workgroups share a CU and one's table builds
+// and start-up latency overlap the others' record streams. The record stream
+// of a wave runs two row groups ahead across block boundaries: the first
+// groups of the next block are in flight while the table for it is built.
 //
-// Runtime layout ("packed"): the GEMV reads indices repacked once by
+// Runtime layout ("packed"): the GEMV reads indices repacked by
 // vq_gemv_pack into blocks of J = 16 slices x 64-row groups. Within a group
 // the records are interleaved in 12-byte chunks (4 records of one row), and
 // each row's slices are rotated by its lane:
@@ -31,6 +34,11 @@
 // so the 16 lanes of a quarter-wave read 16 distinct slices (distinct LDS
 // banks); VQ4P keeps R = 2 replicas, lanes 16-31 (mod 32) reading the second,
 // which makes a half-wave's reads conflict-free; VQ3R keeps one copy.
+//
+// The stored-record entry point (vq_dequant_gemv on [rows][cols/8][3]
+// records) first lists the distinct routed experts (k_gemv_route_stored), packs
+// just those into the workspace (k_gemv_pack over the list) and then runs the
+// same two kernels on the packed copies.
 #include "vq_launch.hpp"
 
 namespace vqk {
@@ -41,6 +49,9 @@ constexpr int GJ = 16;     // slices per block
 constexpr int GROUP = 64;  // rows per interleaved group (one wave)
 constexpr int GEMV_WAVES = 8;
 constexpr int GEMV_THREADS = 64 * GEMV_WAVES;
+#ifndef VQ_GEMV_TILES_PER_CU
+#define VQ_GEMV_TILES_PER_CU 3
+#endif
 
 template <int FMT> struct GemvCfg;
 template <> struct GemvCfg<0> { static constexpr int R = 1; };  // 256 x 3 x 16 x 4 B = 48 KB
@@ -54,30 +65,35 @@ int64_t gemv_packed_bytes(int format, int64_t rows, int64_t cols) {
 }
 
 // ------------------------------------------------------------------ repack
-// One workgroup (256 threads) per tile (expert, block of 16 slices, group of
-// 64 rows): the tile's 64 x 48 record bytes are read row by row (4 threads per
-// row, 12 bytes each: three dword loads when the row segment is 4-byte aligned)
-// into LDS, then written as the 4 x 64 rotated 12-byte chunks of the packed
-// layout, one chunk per thread (contiguous across a wave). Pad rows and slices
-// are 0.
-__global__ __launch_bounds__(256) void k_gemv_pack(const uint8_t* idx, int64_t rows, int64_t V, int64_t n_experts,
-                                                   uint8_t* out, int64_t packed_stride) {
+// One workgroup (256 threads) per tile (expert slot, block of 16 slices, group
+// of 64 rows): the tile's 64 x 48 record bytes are read row by row (4 threads
+// per row, 12 bytes each: three dword loads when the row segment is 4-byte
+// aligned) into LDS, then written as the 4 x 64 rotated 12-byte chunks of the
+// packed layout, one chunk per thread (contiguous across a wave). Pad rows and
+// slices are 0. Output slot i holds expert list[i] (list = NULL: expert i);
+// slots at or past *count (when given) are skipped.
+__global__ __launch_bounds__(256) void k_gemv_pack(const uint8_t* idx, int64_t expert_stride, int64_t rows,
+                                                   int64_t V, int64_t n_slots, const int32_t* list,
+                                                   const int32_t* count, uint8_t* out, int64_t packed_stride) {
   constexpr int NC = GJ / 4, RB = GJ * 3;  // 4 chunks per row, 48 record bytes per row
   __shared__ uint32_t tile[GROUP][RB / 4 + 1];
   const int64_t ng = (rows + GROUP - 1) / GROUP, nblk = (V + GJ - 1) / GJ;
-  const int64_t ntiles = n_experts * nblk * ng;
+  const int64_t ntiles = n_slots * nblk * ng;
+  const int64_t used = count ? (int64_t)*count : n_slots;
   const int tid = threadIdx.x;
   const int r = tid >> 2, part = tid & 3;     // load: row of the group, 12-byte part of its 48 bytes
   const int c = tid >> 6, lane = tid & 63;    // store: chunk c of row `lane`
-  const bool dword_ok = ((V * 3) & 3) == 0 && ((uintptr_t)idx & 3) == 0;
+  const bool dword_ok = ((V * 3) & 3) == 0 && ((uintptr_t)idx & 3) == 0 && (expert_stride & 3) == 0;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int64_t e = t / (nblk * ng), rem = t % (nblk * ng);
+    const int64_t i = t / (nblk * ng), rem = t % (nblk * ng);
+    if (i >= used) break;  // tiles are in slot order
+    const int64_t e = list ? (int64_t)list[i] : i;
     const int64_t b = rem / ng, g = rem % ng;
     const int64_t row = g * GROUP + r;
     const int64_t j0 = b * GJ;
     uint32_t w[3] = {0u, 0u, 0u};
     if (row < rows) {
-      const uint8_t* src = idx + ((e * rows + row) * V + j0) * 3 + part * 12;
+      const uint8_t* src = idx + e * expert_stride + (row * V + j0) * 3 + part * 12;
       const int64_t nbytes = ((V - j0) < GJ ? (V - j0) : GJ) * 3 - part * 12;  // valid bytes of this part
       if (dword_ok && nbytes >= 12) {
         const uint32_t* s4 = reinterpret_cast<const uint32_t*>(src);
@@ -105,34 +121,74 @@ __global__ __launch_bounds__(256) void k_gemv_pack(const uint8_t* idx, int64_t r
       }
     }
     uint32_t* dst =
-        reinterpret_cast<uint32_t*>(out + e * packed_stride + ((b * ng + g) * NC + c) * (GROUP * 12) + lane * 12);
+        reinterpret_cast<uint32_t*>(out + i * packed_stride + ((b * ng + g) * NC + c) * (GROUP * 12) + lane * 12);
 #pragma unroll
     for (int k = 0; k < 3; ++k) dst[k] = o[k];
     __syncthreads();  // the tile buffer is refilled next
   }
 }
 
+// ------------------------------------------------------------------ stored-record routing
+// One workgroup: the distinct valid expert ids of route[] in increasing id
+// order (list[0 .. count)), and for every pair the position of its expert in
+// that list (slot[p]; 0 for an invalid id, whose output the reduce zeroes).
+// mark: n_experts ints of workspace (cleared here).
+__global__ __launch_bounds__(1024) void k_gemv_route_stored(const int32_t* route, int npairs, int n_experts,
+                                                            int32_t* mark, int32_t* slot, int32_t* list,
+                                                            int32_t* count) {
+  __shared__ int32_t part[1024];
+  const int tid = threadIdx.x;
+  const int per = (n_experts + 1023) / 1024;
+  const int e0 = tid * per, e1 = (e0 + per < n_experts) ? e0 + per : n_experts;
+  for (int e = e0; e < e1; ++e) mark[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < npairs; p += 1024) {
+    const int e = route[p];
+    if (e >= 0 && e < n_experts) mark[e] = 1;
+  }
+  __syncthreads();
+  int s = 0;
+  for (int e = e0; e < e1; ++e) s += mark[e];
+  part[tid] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan of the per-thread counts
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int base = part[tid] - s;
+  for (int e = e0; e < e1; ++e) {
+    const int m = mark[e];
+    if (m) list[base] = e;
+    mark[e] = base;  // rank of e among the used ids (read only for used ids)
+    base += m;
+  }
+  if (tid == 1023) *count = part[1023];
+  __syncthreads();
+  for (int p = tid; p < npairs; p += 1024) {
+    const int e = route[p];
+    slot[p] = (e >= 0 && e < n_experts) ? mark[e] : 0;
+  }
+}
+
 // ------------------------------------------------------------------ tables
 // T[(e*S + t)*R + rep][m] = sum_k C_t[e][k] * x[(j0 + m)*8 + k] with fp32
 // matrix cores (32x32x2): codewords on M, slices on N (lanes 16-31 of each
-// half-wave carry zero slices). The operands of a wave's tasks are loaded
-// first (lut_load), the MFMAs run later (lut_compute): the first index loads
-// are issued in between, so waiting for the table operands never waits for
-// the (later) index loads.
+// half-wave carry zero slices). The codebook operands of a wave's tasks are
+// loaded once per tile (CbOps), the activation operand once per block.
 template <int FMT>
-struct LutOps {
+struct CbOps {
   static constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, NT = K / 32, TASKS = S * NT;
   static constexpr int PER_WAVE = (TASKS + GEMV_WAVES - 1) / GEMV_WAVES;
   float a[PER_WAVE][4];
-  uint32_t xb[4];  // the activation operand (fp16 bits), the same for every task of the wave
 };
 
 template <int FMT>
-__device__ inline void lut_load(LutOps<FMT>& op, const float* cb_g, const uint16_t* xrow, int64_t j0, int nsl) {
-  using O = LutOps<FMT>;
+__device__ inline void cb_load(CbOps<FMT>& op, const float* cb_g) {
+  using O = CbOps<FMT>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, i = lane & 31;
-  const int ic = i < nsl ? i : 0;  // clamped slice: loaded but zeroed
 #pragma unroll
   for (int u = 0; u < O::PER_WAVE; ++u) {
     const int task = wave + GEMV_WAVES * u;
@@ -141,20 +197,28 @@ __device__ inline void lut_load(LutOps<FMT>& op, const float* cb_g, const uint16
 #pragma unroll
     for (int s = 0; s < 4; ++s) op.a[u][s] = cb_g[((size_t)t * O::K + ct * 32 + i) * DIM + 2 * s + h];
   }
+}
+
+// The activation operand of block [j0, j0 + nsl): lane (slice i, h) holds x
+// elements 2s + h of slice i (fp16 bits), slice clamped (its column is zeroed).
+__device__ inline void x_load(uint32_t xb[4], const uint16_t* xrow, int64_t j0, int nsl) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, i = lane & 31;
+  const int ic = i < nsl ? i : 0;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) op.xb[s] = xrow[(j0 + ic) * DIM + 2 * s + h];
+  for (int s = 0; s < 4; ++s) xb[s] = xrow[(j0 + ic) * DIM + 2 * s + h];
 }
 
 template <int FMT>
-__device__ inline void lut_compute(const LutOps<FMT>& op, float* lut, int nsl) {
-  using O = LutOps<FMT>;
+__device__ inline void lut_compute(const CbOps<FMT>& op, const uint32_t xb[4], float* lut, int nsl) {
+  using O = CbOps<FMT>;
   constexpr int R = GemvCfg<FMT>::R;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, i = lane & 31;
   const bool sv = i < nsl;  // nsl <= 16: lanes 16-31 of a half-wave compute nothing useful
   float b[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) b[s] = sv ? f16_bits_to_f32((uint16_t)op.xb[s]) : 0.0f;
+  for (int s = 0; s < 4; ++s) b[s] = sv ? f16_bits_to_f32((uint16_t)xb[s]) : 0.0f;
 #pragma unroll
   for (int u = 0; u < O::PER_WAVE; ++u) {
     const int task = wave + GEMV_WAVES * u;
@@ -175,46 +239,54 @@ __device__ inline void lut_compute(const LutOps<FMT>& op, float* lut, int nsl) {
   }
 }
 
-// Tile order: the tiles of each XCD share are contiguous (pair-major, block-minor):
-// workgroups are dealt to the 8 XCDs in turn.
+// Tile order: the tiles of each XCD share are contiguous: workgroups are
+// dealt to the 8 XCDs in turn.
 __device__ inline int64_t tile_of_block(int64_t bid, int64_t ntiles_pad) {
   const int64_t per_xcd = ntiles_pad / 8;
   return (bid % 8) * per_xcd + bid / 8;
 }
 
-// A tile is (slot pair, block of 16 slices, row chunk). Matrices of more than
-// 2048 rows are cut into nsplit chunks of near-equal group counts (at most 32
-// groups each), so that a tile never streams more than 2048 rows and tall
-// matrices still give many tiles. GPW = row groups per wave in a chunk (groups
-// g = g0 + wave + 8k, k < GPW), 1..4, fully unrolled.
+// A tile is (slot pair p, row chunk, range of nb blocks); tile index
+// t = (chunk * nrange + range) * npairs + p. Matrices of more than 8 * GPW row
+// groups are cut into nsplit chunks of near-equal group counts, so a tile never
+// streams more than 8 * GPW * 64 rows and tall matrices still give many tiles.
+// GPW = row groups per wave in a chunk (groups g = g0 + wave + 8k, k < GPW),
+// fully unrolled. remap (may be NULL): packed slot of pair p (the stored-record
+// path packs only the routed experts); else the packed slot is route[p].
 template <int FMT, int GPW>
-__global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_t expert_stride, const float* cb_g,
-                                                       int64_t rows, int64_t cols, int n_experts, const uint16_t* x,
-                                                       int topk, const int32_t* route, float* partials, int nblk,
+__global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_t expert_stride, const int32_t* remap,
+                                                       const float* cb_g, int64_t rows, int64_t cols, int n_experts,
+                                                       const uint16_t* x, int topk, const int32_t* route,
+                                                       float* partials, int npairs, int nblk, int nb, int nrange,
                                                        int nsplit, int64_t ntiles, int64_t ntiles_pad) {
   constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, R = GemvCfg<FMT>::R, NC = GJ / 4;
   constexpr int NW = GEMV_WAVES;
   __shared__ float lut[K * S * R * GJ];
   const int64_t tile = tile_of_block(blockIdx.x, ntiles_pad);
   if (tile >= ntiles) return;
-  const int64_t pb = tile / nsplit, chunk = tile % nsplit;
-  const int p = (int)(pb / nblk), b = (int)(pb % nblk);
-  const int tok = p / topk;
+  const int p = (int)(tile % npairs);
+  const int64_t cq = tile / npairs;
+  const int q = (int)(cq % nrange), chunk = (int)(cq / nrange);
   const int e = route[p];
   if (e < 0 || e >= n_experts) return;  // flagged and zeroed by k_gemv_reduce
+  const int64_t ep = remap ? (int64_t)remap[p] : (int64_t)e;
+  const int tok = p / topk;
   const int64_t V = cols / DIM;
-  const int64_t j0 = (int64_t)b * GJ;
-  const int nsl = (int)((V - j0) < GJ ? (V - j0) : GJ);
+  const int b0 = q * nb, b1 = (b0 + nb < nblk) ? b0 + nb : nblk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t ng = (rows + GROUP - 1) / GROUP;
   const int64_t g0 = chunk * ng / nsplit, g1 = (chunk + 1) * ng / nsplit;  // this tile's groups [g0, g1)
-  const uint8_t* tb = pk + (int64_t)e * expert_stride + (int64_t)b * ng * NC * (GROUP * 12);
-  float* part = partials + ((int64_t)p * nblk + b) * rows;
-  // unconditional loads with a clamped group index keep the wait counts exact
+  const uint8_t* eb = pk + ep * expert_stride;
+  const uint16_t* xrow = x + (int64_t)tok * cols;
+  const int nitems = (b1 - b0) * GPW;  // (block, group) items of this wave, in stream order
+  // unconditional loads with a clamped item keep the wait counts exact
   uint32_t d[2][NC][3];
-  auto load_group = [&](uint32_t (&dg)[NC][3], int64_t g) {
-    const int64_t gc = g < g1 ? g : g1 - 1;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(tb + gc * NC * (GROUP * 12)) + lane * 3;
+  auto load_item = [&](uint32_t (&dg)[NC][3], int it) {
+    const int ic = it < nitems ? it : nitems - 1;
+    const int64_t b = b0 + ic / GPW;
+    int64_t g = g0 + wave + (int64_t)(ic % GPW) * NW;
+    g = g < g1 ? g : g1 - 1;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(eb + (b * ng + g) * NC * (GROUP * 12)) + lane * 3;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
@@ -225,52 +297,79 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
   const uint32_t rep_off = (R == 2) ? (uint32_t)((lane >> 4) & 1) * (GJ * 4) : 0u;
   constexpr uint32_t E_STRIDE = S * R * GJ * 4, T_STRIDE = R * GJ * 4;
   const char* lbase = reinterpret_cast<const char*>(lut);
-  auto consume = [&](const uint32_t (&dg)[NC][3], int64_t g) {
-    float acc = 0.0f;
+  auto row_sum = [&](const uint32_t (&dg)[NC][3]) {
+    float acc;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // record q of the chunk = bytes 3q .. 3q+2 of the 12 bytes
-        const int byte0 = 3 * q, k0 = byte0 >> 2, o = byte0 & 3;
+      for (int qq = 0; qq < 4; ++qq) {
+        // record qq of the chunk = bytes 3qq .. 3qq+2 of the 12 bytes
+        const int byte0 = 3 * qq, k0 = byte0 >> 2, o = byte0 & 3;
         const uint32_t w =
             (o <= 1) ? (dg[c][k0] >> (8 * o)) : ((dg[c][k0] >> (8 * o)) | (dg[c][k0 + 1] << (32 - 8 * o)));
-        const int m = 4 * c + q;
+        const int m = 4 * c + qq;
         const uint32_t soff = (((uint32_t)(m + lane) & (GJ - 1)) << 2) + rep_off;
-        float tsum = 0.0f;
+        // the stage terms summed in stage order, then added to the row sum
+        float tsum = *reinterpret_cast<const float*>(lbase + ((uint32_t)record_index<FMT>(w, 0) * E_STRIDE + soff));
 #pragma unroll
-        for (int t = 0; t < S; ++t) {
+        for (int t = 1; t < S; ++t) {
           const uint32_t ei = (uint32_t)record_index<FMT>(w, t);
           tsum += *reinterpret_cast<const float*>(lbase + (ei * E_STRIDE + soff) + t * T_STRIDE);
         }
-        acc += tsum;
+        acc = (c == 0 && qq == 0) ? tsum : acc + tsum;
       }
     }
-    const int64_t row = g * GROUP + lane;
-    if (row < rows) part[row] = acc;
+    return acc;
   };
-  LutOps<FMT> ops;
-  lut_load<FMT>(ops, cb_g, x + (int64_t)tok * cols, j0, nsl);
+  float rs[GPW];
+#pragma unroll
+  for (int k = 0; k < GPW; ++k) rs[k] = 0.0f;
+  // the GPW groups of one block; item (block, k) uses buffer (parity + k) & 1,
+  // and the load of item + 2 follows its consume
+  auto consume_block = [&](auto par, int i0) {
+    constexpr int P = decltype(par)::value;
+#pragma unroll
+    for (int k = 0; k < GPW; ++k) {
+      const int64_t g = g0 + wave + (int64_t)k * NW;
+      if (g < g1) rs[k] += row_sum(d[(k + P) & 1]);  // wave-uniform
+      load_item(d[(k + P) & 1], i0 + k + 2);
+    }
+  };
+  CbOps<FMT> ops;
+  cb_load<FMT>(ops, cb_g);
+  uint32_t xb[4];
+  x_load(xb, xrow, (int64_t)b0 * GJ, (int)((V - (int64_t)b0 * GJ) < GJ ? (V - (int64_t)b0 * GJ) : GJ));
   __builtin_amdgcn_sched_barrier(0);  // keep the table operand loads ahead of the index stream
-  load_group(d[0], g0 + wave);
-  if (GPW != 1) load_group(d[1], g0 + wave + NW);
+  load_item(d[0], 0);
+  load_item(d[1], 1);
   __builtin_amdgcn_sched_barrier(0);
-  lut_compute<FMT>(ops, lut, nsl);
-  __syncthreads();
-  // two groups in flight: the load of group k + 2 follows the consume of group k
+  for (int b = b0; b < b1; ++b) {
+    const int64_t j0 = (int64_t)b * GJ;
+    const int nsl = (int)((V - j0) < GJ ? (V - j0) : GJ);
+    if (b > b0) {
+      x_load(xb, xrow, j0, nsl);
+      __syncthreads();  // every wave is done with the previous block's table
+    }
+    lut_compute<FMT>(ops, xb, lut, nsl);
+    __syncthreads();
+    const int i0 = (b - b0) * GPW;
+    if ((GPW & 1) == 0 || (i0 & 1) == 0) consume_block(std::integral_constant<int, 0>(), i0);
+    else consume_block(std::integral_constant<int, 1>(), i0);
+  }
+  float* part = partials + ((int64_t)p * nrange + q) * rows;
 #pragma unroll
   for (int k = 0; k < GPW; ++k) {
     const int64_t g = g0 + wave + (int64_t)k * NW;
-    if (g < g1) consume(d[k & 1], g);  // wave-uniform
-    if (k + 2 < GPW) load_group(d[k & 1], g0 + wave + (int64_t)(k + 2) * NW);
+    const int64_t row = g * GROUP + lane;
+    if (g < g1 && row < rows) part[row] = rs[k];
   }
 }
 
-// y[p][r] = s_r * sum over blocks in a fixed order. Also writes the status
+// y[p][r] = s_r * sum over the ranges in a fixed order. Also writes the status
 // flags of the call (route ids outside [0, n_experts)), so no reset is needed.
 __global__ __launch_bounds__(256) void k_gemv_reduce(const float* partials, const uint16_t* scales,
                                                      int64_t scale_stride, const int32_t* route, int n_experts,
-                                                     int64_t rows, int nblk, int npairs, float* y, WsHeader* hdr) {
+                                                     int64_t rows, int nrange, int npairs, float* y, WsHeader* hdr) {
   const int p = blockIdx.y;
   const int e = route[p];
   const bool bad = e < 0 || e >= n_experts;
@@ -284,17 +383,17 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* partials, cons
   if (r >= rows) return;
   float acc = 0.0f;
   if (!bad) {
-    const float* pp = partials + (int64_t)p * nblk * rows + r;
-    // eight independent loads in flight, added in block order
+    const float* pp = partials + (int64_t)p * nrange * rows + r;
+    // eight independent loads in flight, added in range order
     int q = 0;
-    for (; q + 8 <= nblk; q += 8) {
+    for (; q + 8 <= nrange; q += 8) {
       float v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = pp[(int64_t)(q + u) * rows];
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc += v[u];
     }
-    for (; q < nblk; ++q) acc += pp[(int64_t)q * rows];
+    for (; q < nrange; ++q) acc += pp[(int64_t)q * rows];
     acc *= f16_bits_to_f32(scales[(int64_t)e * scale_stride + r]);
   }
   y[(int64_t)p * rows + r] = acc;
@@ -304,29 +403,14 @@ __global__ void k_gemv_clear(WsHeader* hdr) {
   if (threadIdx.x == 0) hdr->flags = 0;
 }
 
-template <int FMT>
-static hipError_t launch_gemv_t(const GemvArgs& a) {
-  const int64_t npairs = (int64_t)a.ntok * a.topk;
-  const int64_t V = a.cols / DIM;
-  const int nblk = (int)((V + GJ - 1) / GJ);
-  const int64_t ng = (a.rows + GROUP - 1) / GROUP;
-  const int nsplit = gemv_row_chunks(a.rows);
-  const int64_t ntiles = npairs * nblk * nsplit;
-  const int64_t ntiles_pad = (ntiles + 7) / 8 * 8;
-  const int64_t gpw = (ng / nsplit + (ng % nsplit != 0) + GEMV_WAVES - 1) / GEMV_WAVES;  // largest chunk
-  auto go = [&](auto kern) {
-    kern<<<(unsigned)ntiles_pad, GEMV_THREADS, 0, a.stream>>>(a.idx, a.expert_stride, a.codebooks, a.rows, a.cols,
-                                                               a.n_experts, a.x, a.topk, a.route, a.partials, nblk,
-                                                               nsplit, ntiles, ntiles_pad);
-  };
-  if (gpw == 1) go(k_gemv<FMT, 1>);
-  else if (gpw == 2) go(k_gemv<FMT, 2>);
-  else if (gpw == 3) go(k_gemv<FMT, 3>);
-  else go(k_gemv<FMT, 4>);
-  dim3 g2((unsigned)((a.rows + 255) / 256), (unsigned)npairs);
-  k_gemv_reduce<<<g2, 256, 0, a.stream>>>(a.partials, a.scales, a.scale_stride, a.route, a.n_experts, a.rows, nblk,
-                                          (int)npairs, a.y, a.hdr);
-  return hipGetLastError();
+// ------------------------------------------------------------------ launch geometry
+// Row groups per wave: 4 (2048-row tiles) unless the matrix has fewer groups.
+static int gemv_gpw(int64_t rows) {
+  const int64_t ng = (rows + GROUP - 1) / GROUP;
+  if (ng <= GEMV_WAVES) return 1;
+  if (ng <= 2 * GEMV_WAVES) return 2;
+  if (ng <= 3 * GEMV_WAVES) return 3;
+  return 4;
 }
 
 int gemv_row_chunks(int64_t rows) {
@@ -334,15 +418,55 @@ int gemv_row_chunks(int64_t rows) {
   return (int)((ng + 4 * GEMV_WAVES - 1) / (4 * GEMV_WAVES));
 }
 
+// Blocks per range: as many as keep about VQ_GEMV_TILES_PER_CU tiles per CU in
+// the launch (fewer, longer tiles mean fewer partial sums and fewer table
+// start-ups; too few tiles leave CUs idle).
+static void gemv_ranges(int64_t npairs, int nsplit, int nblk, int ncu, int* nb, int* nrange) {
+  const int64_t target = (int64_t)VQ_GEMV_TILES_PER_CU * (ncu > 0 ? ncu : 1);
+  int64_t want = target / (npairs * nsplit > 0 ? npairs * nsplit : 1);
+  if (want < 1) want = 1;
+  if (want > nblk) want = nblk;
+  int b = (int)((nblk + want - 1) / want);
+  *nb = b;
+  *nrange = (nblk + b - 1) / b;
+}
+
 int64_t gemv_tiles(int64_t rows, int64_t cols, int64_t npairs) {
   const int64_t nblk = (cols / DIM + GJ - 1) / GJ;
-  return npairs * nblk * gemv_row_chunks(rows);
+  return npairs * nblk * gemv_row_chunks(rows);  // upper bound (one block per range)
 }
 
 int64_t gemv_partials_floats(int format, int64_t rows, int64_t cols, int64_t npairs) {
   (void)format;
   const int64_t nblk = (cols / DIM + GJ - 1) / GJ;
-  return npairs * nblk * rows;
+  return npairs * nblk * rows;  // upper bound (one block per range)
+}
+
+template <int FMT>
+static hipError_t launch_gemv_t(const GemvArgs& a) {
+  const int64_t npairs = (int64_t)a.ntok * a.topk;
+  const int64_t V = a.cols / DIM;
+  const int nblk = (int)((V + GJ - 1) / GJ);
+  const int nsplit = gemv_row_chunks(a.rows);
+  int nb, nrange;
+  gemv_ranges(npairs, nsplit, nblk, a.ncu, &nb, &nrange);
+  const int64_t ntiles = npairs * nsplit * nrange;
+  const int64_t ntiles_pad = (ntiles + 7) / 8 * 8;
+  const int gpw = gemv_gpw(a.rows);
+  auto go = [&](auto kern) {
+    kern<<<(unsigned)ntiles_pad, GEMV_THREADS, 0, a.stream>>>(a.idx, a.expert_stride, a.remap, a.codebooks, a.rows,
+                                                               a.cols, a.n_experts, a.x, a.topk, a.route,
+                                                               a.partials, (int)npairs, nblk, nb, nrange, nsplit,
+                                                               ntiles, ntiles_pad);
+  };
+  if (gpw == 1) go(k_gemv<FMT, 1>);
+  else if (gpw == 2) go(k_gemv<FMT, 2>);
+  else if (gpw == 3) go(k_gemv<FMT, 3>);
+  else go(k_gemv<FMT, 4>);
+  dim3 g2((unsigned)((a.rows + 255) / 256), (unsigned)npairs);
+  k_gemv_reduce<<<g2, 256, 0, a.stream>>>(a.partials, a.scales, a.scale_stride, a.route, a.n_experts, a.rows, nrange,
+                                          (int)npairs, a.y, a.hdr);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv(const GemvArgs& a) {
@@ -353,14 +477,22 @@ hipError_t launch_gemv(const GemvArgs& a) {
   return a.format == 0 ? launch_gemv_t<0>(a) : launch_gemv_t<1>(a);
 }
 
-hipError_t launch_gemv_pack(int format, const uint8_t* idx, int64_t rows, int64_t cols, int64_t n_experts,
-                            uint8_t* out, int ncu, hipStream_t s) {
+hipError_t launch_gemv_pack(int format, const uint8_t* idx, int64_t expert_stride, int64_t rows, int64_t cols,
+                            int64_t n_slots, const int32_t* list, const int32_t* count, uint8_t* out, int ncu,
+                            hipStream_t s) {
   const int64_t V = cols / DIM;
-  const int64_t ntiles = ((V + GJ - 1) / GJ) * ((rows + GROUP - 1) / GROUP) * n_experts;
+  const int64_t ntiles = ((V + GJ - 1) / GJ) * ((rows + GROUP - 1) / GROUP) * n_slots;
   if (ntiles == 0) return hipSuccess;
   int64_t g = ntiles;
   if (g > (int64_t)ncu * 32) g = (int64_t)ncu * 32;
-  k_gemv_pack<<<(unsigned)g, 256, 0, s>>>(idx, rows, V, n_experts, out, gemv_packed_bytes(format, rows, cols));
+  k_gemv_pack<<<(unsigned)g, 256, 0, s>>>(idx, expert_stride, rows, V, n_slots, list, count, out,
+                                          gemv_packed_bytes(format, rows, cols));
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_route_stored(const int32_t* route, int npairs, int n_experts, int32_t* mark, int32_t* slot,
+                                    int32_t* list, int32_t* count, hipStream_t s) {
+  k_gemv_route_stored<<<1, 1024, 0, s>>>(route, npairs, n_experts, mark, slot, list, count);
   return hipGetLastError();
 }
 

@@ -59,6 +59,8 @@ struct ErrorArgs {
   const float* codebooks;
   int64_t n_mats, rows, cols;
   double* sums;
+  double* rel;       // [n_mats][stages] relative errors, or NULL
+  double* rel_all;   // [stages] over all matrices, or NULL
   double* partials;  // [n_mats][error_chunks(rows)][stages+1]
   int blocks;        // grid width per matrix (does not change the result)
   WsHeader* hdr;
@@ -67,8 +69,9 @@ struct ErrorArgs {
 
 struct GemvArgs {
   int format;
-  const uint8_t* idx;
+  const uint8_t* idx;       // packed experts
   int64_t expert_stride;
+  const int32_t* remap;     // packed slot of each pair (NULL: the route id itself)
   const uint16_t* scales;
   int64_t scale_stride;
   const float* codebooks;
@@ -78,7 +81,7 @@ struct GemvArgs {
   int ntok, topk;
   const int32_t* route;
   float* y;
-  float* partials;  // [ntok*topk][nblk][rows]
+  float* partials;  // [ntok*topk][nrange][rows]
   WsHeader* hdr;
   int ncu;
   hipStream_t stream;
@@ -99,8 +102,16 @@ int64_t gemv_partials_floats(int format, int64_t rows, int64_t cols, int64_t npa
 int64_t gemv_packed_bytes(int format, int64_t rows, int64_t cols);
 int gemv_row_chunks(int64_t rows);                                  // row chunks of a GEMV tile column
 int64_t gemv_tiles(int64_t rows, int64_t cols, int64_t npairs);     // GEMV workgroups (before padding)
-hipError_t launch_gemv_pack(int format, const uint8_t* idx, int64_t rows, int64_t cols, int64_t n_experts,
-                            uint8_t* out, int ncu, hipStream_t s);
+// Packs n_slots experts into the GEMV layout: slot i <- expert list[i] (list
+// NULL: expert i) read at idx + expert * expert_stride; slots at or past *count
+// (count may be NULL) are skipped.
+hipError_t launch_gemv_pack(int format, const uint8_t* idx, int64_t expert_stride, int64_t rows, int64_t cols,
+                            int64_t n_slots, const int32_t* list, const int32_t* count, uint8_t* out, int ncu,
+                            hipStream_t s);
+// Distinct valid expert ids of route[] (list, count) and each pair's position
+// in that list (slot); mark = n_experts ints of scratch.
+hipError_t launch_gemv_route_stored(const int32_t* route, int npairs, int n_experts, int32_t* mark, int32_t* slot,
+                                    int32_t* list, int32_t* count, hipStream_t s);
 
 hipError_t launch_reset(WsHeader* hdr, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs& a);
@@ -113,5 +124,6 @@ hipError_t launch_gemv(const GemvArgs& a);
 constexpr int ERR_CHUNK = 16;
 inline int64_t error_chunks(int64_t rows) { return (rows + ERR_CHUNK - 1) / ERR_CHUNK; }
 hipError_t launch_mxfp4(const Mxfp4Args& a);
+hipError_t launch_stream_read(const void* src, uint64_t nbytes, uint32_t* out, int ncu, hipStream_t s);
 
 }  // namespace vqk

@@ -56,10 +56,18 @@ def test_workspace_sizes():
     n = 12 * 2048 * 896
     assert L.vq_fit_workspace_size(0, 12, 2048, 7168) >= 2 * 32 * n
     assert L.vq_fit_workspace_size(1, 1, 0, 64) == 0
-    # header + row sums per (slot, block of 16 slices): 7168 / 8 / 16 = 56 blocks
+    # header + row sums per (slot, range of blocks of 16 slices), at most one
+    # range per block: 7168 / 8 / 16 = 56 blocks
     npairs, nblk = 16 * 8, 56
-    assert L.vq_gemv_workspace_size(0, 2048, 7168, 16, 8) >= 256 + npairs * nblk * 2048 * 4
-    assert L.vq_gemv_workspace_size(0, 2048, 7168, 16, 8) == L.vq_gemv_workspace_size(1, 2048, 7168, 16, 8)
+    packed_ws = L.vq_gemv_packed_workspace_size(0, 2048, 7168, 16, 8)
+    assert packed_ws >= 256 + npairs * nblk * 2048 * 4
+    assert packed_ws == L.vq_gemv_packed_workspace_size(1, 2048, 7168, 16, 8)
+    # the stored-record call also holds packed copies of min(pairs, experts) experts
+    pk = L.vq_gemv_packed_size(0, 2048, 7168)
+    assert L.vq_gemv_workspace_size(0, 2048, 7168, 16, 8, 256) >= packed_ws + npairs * pk
+    assert L.vq_gemv_workspace_size(0, 2048, 7168, 16, 8, 40) >= packed_ws + 40 * pk
+    assert L.vq_gemv_workspace_size(0, 2048, 7168, 16, 8, 40) < packed_ws + 41 * pk + (1 << 16)
+    assert L.vq_gemv_workspace_size(0, 2048, 7168, 16, 8, 0) == 0
     assert L.vq_error_workspace_size(0, 4, 256, 1024) > 256
 
 
@@ -137,24 +145,37 @@ def test_decode_gemv_error_mxfp4_argument_errors():
     assert L.vq_decode(1, None, b.ptr, c.ptr, 4, 64, 4, d.ptr, None) == VQ_EINVAL
     assert L.vq_encode(0, 0, None, 0, 0, 64, None, None, None, None, 0, None) == VQ_OK   # empty: no access
     assert L.vq_decode(0, a.ptr, b.ptr, c.ptr, 0, 64, 3, d.ptr, None) == VQ_OK
-    n_ws = L.vq_gemv_workspace_size(0, 4, 64, 2, 2)
+    n_ws = L.vq_gemv_packed_workspace_size(0, 4, 64, 2, 2)
     pk = L.vq_gemv_packed_size(0, 4, 64)
     assert pk == 64 * 16 * 3            # one 64-row group x one block of 16 slices
     assert L.vq_gemv_packed_size(1, 2048, 7168) == 2048 * 896 * 3
     assert L.vq_gemv_pack(0, a.ptr, 4, 64, 2, ctypes.c_void_p(b.ptr.value + 2), None) == VQ_EINVAL
-    g = lambda **k: L.vq_dequant_gemv(0, a.ptr, k.get("es", pk), b.ptr, 4, c.ptr, 4, 64,
-                                      k.get("ne", 2), d.ptr, k.get("nt", 2), e.ptr, 2, f.ptr, ws.ptr,
-                                      k.get("wsn", n_ws), None)
+    g = lambda **k: L.vq_dequant_gemv_packed(0, a.ptr, k.get("es", pk), b.ptr, 4, c.ptr, 4, 64,
+                                             k.get("ne", 2), d.ptr, k.get("nt", 2), e.ptr, 2, f.ptr, ws.ptr,
+                                             k.get("wsn", n_ws), None)
     assert g(ne=0) == VQ_EINVAL
     assert g(es=pk - 4) == VQ_EINVAL      # stride smaller than one packed expert
     assert g(es=pk + 2) == VQ_EINVAL      # stride not a multiple of 4
     assert g(nt=-1) == VQ_EINVAL
     assert g(wsn=16) == VQ_EWORKSPACE
+    # the stored-record call (and its vq3r / vq4p names): stride of a stored
+    # expert, workspace of the stored call
+    rec = 4 * 8 * 3
+    s_ws = L.vq_gemv_workspace_size(0, 4, 64, 2, 2, 2)
+    assert s_ws > n_ws
+    h = lambda fn, **k: fn(a.ptr, k.get("es", rec), b.ptr, 4, c.ptr, 4, 64, k.get("ne", 2), d.ptr, 2, e.ptr, 2,
+                           f.ptr, ws.ptr, k.get("wsn", s_ws), None)
+    for fn in (L.vq3r_dequant_gemv, L.vq4p_dequant_gemv):
+        assert h(fn, ne=0) == VQ_EINVAL
+        assert h(fn, es=rec - 1) == VQ_EINVAL
+        assert h(fn, wsn=n_ws) == VQ_EWORKSPACE
+    assert L.vq_dequant_gemv(5, a.ptr, rec, b.ptr, 4, c.ptr, 4, 64, 2, d.ptr, 2, e.ptr, 2, f.ptr, ws.ptr, s_ws,
+                             None) == VQ_EINVAL
     # more GEMV workgroups than a launch can hold: 65535 slots x 65536 row chunks
-    huge = L.vq_dequant_gemv(0, a.ptr, 0, b.ptr, 0, c.ptr, 1 << 27, 8, 1, d.ptr, 65535, e.ptr, 1, f.ptr, ws.ptr,
-                             (1 << 63) - 1, None)
+    huge = L.vq_dequant_gemv_packed(0, a.ptr, 0, b.ptr, 0, c.ptr, 1 << 27, 8, 1, d.ptr, 65535, e.ptr, 1, f.ptr,
+                                    ws.ptr, (1 << 63) - 1, None)
     assert huge == VQ_ERANGE
-    assert L.vq_error(0, a.ptr, 0, b.ptr, c.ptr, d.ptr, 0, 4, 64, e.ptr, ws.ptr, 1 << 12, None) == VQ_EINVAL
+    assert L.vq_error(0, a.ptr, 0, b.ptr, c.ptr, d.ptr, 0, 4, 64, e.ptr, None, None, ws.ptr, 1 << 12, None) == VQ_EINVAL
     assert L.vq_mxfp4_qdq(a.ptr, 0, 4, 48, b.ptr, ws.ptr, 256, None) == VQ_EINVAL     # cols % 32
     assert L.vq_mxfp4_qdq(a.ptr, 0, 4, 64, b.ptr, ws.ptr, 16, None) == VQ_EWORKSPACE
     assert L.vq_read_status(None, None, None) == VQ_EWORKSPACE

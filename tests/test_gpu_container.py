@@ -52,7 +52,7 @@ def converted(request, tmp_path_factory):
         rec, s = vq.encode(w, cbd, fmt=fmt)
         recs.append(rec)
         scs.append(s)
-        errs.append(vq.rel_errors(vq.error_sums(w, rec, s, cbd, fmt=fmt))[0])
+        errs.append(vq.rel_errors(w, rec, s, cbd, fmt=fmt)[0][0])
     rec, sc, rel = torch.stack(recs), torch.stack(scs), torch.stack(errs)
     path = tmp_path_factory.mktemp("c") / ("%s.vqc" % fmt)
     vq.write_container(path, fmt, cbd, rec, sc, rel_err=rel)

@@ -80,8 +80,8 @@ def test_encode_decode_gemv_replay_bit_exact(fmt):
     x = torch.from_numpy(synthetic.activations_f16(ntok, cols, seed=3).view(np.float16)).cuda()
     route = torch.from_numpy(synthetic.routing(ntok, E, topk, seed=5)).cuda()
     y = torch.empty((ntok, topk, rows), device="cuda")
-    wsg = vq.gemv_workspace(fmt, rows, cols, ntok, topk)
-    gemv = lambda: vq.dequant_gemv(packed, sc.view(E, rows), cb, x, route, rows, cols, fmt=fmt, y=y,  # noqa: E731
+    wsg = vq.gemv_packed_workspace(fmt, rows, cols, ntok, topk)
+    gemv = lambda: vq.dequant_gemv_packed(packed, sc.view(E, rows), cb, x, route, rows, cols, fmt=fmt, y=y,  # noqa: E731
                                    workspace=wsg)
     gemv()
     torch.cuda.synchronize()

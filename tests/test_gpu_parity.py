@@ -255,12 +255,16 @@ def test_decode_bit_exact_and_error(cfg1, fmt):
         got = vq.decode(rec, sd, cbd, fmt=fmt, stages_used=su).cpu().numpy()
         ref = oracle.decode(idx_o, s_o, cb, stages_used=su)
         assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), su
-    sums = vq.error_sums(to_dev(W), rec, sd, cbd, fmt=fmt).cpu().numpy()[0]
+    rel, rel_all, sums = vq.rel_errors(to_dev(W), rec, sd, cbd, fmt=fmt)
+    e = rel.cpu().numpy()[0]
+    sums = sums.cpu().numpy()[0]
     for su in range(1, S + 1):
         ref = oracle.rel_error(W, oracle.decode(idx_o, s_o, cb, stages_used=su))
-        assert abs(np.sqrt(sums[su - 1] / sums[S]) - ref) < 1e-5
+        assert abs(e[su - 1] - ref) < 1e-5
+        # the library's ratio is the correctly rounded sqrt(sum / sum) of its own sums
+        assert e[su - 1] == np.sqrt(sums[su - 1] / sums[S])
+    assert np.array_equal(rel_all.cpu().numpy(), e)  # one matrix: the aggregate is the same
     # error is non-increasing over the stages on the fit data
-    e = np.sqrt(sums[:S] / sums[S])
     assert np.all(np.diff(e) <= 1e-12)
 
 
@@ -281,7 +285,8 @@ def test_encode_decode_error_full_layer_sampled(cfg1, fmt):
     cbd = to_dev(cb)
     rec, sc = vq.encode(W, cbd, fmt=fmt)
     w_hat = vq.decode(rec, sc, cbd, fmt=fmt)
-    sums = vq.error_sums(W, rec, sc, cbd, fmt=fmt, n_mats=E).cpu().numpy()
+    rel_d, rel_all_d, sums_d = vq.rel_errors(W, rec, sc, cbd, fmt=fmt, n_mats=E)
+    rel, rel_all, sums = rel_d.cpu().numpy(), rel_all_d.cpu().numpy(), sums_d.cpu().numpy()
     torch.cuda.synchronize()
     rows = np.sort(np.random.default_rng(7).choice(E * R, 64, replace=False))
     rt = torch.from_numpy(rows).to(DEV)
@@ -296,7 +301,12 @@ def test_encode_decode_error_full_layer_sampled(cfg1, fmt):
         i_e, s_e = oracle.encode(we, cb)
         for su in range(1, S + 1):
             ref = oracle.rel_error(we, oracle.decode(i_e, s_e, cb, stages_used=su))
-            assert abs(np.sqrt(sums[e, su - 1] / sums[e, S]) - ref) <= 1e-5, (e, su)
+            assert abs(rel[e, su - 1] - ref) <= 1e-5, (e, su)
+    # the aggregate over the layer: ratio of the summed sums, in matrix order
+    tot = np.zeros(S + 1)
+    for m in range(E):
+        tot = tot + sums[m]
+    assert np.array_equal(rel_all, np.sqrt(tot[:S] / tot[S]))
 
 
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
@@ -435,7 +445,8 @@ def _experts(fmt, cb, E, rows, cols, seed):
 
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
 @pytest.mark.parametrize("shape", [(64, 256), (96, 2056), (256, 1024), (32, 448), (1100, 896), (64, 7168),
-                                   (2600, 264), (2112, 64), (4160, 136), (2049, 24)])
+                                   (2600, 264), (2112, 64), (4160, 136), (2049, 24), (1100, 7168), (300, 7168),
+                                   (700, 3976)])
 def test_gemv_matches_oracle(cfg1, fmt, shape):
     say("gemv", fmt, shape)
     rows, cols = shape
@@ -445,23 +456,27 @@ def test_gemv_matches_oracle(cfg1, fmt, shape):
     x = synthetic.activations_f16(ntok, cols, seed=1)
     route = synthetic.routing(ntok, E, topk, seed=2)
     packed = vq.gemv_pack(to_dev(recs), fmt=fmt)
-    y = vq.dequant_gemv(packed, to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
-                        to_dev(route), rows, cols, fmt=fmt).cpu().numpy()
-    xf = synthetic.f16_bits_to_f32(x).reshape(ntok, cols)
-    for b in range(ntok):
-        for k in range(topk):
-            ref, scale = oracle.gemv_ref(whs[route[b, k]], xf[b])
-            err = np.abs(y[b, k] - ref)
-            assert np.all(err <= 1e-3 * scale + 1e-30), (b, k, float((err / scale).max()))
+    y = vq.dequant_gemv_packed(packed, to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
+                               to_dev(route), rows, cols, fmt=fmt).cpu().numpy()
+    _check_gemv(y, whs, synthetic.f16_bits_to_f32(x).reshape(ntok, cols), route)
+    # the stored-record call: same kernels on its own packed copies, same bits
+    ys = vq.dequant_gemv(to_dev(recs), to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
+                         to_dev(route), fmt=fmt).cpu().numpy()
+    assert np.array_equal(ys.view(np.uint32), y.view(np.uint32))
 
 
 def _check_gemv(y, whs, xf, route):
+    """Per element within 1e-3 * sum_k |w_hat_k x_k| (the condition-aware bar),
+    and per output vector ||y - y_ref|| / ||y_ref|| <= 1e-3."""
     ntok, topk = route.shape
     for b in range(ntok):
         for k in range(topk):
             ref, scale = oracle.gemv_ref(whs[route[b, k]], xf[b])
             err = np.abs(y[b, k] - ref)
             assert np.all(err <= 1e-3 * scale + 1e-30), (b, k, float((err / scale).max()))
+            nr = np.linalg.norm(ref)
+            if nr > 0:
+                assert np.linalg.norm(y[b, k] - ref) <= 1e-3 * nr, (b, k)
 
 
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
@@ -476,7 +491,7 @@ def test_gemv_many_slots(cfg1, fmt):
     route = synthetic.routing(ntok, E, 4, seed=4)
     route = np.concatenate([route, route[::-1]], axis=1).astype(np.int32)
     packed = vq.gemv_pack(to_dev(recs), fmt=fmt)
-    y = vq.dequant_gemv(packed, to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
+    y = vq.dequant_gemv_packed(packed, to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
                         to_dev(route), rows, cols, fmt=fmt).cpu().numpy()
     _check_gemv(y, whs, synthetic.f16_bits_to_f32(x).reshape(ntok, cols), route)
 
@@ -498,7 +513,7 @@ def test_gemv_full_layer_sampled(cfg1, fmt):
     scales = to_dev(scs.view(np.float16)).repeat(E // 2, 1)
     x = synthetic.activations_f16(ntok, cols, seed=11)
     route = synthetic.routing(ntok, E, topk, seed=12)
-    y = vq.dequant_gemv(packed, scales, to_dev(cb), to_dev(x.view(np.float16)), to_dev(route), rows, cols,
+    y = vq.dequant_gemv_packed(packed, scales, to_dev(cb), to_dev(x.view(np.float16)), to_dev(route), rows, cols,
                         fmt=fmt).cpu().numpy()
     _check_gemv(y, [whs[e % 2] for e in range(E)], synthetic.f16_bits_to_f32(x).reshape(ntok, cols), route)
 
@@ -519,7 +534,7 @@ def test_gemv_full_layer_w2_sampled(cfg1, fmt):
     scales = to_dev(scs.view(np.float16)).repeat(E // 2, 1)
     x = synthetic.activations_f16(ntok, cols, seed=13)
     route = synthetic.routing(ntok, E, topk, seed=14)
-    y = vq.dequant_gemv(packed, scales, to_dev(cb), to_dev(x.view(np.float16)), to_dev(route), rows, cols,
+    y = vq.dequant_gemv_packed(packed, scales, to_dev(cb), to_dev(x.view(np.float16)), to_dev(route), rows, cols,
                         fmt=fmt).cpu().numpy()
     _check_gemv(y, [whs[e % 2] for e in range(E)], synthetic.f16_bits_to_f32(x).reshape(ntok, cols), route)
 
@@ -532,12 +547,22 @@ def test_gemv_bad_route_flagged(cfg1):
     route = np.array([[0, 5]], np.int32)
     packed = vq.gemv_pack(to_dev(recs))
     with pytest.raises(vq.VQError):
-        vq.dequant_gemv(packed, to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
+        vq.dequant_gemv_packed(packed, to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
                         to_dev(route), 32, 64, check=True)
     # the valid slot is still computed; the bad one is zero
-    y = vq.dequant_gemv(packed, to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
+    y = vq.dequant_gemv_packed(packed, to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
                         to_dev(route), 32, 64).cpu().numpy()
     assert np.all(y[0, 1] == 0) and np.any(y[0, 0] != 0)
+    # the stored-record call reads no expert for the bad id, flags it, zeroes its slot
+    with pytest.raises(vq.VQError):
+        vq.dequant_gemv(to_dev(recs), to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
+                        to_dev(route), check=True)
+    for bad in (-1, 2, 1 << 30):
+        r2 = np.array([[bad, 0, 1, bad]], np.int32)
+        ys = vq.dequant_gemv(to_dev(recs), to_dev(scs.view(np.float16)), to_dev(cb), to_dev(x.view(np.float16)),
+                             to_dev(r2)).cpu().numpy()
+        assert np.all(ys[0, 0] == 0) and np.all(ys[0, 3] == 0)
+        assert np.array_equal(ys[0, 1].view(np.uint32), y[0, 0].view(np.uint32))
 
 
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
@@ -638,18 +663,25 @@ def test_random_shapes_parity(cfg1, seed):
         w_ref = oracle.decode(idx_o, s_o, cb)
         got = vq.decode(rec, s, cbd, fmt=fmt).cpu().numpy()
         assert np.array_equal(got.view(np.uint32), w_ref.view(np.uint32)), tag
-        sums = vq.error_sums(Wd, rec, s, cbd, fmt=fmt).cpu().numpy()[0]
+        rel = vq.rel_errors(Wd, rec, s, cbd, fmt=fmt)[0].cpu().numpy()[0]
         if np.any(W):
             for su in range(1, S + 1):
                 ref = oracle.rel_error(W, oracle.decode(idx_o, s_o, cb, stages_used=su))
-                assert abs(np.sqrt(sums[su - 1] / sums[S]) - ref) <= 1e-5, tag + (su,)
+                assert abs(rel[su - 1] - ref) <= 1e-5, tag + (su,)
+        else:
+            assert np.all(rel == 0), tag  # zeros reconstructed as zeros
         E, ntok = int(rng.integers(1, 5)), int(rng.integers(1, 6))
         topk = int(rng.integers(1, E + 1))
         packed = vq.gemv_pack(rec[None].expand(E, -1, -1, -1).contiguous(), fmt=fmt)
         x = synthetic.activations_f16(ntok, cols, seed=case)
         route = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(ntok)]).astype(np.int32)
-        y = vq.dequant_gemv(packed, s[None].expand(E, -1).contiguous(), cbd, to_dev(x.view(np.float16)),
-                            to_dev(route), rows, cols, fmt=fmt).cpu().numpy()
+        sE = s[None].expand(E, -1).contiguous()
+        y = vq.dequant_gemv_packed(packed, sE, cbd, to_dev(x.view(np.float16)),
+                                   to_dev(route), rows, cols, fmt=fmt).cpu().numpy()
+        # the stored-record call runs the same kernels on its own packed copies
+        ys = vq.dequant_gemv(rec[None].expand(E, -1, -1, -1).contiguous(), sE, cbd, to_dev(x.view(np.float16)),
+                             to_dev(route), fmt=fmt).cpu().numpy()
+        assert np.array_equal(ys.view(np.uint32), y.view(np.uint32)), tag
         xf = synthetic.f16_bits_to_f32(x).reshape(ntok, cols)
         for b in range(ntok):
             ref, scale = oracle.gemv_ref(w_ref, xf[b])
