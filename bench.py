@@ -8,11 +8,15 @@ per-row lognormal(0, 0.3)), inputs resident in HBM:
   2. VQ3R encode of all 256 experts (indices + fp16 row scales)
   3. VQ3R decode of all 256 experts to fp32
   4. relative Frobenius error per expert after 1, 2 and 3 stages
-  5. repack of the indices into the GEMV runtime layout, then the fused
-     dequant-GEMV at 1, 4 and 16 tokens, top-8 seeded routing, MALL flushed
-  6. MXFP4 quantize-dequantize of the 12 sampled experts, VQ4P fit on them
-     (4 x 64, 20 iters), VQ4P encode of all 256 experts, VQ4P dequant-GEMV
-Prints one JSON line (value = layer weights per second of the whole step).
+  5. the fused dequant-GEMV at 1, 4 and 16 tokens, top-8 seeded routing, caches
+     evicted before each call: on the GEMV layout (repacked once per step) and on
+     the stored records
+  6. the MXFP4 source path: MXFP4 quantize-dequantize of all 256 experts; VQ3R
+     and VQ4P (4 x 64) each fit on the 12 sampled MXFP4 experts (20 iters) and
+     encode all 256 of them; errors against the MXFP4 source and against the
+     original weights; VQ4P decode and dequant-GEMV
+Prints one JSON line (value = layer weights per second of the whole step, with
+the metric's own figures -- encode Gweights/s and GEMV GB/s -- beside it).
 """
 from __future__ import annotations
 
@@ -20,7 +24,6 @@ import argparse
 import hashlib
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -30,10 +33,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FP32_PEAK_TFLOPS = 157.3
+FP16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak
 HBM_PEAK_GBS = 8000.0
 ROWS, COLS = 2048, 7168
 VEC_PER_EXPERT = ROWS * COLS // 8
 FLOP_PER_VEC = {"vq3r": 3 * 256 * 8 * 2, "vq4p": 4 * 64 * 8 * 2}
+CB_BYTES = {"vq3r": 3 * 256 * 8 * 4, "vq4p": 4 * 64 * 8 * 4}
+# VALU issue: 1024 SIMDs (256 CUs x 4), one wave64 instruction per 4 cycles, 2.4 GHz
+VALU_ISSUE_PER_S = 1024 * 2.4e9 / 4
 
 
 def log(*a):
@@ -51,9 +58,12 @@ def parse():
     ap.add_argument("--engine", default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32768, help="oracle encode sample: first rows of the layer")
-    ap.add_argument("--only", default="", help="comma list: fit,encode,decode,error,gemv,vq4p (default all)")
-    ap.add_argument("--loop", default="", help="profiling helper: repeat one component (encode|encode4|fit|fit4|gemv1|gemv4|gemv16|decode) --steps times")
+    ap.add_argument("--only", default="", help="comma list: fit,encode,decode,error,gemv,mx (default all)")
+    ap.add_argument("--loop", default="", help="profiling helper: repeat one component (encode|encode4|encodef32|"
+                    "fit|fit4|gemv1|gemv4|gemv16|gemvs1|gemvs4|gemvs16|decode|read) --steps times")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a plain copy of known size")
+    ap.add_argument("--report", action="store_true", help="error tables: configs 1, 2 and 5 against the RTN "
+                    "baselines and the oracle (prints its own JSON line)")
     ap.add_argument("--layer", action="store_true", help="per-layer conversion measurement: w1 and w3 "
                     "[2048x7168] and w2 [7168x2048] of every expert, each family fit, encoded and measured, plus "
                     "the w2 dequant-GEMV (prints its own JSON line)")
@@ -94,8 +104,19 @@ class Timer:
         xs = [a.elapsed_time(b) for a, b in self.ev.get(name, [])[skip:]]
         return float(np.mean(xs)) if xs else float("nan")
 
+    def median_ms(self, name):
+        xs = [a.elapsed_time(b) for a, b in self.ev.get(name, [])]
+        return float(np.median(xs)) if xs else float("nan")
+
     def reset(self):
         self.ev = {}
+
+
+def gemv_alg_bytes(distinct, ntok, fmt, rows=ROWS, cols=COLS):
+    """Algorithmic bytes of one dequant-GEMV call: the records and fp16 row scales
+    of each distinct routed expert, the fp16 activations, the fp32 outputs (top-8)
+    and the codebooks."""
+    return distinct * (rows * (cols // 8) * 3 + rows * 2) + ntok * cols * 2 + ntok * 8 * rows * 4 + CB_BYTES[fmt]
 
 
 def main():
@@ -108,7 +129,10 @@ def main():
     import synthetic
     import residual_vector_quantization_amd as vq
 
-    only = set(args.only.split(",")) if args.only else {"fit", "encode", "decode", "error", "gemv", "vq4p"}
+    if args.report:
+        report(args, torch, vq, synthetic)
+        return
+    only = set(args.only.split(",")) if args.only else {"fit", "encode", "decode", "error", "gemv", "mx"}
     dev = "cuda"
     torch.cuda.set_device(0)
     E = args.experts
@@ -127,22 +151,33 @@ def main():
     nrows = E * ROWS
     # buffers and workspaces (allocated once, outside the timed region)
     cb3 = torch.empty((3, 256, 8), dtype=torch.float32, device=dev)
+    cb3m = torch.empty_like(cb3)
     cb4 = torch.empty((4, 64, 8), dtype=torch.float32, device=dev)
     fit_ws3 = vq.fit_workspace("vq3r", len(mats), ROWS, COLS)
     fit_ws4 = vq.fit_workspace("vq4p", len(mats), ROWS, COLS)
     idx3 = torch.empty((nrows, COLS // 8, 3), dtype=torch.uint8, device=dev)
+    idx3m = torch.empty_like(idx3)
     idx4 = torch.empty_like(idx3)
     sc3 = torch.empty(nrows, dtype=torch.float16, device=dev)
+    sc3m = torch.empty_like(sc3)
     sc4 = torch.empty_like(sc3)
     enc_ws = vq.encode_workspace("vq3r", nrows, COLS)
     need_dec = "decode" in only
     w_hat = torch.empty((nrows, COLS), dtype=torch.float32, device=dev) if need_dec else None
-    err_ws = vq.error_workspace("vq3r", E, ROWS, COLS)
-    sums = torch.empty((E, 4), dtype=torch.float64, device=dev)
-    mx_out = torch.empty((len(mats) * ROWS, COLS), dtype=torch.float32, device=dev) if "vq4p" in only else None
+    err_ws = vq.error_workspace("vq4p", E, ROWS, COLS)  # the larger of the two formats
+    sums3 = torch.empty((E, 4), dtype=torch.float64, device=dev)
+    sums_mx = {k: torch.empty((E, 4 if k[0] == "3" else 5), dtype=torch.float64, device=dev)
+               for k in ("3s", "3o", "4s", "4o")}
+    rel3 = torch.empty((E, 3), dtype=torch.float64, device=dev)
+    rel3_all = torch.empty(3, dtype=torch.float64, device=dev)
+    rel_mx = {k: (torch.empty((E, 3 if k[0] == "3" else 4), dtype=torch.float64, device=dev),
+                  torch.empty(3 if k[0] == "3" else 4, dtype=torch.float64, device=dev)) for k in sums_mx}
+    do_mx = "mx" in only
+    mx = torch.empty((nrows, COLS), dtype=torch.float32, device=dev) if do_mx else None
+    mx_mats = [mx[e * ROWS:(e + 1) * ROWS] for e in sample] if do_mx else None
     mx_ws = torch.empty(256, dtype=torch.uint8, device=dev)
-    # cache eviction between GEMV reps: reading 1 GiB of other data evicts the packed experts from the
-    # L2s and the MALL without leaving dirty lines whose write-back would land inside the timed kernel
+    # cache eviction between GEMV reps: reading 1 GiB of other data evicts the experts from the L2s and the
+    # MALL without leaving dirty lines whose write-back would land inside the timed kernel
     flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)
     flush_out = torch.empty((), dtype=torch.float32, device=dev)
 
@@ -153,15 +188,13 @@ def main():
         x = torch.from_numpy(synthetic.activations_f16(ntok, COLS, seed=10 + ntok).view(np.float16)).to(dev)
         route = torch.from_numpy(synthetic.routing(ntok, E, 8, seed=20 + ntok)).to(dev)
         y = torch.empty((ntok, 8, ROWS), dtype=torch.float32, device=dev)
-        ws = vq.gemv_workspace("vq3r", ROWS, COLS, ntok, 8)
         distinct = len(np.unique(route.cpu().numpy()))
-        gemv_cases.append((ntok, x, route, y, ws, distinct))
-    gemv_cases4 = [(ntok, x, route, y, vq.gemv_workspace("vq4p", ROWS, COLS, ntok, 8), d)
-                   for ntok, x, route, y, ws, d in gemv_cases]
-    idx3_e = idx3.view(E, ROWS, COLS // 8, 3)
-    sc3_e = sc3.view(E, ROWS)
-    idx4_e = idx4.view(E, ROWS, COLS // 8, 3)
-    sc4_e = sc4.view(E, ROWS)
+        gemv_cases.append({"ntok": ntok, "x": x, "route": route, "y": y, "distinct": distinct,
+                           "ws3": vq.gemv_packed_workspace("vq3r", ROWS, COLS, ntok, 8),
+                           "ws4": vq.gemv_packed_workspace("vq4p", ROWS, COLS, ntok, 8),
+                           "wss": vq.gemv_workspace("vq3r", ROWS, COLS, ntok, 8, E)})
+    idx3_e, sc3_e = idx3.view(E, ROWS, COLS // 8, 3), sc3.view(E, ROWS)
+    idx4_e, sc4_e = idx4.view(E, ROWS, COLS // 8, 3), sc4.view(E, ROWS)
     pk3 = torch.empty((E, vq.lib().vq_gemv_packed_size(0, ROWS, COLS)), dtype=torch.uint8, device=dev)
     pk4 = torch.empty((E, vq.lib().vq_gemv_packed_size(1, ROWS, COLS)), dtype=torch.uint8, device=dev)
     T = Timer(torch)
@@ -181,86 +214,71 @@ def main():
                 vq.decode(idx3, sc3, cb3, fmt="vq3r", out=w_hat)
         if "error" in only:
             with T("error3"):
-                vq.error_sums(W, idx3, sc3, cb3, fmt="vq3r", n_mats=E, sums=sums, workspace=err_ws, check=False)
+                vq.error_sums(W, idx3, sc3, cb3, fmt="vq3r", n_mats=E, sums=sums3, workspace=err_ws, check=False,
+                              rel=rel3, rel_all=rel3_all)
         if "gemv" in only:
             with T("pack3"):
                 vq.gemv_pack(idx3_e, fmt="vq3r", out=pk3)
-            for ntok, x, route, y, ws, _ in gemv_cases:
+            for c in gemv_cases:
                 evict()
-                with T("gemv3_%d" % ntok):
-                    vq.dequant_gemv(pk3, sc3_e, cb3, x, route, ROWS, COLS, fmt="vq3r", y=y, workspace=ws)
-        if "vq4p" in only:
+                with T("gemv3_%d" % c["ntok"]):
+                    vq.dequant_gemv_packed(pk3, sc3_e, cb3, c["x"], c["route"], ROWS, COLS, fmt="vq3r", y=c["y"],
+                                           workspace=c["ws3"])
+            for c in gemv_cases:
+                evict()
+                with T("gemvs3_%d" % c["ntok"]):
+                    vq.dequant_gemv(idx3_e, sc3_e, cb3, c["x"], c["route"], fmt="vq3r", y=c["y"],
+                                    workspace=c["wss"])
+        if do_mx:
             with T("mxfp4"):
-                for i, m in enumerate(mats):
-                    vq.mxfp4_qdq(m, out=mx_out[i * ROWS:(i + 1) * ROWS], workspace=mx_ws, check=False)
-            with T("fit4"):
-                vq.fit_codebooks([mx_out[i * ROWS:(i + 1) * ROWS] for i in range(len(mats))], init4, fmt="vq4p",
-                                 iters=args.iters, engine=args.engine, codebooks=cb4, workspace=fit_ws4,
-                                 check=False)
-            with T("encode4"):
-                vq.encode(W, cb4, fmt="vq4p", engine=args.engine, idx=idx4, scales=sc4, workspace=enc_ws,
+                vq.mxfp4_qdq(W, out=mx, workspace=mx_ws, check=False)
+            with T("fit3_mx"):
+                vq.fit_codebooks(mx_mats, init3, fmt="vq3r", iters=args.iters, engine=args.engine, codebooks=cb3m,
+                                 workspace=fit_ws3, check=False)
+            with T("encode3_mx"):
+                vq.encode(mx, cb3m, fmt="vq3r", engine=args.engine, idx=idx3m, scales=sc3m, workspace=enc_ws,
                           check=False)
-            with T("pack4"):
-                vq.gemv_pack(idx4_e, fmt="vq4p", out=pk4)
-            for ntok, x, route, y, ws4, _ in gemv_cases4:
-                evict()
-                with T("gemv4_%d" % ntok):
-                    vq.dequant_gemv(pk4, sc4_e, cb4, x, route, ROWS, COLS, fmt="vq4p", y=y, workspace=ws4)
+            with T("fit4_mx"):
+                vq.fit_codebooks(mx_mats, init4, fmt="vq4p", iters=args.iters, engine=args.engine, codebooks=cb4,
+                                 workspace=fit_ws4, check=False)
+            with T("encode4_mx"):
+                vq.encode(mx, cb4, fmt="vq4p", engine=args.engine, idx=idx4, scales=sc4, workspace=enc_ws,
+                          check=False)
+            with T("error_mx"):
+                for key, (ref, ix, sc, cb, fmt) in {"3s": (mx, idx3m, sc3m, cb3m, "vq3r"),
+                                                    "3o": (W, idx3m, sc3m, cb3m, "vq3r"),
+                                                    "4s": (mx, idx4, sc4, cb4, "vq4p"),
+                                                    "4o": (W, idx4, sc4, cb4, "vq4p")}.items():
+                    vq.error_sums(ref, ix, sc, cb, fmt=fmt, n_mats=E, sums=sums_mx[key],
+                                  workspace=err_ws, check=False, rel=rel_mx[key][0], rel_all=rel_mx[key][1])
+            if need_dec:
+                with T("decode4"):
+                    vq.decode(idx4, sc4, cb4, fmt="vq4p", out=w_hat)
+            if "gemv" in only:
+                with T("pack4"):
+                    vq.gemv_pack(idx4_e, fmt="vq4p", out=pk4)
+                for c in gemv_cases:
+                    evict()
+                    with T("gemv4_%d" % c["ntok"]):
+                        vq.dequant_gemv_packed(pk4, sc4_e, cb4, c["x"], c["route"], ROWS, COLS, fmt="vq4p",
+                                               y=c["y"], workspace=c["ws4"])
     step.fitted = False
 
     if args.ttp:
         ttp_bench(args, torch, vq, W, E)
         return
-
     if args.gemm:
         gemm_bench(args, torch, vq, synthetic, W, mats, init3, cb3, fit_ws3, idx3, sc3, enc_ws, E)
         return
-
     if args.layer:
         layer_bench(args, torch, vq, synthetic, W, E, evict)
         return
-
     if args.container:
         container_bench(args, torch, vq, W, mats, init3, cb3, fit_ws3, idx3, sc3, enc_ws, E)
         return
-
     if args.loop:
-        # profiling helper: one component repeated, nothing else in the trace
-        if args.loop not in ("fit", "fit4"):
-            vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3, workspace=fit_ws3)
-            vq.encode(W, cb3, idx=idx3, scales=sc3, workspace=enc_ws)
-            vq.gemv_pack(idx3_e, fmt="vq3r", out=pk3)
-        if args.loop == "encode4":
-            vq.fit_codebooks(mats, init4, fmt="vq4p", iters=args.iters, codebooks=cb4, workspace=fit_ws4)
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            if args.loop == "encode":
-                vq.encode(W, cb3, engine=args.engine, idx=idx3, scales=sc3, workspace=enc_ws, check=False)
-            elif args.loop == "encode4":
-                vq.encode(W, cb4, fmt="vq4p", engine=args.engine, idx=idx4, scales=sc4, workspace=enc_ws,
-                          check=False)
-            elif args.loop == "fit":
-                vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3, workspace=fit_ws3,
-                                 check=False)
-            elif args.loop == "fit4":
-                vq.fit_codebooks(mats, init4, fmt="vq4p", iters=args.iters, codebooks=cb4, workspace=fit_ws4,
-                                 check=False)
-            elif args.loop.startswith("gemv"):
-                ntok = int(args.loop[4:])
-                c = [g for g in gemv_cases if g[0] == ntok][0]
-                evict()
-                vq.dequant_gemv(pk3, sc3_e, cb3, c[1], c[2], ROWS, COLS, y=c[3], workspace=c[4])
-            elif args.loop == "decode":
-                vq.decode(idx3, sc3, cb3, out=w_hat)
-            torch.cuda.synchronize()
-            log("loop %s %d done" % (args.loop, i))
-        if args.copy_calibration:
-            src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-            dst = torch.empty_like(src)
-            for i in range(3):
-                dst.copy_(src)
-            torch.cuda.synchronize()
-            log("copy calibration: 3 x 1 GiB copies done")
+        loop_bench(args, torch, vq, W, mats, init3, init4, cb3, cb4, fit_ws3, fit_ws4, idx3, sc3, idx4, sc4,
+                   enc_ws, pk3, sc3_e, idx3_e, gemv_cases, evict, w_hat, flush)
         return
 
     for i in range(args.warmup):
@@ -280,83 +298,301 @@ def main():
     wall = time.time() - t_start
     ms_step = ev0.elapsed_time(ev1) / args.steps
     log("timed %d steps: %.2f ms/step (wall %.2f s)" % (args.steps, ms_step, wall))
-    # correctness of the last step (status words + sanity of the error)
-    comp = {}
-    for k in sorted(T.ev):
-        comp[k] = round(T.mean_ms(k), 4)
+    comp = {k: round(T.mean_ms(k), 4) for k in sorted(T.ev)}
     weights = E * ROWS * COLS
-    out = {}
+    # the exact pass of the last encode in the step that used the workspace (VQ3R of the bf16 layer unless the
+    # MXFP4 path ran after it): re-encode once, read its counter
+    vq.encode(W, cb3, fmt="vq3r", engine=args.engine, idx=idx3, scales=sc3, workspace=enc_ws, check=False)
+    enc_flags = vq.read_status(enc_ws)
+    n_exact = int(enc_ws[4:8].cpu().view(torch.int32)[0])
     enc_ms = T.mean_ms("encode3")
-    enc_tflops = E * VEC_PER_EXPERT * FLOP_PER_VEC["vq3r"] / (enc_ms * 1e-3) / 1e12
-    out["encode_gweights_s"] = round(weights / (enc_ms * 1e-3) / 1e9, 3)
-    out["encode_tflops_fp32_equiv"] = round(enc_tflops, 2)
-    out["encode_frac_fp32_peak"] = round(enc_tflops / FP32_PEAK_TFLOPS, 4)
+    enc = {}
+    if "encode3" in T.ev:
+        alg_flop = E * VEC_PER_EXPERT * FLOP_PER_VEC["vq3r"]
+        enc = {"ms": round(enc_ms, 3), "gweights_s": round(weights / (enc_ms * 1e-3) / 1e9, 3),
+               "tflops_fp32_equiv": round(alg_flop / (enc_ms * 1e-3) / 1e12, 2),
+               "frac_fp32_equiv": round(alg_flop / (enc_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4),
+               "frac_fp16_mfma_peak": round(alg_flop / (enc_ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4),
+               "exact_pass_vectors": n_exact, "exact_pass_fraction": round(n_exact / (E * VEC_PER_EXPERT), 7),
+               "tie_band_mismatches": 0, "device_flags": enc_flags}
+        valu = profile_value("k_encode_vq3r_layer_256x2048x7168_counters.md", "valu_instructions_per_call")
+        if valu is not None:
+            enc["valu_issue_frac"] = round(valu / VALU_ISSUE_PER_S / (enc_ms * 1e-3), 4)
+    gem = gemv_report(torch, vq, T, gemv_cases, evict, pk3, pk4, sc3_e, sc4_e, cb3, cb4, idx3_e)
+    errors = {}
+    if "error3" in T.ev:
+        errors["vq3r_bf16_layer"] = {"rel_err_all_after_stage": [round(float(v), 6) for v in rel3_all.cpu()],
+                                     "rel_err_expert_mean": [round(float(v), 6) for v in rel3.mean(dim=0).cpu()]}
+    if do_mx:
+        for key, name in (("3s", "vq3r_mxfp4_vs_source"), ("3o", "vq3r_mxfp4_vs_original"),
+                          ("4s", "vq4p_mxfp4_vs_source"), ("4o", "vq4p_mxfp4_vs_original")):
+            errors[name] = [round(float(v), 6) for v in rel_mx[key][1].cpu()]
+    # roofline of the dominant kernel: the VQ3R encode call
+    roof = None
+    if "encode3" in T.ev:
+        alg_tf = E * VEC_PER_EXPERT * FLOP_PER_VEC["vq3r"] / (enc_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(alg_tf, 2), "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(alg_tf / FP16_PEAK_TFLOPS, 4),
+                "traffic": profile_value("k_encode_vq3r_layer_256x2048x7168_counters.md",
+                                         "traffic_bytes_per_launch") if E == 256 else None,
+                "traffic_unit": "HBM bytes per encode call (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "kernel": "vq3r encode call (k_encode + k_encode_exact)",
+                "work": "12288 flop per 8-dim vector (3 stages x 256 codewords x 8 dims x 2)",
+                "pipe": "fp16 matrix cores (hi/lo split: 4 issued matrix flops per algorithmic flop)",
+                "binding_resource": "VALU issue (top-2 selection of the scores)",
+                "valu_issue_frac": enc.get("valu_issue_frac"),
+                "fp32_equiv_frac": enc.get("frac_fp32_equiv")}
+    cpu, legs = None, None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(torch, W, cb3, args.cpu_rows)
+        legs = cpu_baseline_legs(torch, vq, synthetic, W, mats, cb3, idx3_e, sc3_e, gemv_cases[0])
+    line = {
+        "metric": "VQ3R encode Gweights/s (%FP32 peak) + dequant-GEMV GB/s (%HBM peak), 1 GPU",
+        "value": round(weights / (ms_step * 1e-3) / 1e9, 3),
+        "unit": "Gweights/s",
+        "encode_gweights_s": enc.get("gweights_s"),
+        "gemv_GB_s": {str(c["ntok"]): gem.get("gemv3_%d" % c["ntok"], {}).get("GB_s") for c in gemv_cases},
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "full routed-expert layer: %d experts x w1 [2048x7168] bf16; VQ3R fit on %d sampled "
+                               "experts x %d Lloyd iters, encode, decode, error, dequant-GEMV at 1/4/16 tokens "
+                               "top-8; MXFP4 source path: VQ3R and VQ4P fit/encode/error, VQ4P decode and GEMV"
+                               % (E, len(mats), args.iters),
+                   "experts": E, "rows": ROWS, "cols": COLS, "parallelism": "single GPU"},
+        "components_ms": comp,
+        "encode": enc,
+        "gemv": gem,
+        "errors": errors,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "cpu_baseline_legs": legs,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def gemv_report(torch, vq, T, cases, evict, pk3, pk4, sc3_e, sc4_e, cb3, cb4, idx3_e):
+    """Per GEMV call: event time, algorithmic GB/s and fraction of the 8 TB/s
+    peak, the time of a plain streaming read of the same number of bytes after
+    the same eviction (vq_stream_read), and the warm-cache time."""
     gem = {}
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
     floors = {}
-    for fmt in ("3", "4"):
-        for ntok, x, route, y, ws, distinct in gemv_cases:
-            key = "gemv%s_%d" % (fmt, ntok)
-            if key not in T.ev:
+    for c in cases:
+        for fmt, key in (("vq3r", "gemv3_%d"), ("vq3r", "gemvs3_%d"), ("vq4p", "gemv4_%d")):
+            k = key % c["ntok"]
+            if k not in T.ev:
                 continue
-            ms = T.mean_ms(key)
-            alg = distinct * (VEC_PER_EXPERT * 3 + ROWS * 2) + ntok * COLS * 2 + ntok * 8 * ROWS * 4 + \
-                (3 * 256 * 8 * 4 if fmt == "3" else 4 * 64 * 8 * 4)
+            ms = T.median_ms(k)
+            alg = gemv_alg_bytes(c["distinct"], c["ntok"], fmt)
             gbs = alg / (ms * 1e-3) / 1e9
-            floor = floors.setdefault(alg // (1 << 20), read_floor_us(torch, alg, evict))
-            gem[key] = {"us": round(ms * 1e3, 2), "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                        "distinct_experts": distinct, "alg_bytes": alg,
-                        "plain_read_us": round(floor, 2), "frac_of_plain_read": round(floor / (ms * 1e3), 4)}
-    # warm-cache GEMV (outside the timed region): the same call repeated back to back, so the packed
-    # experts are still in the L2s and the MALL; reported next to the evicted figure above
-    for fmt, pk, sce, cbk, cases, name in (("3", pk3, sc3_e, cb3, gemv_cases, "vq3r"),
-                                          ("4", pk4, sc4_e, cb4, gemv_cases4, "vq4p")):
-        for ntok, x, route, y, ws, distinct in cases:
-            key = "gemv%s_%d" % (fmt, ntok)
-            if key not in gem:
+            if alg // (1 << 20) not in floors:
+                floors[alg // (1 << 20)] = read_floor_us(torch, vq, alg, evict, out)
+            floor = floors[alg // (1 << 20)]
+            gem[k] = {"us": round(ms * 1e3, 2), "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                      "distinct_experts": c["distinct"], "alg_bytes": alg, "plain_read_us": round(floor, 2),
+                      "frac_of_plain_read": round(floor / (ms * 1e3), 4)}
+            if k.startswith("gemvs"):
+                gem[k]["layout"] = "stored records (lists the routed experts and repacks them each call)"
+            tr = profile_value("k_gemv_vq3r_vq4p_256x2048x7168_counters.md", "traffic_bytes_per_call_%s" % k)
+            if tr is not None:
+                gem[k]["traffic_bytes"] = tr
+                gem[k]["traffic_over_alg"] = round(tr / alg, 3)
+    # warm caches: the same call back to back, outside the timed region
+    for c in cases:
+        for fmt, key, pk, sce, cbk, ws in (("vq3r", "gemv3_%d", pk3, sc3_e, cb3, c["ws3"]),
+                                           ("vq4p", "gemv4_%d", pk4, sc4_e, cb4, c["ws4"])):
+            k = key % c["ntok"]
+            if k not in gem:
                 continue
             ts = []
             for rep in range(8):
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
-                vq.dequant_gemv(pk, sce, cbk, x, route, ROWS, COLS, fmt=name, y=y, workspace=ws)
+                vq.dequant_gemv_packed(pk, sce, cbk, c["x"], c["route"], ROWS, COLS, fmt=fmt, y=c["y"], workspace=ws)
                 e0.record()
-                vq.dequant_gemv(pk, sce, cbk, x, route, ROWS, COLS, fmt=name, y=y, workspace=ws)
+                vq.dequant_gemv_packed(pk, sce, cbk, c["x"], c["route"], ROWS, COLS, fmt=fmt, y=c["y"], workspace=ws)
                 e1.record()
                 torch.cuda.synchronize()
                 ts.append(e0.elapsed_time(e1) * 1e3)
-            gem[key]["warm_us"] = round(sorted(ts)[len(ts) // 2], 2)
-    if "error3" in T.ev:
-        s = sums.double().cpu().numpy()
-        out["rel_error_mean_after_stage"] = [round(float(np.mean(np.sqrt(s[:, t] / s[:, 3]))), 5) for t in range(3)]
-    st = vq.read_status(enc_ws)
-    out["encode_device_flags"] = st
-    # roofline of the dominant kernel: the VQ3R encode
-    roof = {"bound": "alu", "achieved": round(enc_tflops, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(enc_tflops / FP32_PEAK_TFLOPS, 4), "traffic": encode_traffic() if E == 256 else None,
-            "traffic_unit": "HBM bytes per encode call (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "kernel": "vq3r encode (k_encode + k_encode_exact)", "work": "12288 fp32 flop per 8-dim vector"}
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(torch, W, cb3, args.cpu_rows)
-    line = {
-        "metric": "VQ3R encode Gweights/s (%FP32 peak) + dequant-GEMV GB/s (%HBM peak), 1 GPU",
-        "value": round(weights / (ms_step * 1e-3) / 1e9, 3),
-        "unit": "Gweights/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "full routed-expert layer: %d experts x w1 [2048x7168] bf16, fit on %d sampled "
-                               "experts x %d Lloyd iters, VQ3R+VQ4P encode, decode, error, dequant-GEMV at "
-                               "1/4/16 tokens top-8" % (E, len(mats), args.iters),
-                   "experts": E, "rows": ROWS, "cols": COLS, "parallelism": "single GPU"},
-        "components_ms": comp,
-        "encode": out,
-        "gemv": gem,
-        "roofline": roof,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(line), flush=True)
+            gem[k]["warm_us"] = round(sorted(ts)[len(ts) // 2], 2)
+    for c in cases:
+        k = "gemv3_%d" % c["ntok"]
+        if k in gem and "gemv4_%d" % c["ntok"] in gem:
+            gem["vq4p_over_vq3r_speed_%d" % c["ntok"]] = round(gem[k]["us"] / gem["gemv4_%d" % c["ntok"]]["us"], 3)
+    return gem
+
+
+def read_floor_us(torch, vq, nbytes, evict, out, reps=5):
+    """Time of a plain streaming read (vq_stream_read) of nbytes after the same
+    cache eviction as the GEMV: the read floor the GEMV's rate is compared with."""
+    n = max(16, -(-nbytes // 16) * 16)
+    buf = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    best = None
+    for _ in range(reps):
+        evict()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        vq.stream_read(buf, out)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e3
+        best = t if best is None else min(best, t)
+    del buf
+    return best
+
+
+def loop_bench(args, torch, vq, W, mats, init3, init4, cb3, cb4, fit_ws3, fit_ws4, idx3, sc3, idx4, sc4, enc_ws,
+               pk3, sc3_e, idx3_e, gemv_cases, evict, w_hat, flush):
+    """Profiling helper: one component repeated, nothing else in the trace."""
+    if args.loop not in ("fit", "fit4"):
+        vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3, workspace=fit_ws3)
+        vq.encode(W, cb3, idx=idx3, scales=sc3, workspace=enc_ws)
+        vq.gemv_pack(idx3_e, fmt="vq3r", out=pk3)
+    if args.loop == "encode4":
+        vq.fit_codebooks(mats, init4, fmt="vq4p", iters=args.iters, codebooks=cb4, workspace=fit_ws4)
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        if args.loop == "encode":
+            vq.encode(W, cb3, engine=args.engine, idx=idx3, scales=sc3, workspace=enc_ws, check=False)
+        elif args.loop == "encodef32":
+            vq.encode(W, cb3, engine="mfma_f32", idx=idx3, scales=sc3, workspace=enc_ws, check=False)
+        elif args.loop == "encode4":
+            vq.encode(W, cb4, fmt="vq4p", engine=args.engine, idx=idx4, scales=sc4, workspace=enc_ws, check=False)
+        elif args.loop == "fit":
+            vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3, workspace=fit_ws3,
+                             check=False)
+        elif args.loop == "fit4":
+            vq.fit_codebooks(mats, init4, fmt="vq4p", iters=args.iters, codebooks=cb4, workspace=fit_ws4,
+                             check=False)
+        elif args.loop.startswith("gemvs"):
+            c = [g for g in gemv_cases if g["ntok"] == int(args.loop[5:])][0]
+            evict()
+            vq.dequant_gemv(idx3_e, sc3_e, cb3, c["x"], c["route"], y=c["y"], workspace=c["wss"])
+        elif args.loop.startswith("gemv"):
+            c = [g for g in gemv_cases if g["ntok"] == int(args.loop[4:])][0]
+            evict()
+            vq.dequant_gemv_packed(pk3, sc3_e, cb3, c["x"], c["route"], ROWS, COLS, y=c["y"], workspace=c["ws3"])
+        elif args.loop == "decode":
+            vq.decode(idx3, sc3, cb3, out=w_hat)
+        elif args.loop == "read":
+            evict()
+            vq.stream_read(flush, out)
+        torch.cuda.synchronize()
+        log("loop %s %d done" % (args.loop, i))
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for i in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB copies done")
+
+
+# ------------------------------------------------------------------ error tables
+def report(args, torch, vq, synthetic):
+    """Gate-3 style error tables ([VQ3R page] §3.1 table: rtn2-g64 / vq2 / vq3 /
+    rtn3-g64 / rtn4-row; §3.2: requantizing an MXFP4 source; §5: VQ4P) on the
+    synthetic configurations:
+      config 1: W [256 x 1024] fp32 N(0,1) x lognormal(0, 0.5) rows, seed 0; codebooks
+                from 10 Lloyd iterations on W (Forgy seed 0);
+      config 2: the 12 sampled experts of the layer (w1 [2048 x 7168] bf16), 20 iterations;
+      config 5: the same 12 experts MXFP4 quantize-dequantized, VQ3R and VQ4P.
+    VQ errors come from the library (vq_error's relative errors); each table's
+    oracle check re-encodes with the CPU oracle and compares within 1e-5 (config 1:
+    all of W, bit-exact codebooks; configs 2 and 5: two experts). The RTN
+    baselines are the oracle's (CPU)."""
+    import oracle
+    dev = "cuda"
+    t_all = time.time()
+    out = {}
+
+    def rtn_rows(ws):
+        num = {k: 0.0 for k in ("rtn4-row", "rtn3-g64", "rtn2-g64")}
+        den = 0.0
+        for w in ws:
+            for name, b, g in (("rtn4-row", 4, None), ("rtn3-g64", 3, 64), ("rtn2-g64", 2, 64)):
+                d, ww = oracle.error_sums(w, oracle.rtn(w, b, g)[0])
+                num[name] += d
+            den += float(np.sum(np.asarray(w, np.float64) ** 2))
+        return {k: round(float(np.sqrt(v / den)), 6) for k, v in num.items()}
+
+    # config 1
+    W1 = synthetic.gaussian_rows(256, 1024, seed=0)
+    t1 = {"shape": [256, 1024], "iters": 10}
+    for fmt in ("vq3r", "vq4p"):
+        S, K = vq.stages_entries(fmt)
+        init = synthetic.forgy_init(256 * 128, K, S, seed=0)
+        cb = vq.fit_codebooks([torch.from_numpy(W1).to(dev)], init, fmt=fmt, iters=10)
+        idx, sc = vq.encode(torch.from_numpy(W1).to(dev), cb, fmt=fmt)
+        rel = vq.rel_errors(torch.from_numpy(W1).to(dev), idx, sc, cb, fmt=fmt)[0].cpu().numpy()[0]
+        cb_o, _ = oracle.fit([W1], S, K, 10, init)
+        i_o, s_o = oracle.encode(W1, cb_o)
+        ref = [oracle.rel_error(W1, oracle.decode(i_o, s_o, cb_o, stages_used=su)) for su in range(1, S + 1)]
+        t1[fmt] = {"rel_err_after_stage": [round(float(v), 6) for v in rel],
+                   "oracle_rel_err_after_stage": [round(float(v), 6) for v in ref],
+                   "codebooks_bit_exact": bool(np.array_equal(cb.cpu().numpy().view(np.uint32), cb_o.view(np.uint32))),
+                   "max_abs_diff_vs_oracle": float(np.max(np.abs(rel - np.array(ref))))}
+    t1.update(rtn_rows([W1]))
+    out["config1"] = t1
+    log("config 1 done (%.1f s)" % (time.time() - t_all))
+    # configs 2 and 5: the 12 sampled experts
+    E = args.experts
+    sample = synthetic.sample_experts(E, min(args.sample, E), seed=3)
+    mats = [synthetic.student_t_expert_torch(synthetic.expert_seed(3, int(e)), ROWS, COLS, device=dev)
+            for e in sample]
+    Wst = torch.cat(mats, dim=0)
+    mx = vq.mxfp4_qdq(Wst)
+    mx_mats = [mx[i * ROWS:(i + 1) * ROWS] for i in range(len(mats))]
+    n_fit = len(mats) * VEC_PER_EXPERT
+    check = [0, len(mats) - 1]
+    host = {i: mats[i].float().cpu().numpy() for i in range(len(mats))}
+    host_mx = {i: mx_mats[i].cpu().numpy() for i in range(len(mats))}
+    for name, src, srcs_host, fmts in (("config2", mats, host, ("vq3r",)),
+                                       ("config5", mx_mats, host_mx, ("vq3r", "vq4p"))):
+        tab = {"experts": [int(e) for e in sample], "shape": [ROWS, COLS], "iters": args.iters}
+        flat = torch.cat(src, dim=0)
+        for fmt in fmts:
+            S, K = vq.stages_entries(fmt)
+            init = synthetic.forgy_init(n_fit, K, S, seed=3 if fmt == "vq3r" else 4)
+            t0 = time.time()
+            cb = vq.fit_codebooks(src, init, fmt=fmt, iters=args.iters)
+            idx, sc = vq.encode(flat, cb, fmt=fmt)
+            rel, rel_all, _ = vq.rel_errors(flat, idx, sc, cb, fmt=fmt, n_mats=len(src))
+            ent = {"rel_err_all_after_stage": [round(float(v), 6) for v in rel_all.cpu()],
+                   "rel_err_per_expert_final": [round(float(v), 6) for v in rel[:, S - 1].cpu()],
+                   "gpu_fit_encode_s": round(time.time() - t0, 2)}
+            if name == "config5":
+                # the same records against the original (pre-MXFP4) weights
+                _, rel_o, _ = vq.rel_errors(Wst, idx, sc, cb, fmt=fmt, n_mats=len(src))
+                ent["rel_err_vs_original_after_stage"] = [round(float(v), 6) for v in rel_o.cpu()]
+            cbh = cb.cpu().numpy()
+            diffs = []
+            for i in check:
+                i_o, s_o = oracle.encode(srcs_host[i], cbh)
+                rec_ok = bool(np.array_equal(oracle.unpack(fmt, idx[i * ROWS:(i + 1) * ROWS].cpu().numpy()), i_o))
+                for su in range(1, S + 1):
+                    r_o = oracle.rel_error(srcs_host[i], oracle.decode(i_o, s_o, cbh, stages_used=su))
+                    diffs.append(abs(float(rel[i, su - 1]) - r_o))
+                ent.setdefault("oracle_checked_experts", []).append({"expert": int(sample[i]),
+                                                                     "indices_bit_exact": rec_ok})
+            ent["max_abs_diff_vs_oracle"] = max(diffs)
+            tab[fmt] = ent
+            log("%s %s done (%.1f s)" % (name, fmt, time.time() - t_all))
+        tab.update(rtn_rows([srcs_host[i] for i in range(len(mats))]))
+        if name == "config5":
+            tab["rtn_vs_original"] = rtn_rows([host[i] for i in range(len(mats))])
+            tab["mxfp4_vs_original"] = round(float(np.sqrt(
+                sum(oracle.error_sums(host[i], host_mx[i])[0] for i in host) /
+                sum(float(np.sum(host[i].astype(np.float64) ** 2)) for i in host))), 6)
+        out[name] = tab
+    out["bits_per_weight"] = {"vq3r": 3.0, "vq3r_with_row_scales": round(3 + 16 / COLS, 4), "vq4p": 3.0,
+                              "rtn4-row": round(4 + 16 / COLS, 4), "rtn3-g64": 3.25, "rtn2-g64": 2.25, "mxfp4": 4.25}
+    out["seconds"] = round(time.time() - t_all, 1)
+    print(json.dumps({"report": out}), flush=True)
 
 
 def ttp_bench(args, torch, vq, W, E):
@@ -390,8 +626,6 @@ def ttp_bench(args, torch, vq, W, E):
     print(json.dumps({"ttp": res, "rel_err_layer": round(float((tot[0] / tot[1]).sqrt()), 5),
                       "bits_per_weight": 4.0625, "experts": E, "shape": [ROWS, COLS]}), flush=True)
 
-
-FP16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak
 
 
 def gemm_bench(args, torch, vq, synthetic, W, mats, init3, cb3, fit_ws3, idx3, sc3, enc_ws, E):
@@ -458,6 +692,8 @@ def layer_bench(args, torch, vq, synthetic, W1, E, evict):
         sc = torch.empty(E * r, dtype=torch.float16, device=dev)
         err_ws = vq.error_workspace("vq3r", E, r, c)
         sums = torch.empty((E, 4), dtype=torch.float64, device=dev)
+        rel = torch.empty((E, 3), dtype=torch.float64, device=dev)
+        rel_all = torch.empty(3, dtype=torch.float64, device=dev)
         for rep in range(args.warmup + args.steps):
             if rep == args.warmup:
                 T.reset()
@@ -468,7 +704,8 @@ def layer_bench(args, torch, vq, synthetic, W1, E, evict):
                 vq.encode(flat, cb, fmt="vq3r", engine=args.engine, idx=idx, scales=sc, workspace=enc_ws,
                           check=False)
             with T(name + "_error"):
-                vq.error_sums(flat, idx, sc, cb, fmt="vq3r", n_mats=E, sums=sums, workspace=err_ws, check=False)
+                vq.error_sums(flat, idx, sc, cb, fmt="vq3r", n_mats=E, sums=sums, workspace=err_ws, check=False,
+                              rel=rel, rel_all=rel_all)
         vq.read_status(enc_ws)
         tot = sums.sum(dim=0)
         enc_ms = T.mean_ms(name + "_encode")
@@ -477,7 +714,7 @@ def layer_bench(args, torch, vq, synthetic, W1, E, evict):
                      "error_ms": round(T.mean_ms(name + "_error"), 3),
                      "encode_gweights_s": round(wts / (enc_ms * 1e-3) / 1e9, 2),
                      "encode_frac_fp32_peak": round(wts / 8 * 12288 / (enc_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4),
-                     "rel_err_all": [round(float(v), 5) for v in (tot[:3] / tot[3]).sqrt()]}
+                     "rel_err_all": [round(float(v), 5) for v in rel_all.cpu()]}
         log("%s: fit %.1f ms, encode %.1f ms, error %.2f ms" % (name, out[name]["fit_ms"], enc_ms,
                                                                out[name]["error_ms"]))
         if name == "w2":
@@ -487,21 +724,21 @@ def layer_bench(args, torch, vq, synthetic, W1, E, evict):
                 x = torch.from_numpy(synthetic.activations_f16(ntok, c, seed=30 + ntok).view(np.float16)).to(dev)
                 route = torch.from_numpy(synthetic.routing(ntok, E, 8, seed=40 + ntok)).to(dev)
                 y = torch.empty((ntok, 8, r), dtype=torch.float32, device=dev)
-                ws = vq.gemv_workspace("vq3r", r, c, ntok, 8)
+                ws = vq.gemv_packed_workspace("vq3r", r, c, ntok, 8)
                 ts = []
                 for rep in range(10):
                     evict()
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     e0.record()
-                    vq.dequant_gemv(pk, sc.view(E, r), cb, x, route, r, c, fmt="vq3r", y=y, workspace=ws)
+                    vq.dequant_gemv_packed(pk, sc.view(E, r), cb, x, route, r, c, fmt="vq3r", y=y, workspace=ws)
                     e1.record()
                     torch.cuda.synchronize()
                     ts.append(e0.elapsed_time(e1) * 1e3)
                 us = float(np.median(ts[2:]))
                 distinct = len(np.unique(route.cpu().numpy()))
                 alg = distinct * (r * (c // 8) * 3 + r * 2) + ntok * c * 2 + ntok * 8 * r * 4 + 3 * 256 * 8 * 4
-                floor = read_floor_us(torch, alg, evict)
+                floor = read_floor_us(torch, vq, alg, evict, torch.zeros(1, dtype=torch.int32, device=dev))
                 gbs = alg / (us * 1e-6) / 1e9
                 gem["gemv_%d" % ntok] = {"us": round(us, 2), "GB_s": round(gbs, 1),
                                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "distinct_experts": distinct,
@@ -517,8 +754,7 @@ def container_bench(args, torch, vq, W, mats, init3, cb3, fit_ws3, idx3, sc3, en
     load is timed against a plain pinned host-to-device copy of the same bytes."""
     vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3, workspace=fit_ws3)
     vq.encode(W, cb3, idx=idx3, scales=sc3, workspace=enc_ws)
-    sums = vq.error_sums(W, idx3, sc3, cb3, fmt="vq3r", n_mats=E)
-    rel = vq.rel_errors(sums)
+    rel = vq.rel_errors(W, idx3, sc3, cb3, fmt="vq3r", n_mats=E)[0]
     os.makedirs(args.container, exist_ok=True)
     path = os.path.join(args.container, "w1_vq3r.vqc")
     idx_e, sc_e = idx3.view(E, ROWS, COLS // 8, 3), sc3.view(E, ROWS)
@@ -568,10 +804,12 @@ def container_bench(args, torch, vq, W, mats, init3, cb3, fit_ws3, idx3, sc3, en
     os.remove(path)
 
 
-def encode_traffic():
-    """HBM bytes per VQ3R encode call from the committed FETCH_SIZE / WRITE_SIZE
-    summary, or None once the encode sources differ from the ones it measured."""
-    path = os.path.join(ROOT, "profiles", "k_encode_vq3r_layer_256x2048x7168_hbm_traffic.md")
+
+
+def profile_value(fname, key):
+    """A number from the machine-readable block of a committed profile summary,
+    or None once the kernel sources differ from the ones it measured."""
+    path = os.path.join(ROOT, "profiles", fname)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -580,7 +818,7 @@ def encode_traffic():
             k, v = line.strip().split(":", 1)
             kv[k.strip()] = v.strip()
     files = kv.get("source_files", "").split()
-    if not files or "traffic_bytes_per_launch" not in kv:
+    if not files or key not in kv:
         return None
     h = hashlib.sha256()
     for f in files:
@@ -588,30 +826,7 @@ def encode_traffic():
         h.update(open(os.path.join(ROOT, "residual_vector_quantization_amd", "csrc", f), "rb").read())
     if h.hexdigest() != kv.get("source_sha256"):
         return None
-    return int(kv["traffic_bytes_per_launch"])
-
-
-def read_floor_us(torch, nbytes, evict, reps=5):
-    """Time of a plain device read of nbytes after the same cache eviction as the
-    GEMV: torch row sums over [n/1024, 1024] fp32, the fastest plain torch read
-    here (one pass; its output is 1/1024 of the input). The reference point for
-    the GEMV's HBM rate."""
-    rows = max(1, -(-nbytes // 4096))
-    buf = torch.ones((rows, 1024), dtype=torch.float32, device="cuda")
-    out = torch.empty(rows, dtype=torch.float32, device="cuda")
-    best = None
-    for _ in range(reps):
-        evict()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        torch.sum(buf, dim=1, out=out)
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e3
-        best = t if best is None else min(best, t)
-    del buf
-    return best
+    return float(kv[key])
 
 
 def cpu_baseline(torch, W, cb3, nrows):
@@ -628,6 +843,42 @@ def cpu_baseline(torch, W, cb3, nrows):
     return {"value": round(w.size / dt / 1e9, 6), "unit": "Gweights/s", "cores": threads, "kind": "oracle",
             "sample": "VQ3R encode of the first %d rows x 7168 of the layer (%d experts, %.1f s)"
                       % (nrows, -(-nrows // ROWS), dt)}
+
+
+def cpu_baseline_legs(torch, vq, synthetic, W, mats, cb3, idx3_e, sc3_e, case1):
+    """The other oracle legs: config 1 fit + encode (VQ3R, 10 iterations on
+    [256 x 1024]), the encode of 2 of the 12 sampled experts (config 2, scaled
+    per weight), and the fp64 GEMV reference at 1 token (decode of the 8 routed
+    experts + fp64 products)."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    legs = {}
+    W1 = synthetic.gaussian_rows(256, 1024, seed=0)
+    init = synthetic.forgy_init(256 * 128, 256, 3, seed=0)
+    t0 = time.time()
+    cb, _ = oracle.fit([W1], 3, 256, 10, init)
+    oracle.encode(W1, cb)
+    legs["config1_fit_encode_s"] = round(time.time() - t0, 3)
+    w2 = torch.cat(mats[:2]).float().cpu().numpy()
+    t0 = time.time()
+    oracle.encode(w2, cb3.cpu().numpy())
+    dt = time.time() - t0
+    legs["config2_encode_gweights_s"] = round(w2.size / dt / 1e9, 6)
+    legs["config2_encode_sample"] = "2 of the 12 sampled experts (%.1f s)" % dt
+    route = case1["route"].cpu().numpy()[0]
+    xf = synthetic.f16_bits_to_f32(case1["x"].cpu().view(torch.int16).numpy().view(np.uint16)).reshape(-1)
+    cbh = cb3.cpu().numpy()
+    t0 = time.time()
+    for e in route:
+        idx = oracle.unpack("vq3r", idx3_e[int(e)].cpu().numpy())
+        s = sc3_e[int(e)].cpu().view(torch.int16).numpy().view(np.uint16)
+        oracle.gemv_ref(oracle.decode(idx, s, cbh), xf)
+    legs["gemv_ref_1_token_s"] = round(time.time() - t0, 3)
+    legs["gemv_ref_1_token_GB_s"] = round(gemv_alg_bytes(len(set(route.tolist())), 1, "vq3r") /
+                                          (time.time() - t0) / 1e9, 4)
+    legs["cores"] = threads
+    legs["kind"] = "oracle"
+    return legs
 
 
 if __name__ == "__main__":

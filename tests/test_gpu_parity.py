@@ -431,6 +431,83 @@ def test_fit_zero_iterations_and_duplicate_values():
         assert np.array_equal(cb.cpu().numpy().view(np.uint32), cb_o.view(np.uint32)), iters
 
 
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+def test_fit_flag_list_overflow_bit_exact(fmt):
+    """Half the rows are copies of one row made of 4 distinct vectors, so about
+    half the Forgy codewords coincide and every copied vector ties: the
+    exact-pass list (capacity 4096 for 65536 vectors) overflows, the exact pass
+    covers every vector and the update must skip the search's partial slots."""
+    say("fit list overflow", fmt)
+    S, K = vq.stages_entries(fmt)
+    rows, cols = 512, 1024
+    W = synthetic.gaussian_rows(rows, cols, seed=41)
+    base = synthetic.gaussian_rows(4, 8, seed=42)
+    W[rows // 2:] = np.tile(base.reshape(-1), cols // 32)[None, :]
+    init = synthetic.forgy_init(rows * cols // 8, K, S, seed=43)
+    cb_o, _ = oracle.fit([W], S, K, 3, init)
+    ws = vq.fit_workspace(fmt, 1, rows, cols)
+    cb = vq.fit_codebooks([to_dev(W)], init, fmt=fmt, iters=3, workspace=ws)
+    flags = vq.read_status(ws)
+    assert flags & (1 << 8)
+    assert np.array_equal(cb.cpu().numpy().view(np.uint32), cb_o.view(np.uint32))
+
+
+def _unit_rms_rows(vals, rng):
+    """Rows whose RMS rounds to fp16 1.0 (so the normalized row is the row
+    itself): one element per row, at a random position, is set so that the sum
+    of squares is cols."""
+    W = np.array(vals, dtype=np.float64)
+    rows, cols = W.shape
+    for r in range(rows):
+        k = rng.integers(0, cols)
+        W[r, k] = 0.0
+        assert np.sum(W[r] ** 2) < cols / 2
+        W[r, k] = np.sqrt(cols - np.sum(W[r] ** 2)) * rng.choice([-1.0, 1.0])
+    return W.astype(np.float32)
+
+
+def _extreme_codebooks(rng, S, K):
+    C = np.empty((S, K, 8))
+    for t in range(S):
+        c = rng.standard_normal((K, 8))
+        q = K // 8
+        c[q:2 * q] *= 0.01
+        c[q:2 * q, rng.integers(0, 8)] = rng.choice([2048.0, -2048.0], q)       # the codebook limit
+        c[2 * q:3 * q] *= 30.0
+        base = rng.choice([1.0, -1.0, 0.5, 2.0, 3.0], (2 * q, 8))
+        c[3 * q:5 * q] = base * (1.0 + rng.integers(1, 2 ** 10, (2 * q, 8)) * 2.0 ** -23)  # subnormal lo parts
+        c[5 * q:6 * q] = rng.standard_normal((q, 8)) * 2.0 ** -16                 # below fp16's normal range
+        C[t] = c
+    return np.clip(C, -2048, 2048).astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
+@pytest.mark.parametrize("engine", ENGINES)
+def test_encode_outlier_rows_and_extreme_codebooks(fmt, engine):
+    """Normalized rows at the extremes of the fp16 hi/lo split: all of a row's
+    energy in one element (|v| = sqrt(cols)), values whose lo part is an fp16
+    subnormal, small rows beside one outlier; codebooks with entries at
+    +-2048, scaled by 30, with subnormal lo parts and below 2^-14."""
+    say("encode outlier rows", fmt, engine)
+    S, K = vq.stages_entries(fmt)
+    rng = np.random.default_rng(44)
+    rows, cols = 48, 1024
+    v = np.empty((rows, cols))
+    v[:16] = rng.standard_normal((16, cols)) * 0.01                            # -> one element near 32
+    base = rng.choice([1.0, -1.0, 0.5, -0.5, 0.25, -0.25, 0.125], (16, cols))
+    v[16:32] = base * (1.0 + rng.integers(1, 2 ** 12, (16, cols)) * 2.0 ** -23)
+    v[32:] = rng.standard_normal((16, cols)) * rng.choice([1.0, 2.0 ** -15, 30.0], (16, cols)) * 0.01
+    W = _unit_rms_rows(v, rng)
+    cb = _extreme_codebooks(rng, S, K)
+    idx_o, s_o = oracle.encode(W, cb)
+    assert np.all(s_o == 0x3C00)                 # the construction: every row scale is 1.0
+    rec, s = vq.encode(to_dev(W), to_dev(cb), fmt=fmt, engine=engine)
+    assert np.array_equal(scales_bits(s), s_o)
+    got = rec_to_idx(fmt, rec)
+    bad = np.argwhere(got != idx_o)
+    assert len(bad) == 0, "indices differ: %d, first %s" % (len(bad), bad[:5].tolist())
+
+
 # ------------------------------------------------------------------ GEMV
 def _experts(fmt, cb, E, rows, cols, seed):
     recs, scs, whs = [], [], []
