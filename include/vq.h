@@ -56,7 +56,8 @@ typedef enum vq_status {
   VQ_EDEVICE = 4,    /* a HIP runtime call failed */
   VQ_EDATA = 5,      /* the device flagged a data error (vq_read_status) */
   VQ_EIO = 6,        /* container file: open, read or write failed or was short */
-  VQ_EFORMAT = 7     /* container file: bad header, checksum mismatch, missing record */
+  VQ_EFORMAT = 7,    /* container file: bad header, checksum mismatch, missing record */
+  VQ_ESCRATCH = 8    /* call too large for the fixed scratch of the no-allocation entry point */
 } vq_status;
 
 typedef enum vq_dtype { VQ_DT_F32 = 0, VQ_DT_BF16 = 1, VQ_DT_F16 = 2 } vq_dtype;
@@ -228,6 +229,27 @@ int vq_dequant_gemv_packed(int format, const uint8_t* packed, int64_t expert_str
                            int64_t scale_stride, const float* codebooks, int64_t rows, int64_t cols,
                            int32_t n_experts, const uint16_t* x, int32_t ntok, const int32_t* route, int32_t topk,
                            float* y, void* workspace, size_t ws_bytes, void* stream);
+
+/* vq_dequant_gemv_packed without a workspace, for callers that cannot
+ * allocate device memory (code under stream capture, serving loops that keep
+ * a fixed memory footprint). Same arguments, result and kernels as
+ * vq_dequant_gemv_packed; its partial sums live in a static device array of
+ * VQ_NOALLOC_SCRATCH_BYTES that each GPU holds from the first call until the
+ * process ends. The call allocates nothing.
+ *   status  optional device buffer (256-byte aligned, >= 4 bytes) that
+ *           receives the call's status word, readable with vq_read_status;
+ *           NULL: the word stays in the scratch
+ * Returns VQ_ESCRATCH (nothing launched) when the call's partial sums
+ * (ntok*topk * ranges * rows floats, the ranges chosen from the device's
+ * compute units, about 2 per compute unit over the pairs) do not fit, e.g.
+ * beyond about 2048 pairs at 2048 rows. All calls on one GPU share its array:
+ * calls that overlap in time on that GPU (other streams, other threads) race
+ * and give wrong results; serialize them. */
+#define VQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+int vq_dequant_gemv_packed_noalloc(int format, const uint8_t* packed, int64_t expert_stride, const uint16_t* scales,
+                                   int64_t scale_stride, const float* codebooks, int64_t rows, int64_t cols,
+                                   int32_t n_experts, const uint16_t* x, int32_t ntok, const int32_t* route,
+                                   int32_t topk, float* y, void* status, void* stream);
 
 /* ------------------------------------------------------------------------
  * Batched dequantize-GEMM for prompt processing ([VQ3R page] §1: every token

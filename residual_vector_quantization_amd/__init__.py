@@ -84,6 +84,8 @@ def lib():
                              ctypes.c_int32, P, P, SZ, P], I),
         "vq_dequant_gemv_packed": ([I, P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32, P,
                                     ctypes.c_int32, P, P, SZ, P], I),
+        "vq_dequant_gemv_packed_noalloc": ([I, P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32,
+                                            P, ctypes.c_int32, P, P, P], I),
         "vq3r_dequant_gemv": ([P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32, P,
                                ctypes.c_int32, P, P, SZ, P], I),
         "vq4p_dequant_gemv": ([P, L64, P, L64, P, L64, L64, ctypes.c_int32, P, ctypes.c_int32, P,
@@ -313,6 +315,22 @@ def dequant_gemv_packed(packed, scales, codebooks, x, route, rows, cols, fmt="vq
                                       _ptr(codebooks), rows, cols, E, _ptr(x), ntok, _ptr(route), topk, _ptr(y),
                                       _ptr(workspace), workspace.numel(), _stream())
     _call("vq_dequant_gemv_packed", st, workspace, check)
+    return y
+
+
+def dequant_gemv_packed_noalloc(packed, scales, codebooks, x, route, rows, cols, fmt="vq3r", y=None, status=None):
+    """dequant_gemv_packed without a workspace (the library's static device
+    scratch holds the partial sums; calls that overlap on one GPU race).
+    status: optional 256-byte uint8 device tensor that receives the status word
+    (read it with read_status)."""
+    E = packed.shape[0]
+    _check_cuda(packed, scales, codebooks, x, route)
+    ntok, topk, y = _gemv_io(x, route, rows, packed.device, y)
+    st = lib().vq_dequant_gemv_packed_noalloc(FORMATS[fmt], _ptr(packed), packed.shape[1], _ptr(scales),
+                                              scales.shape[-1], _ptr(codebooks), rows, cols, E, _ptr(x), ntok,
+                                              _ptr(route), topk, _ptr(y), _ptr(status) if status is not None else None,
+                                              _stream())
+    _call("vq_dequant_gemv_packed_noalloc", st)
     return y
 
 

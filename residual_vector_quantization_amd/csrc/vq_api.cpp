@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/vq.h"
 #include "vq_gemm.hpp"
 #include "vq_ttp.hpp"
@@ -137,7 +139,7 @@ void gemv_fill(GemvArgs& a, int format, const uint16_t* scales, int64_t scale_st
   a.topk = topk;
   a.route = route;
   a.y = y;
-  a.hdr = (WsHeader*)workspace;
+  a.flags = &((WsHeader*)workspace)->flags;
   a.remap = nullptr;
   a.stream = s;
 }
@@ -178,6 +180,36 @@ GemvStoredLayout gemv_stored_layout(int format, int64_t rows, int64_t cols, int3
 
 }  // namespace
 
+// Device scratch of vq_dequant_gemv_packed_noalloc: the status word (when the
+// caller passes no status buffer) followed by the split-K partial sums. Each
+// GPU the library runs on holds its own copy until the process ends. Host code
+// never uses this name as an address: scratch_base() looks the per-device
+// address up once with hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[VQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's scratch array (looked up on the first call
+// on each device, with that device current).
+int scratch_base(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VQ_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return VQ_EDEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VQ_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* vq_status_string(int status) {
@@ -190,6 +222,7 @@ const char* vq_status_string(int status) {
     case VQ_EDATA: return "data error flagged on the device";
     case VQ_EIO: return "container file I/O failed";
     case VQ_EFORMAT: return "container file malformed or corrupt";
+    case VQ_ESCRATCH: return "call too large for the no-allocation scratch";
     default: return "unknown status";
   }
 }
@@ -404,6 +437,31 @@ int vq_dequant_gemv_packed(int format, const uint8_t* packed, int64_t expert_str
   a.expert_stride = expert_stride;
   a.partials = (float*)((char*)workspace + kHeader);
   if ((st = device_cus(&a.ncu)) != VQ_OK) return st;
+  return hip_status(launch_gemv(a));
+}
+
+int vq_dequant_gemv_packed_noalloc(int format, const uint8_t* packed, int64_t expert_stride, const uint16_t* scales,
+                                   int64_t scale_stride, const float* codebooks, int64_t rows, int64_t cols,
+                                   int32_t n_experts, const uint16_t* x, int32_t ntok, const int32_t* route,
+                                   int32_t topk, float* y, void* status, void* stream) {
+  int st = gemv_check(format, rows, cols, n_experts, expert_stride,
+                      fmt_ok(format) ? gemv_packed_bytes(format, rows, cols) : 0, scale_stride, ntok, topk, packed,
+                      scales, codebooks, x, route, y);
+  if (st != VQ_OK) return st;
+  if (expert_stride % 4 != 0 || !aligned(packed, 4)) return VQ_EINVAL;
+  if (status && !aligned(status, 256)) return VQ_EINVAL;
+  GemvArgs a;
+  if ((st = device_cus(&a.ncu)) != VQ_OK) return st;
+  const size_t need =
+      kHeader + sizeof(float) * (size_t)gemv_partials_floats_used(format, rows, cols, (int64_t)ntok * topk, a.ncu);
+  if (need > (size_t)VQ_NOALLOC_SCRATCH_BYTES) return VQ_ESCRATCH;
+  void* base = nullptr;
+  if ((st = scratch_base(&base)) != VQ_OK) return st;
+  gemv_fill(a, format, scales, scale_stride, codebooks, rows, cols, n_experts, x, ntok, route, topk, y,
+            status ? status : base, (hipStream_t)stream);
+  a.idx = packed;
+  a.expert_stride = expert_stride;
+  a.partials = (float*)((char*)base + kHeader);
   return hip_status(launch_gemv(a));
 }
 

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
 // flags of the call (route ids outside [0, n_experts)), so no reset is needed.
 __global__ __launch_bounds__(256) void k_gemv_reduce(const float* partials, const uint16_t* scales,
                                                      int64_t scale_stride, const int32_t* route, int n_experts,
-                                                     int64_t rows, int nrange, int npairs, float* y, WsHeader* hdr) {
+                                                     int64_t rows, int nrange, int npairs, float* y, uint32_t* flags) {
   const int p = blockIdx.y;
   const int e = route[p];
   const bool bad = e < 0 || e >= n_experts;
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* partials, cons
     bool any = false;
     for (int q = threadIdx.x; q < npairs; q += 64) any |= (route[q] < 0 || route[q] >= n_experts);
     any = __any(any);
-    if (threadIdx.x == 0) hdr->flags = any ? ST_ROUTE : 0u;
+    if (threadIdx.x == 0) *flags = any ? ST_ROUTE : 0u;
   }
   const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= rows) return;
@@ -399,8 +399,8 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* partials, cons
   y[(int64_t)p * rows + r] = acc;
 }
 
-__global__ void k_gemv_clear(WsHeader* hdr) {
-  if (threadIdx.x == 0) hdr->flags = 0;
+__global__ void k_gemv_clear(uint32_t* flags) {
+  if (threadIdx.x == 0) *flags = 0;
 }
 
 // ------------------------------------------------------------------ launch geometry
@@ -442,6 +442,16 @@ int64_t gemv_partials_floats(int format, int64_t rows, int64_t cols, int64_t npa
   return npairs * nblk * rows;  // upper bound (one block per range)
 }
 
+// The partial sums one launch on `ncu` compute units writes: one per (pair,
+// range, row).
+int64_t gemv_partials_floats_used(int format, int64_t rows, int64_t cols, int64_t npairs, int ncu) {
+  (void)format;
+  const int nblk = (int)((cols / DIM + GJ - 1) / GJ);
+  int nb, nrange;
+  gemv_ranges(npairs, gemv_row_chunks(rows), nblk, ncu, &nb, &nrange);
+  return npairs * nrange * rows;
+}
+
 template <int FMT>
 static hipError_t launch_gemv_t(const GemvArgs& a) {
   const int64_t npairs = (int64_t)a.ntok * a.topk;
@@ -465,13 +475,13 @@ static hipError_t launch_gemv_t(const GemvArgs& a) {
   else go(k_gemv<FMT, 4>);
   dim3 g2((unsigned)((a.rows + 255) / 256), (unsigned)npairs);
   k_gemv_reduce<<<g2, 256, 0, a.stream>>>(a.partials, a.scales, a.scale_stride, a.route, a.n_experts, a.rows, nrange,
-                                          (int)npairs, a.y, a.hdr);
+                                          (int)npairs, a.y, a.flags);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv(const GemvArgs& a) {
   if ((int64_t)a.ntok * a.topk == 0 || a.rows == 0) {
-    k_gemv_clear<<<1, 64, 0, a.stream>>>(a.hdr);
+    k_gemv_clear<<<1, 64, 0, a.stream>>>(a.flags);
     return hipGetLastError();
   }
   return a.format == 0 ? launch_gemv_t<0>(a) : launch_gemv_t<1>(a);

@@ -82,7 +82,7 @@ struct GemvArgs {
   const int32_t* route;
   float* y;
   float* partials;  // [ntok*topk][nrange][rows]
-  WsHeader* hdr;
+  uint32_t* flags;  // the call's status word (route ids outside [0, n_experts))
   int ncu;
   hipStream_t stream;
 };
@@ -99,6 +99,7 @@ struct Mxfp4Args {
 
 // GEMV sizes: floats of tile partial sums (workspace), bytes of one packed expert.
 int64_t gemv_partials_floats(int format, int64_t rows, int64_t cols, int64_t npairs);
+int64_t gemv_partials_floats_used(int format, int64_t rows, int64_t cols, int64_t npairs, int ncu);
 int64_t gemv_packed_bytes(int format, int64_t rows, int64_t cols);
 int gemv_row_chunks(int64_t rows);                                  // row chunks of a GEMV tile column
 int64_t gemv_tiles(int64_t rows, int64_t cols, int64_t npairs);     // GEMV workgroups (before padding)
