@@ -50,7 +50,7 @@ constexpr int GROUP = 64;  // rows per interleaved group (one wave)
 constexpr int GEMV_WAVES = 8;
 constexpr int GEMV_THREADS = 64 * GEMV_WAVES;
 #ifndef VQ_GEMV_TILES_PER_CU
-#define VQ_GEMV_TILES_PER_CU 3
+#define VQ_GEMV_TILES_PER_CU 2
 #endif
 
 template <int FMT> struct GemvCfg;
