@@ -43,7 +43,7 @@
 
 namespace vqk {
 
-typedef float f16v __attribute__((ext_vector_type(16)));
+typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr int GJ = 16;     // slices per block
 constexpr int GROUP = 64;  // rows per interleaved group (one wave)
@@ -174,67 +174,68 @@ __global__ __launch_bounds__(1024) void k_gemv_route_stored(const int32_t* route
 
 // ------------------------------------------------------------------ tables
 // T[(e*S + t)*R + rep][m] = sum_k C_t[e][k] * x[(j0 + m)*8 + k] with fp32
-// matrix cores (32x32x2): codewords on M, slices on N (lanes 16-31 of each
-// half-wave carry zero slices). The codebook operands of a wave's tasks are
-// loaded once per tile (CbOps), the activation operand once per block.
+// matrix cores (16x16x4: 16 codewords on M, the block's 16 slices on N, two
+// products over k = 0..3 and 4..7). A task is (stage t, 16 codewords); its
+// codebook operands are loaded once per tile (CbOps), the activation operand
+// once per block.
 template <int FMT>
 struct CbOps {
-  static constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, NT = K / 32, TASKS = S * NT;
+  static constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, NT = K / 16, TASKS = S * NT;
   static constexpr int PER_WAVE = (TASKS + GEMV_WAVES - 1) / GEMV_WAVES;
-  float a[PER_WAVE][4];
+  float a[PER_WAVE][2];
 };
 
+// lane (codeword i = lane % 16, k quarter kq = lane / 16) holds C_t[16ct + i][4h + kq]
 template <int FMT>
 __device__ inline void cb_load(CbOps<FMT>& op, const float* cb_g) {
   using O = CbOps<FMT>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = lane >> 5, i = lane & 31;
+  const int i = lane & 15, kq = lane >> 4;
 #pragma unroll
   for (int u = 0; u < O::PER_WAVE; ++u) {
     const int task = wave + GEMV_WAVES * u;
     const int tk = task < O::TASKS ? task : 0;
     const int t = tk / O::NT, ct = tk % O::NT;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) op.a[u][s] = cb_g[((size_t)t * O::K + ct * 32 + i) * DIM + 2 * s + h];
+    for (int h = 0; h < 2; ++h) op.a[u][h] = cb_g[((size_t)t * O::K + ct * 16 + i) * DIM + 4 * h + kq];
   }
 }
 
-// The activation operand of block [j0, j0 + nsl): lane (slice i, h) holds x
-// elements 2s + h of slice i (fp16 bits), slice clamped (its column is zeroed).
-__device__ inline void x_load(uint32_t xb[4], const uint16_t* xrow, int64_t j0, int nsl) {
+// The activation operand of block [j0, j0 + nsl): lane (slice j = lane % 16,
+// kq = lane / 16) holds x elements 4h + kq of slice j (fp16 bits), slice
+// clamped (its column is zeroed).
+__device__ inline void x_load(uint32_t xb[2], const uint16_t* xrow, int64_t j0, int nsl) {
   const int lane = threadIdx.x & 63;
-  const int h = lane >> 5, i = lane & 31;
-  const int ic = i < nsl ? i : 0;
+  const int j = lane & 15, kq = lane >> 4;
+  const int jc = j < nsl ? j : 0;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) xb[s] = xrow[(j0 + ic) * DIM + 2 * s + h];
+  for (int h = 0; h < 2; ++h) xb[h] = xrow[(j0 + jc) * DIM + 4 * h + kq];
 }
 
 template <int FMT>
-__device__ inline void lut_compute(const CbOps<FMT>& op, const uint32_t xb[4], float* lut, int nsl) {
+__device__ inline void lut_compute(const CbOps<FMT>& op, const uint32_t xb[2], float* lut, int nsl) {
   using O = CbOps<FMT>;
   constexpr int R = GemvCfg<FMT>::R;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = lane >> 5, i = lane & 31;
-  const bool sv = i < nsl;  // nsl <= 16: lanes 16-31 of a half-wave compute nothing useful
-  float b[4];
+  const int j = lane & 15, rg = lane >> 4;
+  const bool sv = j < nsl;
+  float b[2];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) b[s] = sv ? f16_bits_to_f32((uint16_t)xb[s]) : 0.0f;
+  for (int h = 0; h < 2; ++h) b[h] = sv ? f16_bits_to_f32((uint16_t)xb[h]) : 0.0f;
 #pragma unroll
   for (int u = 0; u < O::PER_WAVE; ++u) {
     const int task = wave + GEMV_WAVES * u;
     if (task >= O::TASKS) break;  // wave-uniform
     const int t = task / O::NT, ct = task % O::NT;
-    f16v acc = {};
+    f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(op.a[u][0], b[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(op.a[u][1], b[1], acc, 0, 0, 0);
+    // lane (slice j, rg) holds codewords e = 16ct + 4rg + v
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(op.a[u][s], b[s], acc, 0, 0, 0);
-    // lane (n = slice i, h) holds codewords e = 32ct + 8*(v/4) + 4h + v%4
-    if (i < GJ) {
+    for (int v = 0; v < 4; ++v) {
+      const int e = ct * 16 + 4 * rg + v;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int e = ct * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-#pragma unroll
-        for (int rep = 0; rep < R; ++rep) lut[((e * O::S + t) * R + rep) * GJ + i] = acc[v];
-      }
+      for (int rep = 0; rep < R; ++rep) lut[((e * O::S + t) * R + rep) * GJ + j] = acc[v];
     }
   }
 }
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
   };
   CbOps<FMT> ops;
   cb_load<FMT>(ops, cb_g);
-  uint32_t xb[4];
+  uint32_t xb[2];
   x_load(xb, xrow, (int64_t)b0 * GJ, (int)((V - (int64_t)b0 * GJ) < GJ ? (V - (int64_t)b0 * GJ) : GJ));
   __builtin_amdgcn_sched_barrier(0);  // keep the table operand loads ahead of the index stream
   load_item(d[0], 0);
@@ -404,18 +405,27 @@ __global__ void k_gemv_clear(uint32_t* flags) {
 }
 
 // ------------------------------------------------------------------ launch geometry
-// Row groups per wave: 4 (2048-row tiles) unless the matrix has fewer groups.
-static int gemv_gpw(int64_t rows) {
+#ifndef VQ_GEMV_SMALL_PAIRS
+#define VQ_GEMV_SMALL_PAIRS 0
+#endif
+#ifndef VQ_GEMV_SMALL_SPLIT
+#define VQ_GEMV_SMALL_SPLIT 1
+#endif
+// Row chunks of a tile column: enough that no chunk exceeds 4 groups per wave
+// (2048 rows); calls with few pairs may cut the rows further.
+int gemv_row_chunks(int64_t rows, int64_t npairs) {
   const int64_t ng = (rows + GROUP - 1) / GROUP;
-  if (ng <= GEMV_WAVES) return 1;
-  if (ng <= 2 * GEMV_WAVES) return 2;
-  if (ng <= 3 * GEMV_WAVES) return 3;
-  return 4;
+  int64_t n = (ng + 4 * GEMV_WAVES - 1) / (4 * GEMV_WAVES);
+  if (npairs <= VQ_GEMV_SMALL_PAIRS && n < VQ_GEMV_SMALL_SPLIT) n = VQ_GEMV_SMALL_SPLIT;
+  if (n > ng) n = ng > 0 ? ng : 1;
+  return (int)n;
 }
 
-int gemv_row_chunks(int64_t rows) {
+// Row groups per wave: the groups of the largest chunk over the 8 waves.
+static int gemv_gpw(int64_t rows, int nsplit) {
   const int64_t ng = (rows + GROUP - 1) / GROUP;
-  return (int)((ng + 4 * GEMV_WAVES - 1) / (4 * GEMV_WAVES));
+  const int64_t per = (ng + nsplit - 1) / nsplit;
+  return (int)((per + GEMV_WAVES - 1) / GEMV_WAVES);
 }
 
 // Blocks per range: as many as keep about VQ_GEMV_TILES_PER_CU tiles per CU in
@@ -433,7 +443,7 @@ static void gemv_ranges(int64_t npairs, int nsplit, int nblk, int ncu, int* nb, 
 
 int64_t gemv_tiles(int64_t rows, int64_t cols, int64_t npairs) {
   const int64_t nblk = (cols / DIM + GJ - 1) / GJ;
-  return npairs * nblk * gemv_row_chunks(rows);  // upper bound (one block per range)
+  return npairs * nblk * gemv_row_chunks(rows, npairs);  // upper bound (one block per range)
 }
 
 int64_t gemv_partials_floats(int format, int64_t rows, int64_t cols, int64_t npairs) {
@@ -448,7 +458,7 @@ int64_t gemv_partials_floats_used(int format, int64_t rows, int64_t cols, int64_
   (void)format;
   const int nblk = (int)((cols / DIM + GJ - 1) / GJ);
   int nb, nrange;
-  gemv_ranges(npairs, gemv_row_chunks(rows), nblk, ncu, &nb, &nrange);
+  gemv_ranges(npairs, gemv_row_chunks(rows, npairs), nblk, ncu, &nb, &nrange);
   return npairs * nrange * rows;
 }
 
@@ -457,12 +467,12 @@ static hipError_t launch_gemv_t(const GemvArgs& a) {
   const int64_t npairs = (int64_t)a.ntok * a.topk;
   const int64_t V = a.cols / DIM;
   const int nblk = (int)((V + GJ - 1) / GJ);
-  const int nsplit = gemv_row_chunks(a.rows);
+  const int nsplit = gemv_row_chunks(a.rows, npairs);
   int nb, nrange;
   gemv_ranges(npairs, nsplit, nblk, a.ncu, &nb, &nrange);
   const int64_t ntiles = npairs * nsplit * nrange;
   const int64_t ntiles_pad = (ntiles + 7) / 8 * 8;
-  const int gpw = gemv_gpw(a.rows);
+  const int gpw = gemv_gpw(a.rows, nsplit);
   auto go = [&](auto kern) {
     kern<<<(unsigned)ntiles_pad, GEMV_THREADS, 0, a.stream>>>(a.idx, a.expert_stride, a.remap, a.codebooks, a.rows,
                                                                a.cols, a.n_experts, a.x, a.topk, a.route,

@@ -101,7 +101,7 @@ struct Mxfp4Args {
 int64_t gemv_partials_floats(int format, int64_t rows, int64_t cols, int64_t npairs);
 int64_t gemv_partials_floats_used(int format, int64_t rows, int64_t cols, int64_t npairs, int ncu);
 int64_t gemv_packed_bytes(int format, int64_t rows, int64_t cols);
-int gemv_row_chunks(int64_t rows);                                  // row chunks of a GEMV tile column
+int gemv_row_chunks(int64_t rows, int64_t npairs);                  // row chunks of a GEMV tile column
 int64_t gemv_tiles(int64_t rows, int64_t cols, int64_t npairs);     // GEMV workgroups (before padding)
 // Packs n_slots experts into the GEMV layout: slot i <- expert list[i] (list
 // NULL: expert i) read at idx + expert * expert_stride; slots at or past *count
