@@ -53,9 +53,14 @@ constexpr int GEMV_THREADS = 64 * GEMV_WAVES;
 #define VQ_GEMV_TILES_PER_CU 2
 #endif
 
+// Table layouts. VQ3R: T[e][t][slice] with a 256-byte row per codeword
+// (3 x 16 floats and 16 floats of padding; 64 KB): the LDS address of a
+// lookup is (e << 8) | (t*64 + slice*4), so one byte permute forms it from
+// the record and a per-lane offset byte. VQ4P: T[e][t][replica][slice] (32 KB),
+// two replicas.
 template <int FMT> struct GemvCfg;
-template <> struct GemvCfg<0> { static constexpr int R = 1; };  // 256 x 3 x 16 x 4 B = 48 KB
-template <> struct GemvCfg<1> { static constexpr int R = 2; };  // 64 x 4 x 2 x 16 x 4 B = 32 KB
+template <> struct GemvCfg<0> { static constexpr int R = 1, FLOATS = 256 * 64; };
+template <> struct GemvCfg<1> { static constexpr int R = 2, FLOATS = 64 * 4 * 2 * 16; };
 
 int64_t gemv_packed_bytes(int format, int64_t rows, int64_t cols) {
   (void)format;
@@ -234,8 +239,12 @@ __device__ inline void lut_compute(const CbOps<FMT>& op, const uint32_t xb[2], f
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int e = ct * 16 + 4 * rg + v;
+      if constexpr (FMT == 0) {
+        lut[e * 64 + t * GJ + j] = acc[v];
+      } else {
 #pragma unroll
-      for (int rep = 0; rep < R; ++rep) lut[((e * O::S + t) * R + rep) * GJ + j] = acc[v];
+        for (int rep = 0; rep < R; ++rep) lut[((e * O::S + t) * R + rep) * GJ + j] = acc[v];
+      }
     }
   }
 }
@@ -262,7 +271,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
                                                        int nsplit, int64_t ntiles, int64_t ntiles_pad) {
   constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, R = GemvCfg<FMT>::R, NC = GJ / 4;
   constexpr int NW = GEMV_WAVES;
-  __shared__ float lut[K * S * R * GJ];
+  __shared__ float lut[GemvCfg<FMT>::FLOATS];
   const int64_t tile = tile_of_block(blockIdx.x, ntiles_pad);
   if (tile >= ntiles) return;
   const int p = (int)(tile % npairs);
@@ -298,7 +307,60 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
   const uint32_t rep_off = (R == 2) ? (uint32_t)((lane >> 4) & 1) * (GJ * 4) : 0u;
   constexpr uint32_t E_STRIDE = S * R * GJ * 4, T_STRIDE = R * GJ * 4;
   const char* lbase = reinterpret_cast<const char*>(lut);
+  // VQ3R lookups. At step m = 4c + qq, lane l reads slice (m + l) mod 16; its
+  // half-wave bit h = (l >> 4) & 1 rotates the order of the stages (lanes with
+  // h = 1 take stages 1, 2, 0), so that in each lookup instruction the two
+  // 16-lane halves of a half-wave read different stages: with the slice
+  // rotation their 32 addresses fall in 32 distinct banks whatever the
+  // indices. sel[qq] extracts record qq of a 12-byte chunk with its stages in
+  // the lane's order; soff[k][c] holds, in byte qq, t*64 + slice*4 for the
+  // lane's k-th stage t at step 4c + qq.
+  const uint32_t hb = (uint32_t)(lane >> 4) & 1u;
+  uint32_t sel[4], soff[3][NC];
+  if constexpr (FMT == 0) {
+    // bytes of record qq within {hi, lo} (lo = bytes 0-3): qq 0: 0 1 2, 1: 3 4 5 (hi = next dword),
+    // 2: 2 3 4 (lo = dword 1), 3: 5 6 7
+    constexpr uint32_t b0[4] = {0, 3, 2, 5};
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const uint32_t x0 = b0[qq], x1 = b0[qq] + 1, x2 = b0[qq] + 2;
+      sel[qq] = hb ? (x1 | (x2 << 8) | (x0 << 16) | 0x0c000000u) : (x0 | (x1 << 8) | (x2 << 16) | 0x0c000000u);
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const uint32_t t = (uint32_t)((k + (int)hb) % 3);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) v |= (t * 64u + ((uint32_t)(4 * c + qq + lane) & (GJ - 1)) * 4u) << (8 * qq);
+        soff[k][c] = v;
+      }
+    }
+  }
+  auto row_sum3 = [&](const uint32_t (&dg)[NC][3]) {
+    float acc;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const uint32_t lo = dg[c][qq < 2 ? 0 : 1], hi = dg[c][qq < 2 ? 1 : 2];
+        const uint32_t w = __builtin_amdgcn_perm(hi, lo, sel[qq]);  // the lane's stage order in bytes 0-2
+        float tsum;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          // byte 0: offset byte qq of soff[k][c]; byte 1: stage index byte k of w
+          const uint32_t a = __builtin_amdgcn_perm(soff[k][c], w, 0x0c0c0004u | ((uint32_t)k << 8) | (uint32_t)qq);
+          const float v = *reinterpret_cast<const float*>(lbase + a);
+          tsum = k == 0 ? v : tsum + v;
+        }
+        acc = (c == 0 && qq == 0) ? tsum : acc + tsum;
+      }
+    }
+    return acc;
+  };
   auto row_sum = [&](const uint32_t (&dg)[NC][3]) {
+    if constexpr (FMT == 0) return row_sum3(dg);
     float acc;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
