@@ -72,6 +72,9 @@ def lib():
         L.vqo_fixed_point_bits.argtypes = [ctypes.c_float, i64]
         L.vqo_fit.argtypes = [P, i32, i64, i64, i32, i32, i32, P, P, P, P, P]
         L.vqo_lloyd_on_vectors.argtypes = [P, i64, i32, i32, P, P, P, P]
+        L.vqo_splitmix64.argtypes = [P]
+        L.vqo_splitmix64.restype = ctypes.c_uint64
+        L.vqo_forgy_init.argtypes = [i64, i32, i32, ctypes.c_uint64, P]
         L.vqo_ttp_quantize.argtypes = [P, i64, i64, P, P, P]
         L.vqo_ttp_dequantize.argtypes = [P, P, i64, i64, P]
         _lib = L
@@ -184,6 +187,20 @@ def fit(mats, stages: int, K: int, iters: int, init: np.ndarray, want_assign=Fal
                          _p(obj) if obj is not None else None,
                          _p(energy) if energy is not None else None))
     return cb, {"assign": assign, "obj": obj, "energy": energy}
+
+
+def splitmix64(state: int, count: int) -> list:
+    """The first `count` outputs of SplitMix64 from `state` (vq_oracle.c)."""
+    st = ctypes.c_uint64(state)
+    return [int(lib().vqo_splitmix64(ctypes.byref(st))) for _ in range(count)]
+
+
+def forgy_init_seeded(n: int, K: int, stages: int, seed: int) -> np.ndarray:
+    """Seeded Forgy init, int64 [stages, K] (the reading of the configs'
+    "seeded random vectors"; generator and selection rule in vq_oracle.c)."""
+    out = np.zeros((stages, K), dtype=np.int64)
+    _check(lib().vqo_forgy_init(int(n), int(K), int(stages), int(seed) & ((1 << 64) - 1), _p(out)))
+    return out
 
 
 def lloyd_on_vectors(R: np.ndarray, K: int, iters: int, init: np.ndarray):

@@ -347,6 +347,45 @@ int vqo_fit(const float* const* mats, int n_mats, int64_t rows, int64_t cols, in
   return st;
 }
 
+/* ------------------------------------------------------------------------
+ * Seeded Forgy init. The configurations ask for Lloyd started from "seeded
+ * random vectors" and the page names no generator; the reading taken here:
+ * for stage t (0-based), a SplitMix64 stream whose state starts at
+ * seed XOR (0x9E3779B97F4A7C15 * (t + 1)) (mod 2^64); each output d picks
+ * training vector floor(d * n / 2^64) (the high half of the 128-bit product);
+ * a pick already taken for this stage is skipped, until K distinct vectors
+ * are chosen. SplitMix64 is the published generator of Steele, Lea and Flood
+ * (OOPSLA 2014): the state advances by 0x9E3779B97F4A7C15 and each output is
+ * the state mixed by z ^= z >> 30; z *= 0xBF58476D1CE4E5B9; z ^= z >> 27;
+ * z *= 0x94D049BB133111EB; z ^= z >> 31.
+ * ---------------------------------------------------------------------- */
+uint64_t vqo_splitmix64(uint64_t* state) {
+  *state += 0x9E3779B97F4A7C15ull;
+  uint64_t z = *state;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+/* init out: int64 [stages][K]. Error if n < K. */
+int vqo_forgy_init(int64_t n, int K, int stages, uint64_t seed, int64_t* init) {
+  if (K < 1 || stages < 1 || n < K) return VQO_EINVAL;
+  for (int t = 0; t < stages; ++t) {
+    uint64_t state = seed ^ (0x9E3779B97F4A7C15ull * (uint64_t)(t + 1));
+    int64_t* out = init + (int64_t)t * K;
+    int have = 0;
+    while (have < K) {
+      uint64_t d = vqo_splitmix64(&state);
+      int64_t j = (int64_t)(((unsigned __int128)d * (unsigned __int128)(uint64_t)n) >> 64);
+      int taken = 0;
+      for (int q = 0; q < have; ++q)
+        if (out[q] == j) { taken = 1; break; }
+      if (!taken) out[have++] = j;
+    }
+  }
+  return VQO_OK;
+}
+
 /* Lloyd on an explicit training set (n x 8 fp32, used as given), for the
  * closed-form pins; same stage semantics as vqo_fit. R is overwritten with the
  * final residual. */

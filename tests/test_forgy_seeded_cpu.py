@@ -1,0 +1,59 @@
+"""Pins for the oracle's seeded Forgy init (the reading of the configurations'
+"seeded random vectors": SplitMix64 streams, one per stage, multiply-shift
+range reduction, duplicates skipped; definition in oracle/vq_oracle.c)."""
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = 0x9E3779B97F4A7C15
+M64 = (1 << 64) - 1
+
+
+def test_splitmix64_published_outputs():
+    # the generator's published output sequence from state 0
+    assert oracle.splitmix64(0, 4) == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4,
+                                       0x06C45D188009454F, 0xF88BB8A8724C81EC]
+
+
+@pytest.mark.parametrize("k,K,seed", [(10, 16, 0), (20, 256, 12345), (33, 64, (1 << 64) - 1)])
+def test_power_of_two_n_takes_the_top_bits(k, K, seed):
+    """With n = 2^k the pick floor(d n / 2^64) is the top k bits of the draw."""
+    n = 1 << k
+    init = oracle.forgy_init_seeded(n, K, 2, seed)
+    for t in range(2):
+        draws = oracle.splitmix64((seed ^ (GOLDEN * (t + 1))) & M64, 4 * K + 64)
+        want = []
+        for d in draws:
+            j = d >> (64 - k)
+            if j not in want:
+                want.append(j)
+            if len(want) == K:
+                break
+        assert init[t].tolist() == want
+
+
+def test_n_equal_k_gives_a_permutation():
+    for n in (1, 7, 64):
+        init = oracle.forgy_init_seeded(n, n, 3, 99)
+        for t in range(3):
+            assert sorted(init[t].tolist()) == list(range(n))
+
+
+@pytest.mark.parametrize("n,K,S,seed", [(1000, 256, 3, 1), (22020096, 256, 3, 2), (1835008, 64, 4, 3),
+                                        (300, 64, 4, 4)])
+def test_distinct_in_range_and_deterministic(n, K, S, seed):
+    a = oracle.forgy_init_seeded(n, K, S, seed)
+    assert a.shape == (S, K)
+    assert np.all((a >= 0) & (a < n))
+    for t in range(S):
+        assert len(set(a[t].tolist())) == K
+    assert np.array_equal(a, oracle.forgy_init_seeded(n, K, S, seed))
+    assert not np.array_equal(a, oracle.forgy_init_seeded(n, K, S, seed + 1))
+    if n > 10 * K:
+        assert not np.array_equal(a[0], a[1])  # each stage has its own stream
+
+
+def test_fewer_vectors_than_entries_is_an_error():
+    with pytest.raises(oracle.OracleError):
+        oracle.forgy_init_seeded(10, 16, 1, 0)
