@@ -127,6 +127,22 @@ int vq_fit_codebooks(int format, const void* const* mats, int dtype, int64_t n_m
                      int64_t cols, int32_t iters, const int64_t* init_idx, float* codebooks,
                      void* workspace, size_t ws_bytes, int engine, void* stream);
 
+/* Seeded Forgy initialization (the configurations' "seeded random vectors";
+ * the page names no generator, the reading taken): for stage t (0-based), a
+ * SplitMix64 stream (Steele, Lea and Flood, 2014) whose state starts at
+ * seed XOR (0x9E3779B97F4A7C15 * (t + 1)) mod 2^64; each output d picks
+ * training vector floor(d * n_vectors / 2^64), and a pick already taken for the
+ * stage is skipped until `entries` distinct vectors are chosen.
+ * init_out: host int64 [stages][entries]. Host-only (no device work); returns
+ * VQ_EINVAL when n_vectors < entries or a count is not positive. */
+int vq_forgy_init(int64_t n_vectors, int32_t entries, int32_t stages, uint64_t seed, int64_t* init_out);
+
+/* vq_fit_codebooks started from vq_forgy_init(N, entries, stages, seed), N the
+ * training-vector count (the call draws the indices on the host). */
+int vq_fit_codebooks_seeded(int format, const void* const* mats, int dtype, int64_t n_mats, int64_t rows,
+                            int64_t cols, int32_t iters, uint64_t seed, float* codebooks, void* workspace,
+                            size_t ws_bytes, int engine, void* stream);
+
 /* ------------------------------------------------------------------------
  * Encode ([VQ3R page] §2 and §4): per row the fp16 scale s = fp16(RMS(row));
  * every vector v = w[8j..8j+7] / s is encoded greedily: for each stage t,

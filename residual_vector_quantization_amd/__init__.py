@@ -73,6 +73,8 @@ def lib():
         "vq4p_encode": ([P, I, L64, L64, P, P, P, P, SZ, P], I),
         "vq_fit_workspace_size": ([I, L64, L64, L64], SZ),
         "vq_fit_codebooks": ([I, P, I, L64, L64, L64, ctypes.c_int32, P, P, P, SZ, I, P], I),
+        "vq_forgy_init": ([L64, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64, P], I),
+        "vq_fit_codebooks_seeded": ([I, P, I, L64, L64, L64, ctypes.c_int32, ctypes.c_uint64, P, P, SZ, I, P], I),
         "vq_decode": ([I, P, P, P, L64, L64, ctypes.c_int32, P, P], I),
         "vq3r_decode": ([P, P, P, L64, L64, P, P], I),
         "vq4p_decode": ([P, P, P, L64, L64, P, P], I),
@@ -220,10 +222,21 @@ def fit_workspace(fmt, n_mats, rows, cols, device="cuda"):
     return _workspace(n, device)
 
 
-def fit_codebooks(mats, init_idx, fmt="vq3r", iters=20, engine="auto", codebooks=None, workspace=None,
-                  check=True):
+def forgy_init(n_vectors, fmt="vq3r", seed=0):
+    """The library's seeded Forgy init (vq_forgy_init): int64 [stages, entries]
+    distinct training-vector indices. Host-only."""
+    S, K = stages_entries(fmt)
+    out = np.zeros((S, K), dtype=np.int64)
+    _call("vq_forgy_init", lib().vq_forgy_init(int(n_vectors), K, S, int(seed) & ((1 << 64) - 1),
+                                               out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def fit_codebooks(mats, init_idx=None, fmt="vq3r", iters=20, engine="auto", codebooks=None, workspace=None,
+                  check=True, seed=None):
     """Lloyd codebook fit over the vectors of `mats` ([VQ3R page] §2, §4).
-    init_idx: int64 [stages, entries] distinct training-vector indices."""
+    init_idx: int64 [stages, entries] distinct training-vector indices; or
+    init_idx=None and seed=s: the library draws them (vq_fit_codebooks_seeded)."""
     torch = _torch()
     rows, cols = mats[0].shape
     for m in mats:
@@ -231,12 +244,20 @@ def fit_codebooks(mats, init_idx, fmt="vq3r", iters=20, engine="auto", codebooks
         if m.shape != (rows, cols) or m.dtype != mats[0].dtype:
             raise ValueError("all matrices must share shape and dtype")
     S, K = stages_entries(fmt)
-    init = np.ascontiguousarray(init_idx, dtype=np.int64).reshape(S, K)
+    if (init_idx is None) == (seed is None):
+        raise ValueError("give exactly one of init_idx and seed")
     if codebooks is None:
         codebooks = torch.empty((S, K, 8), dtype=torch.float32, device=mats[0].device)
     if workspace is None:
         workspace = fit_workspace(fmt, len(mats), rows, cols, mats[0].device)
     ptrs = (ctypes.c_void_p * len(mats))(*[m.data_ptr() for m in mats])
+    if seed is not None:
+        st = lib().vq_fit_codebooks_seeded(FORMATS[fmt], ptrs, _dtype_code(mats[0]), len(mats), rows, cols,
+                                           int(iters), int(seed) & ((1 << 64) - 1), _ptr(codebooks), _ptr(workspace),
+                                           workspace.numel(), ENGINES[engine], _stream())
+        _call("vq_fit_codebooks_seeded", st, workspace, check)
+        return codebooks
+    init = np.ascontiguousarray(init_idx, dtype=np.int64).reshape(S, K)
     st = lib().vq_fit_codebooks(FORMATS[fmt], ptrs, _dtype_code(mats[0]), len(mats), rows, cols, int(iters),
                                 init.ctypes.data_as(ctypes.c_void_p), _ptr(codebooks), _ptr(workspace),
                                 workspace.numel(), ENGINES[engine], _stream())

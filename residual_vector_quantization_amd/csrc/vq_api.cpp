@@ -4,6 +4,8 @@
 #include <string.h>
 
 #include <mutex>
+#include <unordered_set>
+#include <vector>
 
 #include "../../include/vq.h"
 #include "vq_gemm.hpp"
@@ -359,6 +361,42 @@ int vq_fit_codebooks(int format, const void* const* mats, int dtype, int64_t n_m
   a.ncu = ncu;
   a.stream = s;
   return hip_status(launch_fit(a));
+}
+
+int vq_forgy_init(int64_t n_vectors, int32_t entries, int32_t stages, uint64_t seed, int64_t* init_out) {
+  if (entries < 1 || stages < 1 || n_vectors < entries || !init_out) return VQ_EINVAL;
+  constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+  for (int32_t t = 0; t < stages; ++t) {
+    uint64_t x = seed ^ (kGamma * (uint64_t)(t + 1));  // SplitMix64 state of this stage
+    std::unordered_set<int64_t> taken;
+    int64_t* row = init_out + (int64_t)t * entries;
+    for (int32_t have = 0; have < entries;) {
+      x += kGamma;
+      uint64_t z = x;
+      z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+      z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+      z ^= z >> 31;
+      const int64_t pick = (int64_t)(uint64_t)(((unsigned __int128)z * (uint64_t)n_vectors) >> 64);
+      if (taken.insert(pick).second) row[have++] = pick;
+    }
+  }
+  return VQ_OK;
+}
+
+int vq_fit_codebooks_seeded(int format, const void* const* mats, int dtype, int64_t n_mats, int64_t rows,
+                            int64_t cols, int32_t iters, uint64_t seed, float* codebooks, void* workspace,
+                            size_t ws_bytes, int engine, void* stream) {
+  if (!fmt_ok(format) || n_mats < 1 || rows < 1 || cols < 8 || cols % 8 != 0) return VQ_EINVAL;
+  if (check_shape(rows, cols, false) != VQ_OK ||
+      (uint64_t)n_mats * (uint64_t)rows * (uint64_t)(cols / 8) >= (1ull << 32))
+    return VQ_ERANGE;
+  const int64_t n = n_mats * rows * (cols / 8);
+  const int S = stages_of(format), K = entries_of(format);
+  std::vector<int64_t> init((size_t)S * K);
+  const int st = vq_forgy_init(n, K, S, seed, init.data());
+  if (st != VQ_OK) return st;
+  return vq_fit_codebooks(format, mats, dtype, n_mats, rows, cols, iters, init.data(), codebooks, workspace, ws_bytes,
+                          engine, stream);
 }
 
 // ---------------------------------------------------------------- decode

@@ -57,3 +57,21 @@ def test_distinct_in_range_and_deterministic(n, K, S, seed):
 def test_fewer_vectors_than_entries_is_an_error():
     with pytest.raises(oracle.OracleError):
         oracle.forgy_init_seeded(10, 16, 1, 0)
+
+
+@pytest.mark.parametrize("n,K,S,seed", [(1000, 256, 3, 1), (22020096, 256, 3, 2), (1835008, 64, 4, 3),
+                                        (64, 64, 4, 5), (1 << 20, 256, 3, (1 << 64) - 1)])
+def test_library_init_equals_oracle(n, K, S, seed):
+    """The library's host-side vq_forgy_init (its own SplitMix64 and selection)
+    against the oracle's."""
+    import residual_vector_quantization_amd as vq
+    fmt = "vq3r" if (S, K) == (3, 256) else "vq4p"
+    got = vq.forgy_init(n, fmt=fmt, seed=seed)
+    assert np.array_equal(got, oracle.forgy_init_seeded(n, K, S, seed))
+
+
+def test_library_init_rejects_too_few_vectors():
+    import ctypes
+    import residual_vector_quantization_amd as vq
+    out = np.zeros((3, 256), dtype=np.int64)
+    assert vq.lib().vq_forgy_init(255, 256, 3, 0, out.ctypes.data_as(ctypes.c_void_p)) == 1

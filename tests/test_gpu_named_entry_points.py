@@ -1,5 +1,5 @@
 """The C ABI's hot-path entry points called by name through ctypes (not through
-the Python helpers): vq_fit_codebooks, vq3r_encode / vq4p_encode,
+the Python helpers): vq_fit_codebooks, vq_fit_codebooks_seeded, vq3r_encode / vq4p_encode,
 vq3r_decode / vq4p_decode, vq3r_dequant_gemv / vq4p_dequant_gemv (stored
 records), vq_error with its relative errors, vq_read_device_status and
 vq_status_string, each against the oracle to the parity bar of its operation."""
@@ -60,6 +60,16 @@ def test_named_entry_points_against_oracle(fmt):
     assert L.vq_read_device_status(P(w_fit), stream()) == 0
     cb_o, _ = oracle.fit([W], S, K, iters, init)
     assert np.array_equal(cb.cpu().numpy().view(np.uint32), cb_o.view(np.uint32))
+
+    # vq_fit_codebooks_seeded: the library draws the init (vq_forgy_init); bit-exact
+    # against the oracle started from its own seeded init
+    cb_s = torch.empty((S, K, 8), dtype=torch.float32, device=DEV)
+    st = L.vq_fit_codebooks_seeded(F, mats, 0, 1, rows, cols, iters, 4242, P(cb_s), P(w_fit), w_fit.numel(), 0,
+                                   stream())
+    assert st == 0, L.vq_status_string(st)
+    assert L.vq_read_device_status(P(w_fit), stream()) == 0
+    cb_so, _ = oracle.fit([W], S, K, iters, oracle.forgy_init_seeded(rows * cols // 8, K, S, 4242))
+    assert np.array_equal(cb_s.cpu().numpy().view(np.uint32), cb_so.view(np.uint32))
 
     # vq3r_encode / vq4p_encode: indices and scales bit-exact
     enc = L.vq3r_encode if fmt == "vq3r" else L.vq4p_encode
