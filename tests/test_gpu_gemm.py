@@ -62,6 +62,13 @@ def _check(y, whs, xf, route, sample=None):
         err = np.abs(y[b, k] - ref)
         worst = max(worst, float((err / scale).max()))
         assert np.all(err <= 1e-3 * scale + 1e-30), (b, k, float((err / scale).max()))
+        # and per output vector of at least 64 rows, relative L2 <= 1e-3: the fp16
+        # codeword sums err by about 2^-11 / sqrt(3) of |w_hat x| per term with
+        # random signs, so over many rows the ratio settles near 3e-4, while a
+        # vector of a few rows can be dominated by one cancelling output
+        nr = np.linalg.norm(ref)
+        if nr > 0 and ref.shape[-1] >= 64:
+            assert np.linalg.norm(y[b, k] - ref) <= 1e-3 * nr, (b, k)
     return worst
 
 
@@ -130,6 +137,7 @@ def test_gemm_bad_route_and_empty(books):
     for b, k in [(0, 0), (1, 0), (2, 0), (2, 1)]:
         ref, scale = oracle.gemv_ref(whs[route[b, k]], xf[b])
         assert np.all(np.abs(y[b, k] - ref) <= 1e-3 * scale)
+        assert np.linalg.norm(y[b, k] - ref) <= 1e-3 * np.linalg.norm(ref)
     y0 = vq.dequant_gemm(args[0], args[1], args[2], args[3][:0], args[4][:0], check=True)
     assert y0.shape == (0, 2, 64)
 

@@ -764,3 +764,6 @@ def test_random_shapes_parity(cfg1, seed):
             ref, scale = oracle.gemv_ref(w_ref, xf[b])
             for k in range(topk):
                 assert np.all(np.abs(y[b, k] - ref) <= 1e-3 * scale), tag + (b, k)
+                nr = np.linalg.norm(ref)
+                if nr > 0:
+                    assert np.linalg.norm(y[b, k] - ref) <= 1e-3 * nr, tag + (b, k)
