@@ -33,7 +33,8 @@ template <int K> struct Tables<K, ENG_F16X> {
   h8 nrm[K];
 };
 template <int K> struct Tables<K, ENG_F32> {
-  float a[5][2][K];  // step s < 4: c_i[2s + half]; step 4: half 0 = ||c_i||^2, half 1 = 0
+  float a[4][2][K];             // step s: c_i[2s + half]
+  alignas(16) float nrm[K];     // ||c_i||^2, the accumulators' initial value
 };
 template <int K> struct Tables<K, ENG_VALU> {
   float norm[K];     // ||c_i||^2
@@ -76,8 +77,7 @@ __device__ inline void build_tables(SearchLds<FMT, ENG, NST>& L, const float* cb
         L.tab[t].a[s][0][i] = c[2 * s];
         L.tab[t].a[s][1][i] = c[2 * s + 1];
       }
-      L.tab[t].a[4][0][i] = nf;
-      L.tab[t].a[4][1][i] = 0.0f;
+      L.tab[t].nrm[i] = nf;
     } else if constexpr (ENG == ENG_VALU) {
       L.tab[t].norm[i] = nf;
     } else {
@@ -128,6 +128,23 @@ __device__ inline float norm2_8(const float r[8]) {
   return rr;
 }
 
+// Initial accumulators of the fp32 engine for one 32-codeword tile: lane
+// (vector, half h) holds the scores of codewords 8*(v/4) + 4h + v%4 in v, so
+// they start from those codewords' ||c||^2 (four 16-byte reads) and the matrix
+// products add -2 <r, c> on top.
+__device__ inline f16v norm_init(const float* nrm, int tile, int h) {
+  f16v acc;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 n4 = *reinterpret_cast<const float4*>(nrm + tile * 32 + 8 * q + 4 * h);
+    acc[4 * q] = n4.x;
+    acc[4 * q + 1] = n4.y;
+    acc[4 * q + 2] = n4.z;
+    acc[4 * q + 3] = n4.w;
+  }
+  return acc;
+}
+
 // Lane-local top-2 of the packed group values for stage t (one group of 32
 // vectors per wave; both half-waves hold the same vector).
 template <int FMT, int ENG, int NST>
@@ -160,15 +177,14 @@ __device__ inline void lane_top2(const SearchLds<FMT, ENG, NST>& L, int t, const
                   group_value<PACK, GS>(acc, GS * q + GS, tile * GPT + q + 1));
     }
   } else if constexpr (ENG == ENG_F32) {
-    float b[5];
+    float b[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) b[s] = -2.0f * r[2 * s + h];
-    b[4] = h ? 0.0f : 1.0f;
 #pragma unroll
     for (int tile = 0; tile < TILES; ++tile) {
-      f16v acc = {};
+      f16v acc = norm_init(L.tab[t].nrm, tile, h);
 #pragma unroll
-      for (int s = 0; s < 5; ++s)
+      for (int s = 0; s < 4; ++s)
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(L.tab[t].a[s][h][tile * 32 + i], b[s], acc, 0, 0, 0);
 #pragma unroll
       for (int q = 0; q < GPT; q += 2)
@@ -315,20 +331,17 @@ __device__ inline int search_stage_x2(const SearchLds<FMT, ENG, NST>& L, int t, 
       bg0[s] = __uint_as_float(sw[0]);
       bg1[s] = __uint_as_float(sw[1]);
     }
-    const float b4 = h ? 0.0f : 1.0f;
 #pragma unroll
     for (int tile = 0; tile < TILES; ++tile) {
-      float a[5];
+      float a[4];
 #pragma unroll
-      for (int s = 0; s < 5; ++s) a[s] = L.tab[t].a[s][h][tile * 32 + i];
-      f16v acc0 = {}, acc1 = {};
+      for (int s = 0; s < 4; ++s) a[s] = L.tab[t].a[s][h][tile * 32 + i];
+      f16v acc0 = norm_init(L.tab[t].nrm, tile, h), acc1 = acc0;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], bg0[s], acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], bg1[s], acc1, 0, 0, 0);
       }
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[4], b4, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[4], b4, acc1, 0, 0, 0);
 #pragma unroll
       for (int q = 0; q < GPT; q += 2) {
         top2_pair(m1a, m2a, group_value<PACK, GS>(acc0, GS * q, tile * GPT + q),
