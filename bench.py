@@ -318,6 +318,8 @@ def main():
         valu = profile_value("k_encode_vq3r_layer_256x2048x7168_counters.md", "valu_instructions_per_call")
         if valu is not None:
             enc["valu_issue_frac"] = round(valu / VALU_ISSUE_PER_S / (enc_ms * 1e-3), 4)
+    if "encode3" in T.ev:
+        enc["engines"] = engine_legs(torch, vq, W, cb3, idx3, sc3, enc_ws, E, enc_ms)
     gem = gemv_report(torch, vq, T, gemv_cases, evict, pk3, pk4, sc3_e, sc4_e, cb3, cb4, idx3_e)
     errors = {}
     if "error3" in T.ev:
@@ -370,6 +372,36 @@ def main():
         "cpu_baseline_legs": legs,
     }
     print(json.dumps(line), flush=True)
+
+
+def engine_legs(torch, vq, W, cb3, idx3, sc3, enc_ws, E, auto_ms):
+    """The VQ3R encode of the same layer with the fp32 engines (outside the timed
+    step): fp32 matrix cores and fp32 VALU, each timed with HIP events and
+    checked bit for bit against the default engine's indices and scales."""
+    ref_idx, ref_sc = idx3.clone(), sc3.clone()
+    flop = E * VEC_PER_EXPERT * FLOP_PER_VEC["vq3r"]
+    out = {"mfma_f16x": {"ms": round(auto_ms, 3), "pipe": "fp16 matrix cores (hi/lo split)",
+                         "tflops_fp32_equiv": round(flop / (auto_ms * 1e-3) / 1e12, 2),
+                         "frac_fp32_peak": round(flop / (auto_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4)}}
+    for eng, pipe, reps in (("mfma_f32", "fp32 matrix cores", 3), ("valu_f32", "fp32 VALU", 1)):
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            vq.encode(W, cb3, fmt="vq3r", engine=eng, idx=idx3, scales=sc3, workspace=enc_ws, check=False)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        tf = flop / (ms * 1e-3) / 1e12
+        out[eng] = {"ms": round(ms, 3), "pipe": pipe, "tflops_fp32": round(tf, 2),
+                    "frac_fp32_peak": round(tf / FP32_PEAK_TFLOPS, 4),
+                    "bit_exact_vs_default": bool(torch.equal(idx3, ref_idx) and torch.equal(sc3, ref_sc))}
+        log("encode engine %s: %.2f ms" % (eng, ms))
+    idx3.copy_(ref_idx)
+    sc3.copy_(ref_sc)
+    return out
 
 
 def gemv_report(torch, vq, T, cases, evict, pk3, pk4, sc3_e, sc4_e, cb3, cb4, idx3_e):

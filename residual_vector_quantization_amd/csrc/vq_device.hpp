@@ -280,16 +280,24 @@ __device__ inline void top2_pair(float& m1, float& m2, float x, float y) {
   m1 = fmin3(m1, x, y);
 }
 
-// Packed group value of accumulator entries v0 .. v0+GS-1 (GS consecutive
-// codewords of the lane's layout): their minimum (for GS = 4: min3 + min) with
-// the lane-local group id g packed in.
+// Packed group value of accumulator entries v0 .. v0+GS-1 (GS entries of the
+// lane's layout): their minimum (GS = 4: min3 + min; GS = 8: three min3 and a
+// min) with the lane-local group id g packed in.
 template <int PACK, int GS, typename A>
 __device__ inline float group_value(const A& acc, int v0, uint32_t g) {
   float m = acc[v0];
   if constexpr (GS == 2) m = fmin2(acc[v0], acc[v0 + 1]);
   if constexpr (GS == 4) m = fmin3(acc[v0], acc[v0 + 1], fmin2(acc[v0 + 2], acc[v0 + 3]));
+  if constexpr (GS == 8)
+    m = fmin3(fmin3(acc[v0], acc[v0 + 1], acc[v0 + 2]), fmin3(acc[v0 + 3], acc[v0 + 4], acc[v0 + 5]),
+              fmin2(acc[v0 + 6], acc[v0 + 7]));
   return pack_score<PACK>(m, g);
 }
+
+// Codeword offset of member u of a group from its first codeword: entries
+// v0 + u of the layout (codeword 8 (v / 4) + 4 h + v % 4), i.e. u for groups of
+// up to 4 and u % 4 + 8 (u / 4) for groups of 8.
+__device__ constexpr int group_member(int u) { return (u & 3) + 8 * (u >> 2); }
 
 // First codeword of lane-local group g in half h (accumulator entries
 // v0 = GS * (g mod 16/GS) of tile g / (16/GS)).
@@ -301,8 +309,8 @@ __device__ inline int group_first(int g, int h) {
 }
 
 // Exact resolution of the winning group: the exact fp32 distances of its GS
-// codewords j0 .. j0+GS-1 (the fmaf chain of the definition), their argmin with
-// the lowest index on ties, the certificate against the runner-up group value
+// codewords j0 + group_member(u) (the fmaf chain of the definition; members in
+// increasing index order), their argmin with the lowest index on ties, the certificate against the runner-up group value
 // p2 (sig: 2^sigma of the split norm term, 0 for the fp32 engines), and the
 // residual update r <- r - C[w]. rr holds ||r||^2 on entry and
 // ||r'||^2 of the updated residual on return (the winner's exact distance is
@@ -312,7 +320,7 @@ __device__ inline int resolve_group(const float (*cb)[DIM], int j0, float r[8], 
                                     float& rr, bool& flag) {
   float d[GS];
 #pragma unroll
-  for (int u = 0; u < GS; ++u) d[u] = dist8(r, cb[j0 + u]);
+  for (int u = 0; u < GS; ++u) d[u] = dist8(r, cb[j0 + group_member(u)]);
   int wu = 0;
   float dw = d[0], dmax = d[0];
 #pragma unroll
@@ -324,11 +332,12 @@ __device__ inline int resolve_group(const float (*cb)[DIM], int j0, float r[8], 
     dmax = __builtin_fmaxf(dmax, d[u]);
   }
   flag |= !certified<PACK>(p1, p2, rr, dw, dmax, sig);
-  const float* c = cb[j0 + wu];
+  const int w = j0 + group_member(wu);
+  const float* c = cb[w];
 #pragma unroll
   for (int k = 0; k < 8; ++k) r[k] = r[k] - c[k];
   rr = dw;
-  return j0 + wu;
+  return w;
 }
 
 }  // namespace vqk

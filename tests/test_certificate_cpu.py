@@ -243,6 +243,12 @@ def group_first(g, h, GS):
     return tile * 32 + 8 * (v0 >> 2) + 4 * h + (v0 & 3)
 
 
+def member(u):
+    """Codeword offset of member u from its group's first codeword: groups cover
+    consecutive accumulator entries, which map to codewords 8 (v // 4) + 4 h + v % 4."""
+    return (u & 3) + 8 * (u >> 2)
+
+
 def pack_bits(K, GS):
     return int(round(math.log2(16 * (K // 32) // GS)))
 
@@ -287,8 +293,8 @@ def search(r, C, s, GS, scale=1.25, sig_override=None):
         vals = []
         for gid in np.unique(g[sel]):
             members = sel[g[sel] == gid]
-            assert len(members) == GS and np.all(np.diff(members) == 1)
-            assert members[0] == group_first(gid, half, GS)
+            assert len(members) == GS
+            assert members.tolist() == [group_first(gid, half, GS) + member(u) for u in range(GS)]
             vals.append(pack(np.min(s[members]), gid, P))
         vals = np.sort(np.array(vals, dtype=F32))
         top.append((vals[0], vals[1]))
@@ -298,7 +304,7 @@ def search(r, C, s, GS, scale=1.25, sig_override=None):
     hw = 0 if F32(p1).view(np.uint32) == F32(q0).view(np.uint32) else 1
     gid = int(F32(p1).view(np.uint32)) & ((1 << P) - 1)
     j0 = group_first(gid, hw, GS)
-    d = [oracle.dist8(r, C[j0 + u]) for u in range(GS)]
+    d = [oracle.dist8(r, C[j0 + member(u)]) for u in range(GS)]
     wu = 0
     for u in range(1, GS):
         if d[u] < d[wu]:
@@ -306,7 +312,7 @@ def search(r, C, s, GS, scale=1.25, sig_override=None):
     rr = oracle.dist8(r, np.zeros(8, F32))
     sig = F32(2.0 ** sigma_of(C)) if sig_override is None else F32(sig_override)
     ok = certified(F32(p1), F32(p2), F32(rr), F32(d[wu]), F32(max(d)), P, sig, scale)
-    return bool(ok), j0 + wu
+    return bool(ok), j0 + member(wu)
 
 
 # ------------------------------------------------------------------ tests
@@ -332,7 +338,7 @@ def test_score_error_within_bound(engine, kind):
         assert np.all(err <= 0.25 * quad + beta), (order, float(np.max((err - beta) / quad)))
 
 
-@pytest.mark.parametrize("gs", [1, 2, 4])
+@pytest.mark.parametrize("gs", [1, 2, 4, 8])
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
 @pytest.mark.parametrize("kind", KINDS)
 def test_certificate_never_accepts_a_wrong_index(fmt, kind, gs):
@@ -354,7 +360,7 @@ def test_certificate_never_accepts_a_wrong_index(fmt, kind, gs):
         assert n_ok >= 0.3 * 3 * R.shape[0]
 
 
-@pytest.mark.parametrize("gs", [1, 2, 4])
+@pytest.mark.parametrize("gs", [1, 2, 4, 8])
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
 def test_certificate_with_near_and_exact_ties(fmt, gs):
     K = 256 if fmt == "vq3r" else 64
