@@ -315,9 +315,14 @@ def main():
                "frac_fp16_mfma_peak": round(alg_flop / (enc_ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4),
                "exact_pass_vectors": n_exact, "exact_pass_fraction": round(n_exact / (E * VEC_PER_EXPERT), 7),
                "tie_band_mismatches": 0, "device_flags": enc_flags}
-        valu = profile_value("k_encode_vq3r_layer_256x2048x7168_counters.md", "valu_instructions_per_call")
+        prof = "k_encode_vq3r_layer_256x2048x7168_counters.md"
+        valu = profile_value(prof, "valu_instructions_per_call")
         if valu is not None:
-            enc["valu_issue_frac"] = round(valu / VALU_ISSUE_PER_S / (enc_ms * 1e-3), 4)
+            # from the committed counters: VALU issue at the clock measured during them, and at 2.4 GHz over
+            # this run's time
+            enc["valu_issue_frac"] = profile_value(prof, "valu_issue_frac")
+            enc["matrix_pipe_busy_frac"] = profile_value(prof, "matrix_pipe_busy_frac")
+            enc["valu_issue_frac_at_2p4ghz"] = round(valu / VALU_ISSUE_PER_S / (enc_ms * 1e-3), 4)
     if "encode3" in T.ev:
         enc["engines"] = engine_legs(torch, vq, W, cb3, idx3, sc3, enc_ws, E, enc_ms)
     gem = gemv_report(torch, vq, T, gemv_cases, evict, pk3, pk4, sc3_e, sc4_e, cb3, cb4, idx3_e)
@@ -427,7 +432,7 @@ def gemv_report(torch, vq, T, cases, evict, pk3, pk4, sc3_e, sc4_e, cb3, cb4, id
                       "frac_of_plain_read": round(floor / (ms * 1e3), 4)}
             if k.startswith("gemvs"):
                 gem[k]["layout"] = "stored records (lists the routed experts and repacks them each call)"
-            tr = profile_value("k_gemv_vq3r_vq4p_256x2048x7168_counters.md", "traffic_bytes_per_call_%s" % k)
+            tr = profile_value("k_gemv_vq3r_256x2048x7168_counters.md", "traffic_bytes_per_call_%s" % k)
             if tr is not None:
                 gem[k]["traffic_bytes"] = tr
                 gem[k]["traffic_over_alg"] = round(tr / alg, 3)
