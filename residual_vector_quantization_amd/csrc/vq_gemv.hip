@@ -4,7 +4,7 @@
 //
 // y[p][r] = s_r * sum_j sum_t T_t[j][i_t(r, j)],   T_t[j][e] = <C_t[e], x_j>
 // where x_j is the j-th 8-element slice of the token's activation. A work tile
-// is (token-slot pair p, row chunk of at most 2048 rows, range of NB blocks of
+// is (token-slot pair p, row chunk of at most 4096 rows, range of NB blocks of
 // 16 slices). For each block of its range the workgroup tabulates T for the
 // block's slices in LDS with fp32 matrix-core products (codewords x slices),
 // then streams the block's records, one row per lane: each index costs one
@@ -14,11 +14,12 @@
 // so the result is deterministic. It equals sum_c W_hat[r][c] x[c] up to fp32
 // rounding.
 //
-// Blocks of 16 slices keep a workgroup's tables at 48 KB (VQ3R) / 32 KB
-// (VQ4P), so that three 8-wave workgroups share a CU and one's table builds
-// and start-up latency overlap the others' record streams. The record stream
-// of a wave runs two row groups ahead across block boundaries: the first
-// groups of the next block are in flight while the table for it is built.
+// One 16-wave workgroup per CU keeps two table buffers (2 x 64 KB for VQ3R,
+// 2 x 32 KB for VQ4P): each step builds the next block's table into one while
+// the waves read the current block's from the other, with one barrier per
+// block. The record stream of a wave runs two row groups ahead across block
+// boundaries, so the first groups of the next block are in flight while its
+// table is built.
 //
 // Runtime layout ("packed"): the GEMV reads indices repacked by
 // vq_gemv_pack into blocks of J = 16 slices x 64-row groups. Within a group
@@ -33,7 +34,8 @@
 //   T[(e * S + t) * R + replica][slice],
 // so the 16 lanes of a quarter-wave read 16 distinct slices (distinct LDS
 // banks); VQ4P keeps R = 2 replicas, lanes 16-31 (mod 32) reading the second,
-// which makes a half-wave's reads conflict-free; VQ3R keeps one copy.
+// which makes a half-wave's reads conflict-free; VQ3R keeps stage 0 twice
+// (below).
 //
 // The stored-record entry point (vq_dequant_gemv on [rows][cols/8][3]
 // records) first lists the distinct routed experts (k_gemv_route_stored), packs
@@ -47,17 +49,17 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr int GJ = 16;     // slices per block
 constexpr int GROUP = 64;  // rows per interleaved group (one wave)
-constexpr int GEMV_WAVES = 8;
+constexpr int GEMV_WAVES = 16;
 constexpr int GEMV_THREADS = 64 * GEMV_WAVES;
 #ifndef VQ_GEMV_TILES_PER_CU
-#define VQ_GEMV_TILES_PER_CU 2
+#define VQ_GEMV_TILES_PER_CU 1
 #endif
 
-// Table layouts. VQ3R: T[e][t][slice] with a 256-byte row per codeword
-// (3 x 16 floats and 16 floats of padding; 64 KB): the LDS address of a
-// lookup is (e << 8) | (t*64 + slice*4), so one byte permute forms it from
-// the record and a per-lane offset byte. VQ4P: T[e][t][replica][slice] (32 KB),
-// two replicas.
+// Table layouts. VQ3R: T[e][slot][slice] with a 256-byte row per codeword,
+// four 16-float slots holding stages 0, 1, 2 and stage 0 again (64 KB): the LDS
+// address of a lookup is (e << 8) | (slot*64 + slice*4), so one byte permute
+// forms it from the record and a per-lane offset byte. VQ4P:
+// T[e][t][replica][slice] (32 KB), two replicas.
 template <int FMT> struct GemvCfg;
 template <> struct GemvCfg<0> { static constexpr int R = 1, FLOATS = 256 * 64; };
 template <> struct GemvCfg<1> { static constexpr int R = 2, FLOATS = 64 * 4 * 2 * 16; };
@@ -183,22 +185,22 @@ __global__ __launch_bounds__(1024) void k_gemv_route_stored(const int32_t* route
 // products over k = 0..3 and 4..7). A task is (stage t, 16 codewords); its
 // codebook operands are loaded once per tile (CbOps), the activation operand
 // once per block.
-template <int FMT>
+template <int FMT, int NW>
 struct CbOps {
   static constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, NT = K / 16, TASKS = S * NT;
-  static constexpr int PER_WAVE = (TASKS + GEMV_WAVES - 1) / GEMV_WAVES;
+  static constexpr int PER_WAVE = (TASKS + NW - 1) / NW;
   float a[PER_WAVE][2];
 };
 
 // lane (codeword i = lane % 16, k quarter kq = lane / 16) holds C_t[16ct + i][4h + kq]
-template <int FMT>
-__device__ inline void cb_load(CbOps<FMT>& op, const float* cb_g) {
-  using O = CbOps<FMT>;
+template <int FMT, int NW>
+__device__ inline void cb_load(CbOps<FMT, NW>& op, const float* cb_g) {
+  using O = CbOps<FMT, NW>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, kq = lane >> 4;
 #pragma unroll
   for (int u = 0; u < O::PER_WAVE; ++u) {
-    const int task = wave + GEMV_WAVES * u;
+    const int task = wave + NW * u;
     const int tk = task < O::TASKS ? task : 0;
     const int t = tk / O::NT, ct = tk % O::NT;
 #pragma unroll
@@ -217,9 +219,9 @@ __device__ inline void x_load(uint32_t xb[2], const uint16_t* xrow, int64_t j0, 
   for (int h = 0; h < 2; ++h) xb[h] = xrow[(j0 + jc) * DIM + 4 * h + kq];
 }
 
-template <int FMT>
-__device__ inline void lut_compute(const CbOps<FMT>& op, const uint32_t xb[2], float* lut, int nsl) {
-  using O = CbOps<FMT>;
+template <int FMT, int NW>
+__device__ inline void lut_compute(const CbOps<FMT, NW>& op, const uint32_t xb[2], float* lut, int nsl) {
+  using O = CbOps<FMT, NW>;
   constexpr int R = GemvCfg<FMT>::R;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, rg = lane >> 4;
@@ -229,7 +231,7 @@ __device__ inline void lut_compute(const CbOps<FMT>& op, const uint32_t xb[2], f
   for (int h = 0; h < 2; ++h) b[h] = sv ? f16_bits_to_f32((uint16_t)xb[h]) : 0.0f;
 #pragma unroll
   for (int u = 0; u < O::PER_WAVE; ++u) {
-    const int task = wave + GEMV_WAVES * u;
+    const int task = wave + NW * u;
     if (task >= O::TASKS) break;  // wave-uniform
     const int t = task / O::NT, ct = task % O::NT;
     f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -241,6 +243,7 @@ __device__ inline void lut_compute(const CbOps<FMT>& op, const uint32_t xb[2], f
       const int e = ct * 16 + 4 * rg + v;
       if constexpr (FMT == 0) {
         lut[e * 64 + t * GJ + j] = acc[v];
+        if (t == 0) lut[e * 64 + 3 * GJ + j] = acc[v];  // stage 0 again in the row's fourth slot
       } else {
 #pragma unroll
         for (int rep = 0; rep < R; ++rep) lut[((e * O::S + t) * R + rep) * GJ + j] = acc[v];
@@ -251,16 +254,16 @@ __device__ inline void lut_compute(const CbOps<FMT>& op, const uint32_t xb[2], f
 
 // Tile order: the tiles of each XCD share are contiguous: workgroups are
 // dealt to the 8 XCDs in turn.
-__device__ inline int64_t tile_of_block(int64_t bid, int64_t ntiles_pad) {
-  const int64_t per_xcd = ntiles_pad / 8;
+__device__ inline uint32_t tile_of_block(uint32_t bid, uint32_t ntiles_pad) {
+  const uint32_t per_xcd = ntiles_pad / 8;
   return (bid % 8) * per_xcd + bid / 8;
 }
 
 // A tile is (slot pair p, row chunk, range of nb blocks); tile index
-// t = (chunk * nrange + range) * npairs + p. Matrices of more than 8 * GPW row
+// t = (chunk * nrange + range) * npairs + p. Matrices of more than 16 * GPW row
 // groups are cut into nsplit chunks of near-equal group counts, so a tile never
-// streams more than 8 * GPW * 64 rows and tall matrices still give many tiles.
-// GPW = row groups per wave in a chunk (groups g = g0 + wave + 8k, k < GPW),
+// streams more than 16 * GPW * 64 rows and tall matrices still give many tiles.
+// GPW = row groups per wave in a chunk (groups g = g0 + wave + 16k, k < GPW),
 // fully unrolled. remap (may be NULL): packed slot of pair p (the stored-record
 // path packs only the routed experts); else the packed slot is route[p].
 template <int FMT, int GPW>
@@ -268,25 +271,25 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
                                                        const float* cb_g, int64_t rows, int64_t cols, int n_experts,
                                                        const uint16_t* x, int topk, const int32_t* route,
                                                        float* partials, int npairs, int nblk, int nb, int nrange,
-                                                       int nsplit, int64_t ntiles, int64_t ntiles_pad) {
+                                                       int gper, int grem, uint32_t ntiles, uint32_t ntiles_pad) {
   constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, R = GemvCfg<FMT>::R, NC = GJ / 4;
-  constexpr int NW = GEMV_WAVES;
-  __shared__ float lut[GemvCfg<FMT>::FLOATS];
-  const int64_t tile = tile_of_block(blockIdx.x, ntiles_pad);
+  constexpr int TF = GemvCfg<FMT>::FLOATS, NW = GEMV_WAVES;
+  __shared__ float lut[2 * TF];
+  // 32-bit index arithmetic (the host keeps the grid below 2^31): 64-bit
+  // divisions would cost hundreds of scalar instructions per wave here.
+  const uint32_t tile = tile_of_block(blockIdx.x, ntiles_pad);
   if (tile >= ntiles) return;
-  const int p = (int)(tile % npairs);
-  const int64_t cq = tile / npairs;
-  const int q = (int)(cq % nrange), chunk = (int)(cq / nrange);
-  const int e = route[p];
-  if (e < 0 || e >= n_experts) return;  // flagged and zeroed by k_gemv_reduce
-  const int64_t ep = remap ? (int64_t)remap[p] : (int64_t)e;
-  const int tok = p / topk;
+  const uint32_t cq = tile / (uint32_t)npairs, cc = cq / (uint32_t)nrange;
+  const int p = (int)(tile - cq * (uint32_t)npairs), q = (int)(cq - cc * (uint32_t)nrange), chunk = (int)cc;
+  const int tok = (int)((uint32_t)p / (uint32_t)topk);
   const int64_t V = cols / DIM;
   const int b0 = q * nb, b1 = (b0 + nb < nblk) ? b0 + nb : nblk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t ng = (rows + GROUP - 1) / GROUP;
-  const int64_t g0 = chunk * ng / nsplit, g1 = (chunk + 1) * ng / nsplit;  // this tile's groups [g0, g1)
-  const uint8_t* eb = pk + ep * expert_stride;
+  // this tile's groups [g0, g1): chunks of gper or gper + 1 groups
+  const int64_t g0 = (int64_t)chunk * gper + (chunk < grem ? chunk : grem);
+  const int64_t g1 = g0 + gper + (chunk < grem ? 1 : 0);
+  const uint8_t* eb = pk;  // set once the route id is in
   const uint16_t* xrow = x + (int64_t)tok * cols;
   const int nitems = (b1 - b0) * GPW;  // (block, group) items of this wave, in stream order
   // unconditional loads with a clamped item keep the wait counts exact
@@ -309,12 +312,14 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
   const char* lbase = reinterpret_cast<const char*>(lut);
   // VQ3R lookups. At step m = 4c + qq, lane l reads slice (m + l) mod 16; its
   // half-wave bit h = (l >> 4) & 1 rotates the order of the stages (lanes with
-  // h = 1 take stages 1, 2, 0), so that in each lookup instruction the two
-  // 16-lane halves of a half-wave read different stages: with the slice
-  // rotation their 32 addresses fall in 32 distinct banks whatever the
-  // indices. sel[qq] extracts record qq of a 12-byte chunk with its stages in
-  // the lane's order; soff[k][c] holds, in byte qq, t*64 + slice*4 for the
-  // lane's k-th stage t at step 4c + qq.
+  // h = 1 take stages 1, 2, 0), and its k-th lookup reads slot k + h (slot 3 =
+  // stage 0 again). The bank of a lookup is (slot*16 + slice) mod 32, so in
+  // each lookup instruction the two 16-lane halves of a half-wave, at slots of
+  // different parity, cover all 32 banks whatever the indices (with one copy of
+  // stage 0, the third lookup would pair slots 2 and 0: a two-way conflict).
+  // sel[qq] extracts record qq of a 12-byte chunk with its stages in the lane's
+  // order; soff[k][c] holds, in byte qq, slot*64 + slice*4 for the lane's k-th
+  // lookup at step 4c + qq.
   const uint32_t hb = (uint32_t)(lane >> 4) & 1u;
   uint32_t sel[4], soff[3][NC];
   if constexpr (FMT == 0) {
@@ -328,29 +333,34 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
     }
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-      const uint32_t t = (uint32_t)((k + (int)hb) % 3);
+      const uint32_t slot = (uint32_t)k + hb;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         uint32_t v = 0;
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) v |= (t * 64u + ((uint32_t)(4 * c + qq + lane) & (GJ - 1)) * 4u) << (8 * qq);
+        for (int qq = 0; qq < 4; ++qq) v |= (slot * 64u + ((uint32_t)(4 * c + qq + lane) & (GJ - 1)) * 4u) << (8 * qq);
         soff[k][c] = v;
       }
     }
   }
-  auto row_sum3 = [&](const uint32_t (&dg)[NC][3]) {
+  // lb: the table buffer (double-buffered tables; the odd one sits 64 KB up,
+  // its bit carried in byte 3 of w and moved to address byte 2 by the perm)
+  auto row_sum3 = [&](const uint32_t (&dg)[NC][3], auto lb) {
+    constexpr int LB = decltype(lb)::value;
     float acc;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const uint32_t lo = dg[c][qq < 2 ? 0 : 1], hi = dg[c][qq < 2 ? 1 : 2];
-        const uint32_t w = __builtin_amdgcn_perm(hi, lo, sel[qq]);  // the lane's stage order in bytes 0-2
+        uint32_t w = __builtin_amdgcn_perm(hi, lo, sel[qq]);  // the lane's stage order in bytes 0-2
+        if constexpr (LB == 1) w |= 1u << 24;
         float tsum;
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-          // byte 0: offset byte qq of soff[k][c]; byte 1: stage index byte k of w
-          const uint32_t a = __builtin_amdgcn_perm(soff[k][c], w, 0x0c0c0004u | ((uint32_t)k << 8) | (uint32_t)qq);
+          // byte 0: offset byte qq of soff[k][c]; byte 1: stage index byte k of w;
+          // byte 2: the buffer bit (byte 3 of w)
+          const uint32_t a = __builtin_amdgcn_perm(soff[k][c], w, 0x0c030004u | ((uint32_t)k << 8) | (uint32_t)qq);
           const float v = *reinterpret_cast<const float*>(lbase + a);
           tsum = k == 0 ? v : tsum + v;
         }
@@ -359,8 +369,10 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
     }
     return acc;
   };
-  auto row_sum = [&](const uint32_t (&dg)[NC][3]) {
-    if constexpr (FMT == 0) return row_sum3(dg);
+  auto row_sum = [&](const uint32_t (&dg)[NC][3], auto lb) {
+    constexpr int LB = decltype(lb)::value;
+    if constexpr (FMT == 0) return row_sum3(dg, lb);
+    const char* lb_base = lbase + LB * TF * 4;
     float acc;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -373,11 +385,11 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
         const int m = 4 * c + qq;
         const uint32_t soff = (((uint32_t)(m + lane) & (GJ - 1)) << 2) + rep_off;
         // the stage terms summed in stage order, then added to the row sum
-        float tsum = *reinterpret_cast<const float*>(lbase + ((uint32_t)record_index<FMT>(w, 0) * E_STRIDE + soff));
+        float tsum = *reinterpret_cast<const float*>(lb_base + ((uint32_t)record_index<FMT>(w, 0) * E_STRIDE + soff));
 #pragma unroll
         for (int t = 1; t < S; ++t) {
           const uint32_t ei = (uint32_t)record_index<FMT>(w, t);
-          tsum += *reinterpret_cast<const float*>(lbase + (ei * E_STRIDE + soff) + t * T_STRIDE);
+          tsum += *reinterpret_cast<const float*>(lb_base + (ei * E_STRIDE + soff) + t * T_STRIDE);
         }
         acc = (c == 0 && qq == 0) ? tsum : acc + tsum;
       }
@@ -387,44 +399,67 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
   float rs[GPW];
 #pragma unroll
   for (int k = 0; k < GPW; ++k) rs[k] = 0.0f;
-  // the GPW groups of one block; item (block, k) uses buffer (parity + k) & 1,
-  // and the load of item + 2 follows its consume
-  auto consume_block = [&](auto par, int i0) {
-    constexpr int P = decltype(par)::value;
+  CbOps<FMT, NW> ops;
+  uint32_t xb[2];
+  // Item i = (b - b0) * GPW + k sits in ring slot i % 2; the load of item
+  // i + 2 follows its consume. Blocks are unrolled by two, which fixes both
+  // the slot and the table buffer of every step at compile time.
+  auto consume_block = [&](auto u, int i0) {
+    constexpr int U = decltype(u)::value;
 #pragma unroll
     for (int k = 0; k < GPW; ++k) {
       const int64_t g = g0 + wave + (int64_t)k * NW;
-      if (g < g1) rs[k] += row_sum(d[(k + P) & 1]);  // wave-uniform
-      load_item(d[(k + P) & 1], i0 + k + 2);
+      if (g < g1) rs[k] += row_sum(d[(U * GPW + k) & 1], u);  // wave-uniform
+      load_item(d[(U * GPW + k) & 1], i0 + k + 2);
     }
   };
-  CbOps<FMT> ops;
-  cb_load<FMT>(ops, cb_g);
-  uint32_t xb[2];
-  x_load(xb, xrow, (int64_t)b0 * GJ, (int)((V - (int64_t)b0 * GJ) < GJ ? (V - (int64_t)b0 * GJ) : GJ));
-  __builtin_amdgcn_sched_barrier(0);  // keep the table operand loads ahead of the index stream
-  load_item(d[0], 0);
-  load_item(d[1], 1);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int b = b0; b < b1; ++b) {
+  auto nsl_of = [&](int b) {
     const int64_t j0 = (int64_t)b * GJ;
-    const int nsl = (int)((V - j0) < GJ ? (V - j0) : GJ);
-    if (b > b0) {
-      x_load(xb, xrow, j0, nsl);
-      __syncthreads();  // every wave is done with the previous block's table
+    return (int)((V - j0) < GJ ? (V - j0) : GJ);
+  };
+  // Block b's table is in buffer (b - b0) & 1. Each step builds the next
+  // block's table into the other buffer, then reads this block's; one barrier
+  // per block orders both (the writes of step b + 1 go to the buffer that step
+  // b read).
+  auto step = [&](auto u, int b) {
+    constexpr int U = decltype(u)::value;
+    if (b + 1 < b1) {
+      lut_compute<FMT, NW>(ops, xb, lut + (U ^ 1) * TF, nsl_of(b + 1));
+      if (b + 2 < b1) x_load(xb, xrow, (int64_t)(b + 2) * GJ, nsl_of(b + 2));
     }
-    lut_compute<FMT>(ops, xb, lut, nsl);
+    consume_block(u, (b - b0) * GPW);
     __syncthreads();
-    const int i0 = (b - b0) * GPW;
-    if ((GPW & 1) == 0 || (i0 & 1) == 0) consume_block(std::integral_constant<int, 0>(), i0);
-    else consume_block(std::integral_constant<int, 1>(), i0);
+  };
+  // The table operands (codebooks, activations) do not depend on the route id
+  // and go out first: issued behind the index stream of every CU they would
+  // hold up the first table by several microseconds.
+  cb_load<FMT, NW>(ops, cb_g);
+  x_load(xb, xrow, (int64_t)b0 * GJ, nsl_of(b0));
+  __builtin_amdgcn_sched_barrier(0);
+  // A route id outside [0, n_experts) is flagged and its outputs zeroed by
+  // k_gemv_reduce; its tile runs on expert 0 (there is always one) and stores
+  // nothing, so no branch holds up the loads above.
+  const int e_raw = route[p];
+  const int slot = (remap ? remap : route)[p];
+  const bool bad = e_raw < 0 || e_raw >= n_experts;
+  eb = pk + (int64_t)(remap || !bad ? slot : 0) * expert_stride;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) load_item(d[i], i);  // (as a loop: the register allocation comes out far tighter)
+  __builtin_amdgcn_sched_barrier(0);
+  lut_compute<FMT, NW>(ops, xb, lut, nsl_of(b0));
+  if (b0 + 1 < b1) x_load(xb, xrow, (int64_t)(b0 + 1) * GJ, nsl_of(b0 + 1));
+  __syncthreads();
+  for (int b = b0; b < b1; b += 2) {
+    step(std::integral_constant<int, 0>(), b);
+    if (b + 1 >= b1) break;
+    step(std::integral_constant<int, 1>(), b + 1);
   }
   float* part = partials + ((int64_t)p * nrange + q) * rows;
 #pragma unroll
   for (int k = 0; k < GPW; ++k) {
     const int64_t g = g0 + wave + (int64_t)k * NW;
     const int64_t row = g * GROUP + lane;
-    if (g < g1 && row < rows) part[row] = rs[k];
+    if (!bad && g < g1 && row < rows) part[row] = rs[k];
   }
 }
 
@@ -447,17 +482,18 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* partials, cons
   float acc = 0.0f;
   if (!bad) {
     const float* pp = partials + (int64_t)p * nrange * rows + r;
-    // eight independent loads in flight, added in range order
-    int q = 0;
-    for (; q + 8 <= nrange; q += 8) {
-      float v[8];
+    const float sc = f16_bits_to_f32(scales[(int64_t)e * scale_stride + r]);
+    // up to sixteen loads in flight, then added in range order
+    for (int q = 0; q < nrange; q += 16) {
+      float v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = pp[(int64_t)(q + u) * rows];
+      for (int u = 0; u < 16; ++u) v[u] = (q + u < nrange) ? pp[(int64_t)(q + u) * rows] : 0.0f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc += v[u];
+      for (int u = 0; u < 16; ++u) {
+        if (q + u < nrange) acc += v[u];  // uniform over the workgroup
+      }
     }
-    for (; q < nrange; ++q) acc += pp[(int64_t)q * rows];
-    acc *= f16_bits_to_f32(scales[(int64_t)e * scale_stride + r]);
+    acc *= sc;
   }
   y[(int64_t)p * rows + r] = acc;
 }
@@ -467,20 +503,19 @@ __global__ void k_gemv_clear(uint32_t* flags) {
 }
 
 // ------------------------------------------------------------------ launch geometry
-// Row chunks of a tile column: enough that no chunk exceeds 4 groups per wave
-// (2048 rows). Calls of at most 32 pairs cut the rows into at least 2 chunks:
-// their ranges then span twice the blocks, which halves the partial sums and
-// the reduce's loads per row (VQ3R, 2048 x 7168, 4 tokens top-8: 48.0 ->
-// 45.9 us; 4 chunks: 72.6 us; 1 token: unchanged with 2, 31.9 us with 4).
+// Row chunks of a tile column: as few as keep every chunk within 4 groups per
+// wave (4096 rows). Cutting small calls' rows further (so that their ranges
+// span more blocks) measured no faster with the 16-wave workgroups.
 int gemv_row_chunks(int64_t rows, int64_t npairs) {
+  (void)npairs;
   const int64_t ng = (rows + GROUP - 1) / GROUP;
   int64_t n = (ng + 4 * GEMV_WAVES - 1) / (4 * GEMV_WAVES);
-  if (npairs <= 32 && n < 2) n = 2;
   if (n > ng) n = ng > 0 ? ng : 1;
+  if (n < 1) n = 1;
   return (int)n;
 }
 
-// Row groups per wave: the groups of the largest chunk over the 8 waves.
+// Row groups per wave: the groups of the largest chunk over the 16 waves.
 static int gemv_gpw(int64_t rows, int nsplit) {
   const int64_t ng = (rows + GROUP - 1) / GROUP;
   const int64_t per = (ng + nsplit - 1) / nsplit;
@@ -530,13 +565,15 @@ static hipError_t launch_gemv_t(const GemvArgs& a) {
   int nb, nrange;
   gemv_ranges(npairs, nsplit, nblk, a.ncu, &nb, &nrange);
   const int64_t ntiles = npairs * nsplit * nrange;
-  const int64_t ntiles_pad = (ntiles + 7) / 8 * 8;
+  const int64_t ntiles_pad = (ntiles + 7) / 8 * 8;  // below 2^31 (argument checks)
+  const int64_t ng = (a.rows + GROUP - 1) / GROUP;
   const int gpw = gemv_gpw(a.rows, nsplit);
   auto go = [&](auto kern) {
     kern<<<(unsigned)ntiles_pad, GEMV_THREADS, 0, a.stream>>>(a.idx, a.expert_stride, a.remap, a.codebooks, a.rows,
                                                                a.cols, a.n_experts, a.x, a.topk, a.route,
-                                                               a.partials, (int)npairs, nblk, nb, nrange, nsplit,
-                                                               ntiles, ntiles_pad);
+                                                               a.partials, (int)npairs, nblk, nb, nrange,
+                                                               (int)(ng / nsplit), (int)(ng % nsplit), (uint32_t)ntiles,
+                                                               (uint32_t)ntiles_pad);
   };
   if (gpw == 1) go(k_gemv<FMT, 1>);
   else if (gpw == 2) go(k_gemv<FMT, 2>);

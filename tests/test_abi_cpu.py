@@ -172,7 +172,7 @@ def test_decode_gemv_error_mxfp4_argument_errors():
     assert L.vq_dequant_gemv(5, a.ptr, rec, b.ptr, 4, c.ptr, 4, 64, 2, d.ptr, 2, e.ptr, 2, f.ptr, ws.ptr, s_ws,
                              None) == VQ_EINVAL
     # more GEMV workgroups than a launch can hold: 65535 slots x 65536 row chunks
-    huge = L.vq_dequant_gemv_packed(0, a.ptr, 0, b.ptr, 0, c.ptr, 1 << 27, 8, 1, d.ptr, 65535, e.ptr, 1, f.ptr,
+    huge = L.vq_dequant_gemv_packed(0, a.ptr, 0, b.ptr, 0, c.ptr, 1 << 28, 8, 1, d.ptr, 65535, e.ptr, 1, f.ptr,
                                     ws.ptr, (1 << 63) - 1, None)
     assert huge == VQ_ERANGE
     assert L.vq_error(0, a.ptr, 0, b.ptr, c.ptr, d.ptr, 0, 4, 64, e.ptr, None, None, ws.ptr, 1 << 12, None) == VQ_EINVAL
