@@ -400,7 +400,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
 #pragma unroll
   for (int k = 0; k < GPW; ++k) rs[k] = 0.0f;
   CbOps<FMT, NW> ops;
-  uint32_t xb[2];
+  uint32_t xb[2], xb1[2];
   // Item i = (b - b0) * GPW + k sits in ring slot i % 2; the load of item
   // i + 2 follows its consume. Blocks are unrolled by two, which fixes both
   // the slot and the table buffer of every step at compile time.
@@ -435,6 +435,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
   // hold up the first table by several microseconds.
   cb_load<FMT, NW>(ops, cb_g);
   x_load(xb, xrow, (int64_t)b0 * GJ, nsl_of(b0));
+  const int bx1 = b0 + 1 < b1 ? b0 + 1 : b0;  // the second block's activations come in with the first's
+  x_load(xb1, xrow, (int64_t)bx1 * GJ, nsl_of(bx1));
   __builtin_amdgcn_sched_barrier(0);
   // A route id outside [0, n_experts) is flagged and its outputs zeroed by
   // k_gemv_reduce; its tile runs on expert 0 (there is always one) and stores
@@ -447,7 +449,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
   for (int i = 0; i < 2; ++i) load_item(d[i], i);  // (as a loop: the register allocation comes out far tighter)
   __builtin_amdgcn_sched_barrier(0);
   lut_compute<FMT, NW>(ops, xb, lut, nsl_of(b0));
-  if (b0 + 1 < b1) x_load(xb, xrow, (int64_t)(b0 + 1) * GJ, nsl_of(b0 + 1));
+  xb[0] = xb1[0];
+  xb[1] = xb1[1];
   __syncthreads();
   for (int b = b0; b < b1; b += 2) {
     step(std::integral_constant<int, 0>(), b);
