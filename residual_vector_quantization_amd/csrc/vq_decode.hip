@@ -179,10 +179,53 @@ hipError_t launch_decode(const DecodeArgs& a) {
 // ------------------------------------------------------------------ error
 // [VQ3R page] §3.1: ||W - W_hat||_F / ||W||_F. Per matrix, fp64 sums of
 // (w - w_hat_t)^2 for the partial reconstructions after t = 1..S stages and of
-// w^2. The sums are grouped by fixed chunks of ERR_CHUNK rows: each chunk's
+// w^2, each 8-weight vector's terms first summed in fp32 (fp64 where fp32
+// would lose range). The sums are grouped by fixed chunks of ERR_CHUNK rows: each chunk's
 // partial has its own slot, whichever block computes it, and k_error_reduce
 // adds the slots in chunk order. A matrix's result therefore depends only on
 // its own data, not on the grid or on how many matrices share a call.
+// Raw 8-element vector loads (converted to fp32 only where used, so that a
+// load in flight does not force a wait).
+template <int DT>
+struct RawVec8 {
+  uint4 q[DT == DT_F32 ? 2 : 1];
+};
+template <int DT>
+__device__ inline RawVec8<DT> load_raw8(const void* row, int64_t j) {
+  RawVec8<DT> r;
+  const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(row) + j * 8 * (DT == DT_F32 ? 4 : 2));
+#pragma unroll
+  for (int h = 0; h < (DT == DT_F32 ? 2 : 1); ++h) r.q[h] = p[h];
+  return r;
+}
+template <int DT>
+__device__ inline void raw8_to_f32(const RawVec8<DT>& r, float v[8]) {
+  if constexpr (DT == DT_F32) {
+    const uint32_t u[8] = {r.q[0].x, r.q[0].y, r.q[0].z, r.q[0].w, r.q[1].x, r.q[1].y, r.q[1].z, r.q[1].w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = __uint_as_float(u[k]);
+  } else {
+    const uint32_t u[4] = {r.q[0].x, r.q[0].y, r.q[0].z, r.q[0].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (DT == DT_BF16) {
+        v[2 * k] = __uint_as_float(u[k] << 16);
+        v[2 * k + 1] = __uint_as_float(u[k] & 0xFFFF0000u);
+      } else {
+        v[2 * k] = __half2float(__ushort_as_half((unsigned short)(u[k] & 0xFFFFu)));
+        v[2 * k + 1] = __half2float(__ushort_as_half((unsigned short)(u[k] >> 16)));
+      }
+    }
+  }
+}
+// One item of the error kernel's load stream: its raw inputs.
+template <int DT>
+struct ErrSlot {
+  uint32_t rlo, rhi;
+  uint16_t sc;
+  RawVec8<DT> w;
+};
+
 template <int FMT, int DT>
 __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx, const uint16_t* scales,
                                                const float* cb_g, uint32_t V, int64_t rows_per_mat, int64_t cols,
@@ -198,50 +241,120 @@ __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx
   const uint8_t* idx_m = idx + (uint64_t)m * nvec_per_mat * 3;
   const uint16_t* sc_m = scales + (uint64_t)m * rows_per_mat;
   const char* W_m = (const char*)W + (uint64_t)m * nvec_per_mat * DIM * esz;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  // the wave index is the same on all lanes: readfirstlane tells the compiler,
+  // so the stream bookkeeping below stays in scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nw = blockDim.x >> 6;
   bool nonfinite = false;
+  const uint32_t per_row = (V + 63) / 64;  // vector steps of a wave per row
   for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
     double acc[S + 1];
 #pragma unroll
     for (int t = 0; t <= S; ++t) acc[t] = 0.0;
     const int64_t r1 = (c + 1) * ERR_CHUNK < rows_per_mat ? (c + 1) * ERR_CHUNK : rows_per_mat;
-    // one wave per row: the row's scale once, vectors j = lane, lane + 64, ...
-    for (int64_t row = c * ERR_CHUNK + wave; row < r1; row += nw) {
-      const float s = f16_bits_to_f32(sc_m[row]);
-      const char* wrow = W_m + (uint64_t)row * cols * esz;
-      const uint8_t* rrec = idx_m + (uint64_t)row * V * 3;
-      // the next vector's weights and record are loaded before this one is used
-      float wn[8];
-      uint32_t wordn = 0;
-      if ((uint32_t)lane < V) {
-        load_vec8<DT>(wrow, lane, wn);
-        wordn = load_record(rrec + (uint64_t)lane * 3);
+    // One wave per row (rows c*ERR_CHUNK + wave, + nw, ...), vectors j = lane,
+    // lane + 64, ... The wave's (row, j) items form one stream with two items
+    // in flight: raw weights, record bytes and row scale are loaded two items
+    // ahead, across row boundaries, and converted only when used.
+    ErrSlot<DT> sl[2];
+    const int64_t rbeg = c * ERR_CHUNK + wave;
+    const uint32_t nrows = rbeg < r1 ? (uint32_t)((r1 - rbeg + nw - 1) / nw) : 0u;
+    const uint32_t nit = nrows * per_row;  // the wave's items: (row rbeg + nw * (it / per_row), vector it % per_row)
+    auto load = [&](ErrSlot<DT>& x, uint32_t it) {
+      // unconditional loads from a clamped (row, vector) keep the wait counts
+      // exact; items past the chunk or the row are never used
+      const uint32_t ic = it < nit ? it : nit - 1;
+      const uint32_t rr = ic / per_row;
+      const int64_t row = rbeg + (int64_t)nw * rr;
+      const uint32_t j = (uint32_t)lane + 64u * (ic - rr * per_row);
+      const uint32_t jc = j < V ? j : V - 1;
+      x.w = load_raw8<DT>(W_m + (uint64_t)row * cols * esz, jc);
+      const uint8_t* pr = idx_m + ((uint64_t)row * V + jc) * 3;
+      x.rlo = (uint32_t)pr[0] | ((uint32_t)pr[1] << 8);
+      x.rhi = pr[2];
+      x.sc = sc_m[row];
+    };
+    auto use = [&](const ErrSlot<DT>& x, uint32_t it, auto check) {
+      if constexpr (decltype(check)::value) {
+        const uint32_t rr = it / per_row;
+        const uint32_t j = (uint32_t)lane + 64u * (it - rr * per_row);
+        if (j >= V) return;
       }
-      for (uint32_t j = lane; j < V; j += 64) {
-        float w[8];
+      const float s = f16_bits_to_f32(x.sc);
+      float w[8];
+      raw8_to_f32<DT>(x.w, w);
+      const uint32_t word = x.rlo | (x.rhi << 16);
+      // The vector's sums in fp32 (w_hat_t = s * partial sum of codewords, as
+      // the decoder rounds it; d = w - w_hat_t), then added to the fp64 sums:
+      // a few fp32 roundings per term, about 1e-6 of the vector's sum at most.
+      // Vectors whose fp32 sums could overflow or lose range (non-finite,
+      // above 2^120, or sum of w^2 below 2^-100) take the fp64 path instead.
+      float part[8], e[S + 1];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) w[k] = wn[k];
-        const uint32_t word = wordn;
-        if (j + 64 < V) {
-          load_vec8<DT>(wrow, j + 64, wn);
-          wordn = load_record(rrec + (uint64_t)(j + 64) * 3);
+      for (int t = 0; t < S; ++t) {
+        const float* cw = cb[t][record_index<FMT>(word, t)];
+        float et;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          part[k] = (t == 0) ? cw[k] : part[k] + cw[k];
+          const float d = w[k] - s * part[k];
+          et = (k == 0) ? d * d : __builtin_fmaf(d, d, et);
         }
-        float part[8];
+        e[t] = et;
+      }
+      float ew = w[0] * w[0];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) part[k] = 0.0f;
+      for (int k = 1; k < 8; ++k) ew = __builtin_fmaf(w[k], w[k], ew);
+      e[S] = ew;
+      float emax = e[0];
+#pragma unroll
+      for (int t = 1; t < S; ++t) emax = fmaxf(emax, e[t]);
+      if (emax <= 0x1p120f && ew <= 0x1p120f && ew >= 0x1p-100f) {
+#pragma unroll
+        for (int t = 0; t <= S; ++t) acc[t] += (double)e[t];
+      } else {
+        float p2[8];
 #pragma unroll
         for (int t = 0; t < S; ++t) {
           const float* cw = cb[t][record_index<FMT>(word, t)];
+          double et = 0.0;
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            part[k] = (t == 0) ? cw[k] : part[k] + cw[k];
-            const double d = (double)w[k] - (double)(s * part[k]);
-            acc[t] = __builtin_fma(d, d, acc[t]);
+            p2[k] = (t == 0) ? cw[k] : p2[k] + cw[k];
+            const double d = (double)w[k] - (double)(s * p2[k]);
+            et = __builtin_fma(d, d, et);
           }
+          acc[t] += et;
         }
+        double ewd = 0.0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[S] = __builtin_fma((double)w[k], (double)w[k], acc[S]);
+        for (int k = 0; k < 8; ++k) ewd = __builtin_fma((double)w[k], (double)w[k], ewd);
+        acc[S] += ewd;
       }
+    };
+    // (scheduling barriers keep each reload behind the use of its slot; rows of
+    // a multiple of 64 vectors need no per-lane range check, whose divergent
+    // branch would make the compiler wait for both slots' loads)
+    auto stream = [&](auto check) {
+      load(sl[0], 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(sl[1], 1);
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t it = 0;
+      for (; it + 1 < nit; it += 2) {
+        use(sl[0], it, check);
+        __builtin_amdgcn_sched_barrier(0);
+        load(sl[0], it + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        use(sl[1], it + 1, check);
+        __builtin_amdgcn_sched_barrier(0);
+        load(sl[1], it + 3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (it < nit) use(sl[0], it, check);
+    };
+    if (nit > 0) {
+      if ((V & 63) == 0) stream(std::false_type());
+      else stream(std::true_type());
     }
     // a non-finite weight makes its thread's sum of squares non-finite; finite
     // weights cannot overflow it (|w| < 2^128 and fewer than 2^32 terms)

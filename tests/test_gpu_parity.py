@@ -349,6 +349,28 @@ def test_error_multi_matrix_bf16(cfg1):
         assert abs(np.sqrt(sums[m, 2] / sums[m, 3]) - ref) < 1e-5
 
 
+def test_error_extreme_magnitudes(cfg1):
+    """Vectors whose squares leave fp32's range still give the oracle's relative
+    errors (the kernel sums such vectors in fp64): a tiny matrix (its scales
+    underflow to 0), entries near 1e30 against ordinary records, and rows of
+    1e-19 / 1 / 1e12 in one matrix."""
+    say("error extreme magnitudes")
+    _, cb = cfg1["vq3r"]
+    base = synthetic.gaussian_rows(24, 256, seed=21)
+    idx_b, s_b = oracle.encode(base, cb)
+    tiny = (base * np.float32(1e-19)).astype(np.float32)
+    idx_t, s_t = oracle.encode(tiny, cb)
+    huge = base.copy()
+    huge[::3, ::5] *= np.float32(1e30)
+    mixed = (base * np.array([1e-19] * 8 + [1.0] * 8 + [1e12] * 8, np.float32)[:, None]).astype(np.float32)
+    for tag, W, idx_o, s_o in (("tiny", tiny, idx_t, s_t), ("huge", huge, idx_b, s_b), ("mixed", mixed, idx_b, s_b)):
+        rec, sd, cbd = to_dev(oracle.pack("vq3r", idx_o)), to_dev(s_o.view(np.float16)), to_dev(cb)
+        rel = vq.rel_errors(to_dev(W), rec, sd, cbd, fmt="vq3r")[0].cpu().numpy()[0]
+        for su in (1, 2, 3):
+            ref = oracle.rel_error(W, oracle.decode(idx_o, s_o, cb, stages_used=su))
+            assert np.isfinite(rel[su - 1]) and abs(rel[su - 1] - ref) <= 1e-5, (tag, su, rel[su - 1], ref)
+
+
 def test_error_flags_non_finite_weights(cfg1):
     """A non-finite weight is a data error of the error call (status 5);
     finite weights up to the fp32 maximum are not."""
