@@ -39,6 +39,7 @@ ROWS, COLS = 2048, 7168
 VEC_PER_EXPERT = ROWS * COLS // 8
 FLOP_PER_VEC = {"vq3r": 3 * 256 * 8 * 2, "vq4p": 4 * 64 * 8 * 2}
 CB_BYTES = {"vq3r": 3 * 256 * 8 * 4, "vq4p": 4 * 64 * 8 * 4}
+GEMV_ROUTINGS = 8  # seeded top-8 routings per batch size, one per timed step in turn
 # VALU issue: 1024 SIMDs (256 CUs x 4), one wave64 instruction per 4 cycles, 2.4 GHz
 VALU_ISSUE_PER_S = 1024 * 2.4e9 / 4
 
@@ -50,7 +51,7 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=8)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--experts", type=int, default=256)
     ap.add_argument("--sample", type=int, default=12)
@@ -186,10 +187,13 @@ def main():
     gemv_cases = []
     for ntok in (1, 4, 16):
         x = torch.from_numpy(synthetic.activations_f16(ntok, COLS, seed=10 + ntok).view(np.float16)).to(dev)
-        route = torch.from_numpy(synthetic.routing(ntok, E, 8, seed=20 + ntok)).to(dev)
+        # GEMV_ROUTINGS seeded routings per batch size; timed step i uses routing i mod GEMV_ROUTINGS
+        routes_np = [synthetic.routing(ntok, E, 8, seed=20 + ntok + 1000 * r) for r in range(GEMV_ROUTINGS)]
+        routes = [torch.from_numpy(rt).to(dev) for rt in routes_np]
         y = torch.empty((ntok, 8, ROWS), dtype=torch.float32, device=dev)
-        distinct = len(np.unique(route.cpu().numpy()))
-        gemv_cases.append({"ntok": ntok, "x": x, "route": route, "y": y, "distinct": distinct,
+        distincts = [len(np.unique(rt)) for rt in routes_np]
+        gemv_cases.append({"ntok": ntok, "x": x, "route": routes[0], "y": y, "distinct": distincts[0],
+                           "routes": routes, "distincts": distincts, "calls": {},
                            "ws3": vq.gemv_packed_workspace("vq3r", ROWS, COLS, ntok, 8),
                            "ws4": vq.gemv_packed_workspace("vq4p", ROWS, COLS, ntok, 8),
                            "wss": vq.gemv_workspace("vq3r", ROWS, COLS, ntok, 8, E)})
@@ -216,19 +220,26 @@ def main():
             with T("error3"):
                 vq.error_sums(W, idx3, sc3, cb3, fmt="vq3r", n_mats=E, sums=sums3, workspace=err_ws, check=False,
                               rel=rel3, rel_all=rel3_all)
+        rsel = step.n % GEMV_ROUTINGS
+        step.n += 1
+
+        def routed(c, key):
+            c["calls"].setdefault(key, []).append(c["distincts"][rsel])
+            return c["routes"][rsel]
         if "gemv" in only:
             with T("pack3"):
                 vq.gemv_pack(idx3_e, fmt="vq3r", out=pk3)
             for c in gemv_cases:
                 evict()
+                rt = routed(c, "gemv3_%d" % c["ntok"])
                 with T("gemv3_%d" % c["ntok"]):
-                    vq.dequant_gemv_packed(pk3, sc3_e, cb3, c["x"], c["route"], ROWS, COLS, fmt="vq3r", y=c["y"],
+                    vq.dequant_gemv_packed(pk3, sc3_e, cb3, c["x"], rt, ROWS, COLS, fmt="vq3r", y=c["y"],
                                            workspace=c["ws3"])
             for c in gemv_cases:
                 evict()
+                rt = routed(c, "gemvs3_%d" % c["ntok"])
                 with T("gemvs3_%d" % c["ntok"]):
-                    vq.dequant_gemv(idx3_e, sc3_e, cb3, c["x"], c["route"], fmt="vq3r", y=c["y"],
-                                    workspace=c["wss"])
+                    vq.dequant_gemv(idx3_e, sc3_e, cb3, c["x"], rt, fmt="vq3r", y=c["y"], workspace=c["wss"])
         if do_mx:
             with T("mxfp4"):
                 vq.mxfp4_qdq(W, out=mx, workspace=mx_ws, check=False)
@@ -259,10 +270,12 @@ def main():
                     vq.gemv_pack(idx4_e, fmt="vq4p", out=pk4)
                 for c in gemv_cases:
                     evict()
+                    rt = routed(c, "gemv4_%d" % c["ntok"])
                     with T("gemv4_%d" % c["ntok"]):
-                        vq.dequant_gemv_packed(pk4, sc4_e, cb4, c["x"], c["route"], ROWS, COLS, fmt="vq4p",
+                        vq.dequant_gemv_packed(pk4, sc4_e, cb4, c["x"], rt, ROWS, COLS, fmt="vq4p",
                                                y=c["y"], workspace=c["ws4"])
     step.fitted = False
+    step.n = 0
 
     if args.ttp:
         ttp_bench(args, torch, vq, W, E)
@@ -286,6 +299,8 @@ def main():
         torch.cuda.synchronize()
         log("warmup step %d done" % i)
     T.reset()
+    for c in gemv_cases:
+        c["calls"] = {}
     torch.cuda.synchronize()
     t_start = time.time()
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -421,21 +436,27 @@ def gemv_report(torch, vq, T, cases, evict, pk3, pk4, sc3_e, sc4_e, cb3, cb4, id
             k = key % c["ntok"]
             if k not in T.ev:
                 continue
-            ms = T.median_ms(k)
-            alg = gemv_alg_bytes(c["distinct"], c["ntok"], fmt)
-            gbs = alg / (ms * 1e-3) / 1e9
+            # per call: its routing's distinct experts -> algorithmic bytes -> GB/s; medians over the calls
+            ts = np.array([a.elapsed_time(b) for a, b in T.ev[k]])
+            dist = np.array(c["calls"].get(k, [c["distinct"]] * len(ts))[:len(ts)])
+            algs = np.array([gemv_alg_bytes(int(d), c["ntok"], fmt) for d in dist])
+            ms = float(np.median(ts))
+            gbs = float(np.median(algs / (ts * 1e-3) / 1e9))
+            alg = int(np.median(algs))
             if alg // (1 << 20) not in floors:
                 floors[alg // (1 << 20)] = read_floor_us(torch, vq, alg, evict, out)
             floor = floors[alg // (1 << 20)]
             gem[k] = {"us": round(ms * 1e3, 2), "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                      "distinct_experts": c["distinct"], "alg_bytes": alg, "plain_read_us": round(floor, 2),
-                      "frac_of_plain_read": round(floor / (ms * 1e3), 4)}
+                      "calls": len(ts), "routings": min(len(ts), GEMV_ROUTINGS),
+                      "distinct_experts": round(float(dist.mean()), 2), "alg_bytes": alg,
+                      "plain_read_us": round(floor, 2), "frac_of_plain_read": round(floor / (ms * 1e3), 4)}
             if k.startswith("gemvs"):
                 gem[k]["layout"] = "stored records (lists the routed experts and repacks them each call)"
             tr = profile_value("k_gemv_vq3r_256x2048x7168_counters.md", "traffic_bytes_per_call_%s" % k)
-            if tr is not None:
+            if tr is not None:  # counted on the first routing (the profiling loop's)
+                alg0 = gemv_alg_bytes(c["distinct"], c["ntok"], fmt)
                 gem[k]["traffic_bytes"] = tr
-                gem[k]["traffic_over_alg"] = round(tr / alg, 3)
+                gem[k]["traffic_over_alg"] = round(tr / alg0, 3)
     # warm caches: the same call back to back, outside the timed region
     for c in cases:
         for fmt, key, pk, sce, cbk, ws in (("vq3r", "gemv3_%d", pk3, sc3_e, cb3, c["ws3"]),
