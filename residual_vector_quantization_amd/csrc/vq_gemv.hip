@@ -274,6 +274,9 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
                                                        int gper, int grem, uint32_t ntiles, uint32_t ntiles_pad) {
   constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K, R = GemvCfg<FMT>::R, NC = GJ / 4;
   constexpr int TF = GemvCfg<FMT>::FLOATS, NW = GEMV_WAVES;
+  // VQ3R lookups address the tables straight from the record words (below),
+  // except with four row groups per wave, where its registers would spill
+  constexpr bool DIRECT = FMT == 0 && GPW <= 3;
   __shared__ float lut[2 * TF];
   // 32-bit index arithmetic (the host keeps the grid below 2^31): 64-bit
   // divisions would cost hundreds of scalar instructions per wave here.
@@ -321,8 +324,77 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
   // order; soff[k][c] holds, in byte qq, slot*64 + slice*4 for the lane's k-th
   // lookup at step 4c + qq.
   const uint32_t hb = (uint32_t)(lane >> 4) & 1u;
+  // Addresses straight from the record words. Record qq of a chunk sits at
+  // bytes 3qq .. 3qq+2 of its 12 bytes (stage-minor): qq 0 in word 0, qq 3 in
+  // word 2, qq 1 across words 0 and 1, qq 2 across words 1 and 2.
+  //  - qq 0 and 3: the lane's k-th lookup reads stage (k + h) mod 3 at slot
+  //    k + h, its index byte picked from the word by a per-lane selector.
+  //  - qq 1: both halves read stage 0 (word 0, byte 3) first, at slots 0 and 3;
+  //    then stages 1 and 2 of word 1, the halves in swapped order (slots 1, 2
+  //    and 2, 1). Every instruction still pairs slots of different parity.
+  //  - qq 2: its three index bytes are first gathered into one word (as the
+  //    gathered form below does for every record), then addressed from it.
+  // soffD[par][k][c] holds the offsets slot*64 + slice*4 of the k-th lookups of
+  // records 0, 1 and 3 in bytes 0, 1, 3 and the table buffer's bit in byte 2,
+  // which every direct address takes as its byte 2; soff2[k] holds record 2's
+  // offset of chunk c in byte c.
+  uint32_t soffD[2][3][NC], soff2[3], selA[3], selB[3], selC[2], sel2 = 0;
+  if constexpr (DIRECT) {
+    auto off = [&](uint32_t slot, int m) { return slot * 64u + ((uint32_t)(m + lane) & (GJ - 1)) * 4u; };
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const uint32_t sl = (uint32_t)k + hb;                                      // records 0, 2, 3
+      const uint32_t s1 = k == 0 ? (hb ? 3u : 0u) : (k == 1 ? 1u + hb : 2u - hb);  // record 1
+      soff2[k] = 0;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint32_t v = off(sl, 4 * c) | (off(s1, 4 * c + 1) << 8) | (off(sl, 4 * c + 3) << 24);
+        soffD[0][k][c] = v;
+        soffD[1][k][c] = v | 0x10000u;
+        soff2[k] |= off(sl, 4 * c + 2) << (8 * c);
+      }
+      const uint32_t st = ((uint32_t)k + hb) % 3u;  // stage of the k-th lookup (records 0, 2, 3)
+      selA[k] = 0x0c060004u | (st << 8);            // record 0: word 0, byte st
+      selB[k] = 0x0c060007u | ((1u + st) << 8);     // record 3: word 2, byte 1 + st
+      if (k > 0) selC[k - 1] = 0x0c060005u | (((k == 1) == (hb == 0) ? 0u : 1u) << 8);  // record 1: word 1
+    }
+    // record 2's bytes within {word 2 : word 1}: stage 0 at 2, 1 at 3, 2 at 4
+    sel2 = hb ? (3u | (4u << 8) | (2u << 16) | 0x0c000000u) : (2u | (3u << 8) | (4u << 16) | 0x0c000000u);
+  }
+  auto row_sum3_direct = [&](const uint32_t (&dg)[NC][3], auto lb) {
+    constexpr int LB = decltype(lb)::value;
+    auto look = [&](uint32_t a) { return *reinterpret_cast<const float*>(lbase + a); };
+    float acc;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint32_t w0 = dg[c][0], w1 = dg[c][1], w2 = dg[c][2];
+      // record 0
+      float t = look(__builtin_amdgcn_perm(soffD[LB][0][c], w0, selA[0]));
+      t += look(__builtin_amdgcn_perm(soffD[LB][1][c], w0, selA[1]));
+      t += look(__builtin_amdgcn_perm(soffD[LB][2][c], w0, selA[2]));
+      acc = c == 0 ? t : acc + t;
+      // record 1 (first lookup: word 0, byte 3, offset byte 1 for both halves)
+      t = look(__builtin_amdgcn_perm(soffD[LB][0][c], w0, 0x0c060305u));
+      t += look(__builtin_amdgcn_perm(soffD[LB][1][c], w1, selC[0]));
+      t += look(__builtin_amdgcn_perm(soffD[LB][2][c], w1, selC[1]));
+      acc += t;
+      // record 2
+      uint32_t w = __builtin_amdgcn_perm(w2, w1, sel2);
+      if constexpr (LB == 1) w |= 1u << 24;
+      t = look(__builtin_amdgcn_perm(soff2[0], w, 0x0c030004u | (uint32_t)c));
+      t += look(__builtin_amdgcn_perm(soff2[1], w, 0x0c030104u | (uint32_t)c));
+      t += look(__builtin_amdgcn_perm(soff2[2], w, 0x0c030204u | (uint32_t)c));
+      acc += t;
+      // record 3
+      t = look(__builtin_amdgcn_perm(soffD[LB][0][c], w2, selB[0]));
+      t += look(__builtin_amdgcn_perm(soffD[LB][1][c], w2, selB[1]));
+      t += look(__builtin_amdgcn_perm(soffD[LB][2][c], w2, selB[2]));
+      acc += t;
+    }
+    return acc;
+  };
   uint32_t sel[4], soff[3][NC];
-  if constexpr (FMT == 0) {
+  if constexpr (FMT == 0 && !DIRECT) {
     // bytes of record qq within {hi, lo} (lo = bytes 0-3): qq 0: 0 1 2, 1: 3 4 5 (hi = next dword),
     // 2: 2 3 4 (lo = dword 1), 3: 5 6 7
     constexpr uint32_t b0[4] = {0, 3, 2, 5};
@@ -343,9 +415,11 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
       }
     }
   }
-  // lb: the table buffer (double-buffered tables; the odd one sits 64 KB up,
-  // its bit carried in byte 3 of w and moved to address byte 2 by the perm)
-  auto row_sum3 = [&](const uint32_t (&dg)[NC][3], auto lb) {
+  // Every record's index bytes gathered into one word w first (used where the
+  // direct form needs too many registers: four row groups per wave). lb: the
+  // table buffer (the odd one sits 64 KB up, its bit carried in byte 3 of w and
+  // moved to address byte 2 by the perm).
+  auto row_sum3_perm = [&](const uint32_t (&dg)[NC][3], auto lb) {
     constexpr int LB = decltype(lb)::value;
     float acc;
 #pragma unroll
@@ -368,6 +442,10 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const uint8_t* pk, int64_
       }
     }
     return acc;
+  };
+  auto row_sum3 = [&](const uint32_t (&dg)[NC][3], auto lb) {
+    if constexpr (DIRECT) return row_sum3_direct(dg, lb);
+    else return row_sum3_perm(dg, lb);
   };
   auto row_sum = [&](const uint32_t (&dg)[NC][3], auto lb) {
     constexpr int LB = decltype(lb)::value;
