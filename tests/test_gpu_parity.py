@@ -312,23 +312,27 @@ def test_encode_decode_error_full_layer_sampled(cfg1, fmt):
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
 def test_decode_ragged_rows_and_unaligned_records(cfg1, fmt):
     """The decoder works on chunks of 256 consecutive vectors. Covered here:
-    rows of 13 vectors (several rows per chunk), rows of 256 and 257 vectors
-    (chunk starts inside a row), a ragged last chunk, a matrix smaller than
-    one chunk, and records starting at an odd byte address (byte-wise record
-    loads). All must stay bit-exact."""
+    rows of 13 vectors (several rows per chunk), rows of 256, 257 and 512
+    vectors (chunk starts inside a row), a ragged last chunk, a matrix smaller
+    than one chunk, records starting at an odd byte address (byte-wise record
+    loads), and the partial reconstructions of the aligned cases. All must stay
+    bit-exact."""
     say("decode ragged / unaligned", fmt)
+    S, _ = vq.stages_entries(fmt)
     _, cb = cfg1[fmt]
     cbd = to_dev(cb)
-    for rows, cols, offset in ((37, 104, 0), (16, 256, 1), (5, 104, 3), (300, 2056, 0), (9, 2048, 2)):
+    for rows, cols, offset in ((37, 104, 0), (16, 256, 1), (5, 104, 3), (300, 2056, 0), (9, 2048, 2), (9, 2048, 0),
+                               (41, 4096, 0), (1, 2056, 0)):
         W = synthetic.student_t_rows_f32(rows, cols, seed=rows + cols)
         idx_o, s_o = oracle.encode(W, cb)
         packed = oracle.pack(fmt, idx_o).reshape(-1)
         buf = torch.zeros(packed.size + 8, dtype=torch.uint8, device=DEV)
         buf[offset:offset + packed.size] = to_dev(packed)
         rec = buf[offset:offset + packed.size].view(rows, cols // 8, 3)
-        got = vq.decode(rec, to_dev(s_o.view(np.float16)), cbd, fmt=fmt).cpu().numpy()
-        ref = oracle.decode(idx_o, s_o, cb)
-        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (rows, cols, offset)
+        for su in ((1, S - 1, S) if offset == 0 else (S,)):
+            got = vq.decode(rec, to_dev(s_o.view(np.float16)), cbd, fmt=fmt, stages_used=su).cpu().numpy()
+            ref = oracle.decode(idx_o, s_o, cb, stages_used=su)
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (rows, cols, offset, su)
 
 
 def test_error_multi_matrix_bf16(cfg1):
