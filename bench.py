@@ -887,6 +887,17 @@ def profile_value(fname, key):
     return float(kv[key])
 
 
+def cpu_model():
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(torch, W, cb3, nrows):
     """The oracle (plain C, all host threads) encoding a bounded sample of the
     same workload: the first `nrows` weight rows of the layer (experts 0, 1, ...)
@@ -894,13 +905,13 @@ def cpu_baseline(torch, W, cb3, nrows):
     import oracle
     w = W[:nrows].float().cpu().numpy()
     cb = cb3.cpu().numpy()
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = oracle.max_threads()
     t0 = time.time()
     oracle.encode(w, cb)
     dt = time.time() - t0
     return {"value": round(w.size / dt / 1e9, 6), "unit": "Gweights/s", "cores": threads, "kind": "oracle",
             "sample": "VQ3R encode of the first %d rows x 7168 of the layer (%d experts, %.1f s)"
-                      % (nrows, -(-nrows // ROWS), dt)}
+                      % (nrows, -(-nrows // ROWS), dt), "cpu_model": cpu_model()}
 
 
 def cpu_baseline_legs(torch, vq, synthetic, W, mats, cb3, idx3_e, sc3_e, case1):
@@ -909,7 +920,7 @@ def cpu_baseline_legs(torch, vq, synthetic, W, mats, cb3, idx3_e, sc3_e, case1):
     per weight), and the fp64 GEMV reference at 1 token (decode of the 8 routed
     experts + fp64 products)."""
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = oracle.max_threads()
     legs = {}
     W1 = synthetic.gaussian_rows(256, 1024, seed=0)
     init = synthetic.forgy_init(256 * 128, 256, 3, seed=0)

@@ -77,6 +77,7 @@ def lib():
         L.vqo_forgy_init.argtypes = [i64, i32, i32, ctypes.c_uint64, P]
         L.vqo_ttp_quantize.argtypes = [P, i64, i64, P, P, P]
         L.vqo_ttp_dequantize.argtypes = [P, P, i64, i64, P]
+        L.vqo_max_threads.argtypes = []
         _lib = L
     return _lib
 
@@ -111,6 +112,11 @@ def f16_bits_to_f32(h: int) -> float:
 
 
 # ------------------------------------------------------------------ core
+def max_threads() -> int:
+    """Host threads the oracle's parallel loops run on (its OpenMP setting)."""
+    return int(lib().vqo_max_threads())
+
+
 def row_scales(w: np.ndarray) -> np.ndarray:
     w = _f32(w)
     rows, cols = w.shape

@@ -26,6 +26,7 @@
  * row RMS beyond the fp16 range, fixed-point range too small).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -101,6 +102,10 @@ static int row_scale(const float* w, int64_t n, uint16_t* s_bits) {
   *s_bits = h;
   return VQO_OK;
 }
+
+/* Threads the parallel loops below run on (the OpenMP runtime's setting); no
+   arithmetic depends on it. */
+int vqo_max_threads(void) { return omp_get_max_threads(); }
 
 int vqo_row_scales(const float* w, int64_t rows, int64_t cols, uint16_t* s_bits) {
   int st = VQO_OK;
