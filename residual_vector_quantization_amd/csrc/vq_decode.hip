@@ -283,21 +283,28 @@ __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx
       float w[8];
       raw8_to_f32<DT>(x.w, w);
       const uint32_t word = x.rlo | (x.rhi << 16);
-      // The vector's sums in fp32 (w_hat_t = s * partial sum of codewords, as
-      // the decoder rounds it; d = w - w_hat_t), then added to the fp64 sums:
-      // a few fp32 roundings per term, about 1e-6 of the vector's sum at most.
-      // Vectors whose fp32 sums could overflow or lose range (non-finite,
-      // above 2^120, or sum of w^2 below 2^-100) take the fp64 path instead.
-      float part[8], e[S + 1];
+      // The vector's sums in fp32, then added to the fp64 sums. The difference
+      // after stage t is carried from stage to stage, d_t = d_(t-1) - s C_t[i_t]
+      // (d_(-1) = w), one fused multiply-add per element. Each d_t is within
+      // 2^-24 (|d_0| + ... + |d_t|) of the exact w - s (C_1 + ... + C_t), and
+      // the decoder's w - w_hat_t is within 2^-24 (t + 2) |w_hat_t| of it, so
+      // (with |d| <= |w| and |w_hat| ~ |w|) |d_t - (w - w_hat_t)| <= 7 2^-24 |w|
+      // or so. By Cauchy-Schwarz a matrix's sum of d^2 then moves by at most
+      // 14 2^-24 sqrt(sum d^2 * sum w^2), and its ratio by at most about
+      // 7 2^-24 = 4e-7 in absolute terms (the fp32 sums of each vector's eight
+      // terms add 4 2^-24 of the ratio), far inside the 1e-5 bar. Vectors whose
+      // fp32 sums could overflow or lose range (non-finite, above 2^120, or sum
+      // of w^2 below 2^-100) take the fp64 path instead, which forms w_hat_t as
+      // the decoder does.
+      float dv[8], e[S + 1];
 #pragma unroll
       for (int t = 0; t < S; ++t) {
         const float* cw = cb[t][record_index<FMT>(word, t)];
         float et;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          part[k] = (t == 0) ? cw[k] : part[k] + cw[k];
-          const float d = w[k] - s * part[k];
-          et = (k == 0) ? d * d : __builtin_fmaf(d, d, et);
+          dv[k] = __builtin_fmaf(-s, cw[k], t == 0 ? w[k] : dv[k]);
+          et = (k == 0) ? dv[k] * dv[k] : __builtin_fmaf(dv[k], dv[k], et);
         }
         e[t] = et;
       }
