@@ -287,15 +287,16 @@ __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx
       // after stage t is carried from stage to stage, d_t = d_(t-1) - s C_t[i_t]
       // (d_(-1) = w), one fused multiply-add per element. Each d_t is within
       // 2^-24 (|d_0| + ... + |d_t|) of the exact w - s (C_1 + ... + C_t), and
-      // the decoder's w - w_hat_t is within 2^-24 (t + 2) |w_hat_t| of it, so
-      // (with |d| <= |w| and |w_hat| ~ |w|) |d_t - (w - w_hat_t)| <= 7 2^-24 |w|
-      // or so. By Cauchy-Schwarz a matrix's sum of d^2 then moves by at most
+      // the decoder's w - w_hat_t is within 2^-24 (t + 2) |w_hat_t| of it (for
+      // partial sums no larger than w_hat_t), so with |d| <= |w| and
+      // |w_hat| ~ |w| the two differ by about 7 2^-24 |w| at most. By Cauchy-Schwarz a matrix's sum of d^2 then moves by at most
       // 14 2^-24 sqrt(sum d^2 * sum w^2), and its ratio by at most about
       // 7 2^-24 = 4e-7 in absolute terms (the fp32 sums of each vector's eight
       // terms add 4 2^-24 of the ratio), far inside the 1e-5 bar. Vectors whose
       // fp32 sums could overflow or lose range (non-finite, above 2^120, or sum
       // of w^2 below 2^-100) take the fp64 path instead, which forms w_hat_t as
-      // the decoder does.
+      // the decoder does. tests/test_error_carry_cpu.py emulates this arithmetic
+      // against the oracle, cancelling stages included.
       float dv[8], e[S + 1];
 #pragma unroll
       for (int t = 0; t < S; ++t) {
