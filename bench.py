@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=32768, help="oracle encode sample: first rows of the layer")
     ap.add_argument("--only", default="", help="comma list: fit,encode,decode,error,gemv,mx (default all)")
     ap.add_argument("--loop", default="", help="profiling helper: repeat one component (encode|encode4|encodef32|"
-                    "fit|fit4|gemv1|gemv4|gemv16|gemvs1|gemvs4|gemvs16|decode|read) --steps times")
+                    "fit|fit4|gemv1|gemv4|gemv16|gemvs1|gemvs4|gemvs16|decode|error|read) --steps times")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a plain copy of known size")
     ap.add_argument("--report", action="store_true", help="error tables: configs 1, 2 and 5 against the RTN "
                     "baselines and the oracle (prints its own JSON line)")
@@ -291,7 +291,7 @@ def main():
         return
     if args.loop:
         loop_bench(args, torch, vq, W, mats, init3, init4, cb3, cb4, fit_ws3, fit_ws4, idx3, sc3, idx4, sc4,
-                   enc_ws, pk3, sc3_e, idx3_e, gemv_cases, evict, w_hat, flush)
+                   enc_ws, pk3, sc3_e, idx3_e, gemv_cases, evict, w_hat, flush, (err_ws, sums3, rel3, rel3_all))
         return
 
     for i in range(args.warmup):
@@ -341,6 +341,19 @@ def main():
     if "encode3" in T.ev:
         enc["engines"] = engine_legs(torch, vq, W, cb3, idx3, sc3, enc_ws, E, enc_ms)
     gem = gemv_report(torch, vq, T, gemv_cases, evict, pk3, pk4, sc3_e, sc4_e, cb3, cb4, idx3_e)
+    # the HBM-bound steps of the layer, over their algorithmic bytes: records (3 B per vector), fp16 row
+    # scales and fp32 output for the decodes; bf16 weights, records and scales for the relative errors
+    rec_b, sc_b = weights // 8 * 3, E * ROWS * 2
+    hbm = {}
+    for key, what, nbytes in (("decode3", "VQ3R decode of the layer, fp32 output", rec_b + sc_b + 4 * weights),
+                              ("decode4", "VQ4P decode of the layer (MXFP4 source), fp32 output",
+                               rec_b + sc_b + 4 * weights),
+                              ("error3", "relative errors after each stage, VQ3R, bf16 weights",
+                               2 * weights + rec_b + sc_b)):
+        if key in comp:
+            gbs = nbytes / (comp[key] * 1e-3) / 1e9
+            hbm[key] = {"ms": comp[key], "alg_bytes": nbytes, "GB_s": round(gbs, 1),
+                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "what": what}
     errors = {}
     if "error3" in T.ev:
         errors["vq3r_bf16_layer"] = {"rel_err_all_after_stage": [round(float(v), 6) for v in rel3_all.cpu()],
@@ -386,6 +399,7 @@ def main():
         "components_ms": comp,
         "encode": enc,
         "gemv": gem,
+        "hbm_steps": hbm,
         "errors": errors,
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -503,7 +517,7 @@ def read_floor_us(torch, vq, nbytes, evict, out, reps=5):
 
 
 def loop_bench(args, torch, vq, W, mats, init3, init4, cb3, cb4, fit_ws3, fit_ws4, idx3, sc3, idx4, sc4, enc_ws,
-               pk3, sc3_e, idx3_e, gemv_cases, evict, w_hat, flush):
+               pk3, sc3_e, idx3_e, gemv_cases, evict, w_hat, flush, err_bufs):
     """Profiling helper: one component repeated, nothing else in the trace."""
     if args.loop not in ("fit", "fit4"):
         vq.fit_codebooks(mats, init3, fmt="vq3r", iters=args.iters, codebooks=cb3, workspace=fit_ws3)
@@ -536,6 +550,10 @@ def loop_bench(args, torch, vq, W, mats, init3, init4, cb3, cb4, fit_ws3, fit_ws
             vq.dequant_gemv_packed(pk3, sc3_e, cb3, c["x"], c["route"], ROWS, COLS, y=c["y"], workspace=c["ws3"])
         elif args.loop == "decode":
             vq.decode(idx3, sc3, cb3, out=w_hat)
+        elif args.loop == "error":
+            err_ws, sums3, rel3, rel3_all = err_bufs
+            vq.error_sums(W, idx3, sc3, cb3, fmt="vq3r", n_mats=W.shape[0] // ROWS, sums=sums3, workspace=err_ws,
+                          check=False, rel=rel3, rel_all=rel3_all)
         elif args.loop == "read":
             evict()
             vq.stream_read(flush, out)
