@@ -8,11 +8,11 @@ namespace vqk {
 // [VQ3R page] §2: w_hat = s * (((C1[i1] + C2[i2]) + C3[i3]) [+ C4[i4]]), summed
 // left to right in fp32, then one fp32 multiply: one 8-dim vector into two
 // float4, from codebooks in LDS.
-// The decode kernels pad their LDS codebooks to CbPad<FMT>::P floats per codeword: with
+// The decode and error kernels pad their LDS codebooks to CbPad<FMT>::P floats per codeword: with
 // 32-byte rows codeword j starts on one of only 8 bank groups and the random
 // lookups of a wave collide more often; 48-byte rows spread them (VQ3R decode
-// 3.33 -> 3.02 ms on a 256-expert layer). VQ4P's 64-entry codebooks gain
-// nothing from it and keep 32-byte rows.
+// 3.33 -> 3.02 ms on a 256-expert layer; relative errors 1.74 -> 1.65 ms).
+// VQ4P's 64-entry codebooks gain nothing from it and keep 32-byte rows.
 template <int FMT> struct CbPad { static constexpr int P = FMT == 0 ? 12 : DIM; };
 
 template <int FMT>
@@ -231,9 +231,12 @@ __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx
                                                const float* cb_g, uint32_t V, int64_t rows_per_mat, int64_t cols,
                                                int64_t nchunks, double* partials, WsHeader* hdr) {
   constexpr int S = Fmt<FMT>::S, K = Fmt<FMT>::K;
-  __shared__ float cb[S][K][DIM];  // unpadded: padding costs this kernel a workgroup per CU
+  // codeword rows padded as in the decode (48 bytes for VQ3R): 4 workgroups fit a CU instead of 6, but the
+  // random lookups of 32-byte rows spent about 0.59 of the cycles in bank conflicts
+  constexpr int CBP = CbPad<FMT>::P;
+  __shared__ __align__(16) float cb[S][K][CBP];
   __shared__ double red[S + 1][4];  // per-wave sums of a chunk
-  for (int q = threadIdx.x; q < S * K * DIM; q += blockDim.x) (&cb[0][0][0])[q] = cb_g[q];
+  for (int q = threadIdx.x; q < S * K * DIM; q += blockDim.x) (&cb[0][0][0])[(q >> 3) * CBP + (q & 7)] = cb_g[q];
   __syncthreads();
   const int m = blockIdx.y;
   const size_t esz = DT == DT_F32 ? 4 : 2;
@@ -368,8 +371,7 @@ __global__ __launch_bounds__(256) void k_error(const void* W, const uint8_t* idx
     // weights cannot overflow it (|w| < 2^128 and fewer than 2^32 terms)
     nonfinite |= !__builtin_isfinite(acc[S]);
     // fixed-order reduction (butterfly within each wave, then the 4 waves in
-    // order): a small LDS footprint, so 6 workgroups fit a CU with VQ3R's
-    // 24 KB of codebooks (a 256-entry tree buffer allowed 4)
+    // order): a small LDS footprint next to the codebooks
 #pragma unroll
     for (int t = 0; t <= S; ++t) {
 #pragma unroll
