@@ -9,6 +9,11 @@
 namespace vqk {
 
 constexpr int DIM = 8;
+// Floats per fp32 codeword row in the search's LDS codebooks (8 used). A
+// 48-byte row starts a codeword on any of the 8 16-byte bank groups (a 32-byte
+// row only on every other one), which halves the collisions of the random
+// codeword reads of a wave.
+constexpr int CB_ROW = 12;
 constexpr int WAVE = 64;
 
 // ---------------------------------------------------------------- status
@@ -316,7 +321,7 @@ __device__ inline int group_first(int g, int h) {
 // ||r'||^2 of the updated residual on return (the winner's exact distance is
 // the same fmaf chain over the same differences). Returns w.
 template <int PACK, int GS>
-__device__ inline int resolve_group(const float (*cb)[DIM], int j0, float r[8], float p1, float p2, float sig,
+__device__ inline int resolve_group(const float (*cb)[CB_ROW], int j0, float r[8], float p1, float p2, float sig,
                                     float& rr, bool& flag) {
   float d[GS];
 #pragma unroll

@@ -43,7 +43,7 @@ template <int K> struct Tables<K, ENG_VALU> {
 template <int FMT, int ENG, int NST>
 struct SearchLds {
   static constexpr int K = Fmt<FMT>::K;
-  float cb[NST][K][DIM];       // fp32 codebooks: exact distances, residual updates
+  alignas(16) float cb[NST][K][CB_ROW];  // fp32 codebooks (rows padded): exact distances, residual updates
   Tables<K, ENG> tab[NST];
   float sig[NST];              // 2^sigma of the norm term (F16X)
   uint32_t nmax_bits[NST];
