@@ -9,11 +9,20 @@
 namespace vqk {
 
 constexpr int DIM = 8;
-// Floats per fp32 codeword row in the search's LDS codebooks (8 used). A
-// 48-byte row starts a codeword on any of the 8 16-byte bank groups (a 32-byte
-// row only on every other one), which halves the collisions of the random
-// codeword reads of a wave.
-constexpr int CB_ROW = 12;
+// Layouts of the search's fp32 codebooks in LDS (8 floats used per codeword).
+//  - QUAD (the matrix-core engines): quads of 4 consecutive codewords (128
+//    bytes), quads CB_QUAD floats (144 bytes) apart. A lane's exact resolution
+//    reads the codewords of one group, which starts at a multiple of 4 (VQ3R)
+//    or 2 (VQ4P): with evenly spaced rows the group starts of a wave fall on
+//    few of the 8 16-byte bank groups (one with 32-byte rows, two with 48-byte
+//    rows); quad m starts on bank group m mod 8.
+//  - rows CB_ROW floats (48 bytes) apart (the fp32 VALU engine, whose two
+//    half-waves read codewords 4 apart: 192 bytes, where quads measured slower).
+constexpr int CB_QUAD = 36, CB_ROW = 12;
+template <bool QUAD>
+__device__ inline int cb_offset(int r) { return QUAD ? CB_QUAD * (r >> 2) + 8 * (r & 3) : CB_ROW * r; }
+template <bool QUAD, int K>
+struct CbFloats { static constexpr int N = QUAD ? K / 4 * CB_QUAD : K * CB_ROW; };
 constexpr int WAVE = 64;
 
 // ---------------------------------------------------------------- status
@@ -320,12 +329,18 @@ __device__ inline int group_first(int g, int h) {
 // residual update r <- r - C[w]. rr holds ||r||^2 on entry and
 // ||r'||^2 of the updated residual on return (the winner's exact distance is
 // the same fmaf chain over the same differences). Returns w.
-template <int PACK, int GS>
-__device__ inline int resolve_group(const float (*cb)[CB_ROW], int j0, float r[8], float p1, float p2, float sig,
+template <int PACK, int GS, bool QUAD>
+__device__ inline int resolve_group(const float* cbt, int j0, float r[8], float p1, float p2, float sig,
                                     float& rr, bool& flag) {
   float d[GS];
+  // members u < 4 lie in j0's quad (j0 is a multiple of GS for GS <= 4), so
+  // their rows sit at fixed offsets from the first one's
+  const float* base = cbt + cb_offset<QUAD>(j0);
 #pragma unroll
-  for (int u = 0; u < GS; ++u) d[u] = dist8(r, cb[j0 + group_member(u)]);
+  for (int u = 0; u < GS; ++u) {
+    const int gm = group_member(u);
+    d[u] = dist8(r, gm < 4 ? base + (QUAD ? 8 : CB_ROW) * gm : cbt + cb_offset<QUAD>(j0 + gm));
+  }
   int wu = 0;
   float dw = d[0], dmax = d[0];
 #pragma unroll
@@ -338,7 +353,7 @@ __device__ inline int resolve_group(const float (*cb)[CB_ROW], int j0, float r[8
   }
   flag |= !certified<PACK>(p1, p2, rr, dw, dmax, sig);
   const int w = j0 + group_member(wu);
-  const float* c = cb[w];
+  const float* c = cbt + cb_offset<QUAD>(w);
 #pragma unroll
   for (int k = 0; k < 8; ++k) r[k] = r[k] - c[k];
   rr = dw;

@@ -43,7 +43,11 @@ template <int K> struct Tables<K, ENG_VALU> {
 template <int FMT, int ENG, int NST>
 struct SearchLds {
   static constexpr int K = Fmt<FMT>::K;
-  alignas(16) float cb[NST][K][CB_ROW];  // fp32 codebooks (rows padded): exact distances, residual updates
+  static constexpr bool QUAD = ENG != ENG_VALU;  // codebook layout (vq_device.hpp)
+  // fp32 codebooks: exact distances, residual updates
+  alignas(16) float cb[NST][CbFloats<QUAD, K>::N];
+  __device__ const float* row(int t, int r) const { return cb[t] + cb_offset<QUAD>(r); }
+  __device__ float* row(int t, int r) { return cb[t] + cb_offset<QUAD>(r); }
   Tables<K, ENG> tab[NST];
   float sig[NST];              // 2^sigma of the norm term (F16X)
   uint32_t nmax_bits[NST];
@@ -66,7 +70,7 @@ __device__ inline void build_tables(SearchLds<FMT, ENG, NST>& L, const float* cb
     double n = 0.0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      L.cb[t][i][k] = c[k];
+      L.row(t, i)[k] = c[k];
       bad |= (__float_as_uint(c[k]) & 0x7FFFFFFFu) > 0x45000000u;  // |c| > 2048, inf or NaN (bit test)
       n += (double)c[k] * (double)c[k];
     }
@@ -108,7 +112,7 @@ __device__ inline void build_tables(SearchLds<FMT, ENG, NST>& L, const float* cb
       const int t = q / K, i = q % K;
       double n = 0.0;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) n += (double)L.cb[t][i][k] * (double)L.cb[t][i][k];
+      for (int k = 0; k < 8; ++k) n += (double)L.row(t, i)[k] * (double)L.row(t, i)[k];
       float ns = __double2float_rn(n) / L.sig[t];  // exact: division by a power of two
       _Float16 nh = (_Float16)ns;
       h8 v = {};
@@ -201,7 +205,7 @@ __device__ inline void lane_top2(const SearchLds<FMT, ENG, NST>& L, int t, const
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int ci = tile * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-        const float* c = L.cb[t][ci];
+        const float* c = L.row(t, ci);
         float s = L.tab[t].norm[ci];
 #pragma unroll
         for (int k = 0; k < 8; ++k) s = __builtin_fmaf(nr[k], c[k], s);
@@ -240,7 +244,8 @@ __device__ inline int search_stage(const SearchLds<FMT, ENG, NST>& L, int t, flo
   float p1, p2;
   const int j0 = h ? merge_halves<PACK, GS>(o1, o2, m1, m2, p1, p2) : merge_halves<PACK, GS>(m1, m2, o1, o2, p1, p2);
   float rr = norm2_8(r);
-  return resolve_group<PACK, GS>(L.cb[t], j0, r, p1, p2, ENG == ENG_F16X ? L.sig[t] : 0.0f, rr, flag);
+  return resolve_group<PACK, GS, SearchLds<FMT, ENG, NST>::QUAD>(L.cb[t], j0, r, p1, p2,
+                                                               ENG == ENG_F16X ? L.sig[t] : 0.0f, rr, flag);
 }
 
 // Two groups per pass (the matrix-core engines): lane (i, h) owns vector i of
@@ -360,7 +365,8 @@ __device__ inline int search_stage_x2(const SearchLds<FMT, ENG, NST>& L, int t, 
   const int j0 = merge_halves<PACK, GS>(__uint_as_float(s1[0]), __uint_as_float(s2[0]), __uint_as_float(s1[1]),
                                     __uint_as_float(s2[1]), p1, p2);
   if constexpr (!RR_IN) rr = norm2_8(r);
-  return resolve_group<PACK, GS>(L.cb[t], j0, r, p1, p2, ENG == ENG_F16X ? L.sig[t] : 0.0f, rr, flag);
+  return resolve_group<PACK, GS, SearchLds<FMT, ENG, NST>::QUAD>(L.cb[t], j0, r, p1, p2,
+                                                               ENG == ENG_F16X ? L.sig[t] : 0.0f, rr, flag);
 }
 
 // Per-wave staging of flagged vector ids in LDS. The ids of a wave gather in
