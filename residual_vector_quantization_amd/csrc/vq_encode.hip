@@ -243,8 +243,10 @@ __device__ inline void flush_accum(FitAccum<K>& A, long long* partials, int slot
 // Assignment pass over R_cur. MODE 0 (iteration): certified vectors add their
 // fixed-point coordinates to the block's cluster sums. MODE 1 (after the last
 // update): certified vectors write their residual to R_next. Vectors that fail
-// certification are queued for k_assign_exact. Groups of 64 vectors (one per
-// lane) with the matrix-core engines, 32 with the VALU engine.
+// certification are staged per wave in LDS and resolved exactly at the end of
+// the block; those that overflow a wave's stage are queued for k_assign_exact.
+// Groups of 64 vectors (one per lane) with the matrix-core engines, 32 with the
+// VALU engine.
 template <int FMT, int ENG, int MODE>
 __global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_next, int64_t n, const float* C,
                                                    WsHeader* hdr, uint32_t* list, uint32_t cap,
@@ -323,7 +325,60 @@ __global__ __launch_bounds__(256, 2) void k_assign(const float* R_cur, float* R_
     }
     flag_stage(fs, fl && valid && writer, (uint32_t)j, &hdr->n_flag[parity], list, cap, lane);
   }
-  flag_flush(fs, &hdr->n_flag[parity], list, cap, lane);
+  // The wave's flagged vectors still in its LDS stage (those that overflowed
+  // it went to the global list for k_assign_exact) are resolved here by the
+  // exact search, four lanes per vector, each over a quarter of the codewords
+  // in increasing order; combining them keeps the lowest index among equal
+  // distances. They are then counted or written like the certified ones.
+  {
+    constexpr int PARTS = 4, PER = K / PARTS;
+    const int part = lane & (PARTS - 1);
+    // (rolled loops: the tail is rare work and must not raise the register count)
+#pragma unroll 1
+    for (int q0 = 0; q0 < fs.cnt; q0 += WAVE / PARTS) {  // fs.cnt is wave-uniform
+      const int q = q0 + lane / PARTS;
+      const bool act = q < fs.cnt;
+      const int64_t vid = fs.buf[act ? q : q0];
+      const float4* p = reinterpret_cast<const float4*>(R_cur + vid * DIM);
+      const float4 ra = p[0], rb = p[1];
+      float r[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+      int best = part * PER;
+      float bd = dist8(r, L.row(0, best));
+#pragma unroll 1
+      for (int c = best + 1; c < (part + 1) * PER; ++c) {
+        const float d = dist8(r, L.row(0, c));
+        if (d < bd) {
+          bd = d;
+          best = c;
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < PARTS; o <<= 1) {
+        const float od = __shfl_xor(bd, o);
+        const int oi = __shfl_xor(best, o);
+        if (od < bd || (od == bd && oi < best)) {
+          bd = od;
+          best = oi;
+        }
+      }
+      if (act && part == 0) {
+        if (MODE == 0) {
+          if (biased) accum_vector_biased<K>(A, best, r, fscale, 0, DIM, true);
+          else accum_vector<K>(A, best, r, F, 0, DIM, true);
+        } else {
+          const float* cw = L.row(0, best);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            r[k] = r[k] - cw[k];
+            mx = max(mx, __float_as_uint(__builtin_fabsf(r[k])));
+          }
+          float4* dst = reinterpret_cast<float4*>(R_next + vid * DIM);
+          dst[0] = make_float4(r[0], r[1], r[2], r[3]);
+          dst[1] = make_float4(r[4], r[5], r[6], r[7]);
+        }
+      }
+    }
+  }
   if (MODE == 0) {
     flush_accum<K>(A, partials, blockIdx.x, biased);
   } else {

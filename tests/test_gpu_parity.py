@@ -459,16 +459,19 @@ def test_fit_zero_iterations_and_duplicate_values():
 
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
 def test_fit_flag_list_overflow_bit_exact(fmt):
-    """Half the rows are copies of one row made of 4 distinct vectors, so about
-    half the Forgy codewords coincide and every copied vector ties: the
-    exact-pass list (capacity 4096 for 65536 vectors) overflows, the exact pass
-    covers every vector and the update must skip the search's partial slots."""
+    """Seven eighths of the rows are copies of one row made of 4 distinct
+    vectors, so most Forgy codewords coincide and every copied vector ties. The
+    assign kernel resolves up to 128 flagged vectors per wave itself; with
+    786,432 vectors each wave searches 3 groups of 64, so its stage overflows
+    into the exact-pass list, which (capacity 49,152) overflows in turn: the
+    exact pass covers every vector and the update must skip the search's
+    partial slots."""
     say("fit list overflow", fmt)
     S, K = vq.stages_entries(fmt)
-    rows, cols = 512, 1024
+    rows, cols = 4096, 1536
     W = synthetic.gaussian_rows(rows, cols, seed=41)
     base = synthetic.gaussian_rows(4, 8, seed=42)
-    W[rows // 2:] = np.tile(base.reshape(-1), cols // 32)[None, :]
+    W[rows // 8:] = np.tile(base.reshape(-1), cols // 32)[None, :]
     init = synthetic.forgy_init(rows * cols // 8, K, S, seed=43)
     cb_o, _ = oracle.fit([W], S, K, 3, init)
     ws = vq.fit_workspace(fmt, 1, rows, cols)
