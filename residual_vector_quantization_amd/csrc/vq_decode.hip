@@ -12,7 +12,8 @@ namespace vqk {
 // 32-byte rows codeword j starts on one of only 8 bank groups and the random
 // lookups of a wave collide more often; 48-byte rows spread them (VQ3R decode
 // 3.33 -> 3.02 ms on a 256-expert layer; relative errors 1.74 -> 1.65 ms).
-// VQ4P's 64-entry codebooks gain nothing from it and keep 32-byte rows.
+// VQ4P's 64-entry codebooks gain nothing from it in either kernel and keep
+// 32-byte rows.
 template <int FMT> struct CbPad { static constexpr int P = FMT == 0 ? 12 : DIM; };
 
 template <int FMT>
