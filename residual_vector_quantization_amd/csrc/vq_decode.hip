@@ -8,10 +8,11 @@ namespace vqk {
 // [VQ3R page] §2: w_hat = s * (((C1[i1] + C2[i2]) + C3[i3]) [+ C4[i4]]), summed
 // left to right in fp32, then one fp32 multiply: one 8-dim vector into two
 // float4, from codebooks in LDS.
-// The decode and error kernels pad their LDS codebooks to CbPad<FMT>::P floats per codeword: with
-// 32-byte rows codeword j starts on one of only 8 bank groups and the random
-// lookups of a wave collide more often; 48-byte rows spread them (VQ3R decode
-// 3.33 -> 3.02 ms on a 256-expert layer; relative errors 1.74 -> 1.65 ms).
+// The decode and error kernels pad their LDS codebooks to CbPad<FMT>::P floats
+// per codeword: with 32-byte rows codeword j starts on 16-byte bank group
+// 2j mod 8, one of only 4 of the 8, and the random lookups of a wave collide
+// more often; 48-byte rows (group 3j mod 8) spread them over all 8 (VQ3R
+// decode 3.33 -> 3.02 ms on a 256-expert layer; relative errors 1.74 -> 1.65 ms).
 // VQ4P's 64-entry codebooks gain nothing from it in either kernel and keep
 // 32-byte rows.
 template <int FMT> struct CbPad { static constexpr int P = FMT == 0 ? 12 : DIM; };
