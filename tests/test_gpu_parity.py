@@ -457,6 +457,31 @@ def test_fit_zero_iterations_and_duplicate_values():
         assert np.array_equal(cb.cpu().numpy().view(np.uint32), cb_o.view(np.uint32)), iters
 
 
+@pytest.mark.parametrize("seed", [0, 1])
+def test_fit_random_shapes_bit_exact(seed):
+    """Seeded random fits: format, engine (fp16 split, fp32 matrix cores, fp32
+    VALU), shape (up to 400 rows, 8-2072 columns, at least K vectors),
+    magnitude (10^-2 .. 10^2) and 1-4 iterations; codebooks bit for bit
+    against the oracle's Lloyd fit."""
+    say("fit random sweep", seed)
+    rng = np.random.default_rng(300 + seed)
+    for case in range(20):
+        fmt = ["vq3r", "vq4p"][rng.integers(2)]
+        S, K = vq.stages_entries(fmt)
+        eng = ["auto", "mfma_f32", "valu_f32"][rng.integers(3)]
+        V = int(rng.integers(1, 260))
+        cols = 8 * V
+        rows = int(rng.integers(max(1, -(-K // V)), 400))
+        iters = int(rng.integers(1, 5))
+        W = (synthetic.student_t_rows_f32(rows, cols, seed=7000 + 100 * seed + case) *
+             float(10.0 ** rng.uniform(-2, 2))).astype(np.float32)
+        init = synthetic.forgy_init(rows * V, K, S, seed=case)
+        cb_o, _ = oracle.fit([W], S, K, iters, init)
+        cb = vq.fit_codebooks([to_dev(W)], init, fmt=fmt, iters=iters, engine=eng)
+        assert np.array_equal(cb.cpu().numpy().view(np.uint32), cb_o.view(np.uint32)), \
+            (case, fmt, eng, rows, cols, iters)
+
+
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
 def test_fit_flag_list_overflow_bit_exact(fmt):
     """Seven eighths of the rows are copies of one row made of 4 distinct
