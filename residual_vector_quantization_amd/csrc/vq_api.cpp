@@ -62,10 +62,12 @@ struct FitLayout {
   int ga, gf;
 };
 
-// Grid sizes of the fit kernels are fixed (not taken from the device) so that
-// the workspace size does not depend on the GPU it is queried on. 1024
-// four-wave assign workgroups fill 4 waves per SIMD on a 256-CU part (512
-// left it at 2: the fit took 2-3 % longer).
+// The partial-slot counts of the fit are fixed (not taken from the device) so
+// that the workspace size does not depend on the GPU it is queried on. The
+// assign launches use at most kFitAssignBlocks of them: as many four-wave
+// workgroups as the device holds at once (4 per CU where registers and LDS
+// allow it, 1024 on a 256-CU part; 512 left 2 per CU and the fit took 2-3 %
+// longer).
 constexpr int64_t kFitAssignBlocks = 1024, kFitExactBlocks = 256;
 
 FitLayout fit_layout(int format, int64_t n) {

@@ -250,29 +250,38 @@ __device__ inline int exact_argmin(const float r[8], const float* cb) {
 // two values by at most 2^(PACK-23) (rr + dmax). So p2 <= packed value of j's
 // group <= p1 + delta / 1.25. Vectors that fail the test are re-encoded by the
 // exact search.
+// The test evaluates the bound without square roots (the hardware square root
+// issues at a quarter of the VALU rate, and the test runs once per vector and
+// stage). For a, b >= 0 and e > 0, 2ab <= e a^2 + b^2 / e, so
+// (a + b)^2 <= (1 + e) a^2 + (1 + 1/e) b^2, an equality when b = e a. With
+// e = 1/3 for M_w and e = 5/6 for M_D (the ratios sqrt(d)/(2||r||) of the
+// encoder's residuals: d_w is about a third of rr, the group's farthest member
+// about 2.8 rr), and sqrt(M_D) <= M_D/8 + 2:
+//   M_w <= 16/3 rr + 4.004 d_w,  M_D <= 22/3 rr + 2.2022 dmax,
+//   delta <= 1.25 (c_rr rr + c_w d_w + c_D dmax + 2^-20 + 2^-24 2^sigma + 2^-120),
+// c_rr = 38/3 ALPHA + 2^(PACK-22) + 22/3 2^-24, c_w = 2^-18 + 4.004 ALPHA,
+// c_D = 2.2022 (ALPHA + 2^-24) + 2^(PACK-22). On those residuals this is within
+// 1 % of the bound with its square roots for half of the vectors and within 4 %
+// for 9 in 10. The constants are rounded up (the factor 1 + 2^-20) and each of
+// the four fmas adds a non-negative term and rounds once, so the fp32 value is
+// at least the real bound.
 constexpr float ALPHA = 1.52587890625e-05f;  // 2^-16
-// Square root inside the bound only: the hardware instruction (within 1 ulp
-// for normal arguments) on an argument raised to at least 2^-100. Its error is
-// of the order of the fp32 roundings of the bound itself, which the factors
-// 1.001 and 1.25 absorb; raising tiny arguments only makes the bound larger.
-__device__ inline float bound_sqrt(float x) {
-  return __builtin_amdgcn_sqrtf(__builtin_fmaxf(x, 7.888609052210118e-31f));
-}
 
 // sig = 2^sigma of the split norm term (0 for the fp32 engines).
 template <int PACK>
 __device__ inline bool certified(float p1, float p2, float rr, float dw, float dmax, float sig) {
-  const float sr2 = 2.0f * bound_sqrt(rr);
-  const float mw = sr2 + bound_sqrt(1.001f * dw);    // sqrt(M_w)
-  const float md = sr2 + bound_sqrt(1.001f * dmax);  // sqrt(M_D)
-  const float pk = (float)(1u << PACK) * 2.384185791015625e-07f;  // 2^(PACK-22)
-  float delta = 3.814697265625e-06f * dw;             // 2^-18 d_w
-  delta += ALPHA * (mw * mw + md * md);
-  delta += pk * (rr + dmax);
-  delta += 4.76837158203125e-07f * md;                // 2^-21 sqrt(M_D)
-  delta += 5.9604644775390625e-08f * sig;             // 2^-24 2^sigma
-  delta += 7.52316384526264e-37f;                     // 2^-120
-  delta *= 1.25f;
+  constexpr double A = 1.52587890625e-05, E24 = 5.9604644775390625e-08;  // 2^-16, 2^-24
+  constexpr double PK = (double)(1u << PACK) * 2.384185791015625e-07;    // 2^(PACK-22)
+  constexpr double UP = 1.25 * (1.0 + 9.5367431640625e-07);              // 1.25 (1 + 2^-20)
+  constexpr float c_rr = (float)(UP * (38.0 / 3.0 * A + PK + 22.0 / 3.0 * E24));
+  constexpr float c_w = (float)(UP * (3.814697265625e-06 + 4.004 * A));  // 2^-18 + 4.004 ALPHA
+  constexpr float c_d = (float)(UP * (2.2022 * (A + E24) + PK));
+  constexpr float c_0 = (float)(UP * (9.5367431640625e-07 + 7.52316384526264e-37));  // 2^-20 + 2^-120
+  constexpr float c_s = (float)(UP * E24);
+  float delta = __builtin_fmaf(c_s, sig, c_0);
+  delta = __builtin_fmaf(c_d, dmax, delta);
+  delta = __builtin_fmaf(c_w, dw, delta);
+  delta = __builtin_fmaf(c_rr, rr, delta);
   return (p2 - p1) > delta;
 }
 

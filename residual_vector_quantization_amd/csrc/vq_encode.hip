@@ -543,23 +543,38 @@ hipError_t launch_encode(const EncodeArgs& a) {
   return launch_encode_dt<1, DT_F16>(a);
 }
 
+// Assign workgroups launched: at most the workspace's partial slots, and no
+// more than the device holds at once. The assign loop strides over the groups
+// by the grid size, so a grid past the resident count would leave its last
+// workgroups running alone on a few CUs after the others have finished.
+template <int FMT, int ENG, int MODE>
+static int assign_blocks(const FitArgs& a) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_assign<FMT, ENG, MODE>, 256, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const int64_t g = (int64_t)per_cu * a.ncu;
+  return (int)(g < a.n_assign_blocks ? g : a.n_assign_blocks);
+}
+
 template <int FMT, int ENG>
 static hipError_t fit_stage_iters(const FitArgs& a, int t, const float* Rc, float* Rn, float* C, int cur) {
   constexpr int K = Fmt<FMT>::K;
-  const int ga = a.n_assign_blocks, gf = a.n_exact_blocks;
+  // the iterations' partial slots: [0, ga0) for the assign blocks, then the exact pass's
+  const int ga0 = assign_blocks<FMT, ENG, 0>(a), ga1 = assign_blocks<FMT, ENG, 1>(a), gf = a.n_exact_blocks;
   for (int it = 0; it <= a.iters; ++it) {
     const int parity = it & 1;
     if (it < a.iters) {
-      k_assign<FMT, ENG, 0><<<ga, 256, 0, a.stream>>>(Rc, Rn, a.n, C, a.hdr, a.list, a.cap, a.partials, parity,
-                                                      cur ^ 1);
-      k_assign_exact<FMT, 0><<<gf, 256, 0, a.stream>>>(Rc, Rn, a.n, C, a.hdr, a.list, a.cap, a.partials, ga, parity,
+      k_assign<FMT, ENG, 0><<<ga0, 256, 0, a.stream>>>(Rc, Rn, a.n, C, a.hdr, a.list, a.cap, a.partials, parity,
                                                        cur ^ 1);
-      k_update<FMT><<<K, UPD_THREADS, 0, a.stream>>>(C, a.partials, ga, ga + gf, a.hdr, parity, a.cap);
+      k_assign_exact<FMT, 0><<<gf, 256, 0, a.stream>>>(Rc, Rn, a.n, C, a.hdr, a.list, a.cap, a.partials, ga0,
+                                                       parity, cur ^ 1);
+      k_update<FMT><<<K, UPD_THREADS, 0, a.stream>>>(C, a.partials, ga0, ga0 + gf, a.hdr, parity, a.cap);
     } else {
-      k_assign<FMT, ENG, 1><<<ga, 256, 0, a.stream>>>(Rc, Rn, a.n, C, a.hdr, a.list, a.cap, a.partials, parity,
-                                                      cur ^ 1);
-      k_assign_exact<FMT, 1><<<gf, 256, 0, a.stream>>>(Rc, Rn, a.n, C, a.hdr, a.list, a.cap, a.partials, ga, parity,
+      k_assign<FMT, ENG, 1><<<ga1, 256, 0, a.stream>>>(Rc, Rn, a.n, C, a.hdr, a.list, a.cap, a.partials, parity,
                                                        cur ^ 1);
+      k_assign_exact<FMT, 1><<<gf, 256, 0, a.stream>>>(Rc, Rn, a.n, C, a.hdr, a.list, a.cap, a.partials, ga1,
+                                                       parity, cur ^ 1);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

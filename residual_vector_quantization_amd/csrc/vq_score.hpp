@@ -288,6 +288,12 @@ __device__ inline int search_stage_x2(const SearchLds<FMT, ENG, NST>& L, int t, 
       hw[q] = hp;
       lw[q] = lo;
     }
+    // the high half's operand of the second product: the norm term's factors
+    // (2^sigma, 2^sigma, 0, ...)
+    h8 cst = {};
+    cst[0] = (_Float16)L.sig[t];
+    cst[1] = cst[0];
+    const u4 cw = __builtin_bit_cast(u4, cst);
     u4 hg0, hg1, lg0, lg1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -295,16 +301,13 @@ __device__ inline int search_stage_x2(const SearchLds<FMT, ENG, NST>& L, int t, 
       const auto a = __builtin_amdgcn_permlane32_swap(hw[q], hw[q], false, false);
       hg0[q] = a[0];
       hg1[q] = a[1];
-      const auto b = __builtin_amdgcn_permlane32_swap(lw[q], lw[q], false, false);
+      // swap(lo, cst): result 0 = [low half's lo | cst], result 1 = [high half's lo | cst]
+      const auto b = __builtin_amdgcn_permlane32_swap(lw[q], cw[q], false, false);
       lg0[q] = b[0];
       lg1[q] = b[1];
     }
-    h8 cst = {};
-    cst[0] = (_Float16)L.sig[t];
-    cst[1] = cst[0];
     const h8 b0g0 = __builtin_bit_cast(h8, hg0), b0g1 = __builtin_bit_cast(h8, hg1);
-    const h8 b1g0 = h ? cst : __builtin_bit_cast(h8, lg0);
-    const h8 b1g1 = h ? cst : __builtin_bit_cast(h8, lg1);
+    const h8 b1g0 = __builtin_bit_cast(h8, lg0), b1g1 = __builtin_bit_cast(h8, lg1);
     const h8* pa0 = h ? L.tab[t].lo : L.tab[t].hi;
     const h8* pa1 = h ? L.tab[t].nrm : L.tab[t].hi;
 #pragma unroll

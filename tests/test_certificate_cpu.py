@@ -13,8 +13,14 @@ Per group of GS (1, 2 or 4) consecutive codewords only the minimum score
 survives, with the group's lane-local id packed into its low PACK bits; the two
 smallest packed values p1 <= p2 decide the candidate group, its members are
 resolved with the exact fp32 distance chain, and the winner is accepted when
-  p2 - p1 > 1.25 (2^-18 d_w + ALPHA (M_w + M_D) + 2^(PACK-22)(rr + dmax)
-                  + 2^-21 sqrt(M_D) + 2^-24 2^sigma + 2^-120).
+  p2 - p1 > 1.25 (1 + 2^-20) (c_rr rr + c_w d_w + c_D dmax + 2^-20 + 2^-24 2^sigma + 2^-120),
+  c_rr = 38/3 ALPHA + 2^(PACK-22) + 22/3 2^-24,  c_w = 2^-18 + 4.004 ALPHA,
+  c_D = 2.2022 (ALPHA + 2^-24) + 2^(PACK-22),
+the square-root-free upper bound of
+  1.25 (2^-18 d_w + ALPHA (M_w + M_D) + 2^(PACK-22)(rr + dmax) + 2^-21 sqrt(M_D)
+        + 2^-24 2^sigma + 2^-120),  M = (2 sqrt(rr) + sqrt(1.001 d))^2
+that (a + b)^2 <= (1 + e) a^2 + (1 + 1/e) b^2 (e = 1/3 for M_w, 5/6 for M_D)
+and sqrt(M) <= M/8 + 2 give.
 
 The matrix-core accumulation order is not documented, so the emulation sums the
 terms in several orders (sequential, reversed, pairwise, by increasing and
@@ -258,25 +264,42 @@ def pack(x, g, P):
     return ((b & ~np.uint32((1 << P) - 1)) | np.uint32(g)).view(F32)
 
 
-def _sqrt_arg(x):
-    return F32(math.sqrt(max(float(x), 7.888609052210118e-31)))
+def _fma32(a, b, c):
+    """fp32 fused multiply-add: the fp64 product-sum of fp32 operands rounded
+    once to fp32 (exact but for rare double roundings, each within one ulp)."""
+    return F32(float(F32(a)) * float(F32(b)) + float(F32(c)))
+
+
+def cert_constants(P):
+    """The kernel's fp32 constants (rounded from fp64 values raised by 2^-20)."""
+    A, E24 = 2.0 ** -16, 2.0 ** -24
+    PK = (1 << P) * 2.0 ** -22
+    UP = 1.25 * (1.0 + 2.0 ** -20)
+    return (F32(UP * (38.0 / 3.0 * A + PK + 22.0 / 3.0 * E24)), F32(UP * (2.0 ** -18 + 4.004 * A)),
+            F32(UP * (2.2022 * (A + E24) + PK)), F32(UP * (2.0 ** -20 + 2.0 ** -120)), F32(UP * E24))
+
+
+def delta_linear(rr, dw, dmax, P, sig, scale=1.25):
+    """The kernel's bound in its fp32 operation order; scale replaces the 1.25
+    of the bound (the constants are computed for 1.25 and rescaled)."""
+    c_rr, c_w, c_d, c_0, c_s = (F32(c * (scale / 1.25)) for c in cert_constants(P))
+    delta = _fma32(c_s, sig, c_0)
+    delta = _fma32(c_d, dmax, delta)
+    delta = _fma32(c_w, dw, delta)
+    return _fma32(c_rr, rr, delta)
+
+
+def delta_sqrt_form(rr, dw, dmax, P, sig):
+    """The bound with its square roots, in fp64 (the form the linear one bounds)."""
+    mw = (2.0 * math.sqrt(rr) + math.sqrt(1.001 * dw)) ** 2
+    md = (2.0 * math.sqrt(rr) + math.sqrt(1.001 * dmax)) ** 2
+    return 1.25 * (2.0 ** -18 * dw + 2.0 ** -16 * (mw + md) + (1 << P) * 2.0 ** -22 * (rr + dmax)
+                   + 2.0 ** -21 * math.sqrt(md) + 2.0 ** -24 * sig + 2.0 ** -120)
 
 
 def certified(p1, p2, rr, dw, dmax, P, sig, scale=1.25):
     """The acceptance test in the kernel's fp32 operation order."""
-    f = F32
-    sr2 = f(f(2) * _sqrt_arg(rr))
-    mw = f(sr2 + _sqrt_arg(f(f(1.001) * dw)))
-    md = f(sr2 + _sqrt_arg(f(f(1.001) * dmax)))
-    pk = f((1 << P) * 2.0 ** -22)
-    delta = f(f(2.0 ** -18) * dw)
-    delta = f(delta + f(f(ALPHA) * f(f(mw * mw) + f(md * md))))
-    delta = f(delta + f(pk * f(rr + dmax)))
-    delta = f(delta + f(f(2.0 ** -21) * md))
-    delta = f(delta + f(f(2.0 ** -24) * sig))
-    delta = f(delta + f(2.0 ** -120))
-    delta = f(delta * f(scale))
-    return f(p2 - p1) > delta
+    return F32(F32(p2) - F32(p1)) > delta_linear(rr, dw, dmax, P, sig, scale)
 
 
 def search(r, C, s, GS, scale=1.25, sig_override=None):
@@ -404,3 +427,30 @@ def test_sigma_term_is_needed():
             ok0, w0 = search(R[i], C, S[i], 4, sig_override=0.0)
             wrong_without += int(ok0 and w0 != want)
     assert wrong_with == 0 and wrong_without > 0
+
+
+@pytest.mark.parametrize("P", [4, 5, 6, 7])
+def test_linear_bound_covers_the_square_root_form(P):
+    """The kernel's square-root-free delta (fp32, its operation order) is never
+    below the bound it replaces (square roots, fp64), over ||r||^2, d_w <= dmax
+    and 2^sigma across many magnitudes, and within 5 % of it on residuals like
+    the encoder's."""
+    rng = np.random.default_rng(P)
+    n = 20000
+    rr = 10.0 ** rng.uniform(-12, 8, n)
+    dw = rr * 10.0 ** rng.uniform(-8, 2, n)
+    dmax = dw * 10.0 ** rng.uniform(0, 3, n)
+    sig = 2.0 ** rng.integers(0, 13, n)
+    sig[rng.random(n) < 0.3] = 0.0
+    for a, b, c, g in zip(rr, dw, dmax, sig):
+        a, b, c, g = F32(a), F32(b), F32(c), F32(g)
+        lin = float(delta_linear(a, b, c, P, g))
+        ref = delta_sqrt_form(float(a), float(b), float(c), P, float(g))
+        assert lin >= ref, (a, b, c, g, lin, ref)
+    # residuals like the encoder's: d_w about a third of ||r||^2, the winning
+    # group's farthest member about 2-4 times it
+    for _ in range(2000):
+        a = 10.0 ** rng.uniform(-1, 1)
+        a, b, c = F32(a), F32(a * rng.uniform(0.25, 0.45)), F32(a * rng.uniform(2.0, 4.0))
+        ratio = float(delta_linear(a, b, c, P, F32(1))) / delta_sqrt_form(float(a), float(b), float(c), P, 1.0)
+        assert 1.0 <= ratio <= 1.05, ratio
