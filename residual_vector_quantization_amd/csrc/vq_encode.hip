@@ -544,9 +544,10 @@ hipError_t launch_encode(const EncodeArgs& a) {
 }
 
 // Assign workgroups launched: at most the workspace's partial slots, and no
-// more than the device holds at once. The assign loop strides over the groups
-// by the grid size, so a grid past the resident count would leave its last
-// workgroups running alone on a few CUs after the others have finished.
+// more than the device holds at once. Each workgroup adds a partial-sum slot
+// that k_update reads; workgroups past the resident count only add slots (the
+// VQ3R assign, 3 workgroups per CU, took the same time with 1024 as with 768,
+// and k_update 11.7 instead of 9.6 us).
 template <int FMT, int ENG, int MODE>
 static int assign_blocks(const FitArgs& a) {
   int per_cu = 0;
