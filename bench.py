@@ -174,7 +174,8 @@ def main():
     rel_mx = {k: (torch.empty((E, 3 if k[0] == "3" else 4), dtype=torch.float64, device=dev),
                   torch.empty(3 if k[0] == "3" else 4, dtype=torch.float64, device=dev)) for k in sums_mx}
     do_mx = "mx" in only
-    mx = torch.empty((nrows, COLS), dtype=torch.float32, device=dev) if do_mx else None
+    # the MXFP4 source as bf16 (exact: vq_mxfp4_qdq_bf16)
+    mx = torch.empty((nrows, COLS), dtype=torch.bfloat16, device=dev) if do_mx else None
     mx_mats = [mx[e * ROWS:(e + 1) * ROWS] for e in sample] if do_mx else None
     mx_ws = torch.empty(256, dtype=torch.uint8, device=dev)
     # cache eviction between GEMV reps: reading 1 GiB of other data evicts the experts from the L2s and the

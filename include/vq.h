@@ -360,6 +360,17 @@ int vq_error(int format, const void* W, int dtype, const uint8_t* idx, const uin
 int vq_mxfp4_qdq(const void* W, int dtype, int64_t rows, int64_t cols, float* out, void* workspace,
                  size_t ws_bytes, void* stream);
 
+/* The same quantize-dequantize with the result stored as bf16 (out: device
+ * uint16 [rows][cols], each word the upper half of the fp32 result above).
+ * The format makes this exact: every result X * e2m1 has at most two
+ * significant bits and, for finite input, lies in [2^-128, 1.5 * 2^127]
+ * (X <= 2^125), so its fp32 bits end in 16 zero bits (2^-128 and 3 * 2^-128
+ * are bf16 subnormals). A consumer that reads the MXFP4 source as bf16 gets the
+ * same values from half the bytes. Arguments, workspace and errors as
+ * vq_mxfp4_qdq. */
+int vq_mxfp4_qdq_bf16(const void* W, int dtype, int64_t rows, int64_t cols, uint16_t* out, void* workspace,
+                      size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Bandwidth reference (a measurement helper, not a step of the method): a plain
  * coalesced streaming read of nbytes (a multiple of 16; src 16-byte aligned),

@@ -102,6 +102,7 @@ def lib():
         "vq_error_workspace_size": ([I, L64, L64, L64], SZ),
         "vq_error": ([I, P, I, P, P, P, L64, L64, L64, P, P, P, P, SZ, P], I),
         "vq_mxfp4_qdq": ([P, I, L64, L64, P, P, SZ, P], I),
+        "vq_mxfp4_qdq_bf16": ([P, I, L64, L64, P, P, SZ, P], I),
         "vq_stream_read": ([P, SZ, P, P], I),
         "vqc_layout": ([I, L64, L64, L64, P, P, P], ctypes.c_uint64),
         "vqc_crc32": ([ctypes.c_uint32, P, SZ], ctypes.c_uint32),
@@ -481,17 +482,22 @@ def rel_errors(W, idx, scales, codebooks, fmt="vq3r", n_mats=1, workspace=None, 
 
 # ------------------------------------------------------------------ MXFP4
 def mxfp4_qdq(W, out=None, workspace=None, check=True):
-    """MXFP4 quantize-dequantize ([VQ3R page] §3.2 source format) -> fp32 [rows, cols]."""
+    """MXFP4 quantize-dequantize ([VQ3R page] §3.2 source format) -> [rows, cols], fp32 by default or bf16
+    when `out` is a bfloat16 tensor (exact: vq_mxfp4_qdq_bf16)."""
     torch = _torch()
     rows, cols = W.shape
     _check_cuda(W)
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.float32, device=W.device)
+    _check_cuda(out)
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (rows, cols) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 or bf16 tensor of shape %s" % ((rows, cols),))
     if workspace is None:
         workspace = _workspace(256, W.device)
-    st = lib().vq_mxfp4_qdq(_ptr(W), _dtype_code(W), rows, cols, _ptr(out), _ptr(workspace), workspace.numel(),
-                            _stream())
-    _call("vq_mxfp4_qdq", st, workspace, check)
+    name = "vq_mxfp4_qdq_bf16" if out.dtype == torch.bfloat16 else "vq_mxfp4_qdq"
+    st = getattr(lib(), name)(_ptr(W), _dtype_code(W), rows, cols, _ptr(out), _ptr(workspace), workspace.numel(),
+                              _stream())
+    _call(name, st, workspace, check)
     return out
 
 

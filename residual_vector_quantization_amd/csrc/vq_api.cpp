@@ -698,8 +698,8 @@ int vq_error(int format, const void* W, int dtype, const uint8_t* idx, const uin
 }
 
 // ---------------------------------------------------------------- MXFP4
-int vq_mxfp4_qdq(const void* W, int dtype, int64_t rows, int64_t cols, float* out, void* workspace, size_t ws_bytes,
-                 void* stream) {
+static int mxfp4_qdq(const void* W, int dtype, int64_t rows, int64_t cols, void* out, int out_bf16, void* workspace,
+                     size_t ws_bytes, void* stream) {
   if (!dtype_ok(dtype) || rows < 0 || cols <= 0 || cols % 32 != 0) return VQ_EINVAL;
   if (!W || !out) return VQ_EINVAL;
   if (!workspace || !aligned(workspace, 256) || ws_bytes < kHeader) return VQ_EWORKSPACE;
@@ -709,11 +709,22 @@ int vq_mxfp4_qdq(const void* W, int dtype, int64_t rows, int64_t cols, float* ou
   a.rows = rows;
   a.cols = cols;
   a.out = out;
+  a.out_bf16 = out_bf16;
   a.hdr = (WsHeader*)workspace;
   a.stream = (hipStream_t)stream;
   int st;
   if ((st = device_cus(&a.ncu)) != VQ_OK) return st;
   return hip_status(launch_mxfp4(a));
+}
+
+int vq_mxfp4_qdq(const void* W, int dtype, int64_t rows, int64_t cols, float* out, void* workspace, size_t ws_bytes,
+                 void* stream) {
+  return mxfp4_qdq(W, dtype, rows, cols, out, 0, workspace, ws_bytes, stream);
+}
+
+int vq_mxfp4_qdq_bf16(const void* W, int dtype, int64_t rows, int64_t cols, uint16_t* out, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  return mxfp4_qdq(W, dtype, rows, cols, out, 1, workspace, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- read reference

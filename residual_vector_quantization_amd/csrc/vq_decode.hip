@@ -467,8 +467,11 @@ __device__ inline float e2m1_round(float a) {
   return fminf(q, 6.0f);
 }
 
-template <int DT>
-__global__ __launch_bounds__(256) void k_mxfp4(const void* W, uint64_t nblk, float* out, WsHeader* hdr) {
+// Output: fp32, or (BF) its upper half as bf16. Every result X * e2m1 has at
+// most two significant bits and lies in [2^-128, 1.5 * 2^127], so its fp32 bits
+// end in 16 zero bits and the bf16 word holds it exactly.
+template <int DT, bool BF>
+__global__ __launch_bounds__(256) void k_mxfp4(const void* W, uint64_t nblk, void* out, WsHeader* hdr) {
   // 32 lanes per block of 32 elements (two blocks per wave)
   const int lane = threadIdx.x & 31;
   const uint64_t b0 = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) / 32;
@@ -499,16 +502,18 @@ __global__ __launch_bounds__(256) void k_mxfp4(const void* W, uint64_t nblk, flo
       const float q = e2m1_round(__builtin_fabsf(v));
       r = X * (v < 0.0f ? -q : q);
     }
-    out[e] = r;
+    if constexpr (BF) static_cast<uint16_t*>(out)[e] = (uint16_t)(__float_as_uint(r) >> 16);
+    else static_cast<float*>(out)[e] = r;
   }
 }
 
 // The same with 8 lanes per block, 4 consecutive elements per lane: one 8- or
-// 16-byte load and one float4 store per lane (each store instruction of a wave
-// writes 1 KB of contiguous output). Division by the power of two X is the
-// multiplication by 2^-xe, exact as the correctly rounded quotient.
-template <int DT>
-__global__ __launch_bounds__(256) void k_mxfp4_v4(const void* W, uint64_t nblk, float* out, WsHeader* hdr) {
+// 16-byte load and one 16-byte (fp32) or 8-byte (bf16) store per lane (each
+// store instruction of a wave writes 1 KB or 512 B of contiguous output).
+// Division by the power of two X is the multiplication by 2^-xe, exact as the
+// correctly rounded quotient.
+template <int DT, bool BF>
+__global__ __launch_bounds__(256) void k_mxfp4_v4(const void* W, uint64_t nblk, void* out, WsHeader* hdr) {
   const int sub = threadIdx.x & 7;
   const uint64_t b0 = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3;
   const uint64_t stride = ((uint64_t)gridDim.x * blockDim.x) >> 3;
@@ -556,7 +561,13 @@ __global__ __launch_bounds__(256) void k_mxfp4_v4(const void* W, uint64_t nblk, 
         r[k] = X * (v < 0.0f ? -q : q);
       }
     }
-    *reinterpret_cast<float4*>(out + e) = make_float4(r[0], r[1], r[2], r[3]);
+    if constexpr (BF) {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + e) =
+          make_uint2((__float_as_uint(r[0]) >> 16) | (__float_as_uint(r[1]) & 0xFFFF0000u),
+                     (__float_as_uint(r[2]) >> 16) | (__float_as_uint(r[3]) & 0xFFFF0000u));
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + e) = make_float4(r[0], r[1], r[2], r[3]);
+    }
   }
   if (bad) flag_status(hdr, ST_NONFINITE);
 }
@@ -593,26 +604,32 @@ hipError_t launch_stream_read(const void* src, uint64_t nbytes, uint32_t* out, i
   return hipGetLastError();
 }
 
+template <bool BF>
+static hipError_t launch_mxfp4_t(const Mxfp4Args& a, uint64_t nblk) {
+  const size_t esz = a.dtype == DT_F32 ? 4 : 2;
+  const uintptr_t out_align = BF ? 7 : 15;
+  if (((uintptr_t)a.W & (4 * esz - 1)) == 0 && ((uintptr_t)a.out & out_align) == 0) {
+    uint64_t g = (nblk * 8 + 255) / 256;
+    if (g > (uint64_t)a.ncu * 16) g = (uint64_t)a.ncu * 16;
+    if (a.dtype == DT_F32) k_mxfp4_v4<DT_F32, BF><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
+    else if (a.dtype == DT_BF16) k_mxfp4_v4<DT_BF16, BF><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
+    else k_mxfp4_v4<DT_F16, BF><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
+    return hipGetLastError();
+  }
+  uint64_t g = (nblk * 32 + 255) / 256;
+  if (g > (uint64_t)a.ncu * 16) g = (uint64_t)a.ncu * 16;
+  if (a.dtype == DT_F32) k_mxfp4<DT_F32, BF><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
+  else if (a.dtype == DT_BF16) k_mxfp4<DT_BF16, BF><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
+  else k_mxfp4<DT_F16, BF><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
+  return hipGetLastError();
+}
+
 hipError_t launch_mxfp4(const Mxfp4Args& a) {
   hipError_t e0 = launch_reset(a.hdr, a.stream);
   if (e0 != hipSuccess) return e0;
   const uint64_t nblk = (uint64_t)a.rows * (uint64_t)(a.cols / 32);
   if (nblk == 0) return hipGetLastError();
-  const size_t esz = a.dtype == DT_F32 ? 4 : 2;
-  if (((uintptr_t)a.W & (4 * esz - 1)) == 0 && ((uintptr_t)a.out & 15) == 0) {
-    uint64_t g = (nblk * 8 + 255) / 256;
-    if (g > (uint64_t)a.ncu * 16) g = (uint64_t)a.ncu * 16;
-    if (a.dtype == DT_F32) k_mxfp4_v4<DT_F32><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
-    else if (a.dtype == DT_BF16) k_mxfp4_v4<DT_BF16><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
-    else k_mxfp4_v4<DT_F16><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
-    return hipGetLastError();
-  }
-  uint64_t g = (nblk * 32 + 255) / 256;
-  if (g > (uint64_t)a.ncu * 16) g = (uint64_t)a.ncu * 16;
-  if (a.dtype == DT_F32) k_mxfp4<DT_F32><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
-  else if (a.dtype == DT_BF16) k_mxfp4<DT_BF16><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
-  else k_mxfp4<DT_F16><<<(unsigned)g, 256, 0, a.stream>>>(a.W, nblk, a.out, a.hdr);
-  return hipGetLastError();
+  return a.out_bf16 ? launch_mxfp4_t<true>(a, nblk) : launch_mxfp4_t<false>(a, nblk);
 }
 
 }  // namespace vqk

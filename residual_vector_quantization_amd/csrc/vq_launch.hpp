@@ -91,7 +91,8 @@ struct Mxfp4Args {
   int dtype;
   const void* W;
   int64_t rows, cols;
-  float* out;
+  void* out;     // fp32, or bf16 when out_bf16
+  int out_bf16;
   WsHeader* hdr;
   int ncu;
   hipStream_t stream;

@@ -178,6 +178,10 @@ def test_decode_gemv_error_mxfp4_argument_errors():
     assert L.vq_error(0, a.ptr, 0, b.ptr, c.ptr, d.ptr, 0, 4, 64, e.ptr, None, None, ws.ptr, 1 << 12, None) == VQ_EINVAL
     assert L.vq_mxfp4_qdq(a.ptr, 0, 4, 48, b.ptr, ws.ptr, 256, None) == VQ_EINVAL     # cols % 32
     assert L.vq_mxfp4_qdq(a.ptr, 0, 4, 64, b.ptr, ws.ptr, 16, None) == VQ_EWORKSPACE
+    assert L.vq_mxfp4_qdq_bf16(a.ptr, 0, 4, 48, b.ptr, ws.ptr, 256, None) == VQ_EINVAL     # cols % 32
+    assert L.vq_mxfp4_qdq_bf16(a.ptr, 3, 4, 64, b.ptr, ws.ptr, 256, None) == VQ_EINVAL     # dtype
+    assert L.vq_mxfp4_qdq_bf16(a.ptr, 0, 4, 64, None, ws.ptr, 256, None) == VQ_EINVAL      # out
+    assert L.vq_mxfp4_qdq_bf16(a.ptr, 0, 4, 64, b.ptr, ws.ptr, 16, None) == VQ_EWORKSPACE
     assert L.vq_read_status(None, None, None) == VQ_EWORKSPACE
 
 

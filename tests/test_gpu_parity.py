@@ -725,7 +725,8 @@ def test_gemv_pack_layout(fmt, shape):
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_mxfp4_bit_exact(dtype):
     """Aligned inputs take the 4-elements-per-lane kernel, an input one element
-    off its alignment the one-element-per-lane kernel; both bit-exact."""
+    off its alignment the one-element-per-lane kernel; both bit-exact, with fp32
+    and with bf16 output."""
     say("mxfp4", dtype)
     W = synthetic.student_t_rows_f32(64, 1024, seed=8)
     W[3, :32] = 0.0
@@ -753,6 +754,19 @@ def test_mxfp4_bit_exact(dtype):
     Wu.copy_(Wd)
     got = vq.mxfp4_qdq(Wu).cpu().numpy()
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # bf16 output: the upper halves of the oracle's fp32 bits (exact, its lower
+    # halves are zero); an output one element off its 8-byte alignment takes
+    # the one-element-per-lane kernel
+    want = (ref.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.all((ref.view(np.uint32) & 0xFFFF) == 0)
+    ob = torch.empty(W.shape, dtype=torch.bfloat16, device=DEV)
+    got = vq.mxfp4_qdq(Wd, out=ob).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    obuf = torch.zeros(ob.numel() + 4, dtype=torch.bfloat16, device=DEV)
+    ou = obuf[1:1 + ob.numel()].view(ob.shape)
+    got = vq.mxfp4_qdq(Wu, out=ou).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    assert float(obuf[0]) == 0.0 and float(obuf[-3:].abs().sum()) == 0.0   # nothing written outside
 
 
 # ------------------------------------------------------------------ random sweep

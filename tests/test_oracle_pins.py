@@ -469,6 +469,32 @@ def test_mxfp4_values_round_trip_and_rounding():
     assert np.all(oracle.mxfp4_qdq(np.zeros((2, 64), np.float32)) == 0)
 
 
+def test_mxfp4_results_are_exact_in_bf16():
+    """Every MXFP4 result (a power-of-two block scale times an E2M1 value) has at
+    most two significant bits and is at least 2^-128 in magnitude, so its fp32
+    bits end in 16 zero bits: bf16 (the upper half) holds it exactly. Blocks with
+    amax across the whole finite fp32 range, subnormal and near-overflow ones
+    included."""
+    rng = np.random.default_rng(12)
+    rows = []
+    for e in list(range(-149, 128, 3)) + [127, -126, -127, -128, -133, -140]:
+        blk = (rng.standard_normal(32) * 2.0 ** rng.uniform(-24, 0, 32)).astype(np.float64)
+        blk[0] = np.sign(blk[0]) * 1.9375
+        blk = (blk * 2.0 ** e).astype(np.float32)
+        rows.append(np.nan_to_num(blk, posinf=3.4e38, neginf=-3.4e38))
+    W = np.stack(rows).astype(np.float32)
+    W[-1, :] = np.float32(3.4028235e38) * np.sign(rng.standard_normal(32)).astype(np.float32)   # largest finite
+    out = oracle.mxfp4_qdq(W)
+    bits = out.view(np.uint32)
+    assert np.all((bits & 0xFFFF) == 0)
+    nz = out[out != 0]
+    assert nz.size > 0 and np.abs(nz).min() >= 2.0 ** -128
+    assert np.isfinite(out).all() and np.abs(out).max() <= 1.5 * 2.0 ** 127
+    # the round trip through bf16 words is the identity
+    back = (bits >> 16).astype(np.uint32) << 16
+    assert np.array_equal(back.view(np.float32), out)
+
+
 def test_mxfp4_bits_per_weight_match_pages():
     # 4-bit elements + one 8-bit scale per 32 = 4.25 bits/weight: the K3 release
     # format row of the §1 table and the 190 MB lab fetch of §3.3
