@@ -72,65 +72,90 @@ int64_t gemv_packed_bytes(int format, int64_t rows, int64_t cols) {
 }
 
 // ------------------------------------------------------------------ repack
-// One workgroup (256 threads) per tile (expert slot, block of 16 slices, group
-// of 64 rows): the tile's 64 x 48 record bytes are read row by row (4 threads
-// per row, 12 bytes each: three dword loads when the row segment is 4-byte
-// aligned) into LDS, then written as the 4 x 64 rotated 12-byte chunks of the
-// packed layout, one chunk per thread (contiguous across a wave). Pad rows and
-// slices are 0. Output slot i holds expert list[i] (list = NULL: expert i);
-// slots at or past *count (when given) are skipped.
+// One workgroup (256 threads) per tile (expert slot, run of PACK_SB = 4
+// consecutive blocks of 16 slices, group of 64 rows). Thread (row r, block q)
+// reads the 48 record bytes of block q in row r (three 16-byte loads when the
+// records are 16-byte aligned, else dword or byte loads), so the 4 threads of
+// a row read its 192 contiguous bytes of the run (three whole 64-byte lines for
+// rows of a multiple of 64 slices; one block per tile left most lines partly
+// read). The tile goes through LDS and out as the packed layout's rotated
+// 12-byte chunks, 4 x 64 per block, one chunk per thread and block (contiguous
+// across a wave). Pad rows and slices are 0. Output slot i holds expert list[i]
+// (list = NULL: expert i); slots at or past *count (when given) are skipped.
+constexpr int PACK_SB = 4;
+
 __global__ __launch_bounds__(256) void k_gemv_pack(const uint8_t* idx, int64_t expert_stride, int64_t rows,
                                                    int64_t V, int64_t n_slots, const int32_t* list,
                                                    const int32_t* count, uint8_t* out, int64_t packed_stride) {
-  constexpr int NC = GJ / 4, RB = GJ * 3;  // 4 chunks per row, 48 record bytes per row
-  __shared__ uint32_t tile[GROUP][RB / 4 + 1];
+  constexpr int NC = GJ / 4, RB = GJ * 3;  // 4 chunks per row, 48 record bytes per row and block
+  __shared__ uint32_t tile[PACK_SB][GROUP][RB / 4 + 1];
   const int64_t ng = (rows + GROUP - 1) / GROUP, nblk = (V + GJ - 1) / GJ;
-  const int64_t ntiles = n_slots * nblk * ng;
+  const int64_t nsb = (nblk + PACK_SB - 1) / PACK_SB;
+  const int64_t ntiles = n_slots * nsb * ng;
   const int64_t used = count ? (int64_t)*count : n_slots;
   const int tid = threadIdx.x;
-  const int r = tid >> 2, part = tid & 3;     // load: row of the group, 12-byte part of its 48 bytes
+  const int r = tid >> 2, q = tid & 3;        // load: row of the group, block of the run
   const int c = tid >> 6, lane = tid & 63;    // store: chunk c of row `lane`
+  const bool quad_ok = (V & 15) == 0 && ((uintptr_t)idx & 15) == 0 && (expert_stride & 15) == 0;
   const bool dword_ok = ((V * 3) & 3) == 0 && ((uintptr_t)idx & 3) == 0 && (expert_stride & 3) == 0;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int64_t i = t / (nblk * ng), rem = t % (nblk * ng);
+    const int64_t i = t / (nsb * ng), rem = t % (nsb * ng);
     if (i >= used) break;  // tiles are in slot order
     const int64_t e = list ? (int64_t)list[i] : i;
-    const int64_t b = rem / ng, g = rem % ng;
+    const int64_t sb = rem / ng, g = rem % ng;
     const int64_t row = g * GROUP + r;
-    const int64_t j0 = b * GJ;
-    uint32_t w[3] = {0u, 0u, 0u};
-    if (row < rows) {
-      const uint8_t* src = idx + e * expert_stride + (row * V + j0) * 3 + part * 12;
-      const int64_t nbytes = ((V - j0) < GJ ? (V - j0) : GJ) * 3 - part * 12;  // valid bytes of this part
-      if (dword_ok && nbytes >= 12) {
+    const int64_t b = sb * PACK_SB + q;
+    uint32_t w[12];
+#pragma unroll
+    for (int k = 0; k < 12; ++k) w[k] = 0u;
+    if (row < rows && b < nblk) {
+      const int64_t j0 = b * GJ;
+      const uint8_t* src = idx + e * expert_stride + (row * V + j0) * 3;
+      const int64_t nbytes = ((V - j0) < GJ ? (V - j0) : GJ) * 3;  // valid bytes of this block
+      if (quad_ok && nbytes == RB) {
+        const uint4* s16 = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          const uint4 v = s16[k];
+          w[4 * k] = v.x;
+          w[4 * k + 1] = v.y;
+          w[4 * k + 2] = v.z;
+          w[4 * k + 3] = v.w;
+        }
+      } else if (dword_ok) {
         const uint32_t* s4 = reinterpret_cast<const uint32_t*>(src);
-        w[0] = s4[0];
-        w[1] = s4[1];
-        w[2] = s4[2];
-      } else {
 #pragma unroll
         for (int k = 0; k < 12; ++k)
+          if (4 * k < nbytes) w[k] = s4[k];  // nbytes is a multiple of 12
+      } else {
+#pragma unroll
+        for (int k = 0; k < RB; ++k)
           if (k < nbytes) w[k >> 2] |= (uint32_t)src[k] << (8 * (k & 3));
       }
     }
 #pragma unroll
-    for (int k = 0; k < 3; ++k) tile[r][part * 3 + k] = w[k];
+    for (int k = 0; k < 12; ++k) tile[q][r][k] = w[k];
     __syncthreads();
-    const uint8_t* tb = reinterpret_cast<const uint8_t*>(&tile[lane][0]);
-    uint32_t o[3] = {0u, 0u, 0u};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int sl = (4 * c + q + lane) & (GJ - 1);
+    for (int qb = 0; qb < PACK_SB; ++qb) {
+      const int64_t bb = sb * PACK_SB + qb;
+      if (bb >= nblk) break;  // uniform across the workgroup
+      const uint8_t* tb = reinterpret_cast<const uint8_t*>(&tile[qb][lane][0]);
+      uint32_t o[3] = {0u, 0u, 0u};
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const int ob = 3 * q + k;
-        o[ob >> 2] |= (uint32_t)tb[3 * sl + k] << (8 * (ob & 3));
+      for (int m = 0; m < 4; ++m) {
+        const int sl = (4 * c + m + lane) & (GJ - 1);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          const int ob = 3 * m + k;
+          o[ob >> 2] |= (uint32_t)tb[3 * sl + k] << (8 * (ob & 3));
+        }
       }
-    }
-    uint32_t* dst =
-        reinterpret_cast<uint32_t*>(out + i * packed_stride + ((b * ng + g) * NC + c) * (GROUP * 12) + lane * 12);
+      uint32_t* dst =
+          reinterpret_cast<uint32_t*>(out + i * packed_stride + ((bb * ng + g) * NC + c) * (GROUP * 12) + lane * 12);
 #pragma unroll
-    for (int k = 0; k < 3; ++k) dst[k] = o[k];
+      for (int k = 0; k < 3; ++k) dst[k] = o[k];
+    }
     __syncthreads();  // the tile buffer is refilled next
   }
 }
@@ -678,7 +703,8 @@ hipError_t launch_gemv_pack(int format, const uint8_t* idx, int64_t expert_strid
                             int64_t n_slots, const int32_t* list, const int32_t* count, uint8_t* out, int ncu,
                             hipStream_t s) {
   const int64_t V = cols / DIM;
-  const int64_t ntiles = ((V + GJ - 1) / GJ) * ((rows + GROUP - 1) / GROUP) * n_slots;
+  const int64_t nsb = ((V + GJ - 1) / GJ + PACK_SB - 1) / PACK_SB;
+  const int64_t ntiles = nsb * ((rows + GROUP - 1) / GROUP) * n_slots;
   if (ntiles == 0) return hipSuccess;
   int64_t g = ntiles;
   if (g > (int64_t)ncu * 32) g = (int64_t)ncu * 32;
