@@ -697,11 +697,12 @@ def test_gemv_bad_route_flagged(cfg1):
 
 
 @pytest.mark.parametrize("fmt", ["vq3r", "vq4p"])
-@pytest.mark.parametrize("shape", [(1, 8), (64, 224), (70, 456), (128, 7168)])
+@pytest.mark.parametrize("shape", [(1, 8), (64, 224), (70, 456), (128, 7168), (65, 640), (3, 1152)])
 def test_gemv_pack_layout(fmt, shape):
     """The packed layout is a pure permutation of the stored records: blocks of 16
     slices x 64-row groups, 4 records (12 bytes) per lane chunk, each row's slices
-    rotated by its lane, zero padding."""
+    rotated by its lane, zero padding. The shapes take the repack's byte, dword
+    and 16-byte load paths, with full and partial runs of 4 blocks."""
     say("gemv pack layout", fmt, shape)
     rows, cols = shape
     V = cols // 8
